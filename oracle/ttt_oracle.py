@@ -1,0 +1,319 @@
+"""Plain, slow fp64 CPU oracle of the TTT-with-KV-binding forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run anything here.  The
+product path (the HIP library and its Python binding) never does, and this
+module shares no code with it.
+
+What it computes (sources are the five web pages about "Test-Time Training with
+KV Binding Is Secretly Linear Attention"; readings are marked READING):
+
+* The layer keeps a fixed-size fast-weight matrix per sequence, takes one
+  gradient step on it for every entry of the sequence, and starts every new
+  sequence from a reset state (wpnews.pro "Test Time Training" commentary).
+  READING: the reset state is zero.
+* The step binds the key to the value.  READING: the binding loss is the
+  negative dot product  l_t(S) = -<S phi(k_t), v_t>,  whose gradient
+  -v_t phi(k_t)^T does not depend on S.  A descent step therefore adds the
+  outer product eta_t v_t phi(k_t)^T, i.e. the outer-product accumulation the
+  kualia.ai blog ("The Linear Attention Equivalence") identifies with the
+  numerator of linear attention (phi(Q) phi(K)^T) V.  READING: no denominator.
+* Optional SGD momentum and a per-token learning rate are the inner-loop
+  options that Table 2 of the thelatestinai.com page removes one by one
+  (Variant 3 keeps both, Variant 4 drops the per-token lr, Variant 5 drops
+  momentum).  READING: heavy-ball momentum with the step inside the buffer,
+  M_t = beta M_{t-1} - eta_t G_t,  S_t = S_{t-1} + M_t, no dampening, no
+  Nesterov; per-token lr eta_t = softplus(a_t).
+* Variant 2 of Table 2 keeps a two-layer MLP fast weight and updates only its
+  last layer: the first layer is a frozen feature map.  READING: SwiGLU
+  features phi(x) = silu(W1 x) * (W3 x) with silu(u) = u / (1 + e^-u).
+* READING: the readout of token t uses the state after token t's own update,
+  o_t = S_t phi(q_t).  In the bidirectional (ViT) mode every token updates the
+  state first and every query reads the final state.
+
+``forward`` is the definition, a token-by-token loop.  ``forward_closed_form``
+and ``forward_chunked`` are the parallel forms the blog says the recurrence can
+be rewritten into ("The Cracks in the Memorization Hypothesis": closed form;
+"The Linear Attention Equivalence": sequential or parallel); the tests use them
+only to check that those forms agree with the loop.
+
+Every function here is pinned by a test in ``tests/test_oracle.py``.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "softplus", "silu", "swiglu_features", "features", "learning_rates",
+    "binding_loss", "binding_loss_grad", "forward", "forward_closed_form",
+    "forward_chunked", "rel_err",
+]
+
+
+# ----------------------------------------------------------------------------
+# elementary functions
+# ----------------------------------------------------------------------------
+
+def softplus(a):
+    """softplus(a) = ln(1 + e^a), evaluated as max(a,0) + log1p(e^-|a|).
+
+    Per-token learnable learning rate of Variant 3 (thelatestinai.com,
+    Table 2).  READING: eta_t = softplus(a_t) with a_t given per token.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    return np.maximum(a, 0.0) + np.log1p(np.exp(-np.abs(a)))
+
+
+def silu(u):
+    """silu(u) = u * sigmoid(u) = u / (1 + e^-u)  (gate of the SwiGLU MLP)."""
+    u = np.asarray(u, dtype=np.float64)
+    return u / (1.0 + np.exp(-u))
+
+
+def swiglu_features(x, w1, w3):
+    """phi(x) = silu(W1 x) * (W3 x) for rows x of ``x``.
+
+    x: [..., d_k];  w1, w3: [d_phi, d_k] (out x in).  Returns [..., d_phi].
+    Frozen first layer of Variant 2's two-layer MLP fast weight
+    (thelatestinai.com, Table 2, Variant 2 vs Variant 3).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return silu(x @ np.asarray(w1, np.float64).T) * (x @ np.asarray(w3, np.float64).T)
+
+
+def features(x, phi: str, w1=None, w3=None):
+    """Kernel feature map phi applied to the last axis of x ([N, T, d_k])."""
+    if phi == "identity":
+        return np.asarray(x, dtype=np.float64)
+    if phi == "swiglu":
+        # w1, w3 are per sequence here: [N, d_phi, d_k]
+        x = np.asarray(x, dtype=np.float64)
+        u = np.einsum("ntd,nfd->ntf", x, w1)
+        g = np.einsum("ntd,nfd->ntf", x, w3)
+        return silu(u) * g
+    raise ValueError(f"unknown feature map {phi!r}")
+
+
+def learning_rates(eta_mode: str, T: int, N: int, eta=None, eta_scalar: float = 1.0):
+    """Per-token step sizes, shape [N, T], fp64.
+
+    scalar: eta_scalar for every token; per_token: eta given; softplus:
+    eta = softplus(a) with the logits a given (fp32 values upcast exactly).
+    """
+    if eta_mode == "scalar":
+        return np.full((N, T), float(eta_scalar), dtype=np.float64)
+    e = np.asarray(eta, dtype=np.float64).reshape(N, T)
+    if eta_mode == "per_token":
+        return e.copy()
+    if eta_mode == "softplus":
+        return softplus(e)
+    raise ValueError(f"unknown eta mode {eta_mode!r}")
+
+
+# ----------------------------------------------------------------------------
+# binding loss and its explicit gradient
+# ----------------------------------------------------------------------------
+
+def binding_loss(S, phik, v):
+    """l(S) = -<S phi(k), v>: the dot-product key->value binding loss.
+
+    S: [..., d_v, d_phi], phik: [..., d_phi], v: [..., d_v].  READING of
+    "a training step to bind them together" (kualia.ai blog, "The Cracks in
+    the Memorization Hypothesis").
+    """
+    return -np.einsum("...v,...vf,...f->...", v, S, phik)
+
+
+def binding_loss_grad(S, phik, v):
+    """Gradient of ``binding_loss`` with respect to S: -v phi(k)^T.
+
+    The loss is linear in S, so the gradient is the same at every S (the shape
+    of S is only used to broadcast).
+    """
+    g = -np.einsum("...v,...f->...vf", v, phik)
+    return np.broadcast_to(g, np.shape(S)).copy()
+
+
+# ----------------------------------------------------------------------------
+# the definition: token-by-token recurrence
+# ----------------------------------------------------------------------------
+
+def _flatten(x, d):
+    x = np.asarray(x, dtype=np.float64)
+    return x.reshape(-1, x.shape[-2], d)
+
+
+def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
+            beta: float = 0.0, causal: bool = True, phi: str = "identity",
+            w1=None, w3=None, ascent: bool = False, inner_steps: int = 1,
+            return_state: bool = False):
+    """Recurrent TTT forward, fp64, one gradient step per token.
+
+    q, k: [B, H, T, d_k]; v: [B, H, T, d_v]; eta / a: [B, H, T] (per_token /
+    softplus modes); w1, w3: [H, d_phi, d_k] for the SwiGLU feature map.
+    Returns o: [B, H, T, d_v] (and the final (S, M) if ``return_state``).
+
+    For every sequence (b, h) independently:
+      S = 0, M = 0                                   (reset per sequence)
+      for t = 0 .. T-1:
+        G   = grad_S l_t(S)  = -v_t phi(k_t)^T        (explicit gradient)
+        M   = beta M - eta_t G      (ascent: + eta_t G)
+        S   = S + M
+        o_t = S phi(q_t)                              (causal readout)
+      bidirectional: o_t = S_T phi(q_t) for all t.
+    ``inner_steps`` > 1 repeats the (momentum-free) step on the same token,
+    the "more inner-loop iterations" manipulation of Figure 1; it requires
+    beta == 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, d_k = q.shape
+    d_v = np.shape(v)[-1]
+    N = B * H
+    qf = _flatten(q, d_k)
+    kf = _flatten(k, d_k)
+    vf = _flatten(v, d_v)
+    if phi == "swiglu":
+        w1n = np.broadcast_to(np.asarray(w1, np.float64)[None], (B,) + np.shape(w1)).reshape(N, -1, d_k)
+        w3n = np.broadcast_to(np.asarray(w3, np.float64)[None], (B,) + np.shape(w3)).reshape(N, -1, d_k)
+        pq = features(qf, phi, w1n, w3n)
+        pk = features(kf, phi, w1n, w3n)
+    else:
+        pq = features(qf, phi)
+        pk = features(kf, phi)
+    d_phi = pk.shape[-1]
+    lr = learning_rates(eta_mode, T, N, eta, eta_scalar)
+    if inner_steps != 1 and beta != 0.0:
+        raise ValueError("inner_steps > 1 is defined here for beta == 0 only")
+    sign = 1.0 if ascent else -1.0
+
+    S = np.zeros((N, d_v, d_phi))
+    M = np.zeros((N, d_v, d_phi))
+    o = np.zeros((N, T, d_v))
+    for t in range(T):
+        for _ in range(inner_steps):
+            G = binding_loss_grad(S, pk[:, t], vf[:, t])
+            M = beta * M + sign * lr[:, t, None, None] * G
+            S = S + M
+        if causal:
+            o[:, t] = np.einsum("nvf,nf->nv", S, pq[:, t])
+    if not causal:
+        o = np.einsum("nvf,ntf->ntv", S, pq)
+    o = o.reshape(B, H, T, d_v)
+    if return_state:
+        return o, S.reshape(B, H, d_v, d_phi), M.reshape(B, H, d_v, d_phi)
+    return o
+
+
+# ----------------------------------------------------------------------------
+# parallel forms (used by tests to check the equivalence the pages state)
+# ----------------------------------------------------------------------------
+
+def _momentum_weights(beta: float, n: int):
+    """c_r = sum_{s=0..r} beta^s, r = 0..n-1 (weight of a token r steps back)."""
+    c = np.empty(n)
+    acc = 0.0
+    p = 1.0
+    for r in range(n):
+        acc += p
+        c[r] = acc
+        p *= beta
+    return c
+
+
+def forward_closed_form(q, k, v, *, eta_mode="scalar", eta=None, eta_scalar=1.0,
+                        beta=0.0, causal=True, phi="identity", w1=None, w3=None):
+    """Closed form: O = (Gamma o (Phi_Q Phi_K^T)) diag(eta) V.
+
+    Unrolling the momentum recurrence gives
+      S_t = sum_{s<=t} eta_s c_{t-s} v_s phi(k_s)^T,  c_r = sum_{u=0..r} beta^u,
+    so the causal output is a masked, reweighted product of the feature
+    matrices (Gamma_ts = c_{t-s} for s <= t); bidirectionally every query reads
+    S_{T-1}, i.e. Gamma_ts = c_{T-1-s}.  With beta = 0 and eta = 1 this is the
+    plain causal linear attention of the blog's "(phi(Q) phi(K)^T) V".
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, d_k = q.shape
+    d_v = np.shape(v)[-1]
+    N = B * H
+    qf, kf, vf = _flatten(q, d_k), _flatten(k, d_k), _flatten(v, d_v)
+    if phi == "swiglu":
+        w1n = np.broadcast_to(np.asarray(w1, np.float64)[None], (B,) + np.shape(w1)).reshape(N, -1, d_k)
+        w3n = np.broadcast_to(np.asarray(w3, np.float64)[None], (B,) + np.shape(w3)).reshape(N, -1, d_k)
+        pq, pk = features(qf, phi, w1n, w3n), features(kf, phi, w1n, w3n)
+    else:
+        pq, pk = features(qf, phi), features(kf, phi)
+    lr = learning_rates(eta_mode, T, N, eta, eta_scalar)
+    c = _momentum_weights(beta, T)
+    t_idx = np.arange(T)[:, None]
+    s_idx = np.arange(T)[None, :]
+    if causal:
+        gamma = np.where(s_idx <= t_idx, c[np.clip(t_idx - s_idx, 0, T - 1)], 0.0)
+    else:
+        gamma = np.broadcast_to(c[T - 1 - s_idx], (T, T))
+    scores = np.einsum("ntf,nsf->nts", pq, pk) * gamma[None] * lr[:, None, :]
+    o = np.einsum("nts,nsv->ntv", scores, vf)
+    return o.reshape(B, H, T, d_v)
+
+
+def forward_chunked(q, k, v, *, chunk: int, eta_mode="scalar", eta=None, eta_scalar=1.0,
+                    beta=0.0, causal=True, phi="identity", w1=None, w3=None):
+    """Chunked form: dense blocks inside a chunk, (S, M) carried between chunks.
+
+    For a chunk of n tokens entered with state (S, M) and local indices i, j:
+      o_i = S phi(q_i) + g_i M phi(q_i) + sum_{j<=i} c_{i-j} eta_j (phi(q_i).phi(k_j)) v_j
+      S'  = S + g_{n-1} M + sum_j eta_j c_{n-1-j} v_j phi(k_j)^T
+      M'  = beta^n M + sum_j eta_j beta^{n-1-j} v_j phi(k_j)^T
+    with c_r = sum_{u=0..r} beta^u and g_i = sum_{u=1..i+1} beta^u.
+    Bidirectional: run the state update over all chunks, then o_t = S phi(q_t).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, d_k = q.shape
+    d_v = np.shape(v)[-1]
+    N = B * H
+    qf, kf, vf = _flatten(q, d_k), _flatten(k, d_k), _flatten(v, d_v)
+    if phi == "swiglu":
+        w1n = np.broadcast_to(np.asarray(w1, np.float64)[None], (B,) + np.shape(w1)).reshape(N, -1, d_k)
+        w3n = np.broadcast_to(np.asarray(w3, np.float64)[None], (B,) + np.shape(w3)).reshape(N, -1, d_k)
+        pq, pk = features(qf, phi, w1n, w3n), features(kf, phi, w1n, w3n)
+    else:
+        pq, pk = features(qf, phi), features(kf, phi)
+    d_phi = pk.shape[-1]
+    lr = learning_rates(eta_mode, T, N, eta, eta_scalar)
+    S = np.zeros((N, d_v, d_phi))
+    M = np.zeros((N, d_v, d_phi))
+    o = np.zeros((N, T, d_v))
+    for t0 in range(0, T, chunk):
+        n = min(chunk, T - t0)
+        c = _momentum_weights(beta, n)
+        g = beta * c                                   # g_i = beta * c_i
+        bp = beta ** np.arange(n)                      # beta^r
+        PQ, PK, V, E = pq[:, t0:t0 + n], pk[:, t0:t0 + n], vf[:, t0:t0 + n], lr[:, t0:t0 + n]
+        if causal:
+            ii = np.arange(n)[:, None]
+            jj = np.arange(n)[None, :]
+            gam = np.where(jj <= ii, c[np.clip(ii - jj, 0, n - 1)], 0.0)
+            A = np.einsum("nif,njf->nij", PQ, PK) * gam[None] * E[:, None, :]
+            o[:, t0:t0 + n] = (np.einsum("nvf,nif->niv", S, PQ)
+                               + g[None, :, None] * np.einsum("nvf,nif->niv", M, PQ)
+                               + np.einsum("nij,njv->niv", A, V))
+        wS = E * c[::-1][None, :]                      # eta_j c_{n-1-j}
+        wM = E * bp[::-1][None, :]                     # eta_j beta^{n-1-j}
+        S = S + g[n - 1] * M + np.einsum("nj,njv,njf->nvf", wS, V, PK)
+        M = (beta ** n) * M + np.einsum("nj,njv,njf->nvf", wM, V, PK)
+    if not causal:
+        o = np.einsum("nvf,ntf->ntv", S, pq)
+    return o.reshape(B, H, T, d_v)
+
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / max |ref| over every element (0/0 -> 0)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = float(np.max(np.abs(ref))) if ref.size else 0.0
+    num = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else math.inf
+    return num / den
