@@ -1,0 +1,161 @@
+/*
+ * ttt_la.h - C ABI of libttt_la.so: the forward pass of a test-time-training
+ * (TTT) layer with key-value binding, computed as learned linear attention on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * What the layer computes.  The five web pages about "Test-Time Training with
+ * KV Binding Is Secretly Linear Attention" describe the layer as a fixed-size
+ * fast-weight matrix that takes one gradient step per sequence entry and is
+ * reset for every new sequence (wpnews.pro, "Test Time Training"), whose
+ * update is the outer-product accumulation of linear attention, computable
+ * either as a recurrence or in parallel (kualia.ai blog, "The Linear Attention
+ * Equivalence"), with the inner-loop options removed one by one in the
+ * ablation of the thelatestinai.com page (Table 2: Variant 2 SwiGLU feature
+ * map; Variant 3 per-token learning rate and momentum; Variant 4 no per-token
+ * lr; Variant 5 no momentum).  With the readings adopted here (dot-product
+ * binding loss, zero initial state, readout after the update, heavy-ball
+ * momentum with the step inside the buffer), for every sequence (b, h):
+ *
+ *     M_t = beta * M_{t-1} + eta_t * v_t phi(k_t)^T        (M_{-1} = 0)
+ *     S_t = S_{t-1} + M_t                                   (S_{-1} = 0)
+ *     o_t = S_t phi(q_t)              causal mode
+ *     o_t = S_{T-1} phi(q_t)          bidirectional mode
+ *
+ * with S, M in R^{d_v x d_phi} kept in fp32 and phi the identity
+ * (d_phi = d_k) or the frozen SwiGLU map phi(x) = silu(W1 x) * (W3 x),
+ * silu(u) = u / (1 + e^-u).  The library evaluates this in its chunked
+ * parallel form (dense causal blocks inside a chunk, fp32 state carried from
+ * chunk to chunk); the result equals the recurrence up to rounding.  Gradient
+ * ascent in the inner loop (Table 1 of the same page) is eta -> -eta.
+ *
+ * Conventions for every entry point:
+ *   - Device buffers are plain device pointers owned by the caller.  The
+ *     library never frees them and keeps none of them after a call returns,
+ *     except W1/W3, which are borrowed at create and must outlive the handle.
+ *   - Every call returns a ttt_la_status; no call aborts, throws or prints.
+ *   - Arguments are validated on the host before any HIP call.
+ *   - ttt_la_forward allocates nothing and does not synchronise: it enqueues
+ *     kernels on the given stream and returns.  Device-side faults surface at
+ *     the caller's next synchronisation.  One handle serves one stream at a
+ *     time (its workspace is reused by every call).
+ */
+#ifndef TTT_LA_H
+#define TTT_LA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ttt_la_s* ttt_la_t; /* opaque handle */
+
+typedef enum {
+    TTT_LA_OK = 0,
+    TTT_LA_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size, bad mode bit, beta or eta out of range, overlap */
+    TTT_LA_ERR_UNSUPPORTED = -2, /* well-formed request outside the supported shapes */
+    TTT_LA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+    TTT_LA_ERR_OOM = -4          /* workspace allocation failed */
+} ttt_la_status;
+
+typedef enum { TTT_LA_F32 = 0, TTT_LA_BF16 = 1 } ttt_la_dtype; /* q, k, v, o, W1, W3 */
+
+typedef enum {
+    TTT_LA_PHI_IDENTITY = 0, /* phi(x) = x, d_phi = d_k (Variants 3-5) */
+    TTT_LA_PHI_SWIGLU = 1    /* phi(x) = silu(W1 x) * (W3 x) (Variant 2) */
+} ttt_la_phi;
+
+/* Mode bits for ttt_la_forward.  At most one of the ETA bits may be set. */
+enum {
+    TTT_LA_CAUSAL = 0u,              /* o_t = S_t phi(q_t) */
+    TTT_LA_BIDIRECTIONAL = 1u << 0,  /* o_t = S_{T-1} phi(q_t): all tokens update before any readout */
+    TTT_LA_ETA_SCALAR = 0u,          /* eta_t = eta_scalar; the eta pointer must be NULL */
+    TTT_LA_ETA_PER_TOKEN = 1u << 1,  /* eta_t = eta[b,h,t] */
+    TTT_LA_ETA_SOFTPLUS = 1u << 2    /* eta_t = softplus(eta[b,h,t]) = ln(1 + e^a) (Table 2, Variant 3) */
+};
+
+typedef struct {
+    int32_t B, H, T;           /* batch, heads, sequence length: B, H, T >= 1 */
+    int32_t d_k, d_v, d_phi;   /* key/query width, value width, feature width */
+    int32_t dtype;             /* ttt_la_dtype of q, k, v, o (and W1, W3) */
+    int32_t phi;               /* ttt_la_phi */
+    int32_t chunk;             /* tile length along T: 0 = auto, else 64 or 128 (bf16); it changes
+                                  the result only by rounding */
+    int32_t segments;          /* sequence segments scanned in parallel: 0 = auto, else >= 1 (bf16 causal);
+                                  changes the result only by rounding */
+    const void* w1;            /* SWIGLU: device [H, d_phi, d_k] (out x in) in dtype; else NULL */
+    const void* w3;            /* SWIGLU: device [H, d_phi, d_k] in dtype; else NULL */
+} ttt_la_desc;
+
+/* Supported shapes (anything else well-formed returns TTT_LA_ERR_UNSUPPORTED):
+ *   d_k, d_v in {64, 128}
+ *   identity: d_phi == d_k;  SwiGLU: d_phi in {128, 256, 384, 512}
+ *   B * H * T * max(d_k, d_v, d_phi) < 2^31
+ *
+ * Layout: q, k are [B, H, T, d_k]; v and o are [B, H, T, d_v]; eta is
+ * [B, H, T] fp32; all C-contiguous.  Pointers to q, k, v, o, W1, W3 must be
+ * 16-byte aligned, eta 4-byte aligned. */
+
+/* Creates a handle for one layer shape.  Validates *desc, picks the kernel
+ * plan for the shape and allocates the workspace (hipMalloc on the current
+ * device), once.  On any error *out is set to NULL. */
+int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out);
+
+/* Enqueues one forward pass on hip_stream (a hipStream_t; NULL = the null
+ * stream).
+ *   q, k, v  device inputs as above.  q may alias k ("Replace Q with K",
+ *            Table 1): inputs are only read.
+ *   eta      NULL for TTT_LA_ETA_SCALAR, else device [B, H, T] fp32.
+ *   eta_scalar  the step size when no ETA bit is set; must be finite.
+ *   beta     momentum in [0, 1); 0 turns momentum off (Variant 5).
+ *   mode     TTT_LA_* bits above.
+ *   o        device output [B, H, T, d_v] in dtype; must not overlap any input.
+ * Returns TTT_LA_ERR_INVALID_ARG without any HIP call for bad arguments and
+ * TTT_LA_ERR_HIP if a launch fails. */
+int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
+                   float eta_scalar, float beta, uint32_t mode, void* o, void* hip_stream);
+
+/* Releases the workspace and the handle.  NULL-safe. */
+void ttt_la_destroy(ttt_la_t h);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* ttt_la_status_string(int status);
+
+/* Host-only validation of a descriptor and of the arguments of one forward
+ * call, exactly as ttt_la_create / ttt_la_forward perform it, without any HIP
+ * call (pointers are only compared, never dereferenced).  Pass q == NULL to
+ * check the descriptor alone.  Returns the status create/forward would return
+ * for these arguments before touching the device. */
+int ttt_la_check(const ttt_la_desc* desc, const void* q, const void* k, const void* v,
+                 const float* eta, float eta_scalar, float beta, uint32_t mode, const void* o);
+
+/* Kernel plan chosen at create, for tests and measurement. */
+typedef struct {
+    int32_t path;          /* 0 = generic fp32-accumulate kernels, 1 = bf16 MFMA chunk kernels */
+    int32_t chunk;         /* tokens per chunk */
+    int32_t segments;      /* sequence segments per (b, h) scanned in parallel (1 = none) */
+    int32_t seg_len;       /* tokens per segment (last one may be shorter) */
+    int32_t dv_split;      /* value-column slices per (b, h) */
+    int32_t phi_split;     /* feature slices per (b, h) (partial outputs summed) */
+    int32_t grid_main;     /* workgroups of the output kernel */
+    int32_t n_kernels;     /* kernels enqueued by one causal forward */
+    size_t workspace_bytes;
+} ttt_la_plan;
+
+/* Fills *plan for handle h.  Host only. */
+int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan);
+
+/* Measurement hook.  When n_slots > 0, every following ttt_la_forward records
+ * a pair of HIP events (created here, not device memory) on its stream around
+ * the output kernel, cycling through n_slots pairs; ttt_la_kernel_times then
+ * returns the elapsed milliseconds of the last min(calls, n_slots) pairs
+ * (oldest first) after synchronising on them.  n_slots = 0 turns it off. */
+int ttt_la_enable_kernel_timing(ttt_la_t h, int32_t n_slots);
+int ttt_la_kernel_times(ttt_la_t h, float* ms, int32_t capacity, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTT_LA_H */

@@ -1,0 +1,174 @@
+"""The C ABI on the host: symbols, status codes, argument validation (no GPU).
+
+Every check here runs before the library makes any HIP call, so it works in a
+container without a GPU.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import ttt_weight_layers_amd as tla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt_la.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(tla.LIB_PATH),
+                                reason="libttt_la.so not built (run ttt_weight_layers_amd.build)")
+
+# fake, 16-byte aligned, non-overlapping "device" addresses: only compared
+Q, K, V, O, ETA, W1, W3 = (0x10000000 * (i + 1) for i in range(7))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_la_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = tla.load_library()
+    names = declared_functions()
+    assert set(names) == set(tla.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert tla.ttt_la_status_string(0) == "ok"
+    assert tla.ttt_la_status_string(-1) == "invalid argument"
+    assert tla.ttt_la_status_string(-2).startswith("unsupported")
+    assert tla.ttt_la_status_string(-3).startswith("HIP")
+    assert tla.ttt_la_status_string(-4).startswith("out of")
+    assert tla.ttt_la_status_string(12345) == "unknown status"
+
+
+def desc(**kw):
+    base = dict(B=2, H=3, T=100, d_k=128, d_v=128, d_phi=None, dtype="bf16", phi="identity", chunk=0,
+                segments=0)
+    base.update(kw)
+    return tla.make_desc(**base)
+
+
+def check(d=None, q=Q, k=K, v=V, eta=None, eta_scalar=0.5, beta=0.0, mode=0, o=O):
+    return tla.ttt_la_check(d or desc(), q, k, v, eta, eta_scalar, beta, mode, o)
+
+
+def test_valid_arguments_pass():
+    assert check() == tla.TTT_LA_OK
+    assert check(eta=ETA, mode=tla.TTT_LA_ETA_SOFTPLUS, beta=0.9) == tla.TTT_LA_OK
+    assert check(eta=ETA, mode=tla.TTT_LA_ETA_PER_TOKEN | tla.TTT_LA_BIDIRECTIONAL) == tla.TTT_LA_OK
+    assert check(d=desc(dtype="f32", d_k=64, d_v=64)) == tla.TTT_LA_OK
+
+
+def test_query_may_alias_key():
+    # thelatestinai.com Table 1 'Replace Q with K'
+    assert check(q=K) == tla.TTT_LA_OK
+
+
+@pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", 0), ("T", -5), ("d_k", 0),
+                                         ("d_v", -1), ("dtype", 7), ("phi", 3), ("chunk", -1),
+                                         ("segments", -2)])
+def test_bad_descriptor_fields(field, value):
+    d = desc()
+    setattr(d, field, value)
+    assert check(d=d, q=None) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(d_k=96, d_v=128), dict(d_k=128, d_v=32), dict(d_k=256, d_v=128),
+                                dict(chunk=32), dict(chunk=100)])
+def test_unsupported_shapes(kw):
+    assert check(d=desc(**kw), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+
+
+def test_identity_requires_dphi_equal_dk_and_no_weights():
+    assert check(d=desc(d_phi=64), q=None) == tla.TTT_LA_ERR_INVALID_ARG
+    d = desc()
+    d.w1 = W1
+    assert check(d=d, q=None) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_swiglu_descriptor():
+    assert check(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=W3), q=None) == tla.TTT_LA_OK
+    assert check(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=None), q=None) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check(d=desc(phi="swiglu", d_phi=200, w1=W1, w3=W3), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(phi="swiglu", d_phi=1024, w1=W1, w3=W3), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(phi="swiglu", d_phi=512, w1=W1 + 8, w3=W3), q=None) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_size_limit():
+    assert check(d=desc(B=1024, H=64, T=65536), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_null_and_misaligned_pointers(which):
+    if which != "q":             # q == NULL asks ttt_la_check for the descriptor alone
+        kw = {which: None}
+        assert check(**kw) == tla.TTT_LA_ERR_INVALID_ARG
+    kw = {which: {"q": Q, "k": K, "v": V, "o": O}[which] + 2}
+    assert check(**kw) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_mode_bits():
+    assert check(mode=1 << 5) == tla.TTT_LA_ERR_INVALID_ARG
+    both = tla.TTT_LA_ETA_PER_TOKEN | tla.TTT_LA_ETA_SOFTPLUS
+    assert check(eta=ETA, mode=both) == tla.TTT_LA_ERR_INVALID_ARG
+    # a per-token mode needs a pointer; the scalar mode forbids one
+    assert check(eta=None, mode=tla.TTT_LA_ETA_SOFTPLUS) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check(eta=ETA, mode=tla.TTT_LA_ETA_SCALAR) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check(eta=ETA + 2, mode=tla.TTT_LA_ETA_PER_TOKEN) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("beta", [-0.1, 1.0, 1.5, math.nan, math.inf])
+def test_beta_range(beta):
+    assert check(beta=beta) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("eta", [math.nan, math.inf, -math.inf])
+def test_non_finite_eta_scalar(eta):
+    assert check(eta_scalar=eta) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_negative_eta_is_gradient_ascent_and_allowed():
+    assert check(eta_scalar=-0.5) == tla.TTT_LA_OK
+
+
+def test_output_must_not_overlap_inputs():
+    n = 2 * 3 * 100 * 128 * 2                       # bytes of one bf16 tensor
+    assert check(o=Q) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check(o=K + n - 16) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check(o=V - n + 16) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check(o=V + n) == tla.TTT_LA_OK               # adjacent is fine
+    assert check(o=ETA, eta=ETA, mode=tla.TTT_LA_ETA_PER_TOKEN) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_create_rejects_bad_descriptor_before_device_work():
+    d = desc(T=0)
+    st, h = tla.ttt_la_create(d)
+    assert st == tla.TTT_LA_ERR_INVALID_ARG and not h.value
+    st, h = tla.ttt_la_create(desc(d_k=96))
+    assert st == tla.TTT_LA_ERR_UNSUPPORTED and not h.value
+
+
+def test_null_handle_calls():
+    tla.ttt_la_destroy(None)                      # NULL-safe
+    lib = tla.load_library()
+    assert lib.ttt_la_forward(None, Q, K, V, None, 1.0, 0.0, 0, O, None) == tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_get_plan(None, None) == tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_enable_kernel_timing(None, 4) == tla.TTT_LA_ERR_INVALID_ARG
+    n = ctypes.c_int32(0)
+    assert lib.ttt_la_kernel_times(None, None, 0, ctypes.byref(n)) == tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_create(None, None) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    from ttt_weight_layers_amd import _binding
+    saved = _binding._lib
+    _binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            _binding.load_library(str(tmp_path / "nope.so"))
+    finally:
+        _binding._lib = saved

@@ -1,0 +1,85 @@
+"""GPU parity: the HIP library against the fp64 oracle on seeded inputs.
+
+Bar (per element, over every compared output):
+    max |o_gpu - o_oracle| / max |o_oracle|  <=  1e-4 (fp32 inputs)
+                                              <=  2e-2 (bf16 inputs, fp32 state)
+Reduced shapes compare every output; full shapes run in the same launch
+configuration the benchmark times and compare a fixed subset of heads at full T.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ttt_workloads import WORKLOADS, head_subset, make_inputs
+from _gpu import TOL, make_layer, run_gpu, run_oracle, select_heads, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# reduced shapes: several chunks, a ragged tail, more than one head
+SMALL = {
+    "v5_f32_1x1x256_d64": dict(B=1, H=2, T=77),
+    "v4_momentum_4x8x2048_d128": dict(B=1, H=3, T=64 * 5 + 37),
+    "v3_softplus_8x16x4096_d128": dict(B=2, H=2, T=300),
+    "v2_swiglu_4x16x8192_d128_f512": dict(B=1, H=2, T=64 * 3 + 11),
+    "v5_long_1x16x65536_d128": dict(B=1, H=2, T=128 * 3 + 50),
+    "v3_long_1x16x65536_d128": dict(B=1, H=2, T=128 * 3 + 50),
+    "bidir_vit_256x6x196_d64": dict(B=3, H=2, T=196),
+}
+
+# full shapes: how many heads the oracle recomputes at full T
+FULL_HEADS = {
+    "v5_f32_1x1x256_d64": None,             # all
+    "v4_momentum_4x8x2048_d128": None,      # all 32
+    "v3_softplus_8x16x4096_d128": 8,
+    "v2_swiglu_4x16x8192_d128_f512": 3,
+    "v5_long_1x16x65536_d128": 4,
+    "v3_long_1x16x65536_d128": 4,
+    "bidir_vit_256x6x196_d64": 64,
+}
+
+
+def check(name, got, ref, tol):
+    err = oracle.rel_err(got, ref)
+    say(f"  {name}: rel err {err:.3e} (tol {tol:g}), max|ref| {np.max(np.abs(ref)):.3e}")
+    assert np.all(np.isfinite(got)), "non-finite output"
+    assert err <= tol, f"{name}: rel err {err:.3e} > {tol:g}"
+    return err
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_parity_reduced_shape(name):
+    w = WORKLOADS[name].with_shape(**SMALL[name])
+    say(f"[parity-small] {w.name} dtype={w.dtype} phi={w.phi} eta={w.eta_mode} beta={w.beta} "
+        f"causal={w.causal} chunk={w.chunk}")
+    x = make_inputs(w)
+    d = to_device(x)
+    got = run_gpu(w, d)
+    ref = run_oracle(w, x)
+    check(w.name, got, ref, TOL[w.dtype])
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_parity_full_shape(name):
+    w = WORKLOADS[name]
+    n = FULL_HEADS[name]
+    heads = None if n is None else head_subset(w, n)
+    say(f"[parity-full] {w.name} heads={'all' if heads is None else heads}")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d)
+    p = lay.plan()
+    say(f"  plan: path={p.path} chunk={p.chunk} segments={p.segments} seg_len={p.seg_len} "
+        f"dv_split={p.dv_split} phi_split={p.phi_split} grid={p.grid_main}")
+    got = run_gpu(w, d, layer=lay)
+    ref = run_oracle(w, x, heads=heads)
+    if heads is not None:
+        got = select_heads(got, w, heads)
+    check(w.name, got, ref, TOL[w.dtype])

@@ -1,0 +1,229 @@
+"""ctypes binding of libttt_la.so (argument marshalling only).
+
+The function names match the C ABI in include/ttt_la.h.  Every step of the
+forward runs in the library's HIP kernels; this module only converts Python
+and torch objects to pointers, sizes and status codes.  There is no fallback:
+if the library is missing or fails to load, importing the functions raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libttt_la.so")
+
+# status codes
+TTT_LA_OK = 0
+TTT_LA_ERR_INVALID_ARG = -1
+TTT_LA_ERR_UNSUPPORTED = -2
+TTT_LA_ERR_HIP = -3
+TTT_LA_ERR_OOM = -4
+
+TTT_LA_F32 = 0
+TTT_LA_BF16 = 1
+TTT_LA_PHI_IDENTITY = 0
+TTT_LA_PHI_SWIGLU = 1
+
+TTT_LA_CAUSAL = 0
+TTT_LA_BIDIRECTIONAL = 1 << 0
+TTT_LA_ETA_SCALAR = 0
+TTT_LA_ETA_PER_TOKEN = 1 << 1
+TTT_LA_ETA_SOFTPLUS = 1 << 2
+
+
+class ttt_la_desc(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("d_phi", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("phi", ctypes.c_int32), ("chunk", ctypes.c_int32),
+        ("segments", ctypes.c_int32),
+        ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p),
+    ]
+
+
+class ttt_la_plan(ctypes.Structure):
+    _fields_ = [
+        ("path", ctypes.c_int32), ("chunk", ctypes.c_int32), ("segments", ctypes.c_int32),
+        ("seg_len", ctypes.c_int32), ("dv_split", ctypes.c_int32), ("phi_split", ctypes.c_int32),
+        ("grid_main", ctypes.c_int32), ("n_kernels", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_destroy", "ttt_la_status_string",
+           "ttt_la_check", "ttt_la_get_plan", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times")
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libttt_la.so once and declares the signatures.  Raises if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libttt_la.so is not built ({path}); run "
+                           "`python -m ttt_weight_layers_amd.build` (the HIP library is required, "
+                           "there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
+    lib.ttt_la_create.argtypes = [ctypes.POINTER(ttt_la_desc), ctypes.POINTER(vp)]
+    lib.ttt_la_create.restype = ctypes.c_int
+    lib.ttt_la_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp]
+    lib.ttt_la_forward.restype = ctypes.c_int
+    lib.ttt_la_destroy.argtypes = [vp]
+    lib.ttt_la_destroy.restype = None
+    lib.ttt_la_status_string.argtypes = [ctypes.c_int]
+    lib.ttt_la_status_string.restype = ctypes.c_char_p
+    lib.ttt_la_check.argtypes = [ctypes.POINTER(ttt_la_desc), vp, vp, vp, vp, f32, f32, u32, vp]
+    lib.ttt_la_check.restype = ctypes.c_int
+    lib.ttt_la_get_plan.argtypes = [vp, ctypes.POINTER(ttt_la_plan)]
+    lib.ttt_la_get_plan.restype = ctypes.c_int
+    lib.ttt_la_enable_kernel_timing.argtypes = [vp, i32]
+    lib.ttt_la_enable_kernel_timing.restype = ctypes.c_int
+    lib.ttt_la_kernel_times.argtypes = [vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]
+    lib.ttt_la_kernel_times.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {ttt_la_status_string(status)} ({status})")
+
+
+def ttt_la_status_string(status: int) -> str:
+    return load_library().ttt_la_status_string(int(status)).decode()
+
+
+def ttt_la_create(desc: ttt_la_desc):
+    """Returns (status, handle)."""
+    h = ctypes.c_void_p()
+    st = load_library().ttt_la_create(ctypes.byref(desc), ctypes.byref(h))
+    return st, h
+
+
+def ttt_la_forward(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float,
+                   mode: int, o: int, stream: Optional[int]) -> int:
+    return load_library().ttt_la_forward(h, q, k, v, eta, float(eta_scalar), float(beta),
+                                         int(mode), o, stream)
+
+
+def ttt_la_destroy(h) -> None:
+    load_library().ttt_la_destroy(h)
+
+
+def ttt_la_check(desc: ttt_la_desc, q=None, k=None, v=None, eta=None, eta_scalar=1.0, beta=0.0,
+                 mode=0, o=None) -> int:
+    return load_library().ttt_la_check(ctypes.byref(desc), q, k, v, eta, float(eta_scalar),
+                                       float(beta), int(mode), o)
+
+
+def ttt_la_get_plan(h) -> ttt_la_plan:
+    p = ttt_la_plan()
+    st = load_library().ttt_la_get_plan(h, ctypes.byref(p))
+    if st != TTT_LA_OK:
+        raise TTTError(st, "ttt_la_get_plan")
+    return p
+
+
+def ttt_la_enable_kernel_timing(h, n_slots: int) -> int:
+    return load_library().ttt_la_enable_kernel_timing(h, int(n_slots))
+
+
+def ttt_la_kernel_times(h, capacity: int):
+    buf = (ctypes.c_float * max(1, capacity))()
+    n = ctypes.c_int32(0)
+    st = load_library().ttt_la_kernel_times(h, buf, int(capacity), ctypes.byref(n))
+    if st != TTT_LA_OK:
+        raise TTTError(st, "ttt_la_kernel_times")
+    return [buf[i] for i in range(n.value)]
+
+
+# ----------------------------------------------------------------------------
+# torch-facing convenience wrapper (still marshalling only)
+# ----------------------------------------------------------------------------
+
+_DTYPES = {"f32": TTT_LA_F32, "bf16": TTT_LA_BF16}
+_PHIS = {"identity": TTT_LA_PHI_IDENTITY, "swiglu": TTT_LA_PHI_SWIGLU}
+_ETA = {"scalar": TTT_LA_ETA_SCALAR, "per_token": TTT_LA_ETA_PER_TOKEN, "softplus": TTT_LA_ETA_SOFTPLUS}
+
+
+def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0, segments=0,
+              w1=None, w3=None) -> ttt_la_desc:
+    d = ttt_la_desc()
+    d.B, d.H, d.T, d.d_k, d.d_v = int(B), int(H), int(T), int(d_k), int(d_v)
+    d.d_phi = int(d_k if d_phi is None else d_phi)
+    d.dtype = _DTYPES[dtype]
+    d.phi = _PHIS[phi]
+    d.chunk = int(chunk)
+    d.segments = int(segments)
+    d.w1 = _ptr(w1)
+    d.w3 = _ptr(w3)
+    return d
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return int(t.data_ptr())
+
+
+def mode_bits(eta_mode: str = "scalar", causal: bool = True) -> int:
+    return _ETA[eta_mode] | (0 if causal else TTT_LA_BIDIRECTIONAL)
+
+
+class TTTLinearAttention:
+    """One layer shape bound to a library handle.
+
+    ``forward(q, k, v, ...)`` takes contiguous device tensors shaped
+    [B, H, T, d] (torch.float32 or torch.bfloat16) and writes o.
+    """
+
+    def __init__(self, B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0,
+                 segments=0, w1=None, w3=None):
+        self._keep = (w1, w3)         # W1/W3 are borrowed by the handle
+        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, segments, w1, w3)
+        self.dtype = dtype
+        st, h = ttt_la_create(self.desc)
+        if st != TTT_LA_OK:
+            raise TTTError(st, "ttt_la_create")
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            ttt_la_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def plan(self) -> ttt_la_plan:
+        return ttt_la_get_plan(self.handle)
+
+    def forward(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
+                out=None, stream=None):
+        import torch
+        if out is None:
+            out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
+        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be a device tensor")
+        if eta is not None and (eta.dtype != torch.float32 or not eta.is_contiguous()):
+            raise ValueError("eta must be a contiguous float32 device tensor")
+        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
+        st = ttt_la_forward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta,
+                            mode_bits(eta_mode, causal), _ptr(out), s)
+        if st != TTT_LA_OK:
+            raise TTTError(st, "ttt_la_forward")
+        return out

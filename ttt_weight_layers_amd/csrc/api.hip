@@ -1,0 +1,296 @@
+// C ABI of libttt_la.so: validation, kernel plan, workspace, launches.
+// The operation and every argument are documented in include/ttt_la.h.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "device_common.h"
+#include "internal.h"
+#include "ttt_la.h"
+
+struct ttt_la_s {
+    ttt_la_desc desc;
+    ttt::Shape shape;
+    bool fast;
+    ttt::FastPlan fp;
+    void* workspace;
+    size_t workspace_bytes;
+    int device;
+    int n_kernels;
+    // measurement hook
+    std::vector<hipEvent_t> ev_begin, ev_end;
+    int calls;
+};
+
+namespace {
+
+using ttt::Shape;
+
+constexpr uint32_t kModeMask = TTT_LA_BIDIRECTIONAL | TTT_LA_ETA_PER_TOKEN | TTT_LA_ETA_SOFTPLUS;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(int dtype) { return dtype == TTT_LA_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+int check_desc(const ttt_la_desc* d) {
+    if (!d) return TTT_LA_ERR_INVALID_ARG;
+    if (d->B < 1 || d->H < 1 || d->T < 1) return TTT_LA_ERR_INVALID_ARG;
+    if (d->d_k < 1 || d->d_v < 1 || d->d_phi < 1) return TTT_LA_ERR_INVALID_ARG;
+    if (d->dtype != TTT_LA_F32 && d->dtype != TTT_LA_BF16) return TTT_LA_ERR_INVALID_ARG;
+    if (d->phi != TTT_LA_PHI_IDENTITY && d->phi != TTT_LA_PHI_SWIGLU) return TTT_LA_ERR_INVALID_ARG;
+    if (d->chunk < 0 || d->segments < 0) return TTT_LA_ERR_INVALID_ARG;
+    if (d->phi == TTT_LA_PHI_SWIGLU) {
+        if (!d->w1 || !d->w3) return TTT_LA_ERR_INVALID_ARG;
+        if (!aligned(d->w1, 16) || !aligned(d->w3, 16)) return TTT_LA_ERR_INVALID_ARG;
+    } else {
+        if (d->w1 || d->w3) return TTT_LA_ERR_INVALID_ARG;
+        if (d->d_phi != d->d_k) return TTT_LA_ERR_INVALID_ARG;
+    }
+    // supported shapes
+    if (d->d_k != 64 && d->d_k != 128) return TTT_LA_ERR_UNSUPPORTED;
+    if (d->d_v != 64 && d->d_v != 128) return TTT_LA_ERR_UNSUPPORTED;
+    if (d->phi == TTT_LA_PHI_SWIGLU && (d->d_phi % 128 != 0 || d->d_phi > 512)) return TTT_LA_ERR_UNSUPPORTED;
+    if (d->chunk != 0 && d->chunk != 64 && d->chunk != 128) return TTT_LA_ERR_UNSUPPORTED;
+    const long long widest = std::max(d->d_k, std::max(d->d_v, d->d_phi));
+    if ((long long)d->B * d->H * d->T * widest >= (1LL << 31)) return TTT_LA_ERR_UNSUPPORTED;
+    return TTT_LA_OK;
+}
+
+int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                  float eta_scalar, float beta, uint32_t mode, const void* o) {
+    if (!q || !k || !v || !o) return TTT_LA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return TTT_LA_ERR_INVALID_ARG;
+    if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
+    const bool per_tok = (mode & TTT_LA_ETA_PER_TOKEN) != 0;
+    const bool softp = (mode & TTT_LA_ETA_SOFTPLUS) != 0;
+    if (per_tok && softp) return TTT_LA_ERR_INVALID_ARG;
+    if (per_tok || softp) {
+        if (!eta || !aligned(eta, 4)) return TTT_LA_ERR_INVALID_ARG;
+    } else {
+        if (eta) return TTT_LA_ERR_INVALID_ARG;
+        if (!std::isfinite(eta_scalar)) return TTT_LA_ERR_INVALID_ARG;
+    }
+    if (!(beta >= 0.0f && beta < 1.0f)) return TTT_LA_ERR_INVALID_ARG;  // also rejects NaN
+    const size_t eb = elem_bytes(d->dtype);
+    const size_t nt = (size_t)d->B * d->H * d->T;
+    const size_t qk_bytes = nt * d->d_k * eb, v_bytes = nt * d->d_v * eb;
+    const size_t eta_bytes = (per_tok || softp) ? nt * sizeof(float) : 0;
+    if (overlaps(o, v_bytes, q, qk_bytes) || overlaps(o, v_bytes, k, qk_bytes) ||
+        overlaps(o, v_bytes, v, v_bytes) || overlaps(o, v_bytes, eta, eta_bytes))
+        return TTT_LA_ERR_INVALID_ARG;
+    if (d->phi == TTT_LA_PHI_SWIGLU) {
+        const size_t w_bytes = (size_t)d->H * d->d_phi * d->d_k * eb;
+        if (overlaps(o, v_bytes, d->w1, w_bytes) || overlaps(o, v_bytes, d->w3, w_bytes))
+            return TTT_LA_ERR_INVALID_ARG;
+    }
+    return TTT_LA_OK;
+}
+
+Shape shape_of(const ttt_la_desc& d) {
+    Shape s;
+    s.B = d.B;
+    s.H = d.H;
+    s.T = d.T;
+    s.d_k = d.d_k;
+    s.d_v = d.d_v;
+    s.d_phi = d.d_phi;
+    s.bf16 = d.dtype == TTT_LA_BF16;
+    s.swiglu = d.phi == TTT_LA_PHI_SWIGLU;
+    s.w1 = d.w1;
+    s.w3 = d.w3;
+    return s;
+}
+
+int eta_kind_of(uint32_t mode) {
+    if (mode & TTT_LA_ETA_PER_TOKEN) return ttt::ETA_PER_TOKEN;
+    if (mode & TTT_LA_ETA_SOFTPLUS) return ttt::ETA_SOFTPLUS;
+    return ttt::ETA_SCALAR;
+}
+
+void release_events(ttt_la_s* h) {
+    for (hipEvent_t e : h->ev_begin) (void)hipEventDestroy(e);
+    for (hipEvent_t e : h->ev_end) (void)hipEventDestroy(e);
+    h->ev_begin.clear();
+    h->ev_end.clear();
+    h->calls = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_la_status_string(int status) {
+    switch (status) {
+        case TTT_LA_OK: return "ok";
+        case TTT_LA_ERR_INVALID_ARG: return "invalid argument";
+        case TTT_LA_ERR_UNSUPPORTED: return "unsupported shape or setting";
+        case TTT_LA_ERR_HIP: return "HIP runtime error";
+        case TTT_LA_ERR_OOM: return "out of device memory";
+        default: return "unknown status";
+    }
+}
+
+int ttt_la_check(const ttt_la_desc* desc, const void* q, const void* k, const void* v, const float* eta,
+                 float eta_scalar, float beta, uint32_t mode, const void* o) {
+    int st = check_desc(desc);
+    if (st != TTT_LA_OK || q == nullptr) return st;
+    return check_forward(desc, q, k, v, eta, eta_scalar, beta, mode, o);
+}
+
+int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
+    if (!out) return TTT_LA_ERR_INVALID_ARG;
+    *out = nullptr;
+    int st = check_desc(desc);
+    if (st != TTT_LA_OK) return st;
+
+    ttt_la_s* h = new (std::nothrow) ttt_la_s();
+    if (!h) return TTT_LA_ERR_OOM;
+    h->desc = *desc;
+    h->shape = shape_of(*desc);
+    h->workspace = nullptr;
+    h->workspace_bytes = 0;
+    h->calls = 0;
+    h->fast = desc->dtype == TTT_LA_BF16 && ttt::fast_supported(h->shape, desc->chunk);
+    h->n_kernels = 1;
+    if (h->fast) {
+        h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments);
+        h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes;
+    }
+    if (hipGetDevice(&h->device) != hipSuccess) {
+        delete h;
+        return TTT_LA_ERR_HIP;
+    }
+    if (!h->fast && ttt::generic_smem_bytes(h->shape) > 160 * 1024) {
+        delete h;
+        return TTT_LA_ERR_UNSUPPORTED;
+    }
+    if (h->workspace_bytes) {
+        hipError_t e = hipMalloc(&h->workspace, h->workspace_bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            delete h;
+            return e == hipErrorOutOfMemory ? TTT_LA_ERR_OOM : TTT_LA_ERR_HIP;
+        }
+    }
+    *out = h;
+    return TTT_LA_OK;
+}
+
+int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                   float beta, uint32_t mode, void* o, void* hip_stream) {
+    if (!h) return TTT_LA_ERR_INVALID_ARG;
+    int st = check_forward(&h->desc, q, k, v, eta, eta_scalar, beta, mode, o);
+    if (st != TTT_LA_OK) return st;
+
+    ttt::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.eta = eta;
+    a.eta_scalar = eta_scalar;
+    a.beta = beta;
+    a.eta_kind = eta_kind_of(mode);
+    a.bidirectional = (mode & TTT_LA_BIDIRECTIONAL) != 0;
+    a.o = o;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+
+    hipEvent_t eb = nullptr, ee = nullptr;
+    if (!h->ev_begin.empty()) {
+        const size_t slot = (size_t)h->calls % h->ev_begin.size();
+        eb = h->ev_begin[slot];
+        ee = h->ev_end[slot];
+        h->calls++;
+    }
+    hipError_t e;
+    if (h->fast) {
+        int nk = 0;
+        e = ttt::launch_fast(h->shape, h->fp, h->workspace, a, eb, ee, &nk);
+        h->n_kernels = nk;
+    } else {
+        if (eb && hipEventRecord(eb, a.stream) != hipSuccess) return TTT_LA_ERR_HIP;
+        e = ttt::launch_generic(h->shape, a);
+        if (e == hipSuccess && ee && hipEventRecord(ee, a.stream) != hipSuccess) return TTT_LA_ERR_HIP;
+        h->n_kernels = 1;
+    }
+    return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+void ttt_la_destroy(ttt_la_t h) {
+    if (!h) return;
+    release_events(h);
+    if (h->workspace) (void)hipFree(h->workspace);
+    delete h;
+}
+
+int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
+    if (!h || !plan) return TTT_LA_ERR_INVALID_ARG;
+    std::memset(plan, 0, sizeof(*plan));
+    const Shape& s = h->shape;
+    plan->workspace_bytes = h->workspace_bytes;
+    if (h->fast) {
+        plan->path = 1;
+        plan->chunk = h->fp.chunk;
+        plan->segments = h->fp.segments;
+        plan->seg_len = h->fp.seg_len;
+        plan->dv_split = h->fp.dv_split;
+        plan->phi_split = h->fp.phi_split;
+        plan->grid_main = s.n_seq() * h->fp.dv_split * h->fp.phi_split * h->fp.segments;
+        plan->n_kernels = 1 + (h->fp.segments > 1 ? 2 : 0) + (h->fp.phi_split > 1 ? 1 : 0);
+    } else {
+        plan->path = 0;
+        plan->chunk = 16;
+        plan->segments = 1;
+        plan->seg_len = s.T;
+        plan->dv_split = s.d_v / 16;
+        plan->phi_split = 1;
+        plan->grid_main = s.n_seq() * (s.d_v / 16);
+        plan->n_kernels = 1;
+    }
+    return TTT_LA_OK;
+}
+
+int ttt_la_enable_kernel_timing(ttt_la_t h, int32_t n_slots) {
+    if (!h || n_slots < 0) return TTT_LA_ERR_INVALID_ARG;
+    release_events(h);
+    for (int32_t i = 0; i < n_slots; ++i) {
+        hipEvent_t a = nullptr, b = nullptr;
+        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+            if (a) (void)hipEventDestroy(a);
+            release_events(h);
+            return TTT_LA_ERR_HIP;
+        }
+        h->ev_begin.push_back(a);
+        h->ev_end.push_back(b);
+    }
+    return TTT_LA_OK;
+}
+
+int ttt_la_kernel_times(ttt_la_t h, float* ms, int32_t capacity, int32_t* count) {
+    if (!h || !count || (capacity > 0 && !ms)) return TTT_LA_ERR_INVALID_ARG;
+    *count = 0;
+    const int slots = (int)h->ev_begin.size();
+    if (slots == 0) return TTT_LA_OK;
+    const int n = std::min(h->calls, slots);
+    const int first = h->calls - n;  // oldest call still held
+    for (int i = 0; i < n && *count < capacity; ++i) {
+        const int slot = (first + i) % slots;
+        if (hipEventSynchronize(h->ev_end[slot]) != hipSuccess) return TTT_LA_ERR_HIP;
+        float t = 0.0f;
+        if (hipEventElapsedTime(&t, h->ev_begin[slot], h->ev_end[slot]) != hipSuccess) return TTT_LA_ERR_HIP;
+        ms[(*count)++] = t;
+    }
+    return TTT_LA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Device helpers shared by the kernels of libttt_la.so (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// learning-rate encodings of the mode bits
+enum EtaKind : int { ETA_SCALAR = 0, ETA_PER_TOKEN = 1, ETA_SOFTPLUS = 2 };
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+    __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// packs two fp32 into one dword of two bf16 (lo = a, hi = b)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+}
+
+// softplus(a) = ln(1 + e^a), stable form max(a, 0) + log1p(e^-|a|)
+__device__ __forceinline__ float softplus_f32(float a) {
+    return fmaxf(a, 0.0f) + log1pf(__expf(-fabsf(a)));
+}
+
+__device__ __forceinline__ float silu_f32(float u) {
+    return u / (1.0f + __expf(-u));
+}
+
+template <typename TI> __device__ __forceinline__ float load_as_f32(const TI* p, size_t i);
+template <> __device__ __forceinline__ float load_as_f32<float>(const float* p, size_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, size_t i) {
+    return bf16_bits_to_f32(p[i]);
+}
+
+template <typename TO> __device__ __forceinline__ void store_from_f32(TO* p, size_t i, float x);
+template <> __device__ __forceinline__ void store_from_f32<float>(float* p, size_t i, float x) { p[i] = x; }
+template <> __device__ __forceinline__ void store_from_f32<uint16_t>(uint16_t* p, size_t i, float x) {
+    p[i] = f32_to_bf16_bits(x);
+}
+
+__device__ __forceinline__ float eta_at(int kind, const float* eta, float eta_scalar, size_t idx) {
+    if (kind == ETA_SCALAR) return eta_scalar;
+    float a = eta[idx];
+    return kind == ETA_SOFTPLUS ? softplus_f32(a) : a;
+}
+
+}  // namespace ttt
