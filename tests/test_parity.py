@@ -78,6 +78,8 @@ def test_parity_full_shape(name):
     p = lay.plan()
     say(f"  plan: path={p.path} chunk={p.chunk} segments={p.segments} seg_len={p.seg_len} "
         f"dv_split={p.dv_split} phi_split={p.phi_split} grid={p.grid_main}")
+    # bf16 workloads run on the MFMA path, fp32 on the fp32-arithmetic path
+    assert p.path == (1 if w.dtype == "bf16" else 0)
     got = run_gpu(w, d, layer=lay)
     ref = run_oracle(w, x, heads=heads)
     if heads is not None:

@@ -1,15 +1,752 @@
-// bf16 MFMA chunk kernels (placeholder until the MFMA path lands).
+// bf16 MFMA chunk kernels for gfx950: the hot path of the TTT forward.
+//
+// The layer (one momentum-SGD step per token on the dot-product binding loss,
+// fast weight reset per sequence, readout after the update) unrolls, for a
+// chunk of n tokens entered with fp32 state (S, M), into
+//
+//   o_i = S phi(q_i) + g_i M phi(q_i) + sum_{j<=i} c_{i-j} eta_j (phi(q_i).phi(k_j)) v_j
+//   S  <- S + g_{n-1} M + sum_j eta_j c_{n-1-j} v_j phi(k_j)^T
+//   M  <- beta^n M + sum_j eta_j beta^{n-1-j} v_j phi(k_j)^T
+//
+// with c_r = sum_{u<=r} beta^u and g_i = beta c_i: dense causal blocks inside
+// a chunk and a fixed-size state carried between chunks, the parallel form of
+// the outer-product accumulation that the kualia.ai blog ("The Linear Attention
+// Equivalence") identifies with linear attention, (phi(Q) phi(K)^T) V.  The
+// per-token learning rate, momentum and SwiGLU feature map are the inner-loop
+// options of Table 2 on the thelatestinai.com page (Variants 2-4).
+//
+// Kernels (all bf16 MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation):
+//   chunk_kernel<OUTPUT>   one workgroup per (sequence, segment, feature slice,
+//                          value slice); walks its segment chunk by chunk, keeps
+//                          its slice of (S, M) in registers, writes o.
+//   chunk_kernel<SUMMARY>  same walk without readout: the zero-entry state change
+//                          of every segment but the last (segment summaries).
+//   segment_scan           composes the summaries into each segment's entry state.
+//   chunk_kernel<BIDIR>    bidirectional: all updates, then every query reads S_T.
+//   partial_reduce         sums fp32 partial outputs of feature slices (SwiGLU).
+//
+// Register layouts (lane l of a 64-wide wave, c16 = l % 16, g = l / 16):
+//   MFMA A operand  lane holds A[m = c16][k = 8g .. 8g+7]
+//   MFMA B operand  lane holds B[k = 8g .. 8g+7][n = c16]
+//   MFMA D result   lane holds D[m = 4g .. 4g+3][n = c16]
+// The state is kept transposed, S^T[f][dv], as D tiles: lane holds
+// S^T[16ft + 4g + r][dv0 + c16].  Two such tiles (ft = 2s, 2s+1) form, without
+// any data movement, the A operand of O^T = S Q^T over the permuted contraction
+// set {32s + 4g + r} u {32s + 16 + 4g + r}; the B operand then reads Q with the
+// same permutation (two 8-byte LDS reads).
+
+#include <algorithm>
+#include <cmath>
+
+#include "device_common.h"
 #include "internal.h"
 
 namespace ttt {
+namespace {
 
-bool fast_supported(const Shape&, int) { return false; }
+enum Kind : int { K_OUTPUT = 0, K_SUMMARY = 1, K_BIDIR = 2 };
 
-FastPlan fast_plan(const Shape&, int, int) { return FastPlan{}; }
+struct ChunkParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* eta;
+    const uint16_t* w1;
+    const uint16_t* w3;
+    uint16_t* o;         // bf16 output (phi_split == 1)
+    float* o_partial;    // [phi_split][B*H*T][d_v] fp32 (phi_split > 1)
+    float* state;        // summaries / entry states
+    float eta_scalar;
+    float beta;
+    int eta_kind;
+    int T, H, d_k, d_v, d_phi;
+    int dv_split, phi_split, seg_count, seg_len;
+    int n_units;
+    size_t n_rows;       // B * H * T
+};
 
-hipError_t launch_fast(const Shape&, const FastPlan&, void*, const FwdArgs&, hipEvent_t, hipEvent_t, int* n) {
-    if (n) *n = 0;
-    return hipErrorNotSupported;
+constexpr int PAD = 8;  // bf16 elements of padding per LDS row (16 bytes)
+
+template <int C, int D, int DK, int NW, bool SWIGLU>
+struct Lds {
+    static constexpr int DVWG = 16 * NW;
+    static constexpr int LQ = D + PAD;      // sQ, sK row stride
+    static constexpr int LT = C + PAD;      // sKt, sVt, sA row stride
+    static constexpr int LX = DK + PAD;     // SwiGLU raw staging stride
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_K = OFF_Q + C * LQ;
+    static constexpr int OFF_KT = OFF_K + C * LQ;
+    static constexpr int OFF_VT = OFF_KT + D * LT;
+    static constexpr int OFF_A = OFF_VT + DVWG * LT;
+    static constexpr int OFF_XQ = OFF_A + C * LT;
+    static constexpr int OFF_XK = OFF_XQ + (SWIGLU ? C * LX : 0);
+    static constexpr int N_BF16 = OFF_XK + (SWIGLU ? C * LX : 0);
+    // floats after the bf16 area: eta, wS, wM (C each), c (C + 1), beta^r (C + 1)
+    static constexpr int N_F32 = 5 * C + 2;
+    static constexpr int BYTES = N_BF16 * 2 + N_F32 * 4;
+};
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+__device__ __forceinline__ u32x2 lds_read8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+__device__ __forceinline__ bf16x8 join8(const u32x2& a, const u32x2& b) {
+    u32x4 u = {a[0], a[1], b[0], b[1]};
+    return as_bf16x8(u);
+}
+
+// bf16x8 built from two D tiles (4 floats each): elements 0..3 from x, 4..7 from y
+__device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
+    u32x4 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
+               pack_bf16x2(y[2], y[3])};
+    return as_bf16x8(u);
+}
+
+// scale 8 packed bf16 by 8 fp32 weights and re-round to bf16
+__device__ __forceinline__ bf16x8 scale8(const u32x4& raw, const float* w) {
+    u32x4 u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        float lo = __uint_as_float(raw[p] << 16) * w[2 * p];
+        float hi = __uint_as_float(raw[p] & 0xffff0000u) * w[2 * p + 1];
+        u[p] = pack_bf16x2(lo, hi);
+    }
+    return as_bf16x8(u);
+}
+
+// 8 rows x 8 bf16 block held as 8 x u32x4 (row r, dword p = columns 2p, 2p+1)
+// -> column cc as u32x4 (dword p = rows 2p, 2p+1)
+__device__ __forceinline__ u32x4 block_column(const u32x4 (&r)[8], int cc) {
+    const int p = cc >> 1;
+    u32x4 out;
+    if ((cc & 1) == 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = (r[2 * q][p] & 0xffffu) | (r[2 * q + 1][p] << 16);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) out[q] = (r[2 * q][p] >> 16) | (r[2 * q + 1][p] & 0xffff0000u);
+    }
+    return out;
+}
+
+__device__ __forceinline__ void load_block(u32x4 (&r)[8], const uint16_t* base, size_t ld, int rows_valid) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+        if (rr < rows_valid) r[rr] = *reinterpret_cast<const u32x4*>(base + (size_t)rr * ld);
+        else r[rr] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Momentum coefficient tables by a wavefront prefix scan:
+//   bp[r] = beta^r (prefix product), cc[r] = sum_{u<=r} beta^u (prefix sum), r = 0..C
+template <int C>
+__device__ void coefficient_scan(float beta, float* cc, float* bp) {
+    const int lane = threadIdx.x & 63;
+    float base_p = 1.0f, base_c = 0.0f;
+    for (int r0 = 0; r0 <= C; r0 += 64) {
+        float p = (lane == 0) ? 1.0f : beta;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            float o = __shfl_up(p, d, 64);
+            if (lane >= d) p *= o;
+        }
+        // p = beta^lane; prefix sum of p
+        float s = p;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            float o = __shfl_up(s, d, 64);
+            if (lane >= d) s += o;
+        }
+        const int r = r0 + lane;
+        if (r <= C) {
+            bp[r] = base_p * p;
+            cc[r] = base_c + base_p * s;
+        }
+        // carry into the next 64 entries: beta^(r0+64), c_{r0+63}
+        float p63 = __shfl(p, 63, 64), s63 = __shfl(s, 63, 64);
+        base_c = base_c + base_p * s63;
+        base_p = base_p * p63 * beta;
+    }
+}
+
+// waves per SIMD the kernel is compiled for: two workgroups of 4 waves (or one of
+// 8) when the LDS footprint allows two resident workgroups, else one of 4.
+template <int C, int D, int DK, int NW, bool SWIGLU>
+constexpr int waves_per_eu() {
+    return (NW == 8 || 2 * Lds<C, D, DK, NW, SWIGLU>::BYTES <= 160 * 1024) ? 2 : 1;
+}
+
+template <int C, int D, int DK, int NW, bool MOM, bool SWIGLU, int KIND>
+__global__ void __launch_bounds__(NW * 64, (waves_per_eu<C, D, DK, NW, SWIGLU>()))
+chunk_kernel(ChunkParams p) {
+    using L = Lds<C, D, DK, NW, SWIGLU>;
+    constexpr int NT = NW * 64;
+    constexpr int DVWG = L::DVWG;
+    constexpr int NFT = D / 16;     // feature tiles of the state slice
+    constexpr int NS = D / 32;      // contraction steps over features
+    constexpr int NI = C / 16;      // token blocks per chunk
+    constexpr int NJS = C / 32;     // contraction steps over tokens
+
+    __shared__ __attribute__((aligned(16))) uint16_t smem16[L::N_BF16 + 2 * L::N_F32];
+    uint16_t* sQ = smem16 + L::OFF_Q;
+    uint16_t* sK = smem16 + L::OFF_K;
+    uint16_t* sKt = smem16 + L::OFF_KT;
+    uint16_t* sVt = smem16 + L::OFF_VT;
+    uint16_t* sA = smem16 + L::OFF_A;
+    uint16_t* sXq = smem16 + L::OFF_XQ;
+    uint16_t* sXk = smem16 + L::OFF_XK;
+    float* sEta = reinterpret_cast<float*>(smem16 + L::N_BF16);
+    float* sWS = sEta + C;
+    float* sWM = sWS + C;
+    float* sC = sWM + C;        // C + 1
+    float* sBP = sC + C + 1;    // C + 1
+
+    // ---- unit of work (XCD-aware: consecutive units land on one XCD) --------
+    const int G = gridDim.x;
+    const int u = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (u >= p.n_units) return;
+    const int vs = u % p.dv_split;
+    const int fs = (u / p.dv_split) % p.phi_split;
+    const int rest = u / (p.dv_split * p.phi_split);
+    const int nseg = (KIND == K_SUMMARY) ? p.seg_count - 1 : (KIND == K_BIDIR ? 1 : p.seg_count);
+    const int seg = rest % nseg;
+    const int seq = rest / nseg;
+    const int h = seq % p.H;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int dv_base = vs * DVWG;        // first value column of the workgroup
+    const int dvw = wave * 16;            // wave's columns inside the slice
+    const float beta = p.beta;
+
+    const int t_begin = (KIND == K_BIDIR) ? 0 : seg * p.seg_len;
+    const int t_end = (KIND == K_BIDIR) ? p.T : min(p.T, t_begin + p.seg_len);
+    const size_t seq_row = (size_t)seq * p.T;
+
+    if (wave == 0) coefficient_scan<C>(beta, sC, sBP);
+
+    // zero the A tiles above the diagonal that the token-pair steps read
+    for (int idx = tid; idx < (NI / 2) * 16 * 16; idx += NT) {
+        const int I = 2 * (idx / 256), rr = (idx / 16) % 16, cc = idx % 16;
+        sA[(16 * I + rr) * L::LT + 16 * (I + 1) + cc] = 0;
+    }
+
+    // SwiGLU: this wave's rows of W1/W3 (feature slice fs) as MFMA A operands
+    constexpr int FPW = SWIGLU ? D / NW : 16;       // features computed per wave
+    constexpr int NFW = FPW / 16;
+    constexpr int NSK = DK / 32;
+    bf16x8 w1f[SWIGLU ? NFW : 1][SWIGLU ? NSK : 1];
+    bf16x8 w3f[SWIGLU ? NFW : 1][SWIGLU ? NSK : 1];
+    if constexpr (SWIGLU) {
+        const size_t wrow0 = (size_t)h * p.d_phi + (size_t)fs * D + wave * FPW;
+#pragma unroll
+        for (int a = 0; a < NFW; ++a)
+#pragma unroll
+            for (int s = 0; s < NSK; ++s) {
+                const size_t off = (wrow0 + 16 * a + c16) * DK + 32 * s + 8 * g;
+                w1f[a][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.w1 + off));
+                w3f[a][s] = as_bf16x8(*reinterpret_cast<const u32x4*>(p.w3 + off));
+            }
+    }
+
+    // ---- state slice in registers ------------------------------------------
+    f32x4 S[NFT], M[MOM ? NFT : 1];
+#pragma unroll
+    for (int ft = 0; ft < NFT; ++ft) S[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ft = 0; ft < (MOM ? NFT : 1); ++ft) M[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // summaries / entry states: [slot][wave][ft][lane] f32x4, S then M
+    constexpr size_t SLICE_F4 = (size_t)NW * NFT * 64;
+    const size_t slice_units = (size_t)p.phi_split * p.dv_split;
+    const size_t slot_stride = SLICE_F4 * 2;   // S and M
+    if (KIND == K_OUTPUT && seg > 0) {
+        // entry state of segment seg = scanned slot (seq, seg - 1)
+        const size_t slot = ((size_t)seq * (p.seg_count - 1) + (seg - 1)) * slice_units + (size_t)fs * p.dv_split + vs;
+        const f32x4* src = reinterpret_cast<const f32x4*>(p.state) + slot * slot_stride;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) S[ft] = src[((size_t)wave * NFT + ft) * 64 + lane];
+        if constexpr (MOM) {
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) M[ft] = src[SLICE_F4 + ((size_t)wave * NFT + ft) * 64 + lane];
+        }
+    }
+
+    const int n_passes = (KIND == K_BIDIR) ? 2 : 1;
+
+    for (int pass = 0; pass < n_passes; ++pass) {
+        // pass 0: chunk walk with updates (and causal readout)
+        // pass 1 (bidirectional only): readout of every query from the final S
+        const bool upd = (pass == 0);
+        const bool readq = (KIND == K_OUTPUT) || (KIND == K_BIDIR && pass == 1);
+        for (int t0 = t_begin; t0 < t_end; t0 += C) {
+            const int n = min(C, t_end - t0);
+            const size_t row0 = seq_row + t0;
+            __syncthreads();   // previous chunk's LDS reads are done
+
+            // ---- stage the chunk: q, k rows (features or raw), v^T slice, eta ---
+            {
+                constexpr int QB = C * (SWIGLU ? DK : D) / 64;   // 8x8 blocks of q (or k)
+                constexpr int VB = C * DVWG / 64;
+                constexpr int FB = (SWIGLU ? DK : D) / 8;       // feature blocks per row
+                const int nq = readq ? QB : 0;
+                const int nk = upd ? QB : 0;
+                const int nv = upd || (KIND == K_OUTPUT) ? VB : 0;
+                const int total = nq + nk + nv;
+                const int ldx = SWIGLU ? DK : D;
+                for (int b = tid; b < total; b += NT) {
+                    u32x4 r[8];
+                    if (b < nq) {
+                        const int jb = b / FB, fb = b % FB;
+                        load_block(r, p.q + (row0 + 8 * jb) * ldx + 8 * fb, ldx, n - 8 * jb);
+                        uint16_t* dst = SWIGLU ? sXq + (8 * jb) * L::LX + 8 * fb : sQ + (8 * jb) * L::LQ + 8 * fb;
+                        const int ld = SWIGLU ? L::LX : L::LQ;
+#pragma unroll
+                        for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<u32x4*>(dst + rr * ld) = r[rr];
+                    } else if (b < nq + nk) {
+                        const int bb = b - nq;
+                        const int jb = bb / FB, fb = bb % FB;
+                        load_block(r, p.k + (row0 + 8 * jb) * ldx + 8 * fb, ldx, n - 8 * jb);
+                        if constexpr (SWIGLU) {
+                            uint16_t* dst = sXk + (8 * jb) * L::LX + 8 * fb;
+#pragma unroll
+                            for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<u32x4*>(dst + rr * L::LX) = r[rr];
+                        } else {
+                            if (KIND == K_OUTPUT) {
+                                uint16_t* dst = sK + (8 * jb) * L::LQ + 8 * fb;
+#pragma unroll
+                                for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<u32x4*>(dst + rr * L::LQ) = r[rr];
+                            }
+#pragma unroll
+                            for (int cc = 0; cc < 8; ++cc)
+                                *reinterpret_cast<u32x4*>(sKt + (8 * fb + cc) * L::LT + 8 * jb) = block_column(r, cc);
+                        }
+                    } else {
+                        const int bb = b - nq - nk;
+                        constexpr int FBV = DVWG / 8;
+                        const int jb = bb / FBV, fb = bb % FBV;
+                        load_block(r, p.v + (row0 + 8 * jb) * p.d_v + dv_base + 8 * fb, p.d_v, n - 8 * jb);
+#pragma unroll
+                        for (int cc = 0; cc < 8; ++cc)
+                            *reinterpret_cast<u32x4*>(sVt + (8 * fb + cc) * L::LT + 8 * jb) = block_column(r, cc);
+                    }
+                }
+                if (upd && tid < C) {
+                    float et = 0.0f;
+                    if (tid < n) et = eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + tid);
+                    sEta[tid] = et;
+                    sWS[tid] = tid < n ? et * sC[n - 1 - tid] : 0.0f;     // eta_j c_{n-1-j}
+                    sWM[tid] = tid < n ? et * sBP[n - 1 - tid] : 0.0f;    // eta_j beta^{n-1-j}
+                }
+            }
+            __syncthreads();
+
+            // ---- SwiGLU feature prologue: phi = silu(W1 x) * (W3 x) ------------
+            if constexpr (SWIGLU) {
+#pragma unroll
+                for (int a = 0; a < NFW; ++a) {
+                    const int f0 = wave * FPW + 16 * a;       // feature tile inside the slice
+                    if (readq) {
+#pragma unroll
+                        for (int I = 0; I < NI; ++I) {
+                            f32x4 u1 = {0.f, 0.f, 0.f, 0.f}, u3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s = 0; s < NSK; ++s) {
+                                bf16x8 xb = as_bf16x8(lds_read16(sXq + (16 * I + c16) * L::LX + 32 * s + 8 * g));
+                                u1 = mfma16(w1f[a][s], xb, u1);
+                                u3 = mfma16(w3f[a][s], xb, u3);
+                            }
+                            // lane: features f0 + 4g + r of token 16I + c16
+                            f32x4 ph;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) ph[r] = silu_f32(u1[r]) * u3[r];
+                            u32x2 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])};
+                            *reinterpret_cast<u32x2*>(sQ + (16 * I + c16) * L::LQ + f0 + 4 * g) = pk;
+                        }
+                    }
+                    if (upd) {
+#pragma unroll
+                        for (int J = 0; J < NI; ++J) {
+                            f32x4 u1 = {0.f, 0.f, 0.f, 0.f}, u3 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int s = 0; s < NSK; ++s) {
+                                bf16x8 xb = as_bf16x8(lds_read16(sXk + (16 * J + c16) * L::LX + 32 * s + 8 * g));
+                                u1 = mfma16(w1f[a][s], xb, u1);
+                                u3 = mfma16(w3f[a][s], xb, u3);
+                            }
+                            f32x4 ph;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) ph[r] = silu_f32(u1[r]) * u3[r];
+                            if (KIND == K_OUTPUT) {
+                                u32x2 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])};
+                                *reinterpret_cast<u32x2*>(sK + (16 * J + c16) * L::LQ + f0 + 4 * g) = pk;
+                            }
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                sKt[(f0 + 4 * g + r) * L::LT + 16 * J + c16] = f32_to_bf16_bits(ph[r]);
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+
+            // ---- intra-chunk scores A = (P o Gamma) diag(eta), P = Phi_Q Phi_K^T --
+            if (KIND == K_OUTPUT) {
+                constexpr int NTILE = NI * (NI + 1) / 2;
+                for (int ti = wave; ti < NTILE; ti += NW) {
+                    int I = 0, rem = ti;
+                    while (rem > I) { rem -= I + 1; ++I; }
+                    const int J = rem;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        bf16x8 a = as_bf16x8(lds_read16(sK + (16 * J + c16) * L::LQ + 32 * s + 8 * g));
+                        bf16x8 b = as_bf16x8(lds_read16(sQ + (16 * I + c16) * L::LQ + 32 * s + 8 * g));
+                        acc = mfma16(a, b, acc);
+                    }
+                    // acc[r] = P[i = 16I + c16][j = 16J + 4g + r]
+                    const int i = 16 * I + c16;
+                    float val[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int j = 16 * J + 4 * g + r;
+                        val[r] = (j <= i && i < n) ? acc[r] * sC[max(i - j, 0)] * sEta[j] : 0.0f;
+                    }
+                    u32x2 pk = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+                    *reinterpret_cast<u32x2*>(sA + i * L::LT + 16 * J + 4 * g) = pk;
+                }
+            }
+
+            // ---- readout from the entry state: O^T = S Phi_Q^T (+ g o M Phi_Q^T) ---
+            f32x4 oacc[NI], yacc[MOM ? NI : 1];
+            if (readq) {
+                bf16x8 aS[NS], aM[MOM ? NS : 1];
+#pragma unroll
+                for (int s = 0; s < NS; ++s) aS[s] = pack8(S[2 * s], S[2 * s + 1]);
+                if constexpr (MOM && KIND == K_OUTPUT) {
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) aM[s] = pack8(M[2 * s], M[2 * s + 1]);
+                }
+#pragma unroll
+                for (int I = 0; I < NI; ++I) {
+                    oacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (MOM && KIND == K_OUTPUT) yacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const uint16_t* qrow = sQ + (16 * I + c16) * L::LQ + 4 * g;
+#pragma unroll
+                    for (int s = 0; s < NS; ++s) {
+                        bf16x8 b = join8(lds_read8(qrow + 32 * s), lds_read8(qrow + 32 * s + 16));
+                        oacc[I] = mfma16(aS[s], b, oacc[I]);
+                        if constexpr (MOM) {
+                            if (KIND == K_OUTPUT) yacc[I] = mfma16(aM[s], b, yacc[I]);
+                        }
+                    }
+                }
+            }
+            if (KIND == K_OUTPUT) __syncthreads();   // A tiles complete
+
+            // ---- intra-chunk contribution, combine, store ------------------------
+            if (readq) {
+#pragma unroll
+                for (int I = 0; I < NI; ++I) {
+                    if (KIND == K_OUTPUT) {
+#pragma unroll
+                        for (int t = 0; t <= I / 2; ++t) {
+                            bf16x8 a = as_bf16x8(lds_read16(sVt + (dvw + c16) * L::LT + 32 * t + 8 * g));
+                            bf16x8 b = as_bf16x8(lds_read16(sA + (16 * I + c16) * L::LT + 32 * t + 8 * g));
+                            oacc[I] = mfma16(a, b, oacc[I]);
+                        }
+                    }
+                    const int i = 16 * I + c16;
+                    f32x4 o = oacc[I];
+                    if constexpr (MOM) {
+                        if (KIND == K_OUTPUT) {
+                            const float gi = beta * sC[i];
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) o[r] = fmaf(gi, yacc[I][r], o[r]);
+                        }
+                    }
+                    if (i < n) {
+                        const size_t orow = row0 + i;
+                        const int col = dv_base + dvw + 4 * g;
+                        if (p.phi_split == 1) {
+                            u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                            *reinterpret_cast<u32x2*>(p.o + orow * p.d_v + col) = pk;
+                        } else {
+                            float* dst = p.o_partial + ((size_t)fs * p.n_rows + orow) * p.d_v + col;
+                            *reinterpret_cast<f32x4*>(dst) = o;
+                        }
+                    }
+                }
+            }
+
+            // ---- state update --------------------------------------------------
+            if (upd) {
+                if constexpr (MOM) {
+                    const float gl = beta * sC[n - 1];   // g_{n-1}
+                    const float bn = sBP[n];             // beta^n
+#pragma unroll
+                    for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            S[ft][r] = fmaf(gl, M[ft][r], S[ft][r]);
+                            M[ft][r] *= bn;
+                        }
+                }
+#pragma unroll
+                for (int t = 0; t < NJS; ++t) {
+                    const u32x4 raw = lds_read16(sVt + (dvw + c16) * L::LT + 32 * t + 8 * g);
+                    float ws[8], wm[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) ws[e] = sWS[32 * t + 8 * g + e];
+                    const bf16x8 bS = scale8(raw, ws);
+                    bf16x8 bM;
+                    if constexpr (MOM) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) wm[e] = sWM[32 * t + 8 * g + e];
+                        bM = scale8(raw, wm);
+                    }
+#pragma unroll
+                    for (int ft = 0; ft < NFT; ++ft) {
+                        bf16x8 a = as_bf16x8(lds_read16(sKt + (16 * ft + c16) * L::LT + 32 * t + 8 * g));
+                        S[ft] = mfma16(a, bS, S[ft]);
+                        if constexpr (MOM) M[ft] = mfma16(a, bM, M[ft]);
+                    }
+                }
+            }
+        }
+    }
+
+    if (KIND == K_SUMMARY) {
+        const size_t slot = ((size_t)seq * (p.seg_count - 1) + seg) * slice_units + (size_t)fs * p.dv_split + vs;
+        f32x4* dst = reinterpret_cast<f32x4*>(p.state) + slot * slot_stride;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft) dst[((size_t)wave * NFT + ft) * 64 + lane] = S[ft];
+        if constexpr (MOM) {
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) dst[SLICE_F4 + ((size_t)wave * NFT + ft) * 64 + lane] = M[ft];
+        }
+    }
+}
+
+// Composes segment summaries into entry states, in place:
+//   (S, M) <- (S + G M + dS_p, beta^L M + dM_p),  slot p <- (S, M) = entry of segment p + 1
+// G = sum_{r=1..L} beta^r, L = segment length.  Slots are [seq][step][slice] and
+// hold S then M (slice_f4 float4s each).  One thread per float4 of a slice.
+__global__ void segment_scan(float* state, size_t n_threads, int n_slices, int n_steps, int slice_f4, float G,
+                             float bL, int mom) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_threads) return;
+    const size_t e_per_seq = (size_t)n_slices * slice_f4;
+    const size_t seqi = idx / e_per_seq;
+    const size_t within = idx % e_per_seq;
+    const size_t sl = within / slice_f4, e = within % slice_f4;
+    f32x4* base = reinterpret_cast<f32x4*>(state);
+    f32x4 S = {0.f, 0.f, 0.f, 0.f}, M = {0.f, 0.f, 0.f, 0.f};
+    for (int step = 0; step < n_steps; ++step) {
+        const size_t slot = (seqi * n_steps + step) * n_slices + sl;
+        f32x4* ps = base + slot * 2 * slice_f4 + e;
+        const f32x4 dS = ps[0];
+        if (mom) {
+            const f32x4 dM = ps[slice_f4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                S[r] = fmaf(G, M[r], S[r]) + dS[r];
+                M[r] = fmaf(bL, M[r], dM[r]);
+            }
+            ps[0] = S;
+            ps[slice_f4] = M;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[r] += dS[r];
+            ps[0] = S;
+        }
+    }
+}
+
+// o[row][c] = bf16( sum_{s < n_split} partial[s][row][c] ), fixed order
+__global__ void partial_reduce(const float* partial, uint16_t* o, size_t n_elem4, int n_split) {
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= n_elem4) return;
+    const f32x4* src = reinterpret_cast<const f32x4*>(partial);
+    f32x4 acc = src[idx];
+    for (int s = 1; s < n_split; ++s) {
+        f32x4 x = src[(size_t)s * n_elem4 + idx];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] += x[r];
+    }
+    u32x2 pk = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    reinterpret_cast<u32x2*>(o)[idx] = pk;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// plan and launches
+// ---------------------------------------------------------------------------
+
+bool fast_supported(const Shape& s, int chunk) {
+    if (!s.bf16) return false;
+    if (s.d_k != 64 && s.d_k != 128) return false;
+    if (s.d_v != 64 && s.d_v != 128) return false;
+    if (s.swiglu) {
+        if (s.d_phi % 128 != 0 || s.d_phi > 512) return false;
+    } else if (s.d_phi != s.d_k) {
+        return false;
+    }
+    return chunk == 0 || chunk == 64 || chunk == 128;
+}
+
+FastPlan fast_plan(const Shape& s, int chunk, int segments) {
+    FastPlan p{};
+    // the chunk length is a tiling choice; SwiGLU tiles of 128 tokens do not fit in LDS
+    p.chunk = (chunk == 128 && !s.swiglu) ? 128 : 64;
+    p.phi_split = s.swiglu ? s.d_phi / 128 : 1;
+    p.nwaves = (s.swiglu && s.d_v == 128) ? 8 : 4;
+    p.dv_split = s.d_v / (16 * p.nwaves);
+    const int D = s.swiglu ? 128 : s.d_k;
+    const int n_chunks = (s.T + p.chunk - 1) / p.chunk;
+    const long base = (long)s.n_seq() * p.phi_split * p.dv_split;
+    int S = 1;
+    if (segments > 0) {
+        S = std::min(segments, n_chunks);
+    } else {
+        // aim for two resident workgroups per CU on 256 CUs, segments >= 4 chunks
+        const bool two_per_cu = p.nwaves == 8 || p.chunk == 64;
+        const long target = two_per_cu ? 512 : 256;
+        while (base * S < target && n_chunks >= 8 * S) S *= 2;
+    }
+    const int seg_chunks = (n_chunks + S - 1) / S;
+    p.seg_len = seg_chunks * p.chunk;
+    p.segments = (n_chunks + seg_chunks - 1) / seg_chunks;
+    const size_t slice_floats = (size_t)p.nwaves * (D / 16) * 64 * 4;
+    p.summary_bytes = p.segments > 1
+        ? (size_t)s.n_seq() * (p.segments - 1) * p.phi_split * p.dv_split * slice_floats * 2 * sizeof(float)
+        : 0;
+    p.partial_bytes = p.phi_split > 1 ? (size_t)p.phi_split * s.n_seq() * s.T * s.d_v * sizeof(float) : 0;
+    return p;
+}
+
+namespace {
+
+template <int C, int D, int DK, int NW, bool MOM, bool SW, int KIND>
+hipError_t launch_one(const ChunkParams& cp, hipStream_t st) {
+    const int grid = (cp.n_units + 7) / 8 * 8;
+    hipLaunchKernelGGL((chunk_kernel<C, D, DK, NW, MOM, SW, KIND>), dim3(grid), dim3(NW * 64), 0, st, cp);
+    return hipGetLastError();
+}
+
+template <int C, int D, int DK, int NW, bool SW>
+hipError_t launch_kind(int kind, bool mom, const ChunkParams& cp, hipStream_t st) {
+    if (mom) {
+        if (kind == K_OUTPUT) return launch_one<C, D, DK, NW, true, SW, K_OUTPUT>(cp, st);
+        if (kind == K_SUMMARY) return launch_one<C, D, DK, NW, true, SW, K_SUMMARY>(cp, st);
+        return launch_one<C, D, DK, NW, true, SW, K_BIDIR>(cp, st);
+    }
+    if (kind == K_OUTPUT) return launch_one<C, D, DK, NW, false, SW, K_OUTPUT>(cp, st);
+    if (kind == K_SUMMARY) return launch_one<C, D, DK, NW, false, SW, K_SUMMARY>(cp, st);
+    return launch_one<C, D, DK, NW, false, SW, K_BIDIR>(cp, st);
+}
+
+hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, const ChunkParams& cp,
+                        hipStream_t st) {
+    if (!s.swiglu) {
+        if (p.chunk == 64) {
+            if (s.d_k == 128) return launch_kind<64, 128, 128, 4, false>(kind, mom, cp, st);
+            return launch_kind<64, 64, 64, 4, false>(kind, mom, cp, st);
+        }
+        if (s.d_k == 128) return launch_kind<128, 128, 128, 4, false>(kind, mom, cp, st);
+        return launch_kind<128, 64, 64, 4, false>(kind, mom, cp, st);
+    }
+    if (p.nwaves == 8) {
+        if (s.d_k == 128) return launch_kind<64, 128, 128, 8, true>(kind, mom, cp, st);
+        return launch_kind<64, 128, 64, 8, true>(kind, mom, cp, st);
+    }
+    if (s.d_k == 128) return launch_kind<64, 128, 128, 4, true>(kind, mom, cp, st);
+    return launch_kind<64, 128, 64, 4, true>(kind, mom, cp, st);
+}
+
+}  // namespace
+
+hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
+                       hipEvent_t ev_end, int* n_kernels) {
+    ChunkParams cp{};
+    cp.q = static_cast<const uint16_t*>(a.q);
+    cp.k = static_cast<const uint16_t*>(a.k);
+    cp.v = static_cast<const uint16_t*>(a.v);
+    cp.eta = a.eta;
+    cp.w1 = static_cast<const uint16_t*>(s.w1);
+    cp.w3 = static_cast<const uint16_t*>(s.w3);
+    cp.o = static_cast<uint16_t*>(a.o);
+    cp.state = static_cast<float*>(workspace);
+    cp.o_partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.summary_bytes);
+    cp.eta_scalar = a.eta_scalar;
+    cp.beta = a.beta;
+    cp.eta_kind = a.eta_kind;
+    cp.T = s.T;
+    cp.H = s.H;
+    cp.d_k = s.d_k;
+    cp.d_v = s.d_v;
+    cp.d_phi = s.d_phi;
+    cp.dv_split = p.dv_split;
+    cp.phi_split = p.phi_split;
+    cp.n_rows = (size_t)s.n_seq() * s.T;
+    const bool mom = a.beta != 0.0f;
+    const int slice_units = p.phi_split * p.dv_split;
+    hipStream_t st = a.stream;
+    int nk = 0;
+    hipError_t e = hipSuccess;
+
+    if (a.bidirectional) {
+        cp.seg_count = 1;
+        cp.seg_len = s.T;
+        cp.n_units = s.n_seq() * slice_units;
+        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+        if ((e = launch_chunk(s, p, K_BIDIR, mom, cp, st)) != hipSuccess) return e;
+        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        ++nk;
+    } else {
+        cp.seg_count = p.segments;
+        cp.seg_len = p.seg_len;
+        if (p.segments > 1) {
+            cp.n_units = s.n_seq() * (p.segments - 1) * slice_units;
+            if ((e = launch_chunk(s, p, K_SUMMARY, mom, cp, st)) != hipSuccess) return e;
+            ++nk;
+            const int D = s.swiglu ? 128 : s.d_k;
+            const int slice_f4 = p.nwaves * (D / 16) * 64;
+            const size_t n_threads = (size_t)s.n_seq() * slice_units * slice_f4;
+            double G = 0.0, bL = 1.0;     // G = sum_{r=1..L} beta^r, bL = beta^L
+            for (int r = 0; r < p.seg_len; ++r) {
+                bL *= (double)a.beta;
+                G += bL;
+            }
+            hipLaunchKernelGGL(segment_scan, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
+                               cp.state, n_threads, slice_units, p.segments - 1, slice_f4, (float)G, (float)bL,
+                               mom ? 1 : 0);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+            ++nk;
+        }
+        cp.n_units = s.n_seq() * p.segments * slice_units;
+        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+        if ((e = launch_chunk(s, p, K_OUTPUT, mom, cp, st)) != hipSuccess) return e;
+        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        ++nk;
+    }
+    if (p.phi_split > 1) {
+        const size_t n4 = (size_t)s.n_seq() * s.T * s.d_v / 4;
+        hipLaunchKernelGGL(partial_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, cp.o_partial,
+                           static_cast<uint16_t*>(a.o), n4, p.phi_split);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        ++nk;
+    }
+    if (n_kernels) *n_kernels = nk;
+    return hipSuccess;
 }
 
 }  // namespace ttt
