@@ -1,0 +1,283 @@
+#!/usr/bin/env python3
+"""Throughput of the TTT-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one full forward of the layer (every kernel of the chunked path:
+segment summaries, segment scan, output pass) over one batch of seeded
+synthetic q, k, v already resident in HBM.  The default workload is the
+momentum variant at B=4, H=8, T=2048, d=128, bf16 (Variant 4 of the ablation
+on the thelatestinai.com page, Table 2).  Input sets are rotated so that the
+working set of the timed loop exceeds the 256 MB last-level cache.
+
+Prints one JSON line with tokens/s (tokens = B*T positions), the roofline
+fraction of the dominant kernel (its duration measured with HIP events on the
+stream it runs on, during the timed loop) and the CPU oracle's tokens/s on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TTT-layer fwd tokens/sec (1 GPU) + % MFMA/HBM roofline, Variants 2–5"
+DEFAULT_WORKLOAD = "v4_momentum_4x8x2048_d128"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16, 256 CU x 2.4 GHz x 4096 flop/clk
+MALL_BYTES = 256 * 2 ** 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "ttt_weight_layers_amd", "csrc", "chunk_mfma.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a device copy of MIB mebibytes (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def algorithmic_bytes_per_ht(w) -> int:
+    """q, k, v read once and o written once (+ 4 B of per-token eta / logits)."""
+    e = 4 if w.dtype == "f32" else 2
+    b = (2 * w.d_k + w.d_v) * e + w.d_v * e
+    if w.eta_mode != "scalar":
+        b += 4
+    return b
+
+
+def algorithmic_flops_per_ht(w, chunk: int) -> int:
+    """Causal intra-chunk triangle + state readout and update (x2 with momentum)
+    + SwiGLU feature map for q and k."""
+    if not w.causal:
+        return 4 * w.d_phi * w.d_v
+    f = (chunk + 1) * (w.d_phi + w.d_v) + 4 * w.d_phi * w.d_v * (2 if w.beta != 0.0 else 1)
+    if w.phi == "swiglu":
+        f += 8 * w.d_k * w.d_phi
+    return f
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.dirname(KERNEL_SOURCE))):
+        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the output kernel from the committed counter runs,
+    or None if they were taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, seconds: float):
+    """Times the fp64 oracle on a bounded sample: a few heads at full length."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    # one head first to size the sample
+    with threadpool_limits(limits=1):
+        def run(heads):
+            bs = [h // w.H for h in heads]
+            hs = [h % w.H for h in heads]
+            q = x.q64[bs, hs][:, None]
+            k = x.k64[bs, hs][:, None]
+            v = x.v64[bs, hs][:, None]
+            a = None if x.a32 is None else x.a32[bs, hs][:, None]
+            t0 = time.perf_counter()
+            if w.phi == "swiglu":
+                outs = [oracle.forward(q[i:i + 1], k[i:i + 1], v[i:i + 1], eta_mode=w.eta_mode,
+                                       eta=None if a is None else a[i:i + 1], eta_scalar=w.eta_scalar,
+                                       beta=w.beta, causal=w.causal, phi=w.phi,
+                                       w1=x.w1_64[h:h + 1], w3=x.w3_64[h:h + 1])
+                        for i, h in enumerate(hs)]
+                o = np.concatenate(outs)
+            else:
+                o = oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar,
+                                   beta=w.beta, causal=w.causal)
+            return o, time.perf_counter() - t0
+
+        n_heads = w.B * w.H
+        _, t1 = run([0])
+        n = int(max(1, min(n_heads, seconds / max(t1, 1e-3))))
+        heads = list(range(n))
+        o, dt = run(heads)
+    head_tokens_per_s = n * w.T / dt
+    return {
+        "value": head_tokens_per_s / w.H,          # tokens = positions, all heads
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{n} of {n_heads} (b,h) sequences at full T={w.T}, fp64 numpy recurrence, "
+                  f"{dt:.1f} s; head-tokens/s={head_tokens_per_s:.4g}",
+    }, o, heads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the layer shards over (b, h) with no communication; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ttt_weight_layers_amd as tla
+    from ttt_workloads import WORKLOADS, make_inputs, bf16_bits_to_f64
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
+
+    tla.load_library()
+    w = WORKLOADS[args.workload]
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).to(dev)
+
+    q0, k0, v0 = up(x.q_dev), up(x.k_dev), up(x.v_dev)
+    a0 = torch.from_numpy(x.a32).to(dev) if x.a32 is not None else None
+    w1 = up(x.w1_dev) if x.w1_dev is not None else None
+    w3 = up(x.w3_dev) if x.w3_dev is not None else None
+    bpht = algorithmic_bytes_per_ht(w)
+    set_bytes = w.head_tokens * bpht
+    n_sets = max(1, min(16, -(-2 * MALL_BYTES // set_bytes)))
+    sets = []
+    for i in range(n_sets):
+        s = dict(q=q0 if i == 0 else q0.clone(), k=k0 if i == 0 else k0.clone(),
+                 v=v0 if i == 0 else v0.clone(), a=None if a0 is None else (a0 if i == 0 else a0.clone()),
+                 o=torch.empty_like(v0))
+        sets.append(s)
+
+    layer = tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi,
+                                   chunk=w.chunk, w1=w1, w3=w3)
+    plan = layer.plan()
+    stream = torch.cuda.current_stream()
+    mode = tla.mode_bits(w.eta_mode, w.causal)
+
+    def step(i):
+        s = sets[i % n_sets]
+        st = tla.ttt_la_forward(layer.handle, s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(),
+                                None if s["a"] is None else s["a"].data_ptr(), w.eta_scalar, w.beta, mode,
+                                s["o"].data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise tla.TTTError(st, "ttt_la_forward")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed loop; HIP events around the output kernel inside every forward
+    if tla.ttt_la_enable_kernel_timing(layer.handle, args.steps) != 0:
+        raise RuntimeError("could not create timing events")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    kernel_ms = tla.ttt_la_kernel_times(layer.handle, args.steps)
+    tla.ttt_la_enable_kernel_timing(layer.handle, 0)
+    ms_per_step = total_ms / args.steps
+    tokens_per_s = w.tokens / (ms_per_step * 1e-3)
+    k_avg_ms = float(np.mean(kernel_ms)) if kernel_ms else float("nan")
+
+    flops_ht = algorithmic_flops_per_ht(w, plan.chunk)
+    ai = flops_ht / bpht
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        achieved = w.head_tokens * bpht / (k_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    else:
+        achieved = w.head_tokens * flops_ht / (k_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(w.name)
+    roof["kernel"] = "chunk_kernel<OUTPUT>"
+    roof["kernel_ms"] = round(k_avg_ms, 5)
+
+    # parity of the first input set's output against the oracle on the sampled heads
+    cpu = None
+    check = None
+    if not args.no_cpu_baseline:
+        # the last forward on set 0 is complete after the synchronize above
+        step(0)
+        torch.cuda.synchronize()
+        o_gpu = sets[0]["o"]
+        got = (bf16_bits_to_f64(o_gpu.view(torch.int16).cpu().numpy().view(np.uint16))
+               if w.dtype == "bf16" else o_gpu.cpu().numpy().astype(np.float64))
+        cpu, o_ref, heads = cpu_baseline(w, x, args.cpu_seconds)
+        import oracle
+        sel = got[[h // w.H for h in heads], [h % w.H for h in heads]][:, None]
+        check = {"rel_err_vs_oracle": float(f"{oracle.rel_err(sel, o_ref):.3e}"), "heads": len(heads)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "d_phi": w.d_phi,
+            "phi": w.phi, "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar, "beta": w.beta,
+            "causal": w.causal, "chunk": plan.chunk, "segments": plan.segments, "dv_split": plan.dv_split,
+            "phi_split": plan.phi_split, "kernels_per_step": plan.n_kernels, "input_sets": n_sets,
+            "head_tokens_per_s": round(w.head_tokens / (ms_per_step * 1e-3), 1),
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if check is not None:
+        out["check"] = check
+    print(json.dumps(out), flush=True)
+    layer.close()
+
+
+if __name__ == "__main__":
+    main()

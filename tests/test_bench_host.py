@@ -1,0 +1,36 @@
+"""Host-side pieces of bench.py (no GPU)."""
+import os
+import subprocess
+import sys
+
+import bench
+from ttt_workloads import WORKLOADS, make_inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_and_flops():
+    w = WORKLOADS["v4_momentum_4x8x2048_d128"]
+    assert bench.algorithmic_bytes_per_ht(w) == 1024
+    assert bench.algorithmic_flops_per_ht(w, 64) == 65 * 256 + 4 * 128 * 128 * 2
+    w3 = WORKLOADS["v3_softplus_8x16x4096_d128"]
+    assert bench.algorithmic_bytes_per_ht(w3) == 1028
+    w2 = WORKLOADS["v2_swiglu_4x16x8192_d128_f512"]
+    assert bench.algorithmic_flops_per_ht(w2, 64) == 65 * 640 + 4 * 512 * 128 * 2 + 8 * 128 * 512
+    wb = WORKLOADS["bidir_vit_256x6x196_d64"]
+    assert bench.algorithmic_flops_per_ht(wb, 64) == 4 * 64 * 64
+
+
+def test_cpu_baseline_on_a_small_sample():
+    w = WORKLOADS["v4_momentum_4x8x2048_d128"].with_shape(B=1, H=2, T=64)
+    x = make_inputs(w)
+    cpu, o, heads = bench.cpu_baseline(w, x, seconds=0.2)
+    assert cpu["kind"] == "oracle" and cpu["cores"] == 1 and cpu["value"] > 0
+    assert o.shape == (len(heads), 1, 64, 128)
