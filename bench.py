@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--segments", type=int, default=0, help="plan override: sequence segments (0 = auto)")
+    ap.add_argument("--value-split", type=int, default=0, help="plan override: workgroups per value width")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -185,7 +187,8 @@ def main():
         sets.append(s)
 
     layer = tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi,
-                                   chunk=w.chunk, w1=w1, w3=w3)
+                                   chunk=w.chunk, segments=args.segments, w1=w1, w3=w3,
+                                   value_split=args.value_split)
     plan = layer.plan()
     stream = torch.cuda.current_stream()
     mode = tla.mode_bits(w.eta_mode, w.causal)

@@ -84,6 +84,8 @@ typedef struct {
                                   the result only by rounding */
     int32_t segments;          /* sequence segments scanned in parallel: 0 = auto, else >= 1 (bf16 causal);
                                   changes the result only by rounding */
+    int32_t value_split;       /* workgroups sharing one segment's value columns: 0 = auto, 1 or 2
+                                  (2 is used for d_k = d_v = 128 with the identity map); tiling only */
     const void* w1;            /* SWIGLU: device [H, d_phi, d_k] (out x in) in dtype; else NULL */
     const void* w3;            /* SWIGLU: device [H, d_phi, d_k] in dtype; else NULL */
 } ttt_la_desc;

@@ -42,18 +42,18 @@ def from_device(t, dtype: str) -> np.ndarray:
     return t.cpu().numpy().astype(np.float64)
 
 
-def make_layer(w: Workload, d, chunk=None, segments=0):
+def make_layer(w: Workload, d, chunk=None, segments=0, value_split=0):
     import ttt_weight_layers_amd as tla
     return tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi,
                                   chunk=w.chunk if chunk is None else chunk, segments=segments,
-                                  w1=d["w1"], w3=d["w3"])
+                                  w1=d["w1"], w3=d["w3"], value_split=value_split)
 
 
 def run_gpu(w: Workload, d, chunk=None, segments=0, eta_sign=1.0, q_override=None, v_scale=None,
-            layer=None):
+            layer=None, value_split=0):
     """Runs the library once on device tensors d; returns o as fp64 numpy."""
     torch = torch_mod()
-    lay = layer or make_layer(w, d, chunk, segments)
+    lay = layer or make_layer(w, d, chunk, segments, value_split)
     eta = None
     eta_scalar = w.eta_scalar * eta_sign
     if w.eta_mode != "scalar":

@@ -137,13 +137,14 @@ def test_swiglu_small_feature_width_and_bidirectional():
 
 @pytest.mark.parametrize("chunk", [64, 128])
 @pytest.mark.parametrize("segments", [1, 2, 3, 5])
-def test_tiling_does_not_change_the_result(chunk, segments):
-    # chunk and segment count are tiling choices: results agree with the oracle
+@pytest.mark.parametrize("value_split", [1, 2])
+def test_tiling_does_not_change_the_result(chunk, segments, value_split):
+    # chunk, segment count and value split are tiling choices: results agree with the oracle
     w = small("v3_long_1x16x65536_d128", B=1, H=2, T=1000)
-    say(f"[tiling] chunk={chunk} segments={segments}")
+    say(f"[tiling] chunk={chunk} segments={segments} value_split={value_split}")
     x = make_inputs(w)
     d = to_device(x)
-    got = run_gpu(w, d, chunk=chunk, segments=segments)
+    got = run_gpu(w, d, chunk=chunk, segments=segments, value_split=value_split)
     assert oracle.rel_err(got, run_oracle(w, x)) <= TOL[w.dtype]
 
 

@@ -38,7 +38,7 @@ class ttt_la_desc(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("d_phi", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("phi", ctypes.c_int32), ("chunk", ctypes.c_int32),
-        ("segments", ctypes.c_int32),
+        ("segments", ctypes.c_int32), ("value_split", ctypes.c_int32),
         ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p),
     ]
 
@@ -153,7 +153,7 @@ _ETA = {"scalar": TTT_LA_ETA_SCALAR, "per_token": TTT_LA_ETA_PER_TOKEN, "softplu
 
 
 def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0, segments=0,
-              w1=None, w3=None) -> ttt_la_desc:
+              w1=None, w3=None, value_split=0) -> ttt_la_desc:
     d = ttt_la_desc()
     d.B, d.H, d.T, d.d_k, d.d_v = int(B), int(H), int(T), int(d_k), int(d_v)
     d.d_phi = int(d_k if d_phi is None else d_phi)
@@ -161,6 +161,7 @@ def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk
     d.phi = _PHIS[phi]
     d.chunk = int(chunk)
     d.segments = int(segments)
+    d.value_split = int(value_split)
     d.w1 = _ptr(w1)
     d.w3 = _ptr(w3)
     return d
@@ -186,9 +187,9 @@ class TTTLinearAttention:
     """
 
     def __init__(self, B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0,
-                 segments=0, w1=None, w3=None):
+                 segments=0, w1=None, w3=None, value_split=0):
         self._keep = (w1, w3)         # W1/W3 are borrowed by the handle
-        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, segments, w1, w3)
+        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, segments, w1, w3, value_split)
         self.dtype = dtype
         st, h = ttt_la_create(self.desc)
         if st != TTT_LA_OK:

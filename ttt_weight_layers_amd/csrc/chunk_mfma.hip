@@ -15,25 +15,46 @@
 // per-token learning rate, momentum and SwiGLU feature map are the inner-loop
 // options of Table 2 on the thelatestinai.com page (Variants 2-4).
 //
-// Kernels (all bf16 MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation):
+// Carried state.  Instead of (S, M) the kernels carry (T, M) with
+// T = S + kappa M, kappa = beta / (1 - beta).  Substituting into the chunk step
+// above gives
+//   T <- T + (1 / (1 - beta)) sum_j eta_j v_j phi(k_j)^T           (no decay)
+//   M <- beta^n M + sum_j eta_j beta^{n-1-j} v_j phi(k_j)^T
+//   o_i = T phi(q_i) - (beta^{i+2} / (1 - beta)) M phi(q_i) + intra-chunk part
+// so T is a plain accumulation: it needs no per-chunk transition and, for a
+// scalar step size, no per-token weights (T is kept as sum_j v_j phi(k_j)^T
+// and scaled by eta / (1 - beta) when read).  S = T - kappa M is formed only
+// where the bidirectional readout needs it.  beta = 0 gives T = S, no M.
+//
+// Kernels (bf16 MFMA v_mfma_f32_16x16x32_bf16, fp32 accumulation and state):
 //   chunk_kernel<OUTPUT>   one workgroup per (sequence, segment, feature slice,
 //                          value slice); walks its segment chunk by chunk, keeps
 //                          its slice of (S, M) in registers, writes o.
-//   chunk_kernel<SUMMARY>  same walk without readout: the zero-entry state change
-//                          of every segment but the last (segment summaries).
-//   segment_scan           composes the summaries into each segment's entry state.
+//   chunk_kernel<SUMMARY>  the same walk without readout: the zero-entry state
+//                          change of every segment but the last.
+//   segment_scan           composes those summaries into entry states.
 //   chunk_kernel<BIDIR>    bidirectional: all updates, then every query reads S_T.
 //   partial_reduce         sums fp32 partial outputs of feature slices (SwiGLU).
+//
+// Staging.  Every chunk's q, k (or raw SwiGLU inputs) and v rows are fetched
+// with 16-byte global loads into registers one chunk ahead, then written to
+// row-major LDS tiles whose 16-byte chunks are XOR-swizzled per row, so that
+// both row reads (16 B per lane) and gfx950 transpose reads (ds_read_b64_tr_b16,
+// 4 rows x 16 columns per 16-lane group) avoid bank conflicts.  Operands whose
+// contraction runs over tokens (K^T, V^T) come from the transpose read; no
+// transposed copy is stored.
 //
 // Register layouts (lane l of a 64-wide wave, c16 = l % 16, g = l / 16):
 //   MFMA A operand  lane holds A[m = c16][k = 8g .. 8g+7]
 //   MFMA B operand  lane holds B[k = 8g .. 8g+7][n = c16]
 //   MFMA D result   lane holds D[m = 4g .. 4g+3][n = c16]
-// The state is kept transposed, S^T[f][dv], as D tiles: lane holds
-// S^T[16ft + 4g + r][dv0 + c16].  Two such tiles (ft = 2s, 2s+1) form, without
-// any data movement, the A operand of O^T = S Q^T over the permuted contraction
-// set {32s + 4g + r} u {32s + 16 + 4g + r}; the B operand then reads Q with the
-// same permutation (two 8-byte LDS reads).
+// The state is kept transposed, S^T[f][dv], as D tiles.  Tile ft covers the
+// features 32(ft/2) + 8a + 4(ft%2) + b (a, b = 0..3), so lane (g, c16) holds
+// S^T[32(ft/2) + 8g + 4(ft%2) + r][dv0 + c16]: the two tiles ft = 2s, 2s+1
+// together give each lane 8 consecutive features 32s + 8g .. +7, i.e. without
+// any data movement the A operand of O^T = S Q^T whose B operand is one
+// 16-byte row read of Q.  The update builds the tiles in that order by pointing
+// the transpose reads of K at the matching column groups.
 
 #include <algorithm>
 #include <cmath>
@@ -41,10 +62,14 @@
 #include "device_common.h"
 #include "internal.h"
 
+#define TTT_LDS __attribute__((address_space(3)))
+
 namespace ttt {
 namespace {
 
 enum Kind : int { K_OUTPUT = 0, K_SUMMARY = 1, K_BIDIR = 2 };
+
+constexpr int CH = 64;   // tokens per chunk
 
 struct ChunkParams {
     const uint16_t* q;
@@ -65,26 +90,25 @@ struct ChunkParams {
     size_t n_rows;       // B * H * T
 };
 
-constexpr int PAD = 8;  // bf16 elements of padding per LDS row (16 bytes)
-
-template <int C, int D, int DK, int NW, bool SWIGLU>
-struct Lds {
-    static constexpr int DVWG = 16 * NW;
-    static constexpr int LQ = D + PAD;      // sQ, sK row stride
-    static constexpr int LT = C + PAD;      // sKt, sVt, sA row stride
-    static constexpr int LX = DK + PAD;     // SwiGLU raw staging stride
-    static constexpr int OFF_Q = 0;
-    static constexpr int OFF_K = OFF_Q + C * LQ;
-    static constexpr int OFF_KT = OFF_K + C * LQ;
-    static constexpr int OFF_VT = OFF_KT + D * LT;
-    static constexpr int OFF_A = OFF_VT + DVWG * LT;
-    static constexpr int OFF_XQ = OFF_A + C * LT;
-    static constexpr int OFF_XK = OFF_XQ + (SWIGLU ? C * LX : 0);
-    static constexpr int N_BF16 = OFF_XK + (SWIGLU ? C * LX : 0);
-    // floats after the bf16 area: eta, wS, wM (C each), c (C + 1), beta^r (C + 1)
-    static constexpr int N_F32 = 5 * C + 2;
-    static constexpr int BYTES = N_BF16 * 2 + N_F32 * 4;
-};
+// Element offset of (row, col) in a row-major tile of W bf16 columns whose
+// 16-byte chunks are permuted per row: chunk c of row r is stored at c ^ f(r).
+// f is a bijection over 16 consecutive rows (so 16 lanes reading one chunk of
+// 16 rows hit 16 different bank groups) whose high bits follow the row within
+// a group of 4 (so the 4 rows of a transpose read, each read at up to 4
+// chunks, never share a bank).  W is 64 or 128; col may point inside a chunk.
+template <int W>
+__device__ __forceinline__ int swz(int row, int col) {
+    constexpr int NCH = W / 8;
+    static_assert(NCH == 8 || NCH == 16, "tile width");
+    int f;
+    if constexpr (NCH == 16) {
+        f = 4 * (row & 3) + ((row >> 2) & 3);
+    } else {          // two rows per 64 banks
+        const int h = row >> 1;
+        f = 4 * (h & 1) + ((h >> 1) & 3);
+    }
+    return row * W + (((col >> 3) ^ f) << 3) + (col & 7);
+}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -99,6 +123,26 @@ __device__ __forceinline__ u32x2 lds_read8(const uint16_t* p) { return *reinterp
 __device__ __forceinline__ bf16x8 join8(const u32x2& a, const u32x2& b) {
     u32x4 u = {a[0], a[1], b[0], b[1]};
     return as_bf16x8(u);
+}
+
+// Transpose read of a swizzled W-wide tile.  Lane L = 4e + q of each 16-lane
+// group points at row r0 + e, columns col(q) .. col(q) + 3; lane i of the group
+// receives rows r0 .. r0+3 of column col(i / 4) + i % 4.
+template <int W>
+__device__ __forceinline__ u32x2 tr_read(const uint16_t* tile, int r0, int col_q) {
+    const int L = threadIdx.x & 15;
+    const uint16_t* p = tile + swz<W>(r0 + (L >> 2), col_q);
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TTT_LDS bf16x4_t*)(p));
+    return __builtin_bit_cast(u32x2, x);
+}
+
+// 8 consecutive tokens (r0 .. r0+7) as one MFMA operand; see tr_read for col_q
+template <int W>
+__device__ __forceinline__ u32x4 tr_read8(const uint16_t* tile, int r0, int col_q) {
+    const u32x2 a = tr_read<W>(tile, r0, col_q);
+    const u32x2 b = tr_read<W>(tile, r0 + 4, col_q);
+    return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // bf16x8 built from two D tiles (4 floats each): elements 0..3 from x, 4..7 from y
@@ -120,30 +164,7 @@ __device__ __forceinline__ bf16x8 scale8(const u32x4& raw, const float* w) {
     return as_bf16x8(u);
 }
 
-// 8 rows x 8 bf16 block held as 8 x u32x4 (row r, dword p = columns 2p, 2p+1)
-// -> column cc as u32x4 (dword p = rows 2p, 2p+1)
-__device__ __forceinline__ u32x4 block_column(const u32x4 (&r)[8], int cc) {
-    const int p = cc >> 1;
-    u32x4 out;
-    if ((cc & 1) == 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = (r[2 * q][p] & 0xffffu) | (r[2 * q + 1][p] << 16);
-    } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) out[q] = (r[2 * q][p] >> 16) | (r[2 * q + 1][p] & 0xffff0000u);
-    }
-    return out;
-}
-
-__device__ __forceinline__ void load_block(u32x4 (&r)[8], const uint16_t* base, size_t ld, int rows_valid) {
-#pragma unroll
-    for (int rr = 0; rr < 8; ++rr) {
-        if (rr < rows_valid) r[rr] = *reinterpret_cast<const u32x4*>(base + (size_t)rr * ld);
-        else r[rr] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-// Momentum coefficient tables by a wavefront prefix scan:
+// Momentum coefficient tables by a wavefront prefix scan (one wave):
 //   bp[r] = beta^r (prefix product), cc[r] = sum_{u<=r} beta^u (prefix sum), r = 0..C
 template <int C>
 __device__ void coefficient_scan(float beta, float* cc, float* bp) {
@@ -156,8 +177,7 @@ __device__ void coefficient_scan(float beta, float* cc, float* bp) {
             float o = __shfl_up(p, d, 64);
             if (lane >= d) p *= o;
         }
-        // p = beta^lane; prefix sum of p
-        float s = p;
+        float s = p;   // p = beta^lane; now the prefix sum of p
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             float o = __shfl_up(s, d, 64);
@@ -168,44 +188,72 @@ __device__ void coefficient_scan(float beta, float* cc, float* bp) {
             bp[r] = base_p * p;
             cc[r] = base_c + base_p * s;
         }
-        // carry into the next 64 entries: beta^(r0+64), c_{r0+63}
-        float p63 = __shfl(p, 63, 64), s63 = __shfl(s, 63, 64);
+        const float p63 = __shfl(p, 63, 64), s63 = __shfl(s, 63, 64);
         base_c = base_c + base_p * s63;
         base_p = base_p * p63 * beta;
     }
 }
 
-// waves per SIMD the kernel is compiled for: two workgroups of 4 waves (or one of
-// 8) when the LDS footprint allows two resident workgroups, else one of 4.
-template <int C, int D, int DK, int NW, bool SWIGLU>
-constexpr int waves_per_eu() {
-    return (NW == 8 || 2 * Lds<C, D, DK, NW, SWIGLU>::BYTES <= 160 * 1024) ? 2 : 1;
-}
+// LDS layout of one workgroup (bf16 elements, then floats).  The staged tiles
+// (q or raw q, k or raw k, v) and the score tiles are double-buffered so that
+// one barrier per chunk suffices: chunk c is written into buffer c & 1 while
+// other waves may still be finishing the deferred work of chunk c - 1.
+template <int D, int DK, int NW, bool SWIGLU>
+struct Lds {
+    static constexpr int DVWG = 16 * NW;                 // value columns of one workgroup
+    static constexpr int WX = SWIGLU ? DK : D;           // width of the staged q/k rows
+    static constexpr int TX = CH * WX, TV = CH * DVWG;
+    static constexpr int STAGE = 2 * TX + TV;            // one buffer: x_q, x_k, v
+    static constexpr int OFF_PHI = 2 * STAGE;            // SwiGLU features phi(q), phi(k): [CH][D] each
+    static constexpr int OFF_A = OFF_PHI + (SWIGLU ? 2 * CH * D : 0);   // 2 x [CH][CH] scores
+    static constexpr int N_BF16 = OFF_A + 2 * CH * CH;
+    // floats: 2 x (eta, eta/(1-beta), eta beta^{n-1-j}) [CH each], c[CH+1], beta^r[CH+1]
+    static constexpr int N_F32 = 6 * CH + 2 * (CH + 1);
+    static constexpr int BYTES = 2 * N_BF16 + 4 * N_F32;
+};
 
-template <int C, int D, int DK, int NW, bool MOM, bool SWIGLU, int KIND>
-__global__ void __launch_bounds__(NW * 64, (waves_per_eu<C, D, DK, NW, SWIGLU>()))
+// Global -> register prefetch of one chunk: each thread owns 16-byte pieces of
+// the x (q or raw q), y (k or raw k) and v tiles plus one eta value.
+template <int WX, int DVWG, int NT>
+struct Prefetch {
+    static constexpr int PX = CH * WX / 8 / NT;       // pieces of a q/k tile per thread
+    static constexpr int PV = CH * DVWG / 8 / NT;     // pieces of the v tile per thread
+    static_assert(PX * NT * 8 == CH * WX && PV * NT * 8 == CH * DVWG, "tile split");
+    u32x4 x[PX], y[PX], v[PV];
+    float eta;
+};
+
+// NW waves of 64 lanes; each wave owns DVT tiles of 16 value columns (and the
+// matching d_phi x 16 DVT slice of T and M in registers).  DV is the value
+// width of the layer; DV / (16 NW DVT) workgroups share one sequence segment.
+// ETAV: the step size varies per token (otherwise it is the scalar eta).
+template <int D, int DK, int DV, int NW, int DVT, bool MOM, bool ETAV, bool SWIGLU, int KIND>
+__global__ void __launch_bounds__(NW * 64, (NW == 4 && 2 * Lds<D, DK, NW, SWIGLU>::BYTES <= 160 * 1024) ? 2 : 1)
 chunk_kernel(ChunkParams p) {
-    using L = Lds<C, D, DK, NW, SWIGLU>;
+    static_assert(DVT == 1, "one 16-column value tile per wave");
+    using L = Lds<D, DK, NW, SWIGLU>;
     constexpr int NT = NW * 64;
     constexpr int DVWG = L::DVWG;
-    constexpr int NFT = D / 16;     // feature tiles of the state slice
-    constexpr int NS = D / 32;      // contraction steps over features
-    constexpr int NI = C / 16;      // token blocks per chunk
-    constexpr int NJS = C / 32;     // contraction steps over tokens
+    constexpr int WX = L::WX;
+    constexpr int NFT = D / 16;           // feature tiles of the state slice
+    constexpr int NS = D / 32;            // contraction steps over features
+    constexpr int NI = CH / 16;           // token blocks per chunk
+    constexpr int NJS = CH / 32;          // contraction steps over tokens
 
     __shared__ __attribute__((aligned(16))) uint16_t smem16[L::N_BF16 + 2 * L::N_F32];
-    uint16_t* sQ = smem16 + L::OFF_Q;
-    uint16_t* sK = smem16 + L::OFF_K;
-    uint16_t* sKt = smem16 + L::OFF_KT;
-    uint16_t* sVt = smem16 + L::OFF_VT;
-    uint16_t* sA = smem16 + L::OFF_A;
-    uint16_t* sXq = smem16 + L::OFF_XQ;
-    uint16_t* sXk = smem16 + L::OFF_XK;
-    float* sEta = reinterpret_cast<float*>(smem16 + L::N_BF16);
-    float* sWS = sEta + C;
-    float* sWM = sWS + C;
-    float* sC = sWM + C;        // C + 1
-    float* sBP = sC + C + 1;    // C + 1
+    float* sF = reinterpret_cast<float*>(smem16 + L::N_BF16);
+    float* sC = sF + 6 * CH;        // c_r, r = 0..CH
+    float* sBP = sC + CH + 1;       // beta^r, r = 0..CH
+    auto stage_x = [&](int buf) { return smem16 + buf * L::STAGE; };
+    auto stage_y = [&](int buf) { return smem16 + buf * L::STAGE + L::TX; };
+    auto stage_v = [&](int buf) { return smem16 + buf * L::STAGE + 2 * L::TX; };
+    auto tile_a = [&](int buf) { return smem16 + L::OFF_A + buf * CH * CH; };
+    auto s_eta = [&](int buf) { return sF + buf * 3 * CH; };
+    auto s_wt = [&](int buf) { return sF + buf * 3 * CH + CH; };    // eta_j / (1 - beta)
+    auto s_wm = [&](int buf) { return sF + buf * 3 * CH + 2 * CH; }; // eta_j beta^{n-1-j}
+    // feature rows read by the contractions: the staged rows (identity) or phi (SwiGLU)
+    auto tile_q = [&](int buf) { return SWIGLU ? smem16 + L::OFF_PHI : stage_x(buf); };
+    auto tile_k = [&](int buf) { return SWIGLU ? smem16 + L::OFF_PHI + CH * D : stage_y(buf); };
 
     // ---- unit of work (XCD-aware: consecutive units land on one XCD) --------
     const int G = gridDim.x;
@@ -222,28 +270,34 @@ chunk_kernel(ChunkParams p) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4;
-    const int dv_base = vs * DVWG;        // first value column of the workgroup
-    const int dvw = wave * 16;            // wave's columns inside the slice
+    const int dvw = wave * 16;            // wave's first value column inside the slice
+    const int dv_base = vs * DVWG;        // workgroup's first value column
     const float beta = p.beta;
+    const float inv1mb = 1.0f / (1.0f - beta);
+    // scale applied to the stored T when it is read: eta / (1 - beta) for a scalar step
+    const float t_scale = ETAV ? 1.0f : p.eta_scalar * inv1mb;
 
     const int t_begin = (KIND == K_BIDIR) ? 0 : seg * p.seg_len;
     const int t_end = (KIND == K_BIDIR) ? p.T : min(p.T, t_begin + p.seg_len);
     const size_t seq_row = (size_t)seq * p.T;
 
-    if (wave == 0) coefficient_scan<C>(beta, sC, sBP);
+    if (wave == 0) coefficient_scan<CH>(beta, sC, sBP);
 
-    // zero the A tiles above the diagonal that the token-pair steps read
-    for (int idx = tid; idx < (NI / 2) * 16 * 16; idx += NT) {
-        const int I = 2 * (idx / 256), rr = (idx / 16) % 16, cc = idx % 16;
-        sA[(16 * I + rr) * L::LT + 16 * (I + 1) + cc] = 0;
+    // zero the score tiles above the diagonal that the token-pair steps read
+    if (KIND == K_OUTPUT) {
+        for (int idx = tid; idx < 2 * (NI / 2) * 16 * 4; idx += NT) {
+            const int buf = idx / ((NI / 2) * 64), w = idx % ((NI / 2) * 64);
+            const int I = 2 * (w / 64), rr = (w / 4) % 16, q4 = w % 4;
+            *reinterpret_cast<u32x2*>(tile_a(buf) + swz<CH>(16 * I + rr, 16 * (I + 1) + 4 * q4)) = u32x2{0u, 0u};
+        }
     }
 
     // SwiGLU: this wave's rows of W1/W3 (feature slice fs) as MFMA A operands
     constexpr int FPW = SWIGLU ? D / NW : 16;       // features computed per wave
-    constexpr int NFW = FPW / 16;
-    constexpr int NSK = DK / 32;
-    bf16x8 w1f[SWIGLU ? NFW : 1][SWIGLU ? NSK : 1];
-    bf16x8 w3f[SWIGLU ? NFW : 1][SWIGLU ? NSK : 1];
+    constexpr int NFW = SWIGLU ? FPW / 16 : 1;
+    constexpr int NSK = SWIGLU ? DK / 32 : 1;
+    bf16x8 w1f[NFW][NSK];
+    bf16x8 w3f[NFW][NSK];
     if constexpr (SWIGLU) {
         const size_t wrow0 = (size_t)h * p.d_phi + (size_t)fs * D + wave * FPW;
 #pragma unroll
@@ -257,290 +311,363 @@ chunk_kernel(ChunkParams p) {
     }
 
     // ---- state slice in registers ------------------------------------------
-    f32x4 S[NFT], M[MOM ? NFT : 1];
+    f32x4 St[NFT], M[MOM ? NFT : 1];
 #pragma unroll
-    for (int ft = 0; ft < NFT; ++ft) S[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ft = 0; ft < NFT; ++ft) St[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ft = 0; ft < (MOM ? NFT : 1); ++ft) M[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // summaries / entry states: [slot][wave][ft][lane] f32x4, S then M
+    // summaries / entry states: [slot][wave][ft][lane] f32x4, T then M
     constexpr size_t SLICE_F4 = (size_t)NW * NFT * 64;
     const size_t slice_units = (size_t)p.phi_split * p.dv_split;
-    const size_t slot_stride = SLICE_F4 * 2;   // S and M
+    const size_t slot_stride = SLICE_F4 * 2;
     if (KIND == K_OUTPUT && seg > 0) {
-        // entry state of segment seg = scanned slot (seq, seg - 1)
         const size_t slot = ((size_t)seq * (p.seg_count - 1) + (seg - 1)) * slice_units + (size_t)fs * p.dv_split + vs;
         const f32x4* src = reinterpret_cast<const f32x4*>(p.state) + slot * slot_stride;
 #pragma unroll
-        for (int ft = 0; ft < NFT; ++ft) S[ft] = src[((size_t)wave * NFT + ft) * 64 + lane];
+        for (int ft = 0; ft < NFT; ++ft) St[ft] = src[((size_t)wave * NFT + ft) * 64 + lane];
         if constexpr (MOM) {
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft) M[ft] = src[SLICE_F4 + ((size_t)wave * NFT + ft) * 64 + lane];
         }
     }
 
-    const int n_passes = (KIND == K_BIDIR) ? 2 : 1;
+    using PF = Prefetch<WX, DVWG, NT>;
+    constexpr int XCH = WX / 8;     // 16-byte pieces per q/k row
+    constexpr int VCH = DVWG / 8;   // 16-byte pieces per v row
 
-    for (int pass = 0; pass < n_passes; ++pass) {
-        // pass 0: chunk walk with updates (and causal readout)
-        // pass 1 (bidirectional only): readout of every query from the final S
-        const bool upd = (pass == 0);
-        const bool readq = (KIND == K_OUTPUT) || (KIND == K_BIDIR && pass == 1);
-        for (int t0 = t_begin; t0 < t_end; t0 += C) {
-            const int n = min(C, t_end - t0);
-            const size_t row0 = seq_row + t0;
-            __syncthreads();   // previous chunk's LDS reads are done
+    // issue the global loads of the chunk starting at t0 into registers
+    auto fetch = [&](PF& f, int t0, bool want_q, bool want_k, bool want_v, bool want_eta) {
+        const int n = min(CH, t_end - t0);
+        const size_t row0 = seq_row + t0;
+#pragma unroll
+        for (int i = 0; i < PF::PX; ++i) {
+            const int idx = tid + i * NT;
+            const int r = idx / XCH, c = idx % XCH;
+            const size_t off = (row0 + r) * WX + 8 * c;
+            f.x[i] = (want_q && r < n) ? *reinterpret_cast<const u32x4*>(p.q + off) : u32x4{0u, 0u, 0u, 0u};
+            f.y[i] = (want_k && r < n) ? *reinterpret_cast<const u32x4*>(p.k + off) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < PF::PV; ++i) {
+            const int idx = tid + i * NT;
+            const int r = idx / VCH, c = idx % VCH;
+            const size_t off = (row0 + r) * DV + dv_base + 8 * c;
+            f.v[i] = (want_v && r < n) ? *reinterpret_cast<const u32x4*>(p.v + off) : u32x4{0u, 0u, 0u, 0u};
+        }
+        f.eta = 0.0f;
+        if (want_eta && tid < n) f.eta = ETAV ? p.eta[row0 + tid] : p.eta_scalar;
+    };
 
-            // ---- stage the chunk: q, k rows (features or raw), v^T slice, eta ---
-            {
-                constexpr int QB = C * (SWIGLU ? DK : D) / 64;   // 8x8 blocks of q (or k)
-                constexpr int VB = C * DVWG / 64;
-                constexpr int FB = (SWIGLU ? DK : D) / 8;       // feature blocks per row
-                const int nq = readq ? QB : 0;
-                const int nk = upd ? QB : 0;
-                const int nv = upd || (KIND == K_OUTPUT) ? VB : 0;
-                const int total = nq + nk + nv;
-                const int ldx = SWIGLU ? DK : D;
-                for (int b = tid; b < total; b += NT) {
-                    u32x4 r[8];
-                    if (b < nq) {
-                        const int jb = b / FB, fb = b % FB;
-                        load_block(r, p.q + (row0 + 8 * jb) * ldx + 8 * fb, ldx, n - 8 * jb);
-                        uint16_t* dst = SWIGLU ? sXq + (8 * jb) * L::LX + 8 * fb : sQ + (8 * jb) * L::LQ + 8 * fb;
-                        const int ld = SWIGLU ? L::LX : L::LQ;
+    // write a prefetched chunk into buffer buf of the swizzled LDS tiles (and its token weights)
+    auto commit = [&](const PF& f, int buf, int n, bool want_q, bool want_k, bool want_v, bool want_eta) {
 #pragma unroll
-                        for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<u32x4*>(dst + rr * ld) = r[rr];
-                    } else if (b < nq + nk) {
-                        const int bb = b - nq;
-                        const int jb = bb / FB, fb = bb % FB;
-                        load_block(r, p.k + (row0 + 8 * jb) * ldx + 8 * fb, ldx, n - 8 * jb);
-                        if constexpr (SWIGLU) {
-                            uint16_t* dst = sXk + (8 * jb) * L::LX + 8 * fb;
+        for (int i = 0; i < PF::PX; ++i) {
+            const int idx = tid + i * NT;
+            const int r = idx / XCH, c = idx % XCH;
+            if (want_q) *reinterpret_cast<u32x4*>(stage_x(buf) + swz<WX>(r, 8 * c)) = f.x[i];
+            if (want_k) *reinterpret_cast<u32x4*>(stage_y(buf) + swz<WX>(r, 8 * c)) = f.y[i];
+        }
+        if (want_v) {
 #pragma unroll
-                            for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<u32x4*>(dst + rr * L::LX) = r[rr];
-                        } else {
-                            if (KIND == K_OUTPUT) {
-                                uint16_t* dst = sK + (8 * jb) * L::LQ + 8 * fb;
-#pragma unroll
-                                for (int rr = 0; rr < 8; ++rr) *reinterpret_cast<u32x4*>(dst + rr * L::LQ) = r[rr];
-                            }
-#pragma unroll
-                            for (int cc = 0; cc < 8; ++cc)
-                                *reinterpret_cast<u32x4*>(sKt + (8 * fb + cc) * L::LT + 8 * jb) = block_column(r, cc);
-                        }
-                    } else {
-                        const int bb = b - nq - nk;
-                        constexpr int FBV = DVWG / 8;
-                        const int jb = bb / FBV, fb = bb % FBV;
-                        load_block(r, p.v + (row0 + 8 * jb) * p.d_v + dv_base + 8 * fb, p.d_v, n - 8 * jb);
-#pragma unroll
-                        for (int cc = 0; cc < 8; ++cc)
-                            *reinterpret_cast<u32x4*>(sVt + (8 * fb + cc) * L::LT + 8 * jb) = block_column(r, cc);
-                    }
-                }
-                if (upd && tid < C) {
-                    float et = 0.0f;
-                    if (tid < n) et = eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + tid);
-                    sEta[tid] = et;
-                    sWS[tid] = tid < n ? et * sC[n - 1 - tid] : 0.0f;     // eta_j c_{n-1-j}
-                    sWM[tid] = tid < n ? et * sBP[n - 1 - tid] : 0.0f;    // eta_j beta^{n-1-j}
-                }
+            for (int i = 0; i < PF::PV; ++i) {
+                const int idx = tid + i * NT;
+                const int r = idx / VCH, c = idx % VCH;
+                *reinterpret_cast<u32x4*>(stage_v(buf) + swz<DVWG>(r, 8 * c)) = f.v[i];
             }
-            __syncthreads();
+        }
+        if (want_eta && tid < CH) {
+            float et = tid < n ? f.eta : 0.0f;
+            if (ETAV && p.eta_kind == ETA_SOFTPLUS && tid < n) et = softplus_f32(et);
+            s_eta(buf)[tid] = et;
+            s_wt(buf)[tid] = tid < n ? et * inv1mb : 0.0f;                // eta_j / (1 - beta)
+            s_wm(buf)[tid] = tid < n ? et * sBP[n - 1 - tid] : 0.0f;      // eta_j beta^{n-1-j}
+        }
+    };
 
-            // ---- SwiGLU feature prologue: phi = silu(W1 x) * (W3 x) ------------
-            if constexpr (SWIGLU) {
+    // SwiGLU feature prologue: phi = silu(W1 x) * (W3 x) of the staged rows
+    auto features = [&](int buf, bool do_q, bool do_k) {
+        if constexpr (SWIGLU) {
 #pragma unroll
-                for (int a = 0; a < NFW; ++a) {
-                    const int f0 = wave * FPW + 16 * a;       // feature tile inside the slice
-                    if (readq) {
+            for (int a = 0; a < NFW; ++a) {
+                const int f0 = wave * FPW + 16 * a;       // feature tile inside the slice
 #pragma unroll
-                        for (int I = 0; I < NI; ++I) {
-                            f32x4 u1 = {0.f, 0.f, 0.f, 0.f}, u3 = {0.f, 0.f, 0.f, 0.f};
+                for (int which = 0; which < 2; ++which) {
+                    if (which == 0 && !do_q) continue;
+                    if (which == 1 && !do_k) continue;
+                    const uint16_t* X = which == 0 ? stage_x(buf) : stage_y(buf);
+                    uint16_t* dst = which == 0 ? tile_q(buf) : tile_k(buf);
 #pragma unroll
-                            for (int s = 0; s < NSK; ++s) {
-                                bf16x8 xb = as_bf16x8(lds_read16(sXq + (16 * I + c16) * L::LX + 32 * s + 8 * g));
-                                u1 = mfma16(w1f[a][s], xb, u1);
-                                u3 = mfma16(w3f[a][s], xb, u3);
-                            }
-                            // lane: features f0 + 4g + r of token 16I + c16
-                            f32x4 ph;
+                    for (int I = 0; I < NI; ++I) {
+                        f32x4 u1 = {0.f, 0.f, 0.f, 0.f}, u3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) ph[r] = silu_f32(u1[r]) * u3[r];
-                            u32x2 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])};
-                            *reinterpret_cast<u32x2*>(sQ + (16 * I + c16) * L::LQ + f0 + 4 * g) = pk;
+                        for (int s = 0; s < NSK; ++s) {
+                            bf16x8 xb = as_bf16x8(lds_read16(X + swz<DK>(16 * I + c16, 32 * s + 8 * g)));
+                            u1 = mfma16(w1f[a][s], xb, u1);
+                            u3 = mfma16(w3f[a][s], xb, u3);
                         }
-                    }
-                    if (upd) {
+                        // lane: features f0 + 4g + r of token 16I + c16
+                        f32x4 ph;
 #pragma unroll
-                        for (int J = 0; J < NI; ++J) {
-                            f32x4 u1 = {0.f, 0.f, 0.f, 0.f}, u3 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                            for (int s = 0; s < NSK; ++s) {
-                                bf16x8 xb = as_bf16x8(lds_read16(sXk + (16 * J + c16) * L::LX + 32 * s + 8 * g));
-                                u1 = mfma16(w1f[a][s], xb, u1);
-                                u3 = mfma16(w3f[a][s], xb, u3);
-                            }
-                            f32x4 ph;
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) ph[r] = silu_f32(u1[r]) * u3[r];
-                            if (KIND == K_OUTPUT) {
-                                u32x2 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])};
-                                *reinterpret_cast<u32x2*>(sK + (16 * J + c16) * L::LQ + f0 + 4 * g) = pk;
-                            }
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                sKt[(f0 + 4 * g + r) * L::LT + 16 * J + c16] = f32_to_bf16_bits(ph[r]);
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-
-            // ---- intra-chunk scores A = (P o Gamma) diag(eta), P = Phi_Q Phi_K^T --
-            if (KIND == K_OUTPUT) {
-                constexpr int NTILE = NI * (NI + 1) / 2;
-                for (int ti = wave; ti < NTILE; ti += NW) {
-                    int I = 0, rem = ti;
-                    while (rem > I) { rem -= I + 1; ++I; }
-                    const int J = rem;
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) {
-                        bf16x8 a = as_bf16x8(lds_read16(sK + (16 * J + c16) * L::LQ + 32 * s + 8 * g));
-                        bf16x8 b = as_bf16x8(lds_read16(sQ + (16 * I + c16) * L::LQ + 32 * s + 8 * g));
-                        acc = mfma16(a, b, acc);
-                    }
-                    // acc[r] = P[i = 16I + c16][j = 16J + 4g + r]
-                    const int i = 16 * I + c16;
-                    float val[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = 16 * J + 4 * g + r;
-                        val[r] = (j <= i && i < n) ? acc[r] * sC[max(i - j, 0)] * sEta[j] : 0.0f;
-                    }
-                    u32x2 pk = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
-                    *reinterpret_cast<u32x2*>(sA + i * L::LT + 16 * J + 4 * g) = pk;
-                }
-            }
-
-            // ---- readout from the entry state: O^T = S Phi_Q^T (+ g o M Phi_Q^T) ---
-            f32x4 oacc[NI], yacc[MOM ? NI : 1];
-            if (readq) {
-                bf16x8 aS[NS], aM[MOM ? NS : 1];
-#pragma unroll
-                for (int s = 0; s < NS; ++s) aS[s] = pack8(S[2 * s], S[2 * s + 1]);
-                if constexpr (MOM && KIND == K_OUTPUT) {
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) aM[s] = pack8(M[2 * s], M[2 * s + 1]);
-                }
-#pragma unroll
-                for (int I = 0; I < NI; ++I) {
-                    oacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (MOM && KIND == K_OUTPUT) yacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    const uint16_t* qrow = sQ + (16 * I + c16) * L::LQ + 4 * g;
-#pragma unroll
-                    for (int s = 0; s < NS; ++s) {
-                        bf16x8 b = join8(lds_read8(qrow + 32 * s), lds_read8(qrow + 32 * s + 16));
-                        oacc[I] = mfma16(aS[s], b, oacc[I]);
-                        if constexpr (MOM) {
-                            if (KIND == K_OUTPUT) yacc[I] = mfma16(aM[s], b, yacc[I]);
-                        }
-                    }
-                }
-            }
-            if (KIND == K_OUTPUT) __syncthreads();   // A tiles complete
-
-            // ---- intra-chunk contribution, combine, store ------------------------
-            if (readq) {
-#pragma unroll
-                for (int I = 0; I < NI; ++I) {
-                    if (KIND == K_OUTPUT) {
-#pragma unroll
-                        for (int t = 0; t <= I / 2; ++t) {
-                            bf16x8 a = as_bf16x8(lds_read16(sVt + (dvw + c16) * L::LT + 32 * t + 8 * g));
-                            bf16x8 b = as_bf16x8(lds_read16(sA + (16 * I + c16) * L::LT + 32 * t + 8 * g));
-                            oacc[I] = mfma16(a, b, oacc[I]);
-                        }
-                    }
-                    const int i = 16 * I + c16;
-                    f32x4 o = oacc[I];
-                    if constexpr (MOM) {
-                        if (KIND == K_OUTPUT) {
-                            const float gi = beta * sC[i];
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) o[r] = fmaf(gi, yacc[I][r], o[r]);
-                        }
-                    }
-                    if (i < n) {
-                        const size_t orow = row0 + i;
-                        const int col = dv_base + dvw + 4 * g;
-                        if (p.phi_split == 1) {
-                            u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-                            *reinterpret_cast<u32x2*>(p.o + orow * p.d_v + col) = pk;
-                        } else {
-                            float* dst = p.o_partial + ((size_t)fs * p.n_rows + orow) * p.d_v + col;
-                            *reinterpret_cast<f32x4*>(dst) = o;
-                        }
-                    }
-                }
-            }
-
-            // ---- state update --------------------------------------------------
-            if (upd) {
-                if constexpr (MOM) {
-                    const float gl = beta * sC[n - 1];   // g_{n-1}
-                    const float bn = sBP[n];             // beta^n
-#pragma unroll
-                    for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            S[ft][r] = fmaf(gl, M[ft][r], S[ft][r]);
-                            M[ft][r] *= bn;
-                        }
-                }
-#pragma unroll
-                for (int t = 0; t < NJS; ++t) {
-                    const u32x4 raw = lds_read16(sVt + (dvw + c16) * L::LT + 32 * t + 8 * g);
-                    float ws[8], wm[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) ws[e] = sWS[32 * t + 8 * g + e];
-                    const bf16x8 bS = scale8(raw, ws);
-                    bf16x8 bM;
-                    if constexpr (MOM) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) wm[e] = sWM[32 * t + 8 * g + e];
-                        bM = scale8(raw, wm);
-                    }
-#pragma unroll
-                    for (int ft = 0; ft < NFT; ++ft) {
-                        bf16x8 a = as_bf16x8(lds_read16(sKt + (16 * ft + c16) * L::LT + 32 * t + 8 * g));
-                        S[ft] = mfma16(a, bS, S[ft]);
-                        if constexpr (MOM) M[ft] = mfma16(a, bM, M[ft]);
+                        for (int r = 0; r < 4; ++r) ph[r] = silu_f32(u1[r]) * u3[r];
+                        u32x2 pk = {pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])};
+                        *reinterpret_cast<u32x2*>(dst + swz<D>(16 * I + c16, f0 + 4 * g)) = pk;
                     }
                 }
             }
         }
-    }
+    };
 
-    if (KIND == K_SUMMARY) {
+    // readout of buffer buf from the current state into oacc (T part) and yacc (M part)
+    f32x4 oacc[NI], yacc[MOM ? NI : 1];
+    auto readout = [&](int buf, float scale, bool with_m) {
+        const uint16_t* Q = tile_q(buf);
+#pragma unroll
+        for (int I = 0; I < NI; ++I) {
+            oacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (MOM) yacc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const bf16x8 aS = pack8(St[2 * s], St[2 * s + 1]);
+            bf16x8 aM;
+            if constexpr (MOM) {
+                if (with_m) aM = pack8(M[2 * s], M[2 * s + 1]);
+            }
+#pragma unroll
+            for (int I = 0; I < NI; ++I) {
+                const bf16x8 b = as_bf16x8(lds_read16(Q + swz<D>(16 * I + c16, 32 * s + 8 * g)));
+                oacc[I] = mfma16(aS, b, oacc[I]);
+                if constexpr (MOM) {
+                    if (with_m) yacc[I] = mfma16(aM, b, yacc[I]);
+                }
+            }
+        }
+        if (scale != 1.0f) {
+#pragma unroll
+            for (int I = 0; I < NI; ++I)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) oacc[I][r] *= scale;
+        }
+    };
+
+    // one output tile: lane holds O[row0 + 16I + c16][dv_base + dvw + 4g + r]
+    auto store = [&](const f32x4& o, int I, int n, size_t row0) {
+        const int i = 16 * I + c16;
+        if (i < n) {
+            const size_t orow = row0 + i;
+            const int col = dv_base + dvw + 4 * g;
+            if (p.phi_split == 1) {
+                u32x2 pk = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+                *reinterpret_cast<u32x2*>(p.o + orow * DV + col) = pk;
+            } else {
+                float* dst = p.o_partial + ((size_t)fs * p.n_rows + orow) * DV + col;
+                *reinterpret_cast<f32x4*>(dst) = o;
+            }
+        }
+    };
+
+    // v^T fragments of buffer buf: tokens 32t + 8g .. +7 of this wave's 16 columns
+    u32x4 vt[NJS];
+    auto read_vt = [&](int buf) {
+#pragma unroll
+        for (int t = 0; t < NJS; ++t) vt[t] = tr_read8<DVWG>(stage_v(buf), 32 * t + 8 * g, dvw + 4 * (lane & 3));
+    };
+
+    // state update with chunk buf (n tokens): T += K^T (w_T v), M = beta^n M + K^T (w_M v)
+    auto update = [&](int buf, int n) {
+        if constexpr (MOM) {
+            const float bn = sBP[n];             // beta^n
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) M[ft][r] *= bn;
+        }
+        const uint16_t* K = tile_k(buf);
+#pragma unroll
+        for (int t = 0; t < NJS; ++t) {
+            float wt[8], wm[8];
+            if constexpr (ETAV) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wt[e] = s_wt(buf)[32 * t + 8 * g + e];
+            }
+            if constexpr (MOM) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) wm[e] = s_wm(buf)[32 * t + 8 * g + e];
+            }
+            // rows beyond the chunk end are zero in the v tile
+            const bf16x8 bT = ETAV ? scale8(vt[t], wt) : as_bf16x8(vt[t]);
+            bf16x8 bM;
+            if constexpr (MOM) bM = scale8(vt[t], wm);
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft) {
+                const int colq = 32 * (ft >> 1) + 8 * (lane & 3) + 4 * (ft & 1);
+                const bf16x8 a = as_bf16x8(tr_read8<D>(K, 32 * t + 8 * g, colq));
+                St[ft] = mfma16(a, bT, St[ft]);
+                if constexpr (MOM) M[ft] = mfma16(a, bM, M[ft]);
+            }
+        }
+    };
+
+    // scores of chunk buf: A = (P o Gamma) diag(eta), P = Phi_Q Phi_K^T, into tile_a(buf)
+    auto scores = [&](int buf, int n) {
+        constexpr int NTILE = NI * (NI + 1) / 2;
+        const uint16_t* Q = tile_q(buf);
+        const uint16_t* K = tile_k(buf);
+        const float* eta = s_eta(buf);
+        for (int ti = wave; ti < NTILE; ti += NW) {
+            int I = 0, rem = ti;
+            while (rem > I) { rem -= I + 1; ++I; }
+            const int J = rem;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 a = as_bf16x8(lds_read16(K + swz<D>(16 * J + c16, 32 * s + 8 * g)));
+                bf16x8 b = as_bf16x8(lds_read16(Q + swz<D>(16 * I + c16, 32 * s + 8 * g)));
+                acc = mfma16(a, b, acc);
+            }
+            // acc[r] = P[i = 16I + c16][j = 16J + 4g + r]
+            const int i = 16 * I + c16;
+            float val[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int j = 16 * J + 4 * g + r;
+                val[r] = (j <= i && i < n) ? acc[r] * sC[max(i - j, 0)] * eta[j] : 0.0f;
+            }
+            u32x2 pk = {pack_bf16x2(val[0], val[1]), pack_bf16x2(val[2], val[3])};
+            *reinterpret_cast<u32x2*>(tile_a(buf) + swz<CH>(i, 16 * J + 4 * g)) = pk;
+        }
+    };
+
+    // intra-chunk term of chunk buf (scores and v^T fragments ready), combine, store
+    auto intra_and_store = [&](int buf, int n, size_t row0) {
+#pragma unroll
+        for (int I = 0; I < NI; ++I) {
+#pragma unroll
+            for (int t = 0; t <= I / 2; ++t) {
+                bf16x8 b = as_bf16x8(lds_read16(tile_a(buf) + swz<CH>(16 * I + c16, 32 * t + 8 * g)));
+                oacc[I] = mfma16(as_bf16x8(vt[t]), b, oacc[I]);
+            }
+            f32x4 o = oacc[I];
+            if constexpr (MOM) {
+                const float gi = -beta * beta * sBP[16 * I + c16] * inv1mb;   // -beta^{i+2} / (1 - beta)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = fmaf(gi, yacc[I][r], o[r]);
+            }
+            store(o, I, n, row0);
+        }
+    };
+
+    __syncthreads();   // coefficient tables and zeroed score tiles are visible
+
+    if constexpr (KIND == K_OUTPUT) {
+        // chunk c is staged in buffer c & 1; its intra-chunk term and store run in
+        // the next iteration, after the one barrier that also publishes its scores
+        PF pf;
+        if (t_begin < t_end) fetch(pf, t_begin, true, true, true, true);
+        int buf = 0, n_prev = 0;
+        size_t row_prev = 0;
+        for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+            const int n = min(CH, t_end - t0);
+            const size_t row0 = seq_row + t0;
+            commit(pf, buf, n, true, true, true, true);
+            __syncthreads();
+            if (t0 + CH < t_end) fetch(pf, t0 + CH, true, true, true, true);   // in flight during compute
+            if (t0 > t_begin) intra_and_store(buf ^ 1, n_prev, row_prev);
+            if constexpr (SWIGLU) {
+                features(buf, true, true);
+                __syncthreads();
+            }
+            scores(buf, n);
+            readout(buf, t_scale, true);
+            read_vt(buf);
+            update(buf, n);
+            n_prev = n;
+            row_prev = row0;
+            buf ^= 1;
+        }
+        __syncthreads();
+        if (t_begin < t_end) intra_and_store(buf ^ 1, n_prev, row_prev);
+    } else if constexpr (KIND == K_SUMMARY) {
+        PF pf;
+        if (t_begin < t_end) fetch(pf, t_begin, false, true, true, true);
+        int buf = 0;
+        for (int t0 = t_begin; t0 < t_end; t0 += CH) {
+            const int n = min(CH, t_end - t0);
+            commit(pf, buf, n, false, true, true, true);
+            __syncthreads();
+            if (t0 + CH < t_end) fetch(pf, t0 + CH, false, true, true, true);
+            if constexpr (SWIGLU) {
+                features(buf, false, true);
+                __syncthreads();
+            }
+            read_vt(buf);
+            update(buf, n);
+            buf ^= 1;
+        }
         const size_t slot = ((size_t)seq * (p.seg_count - 1) + seg) * slice_units + (size_t)fs * p.dv_split + vs;
         f32x4* dst = reinterpret_cast<f32x4*>(p.state) + slot * slot_stride;
 #pragma unroll
-        for (int ft = 0; ft < NFT; ++ft) dst[((size_t)wave * NFT + ft) * 64 + lane] = S[ft];
+        for (int ft = 0; ft < NFT; ++ft) dst[((size_t)wave * NFT + ft) * 64 + lane] = St[ft];
         if constexpr (MOM) {
 #pragma unroll
             for (int ft = 0; ft < NFT; ++ft) dst[SLICE_F4 + ((size_t)wave * NFT + ft) * 64 + lane] = M[ft];
         }
+    } else {
+        // bidirectional: pass 0 accumulates the state over all tokens ...
+        PF pf;
+        fetch(pf, 0, false, true, true, true);
+        int buf = 0;
+        for (int t0 = 0; t0 < t_end; t0 += CH) {
+            const int n = min(CH, t_end - t0);
+            commit(pf, buf, n, false, true, true, true);
+            __syncthreads();
+            if (t0 + CH < t_end) fetch(pf, t0 + CH, false, true, true, true);
+            if constexpr (SWIGLU) {
+                features(buf, false, true);
+                __syncthreads();
+            }
+            read_vt(buf);
+            update(buf, n);
+            buf ^= 1;
+        }
+        // ... then every query reads the final S = t_scale T - kappa M
+        const float kappa = beta * inv1mb;
+#pragma unroll
+        for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = St[ft][r] * t_scale;
+                if constexpr (MOM) v = fmaf(-kappa, M[ft][r], v);
+                St[ft][r] = v;
+            }
+        __syncthreads();
+        fetch(pf, 0, true, false, false, false);
+        buf = 0;
+        for (int t0 = 0; t0 < t_end; t0 += CH) {
+            const int n = min(CH, t_end - t0);
+            const size_t row0 = seq_row + t0;
+            commit(pf, buf, n, true, false, false, false);
+            __syncthreads();
+            if (t0 + CH < t_end) fetch(pf, t0 + CH, true, false, false, false);
+            if constexpr (SWIGLU) {
+                features(buf, true, false);
+                __syncthreads();
+            }
+            readout(buf, 1.0f, false);
+#pragma unroll
+            for (int I = 0; I < NI; ++I) store(oacc[I], I, n, row0);
+            buf ^= 1;
+        }
     }
 }
 
-// Composes segment summaries into entry states, in place:
-//   (S, M) <- (S + G M + dS_p, beta^L M + dM_p),  slot p <- (S, M) = entry of segment p + 1
-// G = sum_{r=1..L} beta^r, L = segment length.  Slots are [seq][step][slice] and
-// hold S then M (slice_f4 float4s each).  One thread per float4 of a slice.
-__global__ void segment_scan(float* state, size_t n_threads, int n_slices, int n_steps, int slice_f4, float G,
-                             float bL, int mom) {
+// Composes segment summaries into entry states, in place, for the (T, M) state:
+//   T <- T + dT_p,  M <- beta^L M + dM_p,  slot p <- (T, M) = entry of segment p + 1
+// (L = segment length).  Slots are [seq][step][slice] and hold T then M
+// (slice_f4 float4s each).  One thread per float4 of a slice.
+__global__ void segment_scan(float* state, size_t n_threads, int n_slices, int n_steps, int slice_f4, float bL,
+                             int mom) {
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n_threads) return;
     const size_t e_per_seq = (size_t)n_slices * slice_f4;
@@ -548,24 +675,19 @@ __global__ void segment_scan(float* state, size_t n_threads, int n_slices, int n
     const size_t within = idx % e_per_seq;
     const size_t sl = within / slice_f4, e = within % slice_f4;
     f32x4* base = reinterpret_cast<f32x4*>(state);
-    f32x4 S = {0.f, 0.f, 0.f, 0.f}, M = {0.f, 0.f, 0.f, 0.f};
+    f32x4 T = {0.f, 0.f, 0.f, 0.f}, M = {0.f, 0.f, 0.f, 0.f};
     for (int step = 0; step < n_steps; ++step) {
         const size_t slot = (seqi * n_steps + step) * n_slices + sl;
         f32x4* ps = base + slot * 2 * slice_f4 + e;
-        const f32x4 dS = ps[0];
+        const f32x4 dT = ps[0];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) T[r] += dT[r];
+        ps[0] = T;
         if (mom) {
             const f32x4 dM = ps[slice_f4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                S[r] = fmaf(G, M[r], S[r]) + dS[r];
-                M[r] = fmaf(bL, M[r], dM[r]);
-            }
-            ps[0] = S;
+            for (int r = 0; r < 4; ++r) M[r] = fmaf(bL, M[r], dM[r]);
             ps[slice_f4] = M;
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) S[r] += dS[r];
-            ps[0] = S;
         }
     }
 }
@@ -603,29 +725,32 @@ bool fast_supported(const Shape& s, int chunk) {
     return chunk == 0 || chunk == 64 || chunk == 128;
 }
 
-FastPlan fast_plan(const Shape& s, int chunk, int segments) {
+FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split) {
     FastPlan p{};
-    // the chunk length is a tiling choice; SwiGLU tiles of 128 tokens do not fit in LDS
-    p.chunk = (chunk == 128 && !s.swiglu) ? 128 : 64;
+    // The chunk length is a tiling choice (results differ only by rounding);
+    // this path always tiles at 64 tokens.
+    p.chunk = CH;
     p.phi_split = s.swiglu ? s.d_phi / 128 : 1;
-    p.nwaves = (s.swiglu && s.d_v == 128) ? 8 : 4;
-    p.dv_split = s.d_v / (16 * p.nwaves);
+    // one wave per 16 value columns; identity maps with d = 128 may split the
+    // value columns over two workgroups of four waves
+    p.dvt = 1;
+    p.dv_split = (value_split == 2 && !s.swiglu && s.d_k == 128 && s.d_v == 128) ? 2 : 1;
+    p.nwaves = s.d_v / (16 * p.dv_split);
     const int D = s.swiglu ? 128 : s.d_k;
-    const int n_chunks = (s.T + p.chunk - 1) / p.chunk;
+    const int n_chunks = (s.T + CH - 1) / CH;
     const long base = (long)s.n_seq() * p.phi_split * p.dv_split;
     int S = 1;
     if (segments > 0) {
         S = std::min(segments, n_chunks);
     } else {
-        // aim for two resident workgroups per CU on 256 CUs, segments >= 4 chunks
-        const bool two_per_cu = p.nwaves == 8 || p.chunk == 64;
-        const long target = two_per_cu ? 512 : 256;
+        // enough workgroups for 256 CUs, segments of at least 4 chunks
+        const long target = p.nwaves == 8 ? 256 : 512;
         while (base * S < target && n_chunks >= 8 * S) S *= 2;
     }
     const int seg_chunks = (n_chunks + S - 1) / S;
-    p.seg_len = seg_chunks * p.chunk;
+    p.seg_len = seg_chunks * CH;
     p.segments = (n_chunks + seg_chunks - 1) / seg_chunks;
-    const size_t slice_floats = (size_t)p.nwaves * (D / 16) * 64 * 4;
+    const size_t slice_floats = (size_t)p.nwaves * (D / 16) * p.dvt * 64 * 4;
     p.summary_bytes = p.segments > 1
         ? (size_t)s.n_seq() * (p.segments - 1) * p.phi_split * p.dv_split * slice_floats * 2 * sizeof(float)
         : 0;
@@ -635,41 +760,51 @@ FastPlan fast_plan(const Shape& s, int chunk, int segments) {
 
 namespace {
 
-template <int C, int D, int DK, int NW, bool MOM, bool SW, int KIND>
+template <int D, int DK, int DV, int NW, bool MOM, bool ETAV, bool SW, int KIND>
 hipError_t launch_one(const ChunkParams& cp, hipStream_t st) {
     const int grid = (cp.n_units + 7) / 8 * 8;
-    hipLaunchKernelGGL((chunk_kernel<C, D, DK, NW, MOM, SW, KIND>), dim3(grid), dim3(NW * 64), 0, st, cp);
+    hipLaunchKernelGGL((chunk_kernel<D, DK, DV, NW, 1, MOM, ETAV, SW, KIND>), dim3(grid), dim3(NW * 64), 0, st,
+                       cp);
     return hipGetLastError();
 }
 
-template <int C, int D, int DK, int NW, bool SW>
-hipError_t launch_kind(int kind, bool mom, const ChunkParams& cp, hipStream_t st) {
-    if (mom) {
-        if (kind == K_OUTPUT) return launch_one<C, D, DK, NW, true, SW, K_OUTPUT>(cp, st);
-        if (kind == K_SUMMARY) return launch_one<C, D, DK, NW, true, SW, K_SUMMARY>(cp, st);
-        return launch_one<C, D, DK, NW, true, SW, K_BIDIR>(cp, st);
-    }
-    if (kind == K_OUTPUT) return launch_one<C, D, DK, NW, false, SW, K_OUTPUT>(cp, st);
-    if (kind == K_SUMMARY) return launch_one<C, D, DK, NW, false, SW, K_SUMMARY>(cp, st);
-    return launch_one<C, D, DK, NW, false, SW, K_BIDIR>(cp, st);
+template <int D, int DK, int DV, int NW, bool MOM, bool ETAV, bool SW>
+hipError_t launch_k(int kind, const ChunkParams& cp, hipStream_t st) {
+    if (kind == K_OUTPUT) return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_OUTPUT>(cp, st);
+    if (kind == K_SUMMARY) return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_SUMMARY>(cp, st);
+    return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_BIDIR>(cp, st);
 }
 
-hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, const ChunkParams& cp,
+template <int D, int DK, int DV, int NW, bool SW>
+hipError_t launch_kind(int kind, bool mom, bool etav, const ChunkParams& cp, hipStream_t st) {
+    if (mom) {
+        return etav ? launch_k<D, DK, DV, NW, true, true, SW>(kind, cp, st)
+                    : launch_k<D, DK, DV, NW, true, false, SW>(kind, cp, st);
+    }
+    return etav ? launch_k<D, DK, DV, NW, false, true, SW>(kind, cp, st)
+                : launch_k<D, DK, DV, NW, false, false, SW>(kind, cp, st);
+}
+
+// one wave per 16 value columns of the workgroup; DV / (16 NW) workgroups per sequence
+hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, bool etav, const ChunkParams& cp,
                         hipStream_t st) {
     if (!s.swiglu) {
-        if (p.chunk == 64) {
-            if (s.d_k == 128) return launch_kind<64, 128, 128, 4, false>(kind, mom, cp, st);
-            return launch_kind<64, 64, 64, 4, false>(kind, mom, cp, st);
+        if (s.d_k == 128) {
+            if (s.d_v == 128) {
+                return p.nwaves == 8 ? launch_kind<128, 128, 128, 8, false>(kind, mom, etav, cp, st)
+                                     : launch_kind<128, 128, 128, 4, false>(kind, mom, etav, cp, st);
+            }
+            return launch_kind<128, 128, 64, 4, false>(kind, mom, etav, cp, st);
         }
-        if (s.d_k == 128) return launch_kind<128, 128, 128, 4, false>(kind, mom, cp, st);
-        return launch_kind<128, 64, 64, 4, false>(kind, mom, cp, st);
+        return s.d_v == 128 ? launch_kind<64, 64, 128, 8, false>(kind, mom, etav, cp, st)
+                            : launch_kind<64, 64, 64, 4, false>(kind, mom, etav, cp, st);
     }
-    if (p.nwaves == 8) {
-        if (s.d_k == 128) return launch_kind<64, 128, 128, 8, true>(kind, mom, cp, st);
-        return launch_kind<64, 128, 64, 8, true>(kind, mom, cp, st);
+    if (s.d_k == 128) {
+        return s.d_v == 128 ? launch_kind<128, 128, 128, 8, true>(kind, mom, etav, cp, st)
+                            : launch_kind<128, 128, 64, 4, true>(kind, mom, etav, cp, st);
     }
-    if (s.d_k == 128) return launch_kind<64, 128, 128, 4, true>(kind, mom, cp, st);
-    return launch_kind<64, 128, 64, 4, true>(kind, mom, cp, st);
+    return s.d_v == 128 ? launch_kind<128, 64, 128, 8, true>(kind, mom, etav, cp, st)
+                        : launch_kind<128, 64, 64, 4, true>(kind, mom, etav, cp, st);
 }
 
 }  // namespace
@@ -698,6 +833,7 @@ hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const
     cp.phi_split = p.phi_split;
     cp.n_rows = (size_t)s.n_seq() * s.T;
     const bool mom = a.beta != 0.0f;
+    const bool etav = a.eta_kind != ETA_SCALAR;
     const int slice_units = p.phi_split * p.dv_split;
     hipStream_t st = a.stream;
     int nk = 0;
@@ -708,7 +844,7 @@ hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const
         cp.seg_len = s.T;
         cp.n_units = s.n_seq() * slice_units;
         if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_chunk(s, p, K_BIDIR, mom, cp, st)) != hipSuccess) return e;
+        if ((e = launch_chunk(s, p, K_BIDIR, mom, etav, cp, st)) != hipSuccess) return e;
         if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
         ++nk;
     } else {
@@ -716,25 +852,24 @@ hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const
         cp.seg_len = p.seg_len;
         if (p.segments > 1) {
             cp.n_units = s.n_seq() * (p.segments - 1) * slice_units;
-            if ((e = launch_chunk(s, p, K_SUMMARY, mom, cp, st)) != hipSuccess) return e;
+            if ((e = launch_chunk(s, p, K_SUMMARY, mom, etav, cp, st)) != hipSuccess) return e;
             ++nk;
-            const int D = s.swiglu ? 128 : s.d_k;
-            const int slice_f4 = p.nwaves * (D / 16) * 64;
-            const size_t n_threads = (size_t)s.n_seq() * slice_units * slice_f4;
-            double G = 0.0, bL = 1.0;     // G = sum_{r=1..L} beta^r, bL = beta^L
-            for (int r = 0; r < p.seg_len; ++r) {
-                bL *= (double)a.beta;
-                G += bL;
+            if (p.segments > 2) {
+                // with two segments the one summary already is the entry state
+                const int D = s.swiglu ? 128 : s.d_k;
+                const int slice_f4 = p.nwaves * (D / 16) * p.dvt * 64;
+                const size_t n_threads = (size_t)s.n_seq() * slice_units * slice_f4;
+                const double bL = std::pow((double)a.beta, (double)p.seg_len);   // beta^L
+                hipLaunchKernelGGL(segment_scan, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
+                                   cp.state, n_threads, slice_units, p.segments - 1, slice_f4, (float)bL,
+                                   mom ? 1 : 0);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                ++nk;
             }
-            hipLaunchKernelGGL(segment_scan, dim3((unsigned)((n_threads + 255) / 256)), dim3(256), 0, st,
-                               cp.state, n_threads, slice_units, p.segments - 1, slice_f4, (float)G, (float)bL,
-                               mom ? 1 : 0);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
-            ++nk;
         }
         cp.n_units = s.n_seq() * p.segments * slice_units;
         if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_chunk(s, p, K_OUTPUT, mom, cp, st)) != hipSuccess) return e;
+        if ((e = launch_chunk(s, p, K_OUTPUT, mom, etav, cp, st)) != hipSuccess) return e;
         if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
         ++nk;
     }

@@ -25,9 +25,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
-// packs two fp32 into one dword of two bf16 (lo = a, hi = b)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// packs two fp32 into one dword of two bf16 (lo = a, hi = b), round to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+    const bf16x2 r = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    return __builtin_bit_cast(uint32_t, r);
 }
 
 // softplus(a) = ln(1 + e^a), stable form max(a, 0) + log1p(e^-|a|)

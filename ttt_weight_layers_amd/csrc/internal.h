@@ -34,7 +34,7 @@ struct Shape {
     int n_seq() const { return B * H; }
 };
 
-// ---- generic path: fp32 arithmetic on CUDA-core-style vector ALUs ----------
+// ---- generic path: fp32 arithmetic on the vector ALUs ----------
 // Handles every supported shape and mode, fp32 or bf16 inputs.
 size_t generic_smem_bytes(const Shape& s);
 hipError_t launch_generic(const Shape& s, const FwdArgs& a);
@@ -42,7 +42,8 @@ hipError_t launch_generic(const Shape& s, const FwdArgs& a);
 // ---- bf16 MFMA path --------------------------------------------------------
 struct FastPlan {
     int chunk;        // C
-    int nwaves;       // waves per workgroup (each owns 16 value columns)
+    int nwaves;       // waves per workgroup
+    int dvt;          // 16-column value tiles per wave
     int dv_split;     // value-column slices per sequence
     int phi_split;    // 128-wide feature slices per sequence (SwiGLU)
     int segments;     // segments per sequence
@@ -52,7 +53,7 @@ struct FastPlan {
 };
 
 bool fast_supported(const Shape& s, int chunk);
-FastPlan fast_plan(const Shape& s, int chunk, int segments);
+FastPlan fast_plan(const Shape& s, int chunk, int segments, int value_split);
 // Enqueues the whole forward (all kernels).  If ev_begin/ev_end are non-null
 // they are recorded around the output kernel.
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a,
