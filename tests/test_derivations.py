@@ -1,0 +1,104 @@
+"""CPU checks (fp64) of the identities the HIP kernels are built on, against the
+oracle's token-by-token recurrence.  They use no GPU and no kernel code: each
+identity is written out here from its derivation and compared with
+``oracle.forward``.
+
+T-form of the momentum state (kappa = beta / (1 - beta), T = S + kappa M):
+  T_t = T_{t-1} + eta_t v_t k_t^T / (1 - beta)     (no transition)
+  M_t = beta M_{t-1} + eta_t v_t k_t^T
+Chunk step with entry (T, M), local index i, chunk length n:
+  o_i = T q_i - beta^{i+2}/(1-beta) M q_i + sum_{j<=i} eta_j c_{i-j} (q_i.k_j) v_j
+  T'  = T + sum_j eta_j v_j k_j^T / (1 - beta)
+  M'  = beta^n M + sum_j eta_j beta^{n-1-j} v_j k_j^T
+with c_r = (1 - beta^{r+1}) / (1 - beta).  Segments of length L compose as
+T += dT, M = beta^L M + dM.  Bidirectional: S_{T-1} = T_{T-1} - kappa M_{T-1}.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+
+def _inputs(T, dk, dv, seed):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, dk)) / np.sqrt(dk)
+    k = rng.standard_normal((T, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((T, dv))
+    eta = np.exp(rng.standard_normal(T) * 0.3 - 1.0)
+    return q, k, v, eta
+
+
+def _ref(q, k, v, eta, beta, causal=True):
+    o = oracle.forward(q[None, None], k[None, None], v[None, None], eta_mode="per_token",
+                       eta=eta[None, None], beta=beta, causal=causal)
+    return o[0, 0]
+
+
+def _chunk_step(Tst, M, q, k, v, eta, beta):
+    n = q.shape[0]
+    idx = np.arange(n)
+    diff = idx[:, None] - idx[None, :]
+    c = np.where(diff >= 0, (1.0 - beta ** (np.maximum(diff, 0) + 1)) / (1.0 - beta), 0.0)
+    scores = (q @ k.T) * c * eta[None, :]
+    o = q @ Tst.T - (beta ** (idx + 2) / (1.0 - beta))[:, None] * (q @ M.T) + scores @ v
+    Tn = Tst + (v * eta[:, None]).T @ k / (1.0 - beta)
+    Mn = beta ** n * M + (v * (eta * beta ** (n - 1 - idx))[:, None]).T @ k
+    return o, Tn, Mn
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 0.9, 0.99])
+@pytest.mark.parametrize("chunk", [1, 7, 16])
+def test_t_form_chunk_step_equals_recurrence(beta, chunk):
+    q, k, v, eta = _inputs(45, 6, 5, 11)
+    ref = _ref(q, k, v, eta, beta)
+    Tst = np.zeros((5, 6))
+    M = np.zeros((5, 6))
+    out = []
+    for s in range(0, 45, chunk):
+        o, Tst, M = _chunk_step(Tst, M, q[s:s + chunk], k[s:s + chunk], v[s:s + chunk], eta[s:s + chunk], beta)
+        out.append(o)
+    got = np.concatenate(out)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_segment_summaries_compose(beta):
+    # entry state of segment s from the zero-entry summaries of segments < s
+    q, k, v, eta = _inputs(60, 4, 3, 12)
+    L = 12
+    ref = _ref(q, k, v, eta, beta)
+    summaries = []
+    for s in range(0, 60, L):
+        _, dT, dM = _chunk_step(np.zeros((3, 4)), np.zeros((3, 4)), q[s:s + L], k[s:s + L], v[s:s + L],
+                                eta[s:s + L], beta)
+        summaries.append((dT, dM))
+    Tst = np.zeros((3, 4))
+    M = np.zeros((3, 4))
+    out = []
+    for i, s in enumerate(range(0, 60, L)):
+        o, _, _ = _chunk_step(Tst, M, q[s:s + L], k[s:s + L], v[s:s + L], eta[s:s + L], beta)
+        out.append(o)
+        dT, dM = summaries[i]
+        Tst = Tst + dT
+        M = beta ** L * M + dM
+    got = np.concatenate(out)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 0.9])
+def test_bidirectional_state_from_t_form(beta):
+    q, k, v, eta = _inputs(30, 4, 3, 13)
+    ref = _ref(q, k, v, eta, beta, causal=False)
+    _, Tst, M = _chunk_step(np.zeros((3, 4)), np.zeros((3, 4)), q, k, v, eta, beta)
+    S = Tst - beta / (1.0 - beta) * M
+    got = q @ S.T
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_t_form_is_not_the_plain_state():
+    # a dropped kappa M term must be visible: T differs from S when beta > 0
+    q, k, v, eta = _inputs(20, 4, 3, 14)
+    beta = 0.9
+    ref = _ref(q, k, v, eta, beta, causal=False)
+    _, Tst, _ = _chunk_step(np.zeros((3, 4)), np.zeros((3, 4)), q, k, v, eta, beta)
+    assert np.max(np.abs(q @ Tst.T - ref)) > 1e-3
