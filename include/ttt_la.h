@@ -75,6 +75,15 @@ enum {
     TTT_LA_ETA_SOFTPLUS = 1u << 2    /* eta_t = softplus(eta[b,h,t]) = ln(1 + e^a) (Table 2, Variant 3) */
 };
 
+/* Launch choice for a causal forward split into segments (ttt_la_desc.launch). */
+enum {
+    TTT_LA_LAUNCH_AUTO = 0,      /* the library's choice (currently: separate kernels) */
+    TTT_LA_LAUNCH_SEPARATE = 1,  /* segment summaries, their scan and the outputs as three kernels */
+    TTT_LA_LAUNCH_SINGLE = 2     /* one cooperative kernel whose workgroups exchange the segment
+                                    summaries through device memory, when the device can keep the
+                                    whole grid resident (32x32-tile path only); else as SEPARATE */
+};
+
 typedef struct {
     int32_t B, H, T;           /* batch, heads, sequence length: B, H, T >= 1 */
     int32_t d_k, d_v, d_phi;   /* key/query width, value width, feature width */
@@ -86,6 +95,7 @@ typedef struct {
                                   changes the result only by rounding */
     int32_t value_split;       /* workgroups sharing one segment's value columns: 0 = auto, 1 or 2
                                   (2 is used for d_k = d_v = 128 with the identity map); tiling only */
+    int32_t launch;            /* TTT_LA_LAUNCH_*: how a segmented causal forward is launched */
     const void* w1;            /* SWIGLU: device [H, d_phi, d_k] (out x in) in dtype; else NULL */
     const void* w3;            /* SWIGLU: device [H, d_phi, d_k] in dtype; else NULL */
 } ttt_la_desc;
@@ -134,7 +144,8 @@ int ttt_la_check(const ttt_la_desc* desc, const void* q, const void* k, const vo
 
 /* Kernel plan chosen at create, for tests and measurement. */
 typedef struct {
-    int32_t path;          /* 0 = generic fp32-accumulate kernels, 1 = bf16 MFMA chunk kernels */
+    int32_t path;          /* 0 = generic fp32-accumulate kernels, 1 = bf16 16x16-tile MFMA chunk
+                              kernels, 2 = bf16 32x32-tile MFMA chunk kernels (identity map, d = 128) */
     int32_t chunk;         /* tokens per chunk */
     int32_t segments;      /* sequence segments per (b, h) scanned in parallel (1 = none) */
     int32_t seg_len;       /* tokens per segment (last one may be shorter) */
@@ -147,6 +158,13 @@ typedef struct {
 
 /* Fills *plan for handle h.  Host only. */
 int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan);
+
+/* Diagnostic of the single-launch causal path (path 2 with n_kernels == 1):
+ * the workgroups of one sequence wait for each other twice per forward, each
+ * wait bounded so that a kernel always terminates.  *failed is set to 1 if any
+ * wait of any earlier forward on h gave up (its output is then invalid), else
+ * 0; always 0 for other plans.  Synchronises with the device (a blocking copy). */
+int ttt_la_wait_status(ttt_la_t h, int32_t* failed);
 
 /* Measurement hook.  When n_slots > 0, every following ttt_la_forward records
  * a pair of HIP events (created here, not device memory) on its stream around

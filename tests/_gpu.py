@@ -42,11 +42,11 @@ def from_device(t, dtype: str) -> np.ndarray:
     return t.cpu().numpy().astype(np.float64)
 
 
-def make_layer(w: Workload, d, chunk=None, segments=0, value_split=0):
+def make_layer(w: Workload, d, chunk=None, segments=0, value_split=0, launch="auto"):
     import ttt_weight_layers_amd as tla
     return tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi,
                                   chunk=w.chunk if chunk is None else chunk, segments=segments,
-                                  w1=d["w1"], w3=d["w3"], value_split=value_split)
+                                  w1=d["w1"], w3=d["w3"], value_split=value_split, launch=launch)
 
 
 def run_gpu(w: Workload, d, chunk=None, segments=0, eta_sign=1.0, q_override=None, v_scale=None,

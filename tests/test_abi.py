@@ -70,7 +70,8 @@ def test_query_may_alias_key():
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", 0), ("T", -5), ("d_k", 0),
                                          ("d_v", -1), ("dtype", 7), ("phi", 3), ("chunk", -1),
-                                         ("segments", -2)])
+                                         ("segments", -2), ("value_split", 3), ("launch", 3),
+                                         ("launch", -1)])
 def test_bad_descriptor_fields(field, value):
     d = desc()
     setattr(d, field, value)
@@ -161,6 +162,7 @@ def test_null_handle_calls():
     n = ctypes.c_int32(0)
     assert lib.ttt_la_kernel_times(None, None, 0, ctypes.byref(n)) == tla.TTT_LA_ERR_INVALID_ARG
     assert lib.ttt_la_create(None, None) == tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_wait_status(None, ctypes.byref(n)) == tla.TTT_LA_ERR_INVALID_ARG
 
 
 def test_binding_refuses_missing_library(tmp_path):

@@ -26,6 +26,11 @@ TTT_LA_BF16 = 1
 TTT_LA_PHI_IDENTITY = 0
 TTT_LA_PHI_SWIGLU = 1
 
+TTT_LA_LAUNCH_AUTO = 0
+TTT_LA_LAUNCH_SEPARATE = 1
+TTT_LA_LAUNCH_SINGLE = 2
+_LAUNCH = {"auto": TTT_LA_LAUNCH_AUTO, "separate": TTT_LA_LAUNCH_SEPARATE, "single": TTT_LA_LAUNCH_SINGLE}
+
 TTT_LA_CAUSAL = 0
 TTT_LA_BIDIRECTIONAL = 1 << 0
 TTT_LA_ETA_SCALAR = 0
@@ -38,7 +43,7 @@ class ttt_la_desc(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("d_phi", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("phi", ctypes.c_int32), ("chunk", ctypes.c_int32),
-        ("segments", ctypes.c_int32), ("value_split", ctypes.c_int32),
+        ("segments", ctypes.c_int32), ("value_split", ctypes.c_int32), ("launch", ctypes.c_int32),
         ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p),
     ]
 
@@ -53,7 +58,8 @@ class ttt_la_plan(ctypes.Structure):
 
 
 EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_destroy", "ttt_la_status_string",
-           "ttt_la_check", "ttt_la_get_plan", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times")
+           "ttt_la_check", "ttt_la_get_plan", "ttt_la_wait_status", "ttt_la_enable_kernel_timing",
+           "ttt_la_kernel_times")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -81,6 +87,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_check.restype = ctypes.c_int
     lib.ttt_la_get_plan.argtypes = [vp, ctypes.POINTER(ttt_la_plan)]
     lib.ttt_la_get_plan.restype = ctypes.c_int
+    lib.ttt_la_wait_status.argtypes = [vp, ctypes.POINTER(i32)]
+    lib.ttt_la_wait_status.restype = ctypes.c_int
     lib.ttt_la_enable_kernel_timing.argtypes = [vp, i32]
     lib.ttt_la_enable_kernel_timing.restype = ctypes.c_int
     lib.ttt_la_kernel_times.argtypes = [vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]
@@ -130,6 +138,15 @@ def ttt_la_get_plan(h) -> ttt_la_plan:
     return p
 
 
+def ttt_la_wait_status(h) -> int:
+    """1 if a bounded wait of the single-launch path gave up on h, else 0."""
+    f = ctypes.c_int32(0)
+    st = load_library().ttt_la_wait_status(h, ctypes.byref(f))
+    if st != TTT_LA_OK:
+        raise TTTError(st, "ttt_la_wait_status")
+    return f.value
+
+
 def ttt_la_enable_kernel_timing(h, n_slots: int) -> int:
     return load_library().ttt_la_enable_kernel_timing(h, int(n_slots))
 
@@ -153,7 +170,7 @@ _ETA = {"scalar": TTT_LA_ETA_SCALAR, "per_token": TTT_LA_ETA_PER_TOKEN, "softplu
 
 
 def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0, segments=0,
-              w1=None, w3=None, value_split=0) -> ttt_la_desc:
+              w1=None, w3=None, value_split=0, launch="auto") -> ttt_la_desc:
     d = ttt_la_desc()
     d.B, d.H, d.T, d.d_k, d.d_v = int(B), int(H), int(T), int(d_k), int(d_v)
     d.d_phi = int(d_k if d_phi is None else d_phi)
@@ -162,6 +179,7 @@ def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk
     d.chunk = int(chunk)
     d.segments = int(segments)
     d.value_split = int(value_split)
+    d.launch = _LAUNCH[launch]
     d.w1 = _ptr(w1)
     d.w3 = _ptr(w3)
     return d
@@ -187,9 +205,10 @@ class TTTLinearAttention:
     """
 
     def __init__(self, B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0,
-                 segments=0, w1=None, w3=None, value_split=0):
+                 segments=0, w1=None, w3=None, value_split=0, launch="auto"):
         self._keep = (w1, w3)         # W1/W3 are borrowed by the handle
-        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, segments, w1, w3, value_split)
+        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, segments, w1, w3, value_split,
+                              launch)
         self.dtype = dtype
         st, h = ttt_la_create(self.desc)
         if st != TTT_LA_OK:
@@ -209,6 +228,9 @@ class TTTLinearAttention:
 
     def plan(self) -> ttt_la_plan:
         return ttt_la_get_plan(self.handle)
+
+    def wait_failed(self) -> int:
+        return ttt_la_wait_status(self.handle)
 
     def forward(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
                 out=None, stream=None):

@@ -39,6 +39,15 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libttt_la.so)")
 
 
+# Per-file options.  The 32x32-tile kernels keep their fp32 state in MFMA
+# accumulators that the vector ALUs also scale and convert every chunk; asking
+# for the VGPR form of the MFMA results keeps the state in ordinary VGPRs
+# instead of AGPRs, which would need a copy for every such operation.
+FILE_FLAGS = {
+    "chunk_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -62,7 +71,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     for src in sources:
         obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, "-c", src, "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()

@@ -22,6 +22,7 @@ struct ttt_la_s {
     size_t workspace_bytes;
     int device;
     int n_kernels;
+    unsigned epoch;      // completed launches of the fused path (its counter targets)
     // measurement hook
     std::vector<hipEvent_t> ev_begin, ev_end;
     int calls;
@@ -51,6 +52,7 @@ int check_desc(const ttt_la_desc* d) {
     if (d->phi != TTT_LA_PHI_IDENTITY && d->phi != TTT_LA_PHI_SWIGLU) return TTT_LA_ERR_INVALID_ARG;
     if (d->chunk < 0 || d->segments < 0) return TTT_LA_ERR_INVALID_ARG;
     if (d->value_split < 0 || d->value_split > 2) return TTT_LA_ERR_INVALID_ARG;
+    if (d->launch < TTT_LA_LAUNCH_AUTO || d->launch > TTT_LA_LAUNCH_SINGLE) return TTT_LA_ERR_INVALID_ARG;
     if (d->phi == TTT_LA_PHI_SWIGLU) {
         if (!d->w1 || !d->w3) return TTT_LA_ERR_INVALID_ARG;
         if (!aligned(d->w1, 16) || !aligned(d->w3, 16)) return TTT_LA_ERR_INVALID_ARG;
@@ -125,6 +127,7 @@ void release_events(ttt_la_s* h) {
     h->ev_begin.clear();
     h->ev_end.clear();
     h->calls = 0;
+    h->epoch = 0;
 }
 
 }  // namespace
@@ -162,11 +165,13 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     h->workspace = nullptr;
     h->workspace_bytes = 0;
     h->calls = 0;
+    h->epoch = 0;
     h->fast = desc->dtype == TTT_LA_BF16 && ttt::fast_supported(h->shape, desc->chunk);
     h->n_kernels = 1;
     if (h->fast) {
-        h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments, desc->value_split);
-        h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes;
+        h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments, desc->value_split,
+                               desc->launch == TTT_LA_LAUNCH_SINGLE);
+        h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes + h->fp.zero_bytes;
     }
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
@@ -183,6 +188,16 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
             delete h;
             return e == hipErrorOutOfMemory ? TTT_LA_ERR_OOM : TTT_LA_ERR_HIP;
         }
+        if (h->fast && h->fp.zero_bytes) {
+            // the zeroed page is read, never written, by the kernels
+            char* zp = static_cast<char*>(h->workspace) + h->fp.summary_bytes + h->fp.partial_bytes;
+            if (hipMemset(zp, 0, h->fp.zero_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+                (void)hipGetLastError();
+                (void)hipFree(h->workspace);
+                delete h;
+                return TTT_LA_ERR_HIP;
+            }
+        }
     }
     *out = h;
     return TTT_LA_OK;
@@ -194,7 +209,7 @@ int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, cons
     int st = check_forward(&h->desc, q, k, v, eta, eta_scalar, beta, mode, o);
     if (st != TTT_LA_OK) return st;
 
-    ttt::FwdArgs a;
+    ttt::FwdArgs a{};
     a.q = q;
     a.k = k;
     a.v = v;
@@ -216,7 +231,16 @@ int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, cons
     hipError_t e;
     if (h->fast) {
         int nk = 0;
+        a.epoch = h->epoch + 1;
         e = ttt::launch_fast(h->shape, h->fp, h->workspace, a, eb, ee, &nk);
+        if (e == hipErrorCooperativeLaunchTooLarge && h->fp.fused) {
+            // the fused grid cannot be resident right now: same result in three launches
+            ttt::FastPlan p3 = h->fp;
+            p3.fused = false;
+            e = ttt::launch_fast(h->shape, p3, h->workspace, a, eb, ee, &nk);
+        } else if (e == hipSuccess && h->fp.fused && !a.bidirectional) {
+            h->epoch++;
+        }
         h->n_kernels = nk;
     } else {
         if (eb && hipEventRecord(eb, a.stream) != hipSuccess) return TTT_LA_ERR_HIP;
@@ -240,15 +264,16 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
     const Shape& s = h->shape;
     plan->workspace_bytes = h->workspace_bytes;
     if (h->fast) {
-        plan->path = 1;
+        plan->path = h->fp.wide ? 2 : 1;
         plan->chunk = h->fp.chunk;
         plan->segments = h->fp.segments;
         plan->seg_len = h->fp.seg_len;
         plan->dv_split = h->fp.dv_split;
         plan->phi_split = h->fp.phi_split;
         plan->grid_main = s.n_seq() * h->fp.dv_split * h->fp.phi_split * h->fp.segments;
-        plan->n_kernels = 1 + (h->fp.segments > 1 ? 1 : 0) + (h->fp.segments > 2 ? 1 : 0) +
-                           (h->fp.phi_split > 1 ? 1 : 0);
+        plan->n_kernels = h->fp.fused ? 1
+                                      : 1 + (h->fp.segments > 1 ? 1 : 0) + (h->fp.segments > 2 ? 1 : 0) +
+                                            (h->fp.phi_split > 1 ? 1 : 0);
     } else {
         plan->path = 0;
         plan->chunk = 16;
@@ -259,6 +284,20 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
         plan->grid_main = s.n_seq() * (s.d_v / 16);
         plan->n_kernels = 1;
     }
+    return TTT_LA_OK;
+}
+
+int ttt_la_wait_status(ttt_la_t h, int32_t* failed) {
+    if (!h || !failed) return TTT_LA_ERR_INVALID_ARG;
+    *failed = 0;
+    if (!(h->fast && h->fp.wide && h->fp.fused)) return TTT_LA_OK;
+    unsigned flag = 0;
+    const char* src = static_cast<const char*>(h->workspace) + ttt::wide_flag_offset(h->shape, h->fp);
+    if (hipMemcpy(&flag, src, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) {
+        (void)hipGetLastError();
+        return TTT_LA_ERR_HIP;
+    }
+    *failed = flag != 0;
     return TTT_LA_OK;
 }
 

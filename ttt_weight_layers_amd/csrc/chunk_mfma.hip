@@ -61,8 +61,7 @@
 
 #include "device_common.h"
 #include "internal.h"
-
-#define TTT_LDS __attribute__((address_space(3)))
+#include "lds_tiles.h"
 
 namespace ttt {
 namespace {
@@ -90,108 +89,11 @@ struct ChunkParams {
     size_t n_rows;       // B * H * T
 };
 
-// Element offset of (row, col) in a row-major tile of W bf16 columns whose
-// 16-byte chunks are permuted per row: chunk c of row r is stored at c ^ f(r).
-// f is a bijection over 16 consecutive rows (so 16 lanes reading one chunk of
-// 16 rows hit 16 different bank groups) whose high bits follow the row within
-// a group of 4 (so the 4 rows of a transpose read, each read at up to 4
-// chunks, never share a bank).  W is 64 or 128; col may point inside a chunk.
-template <int W>
-__device__ __forceinline__ int swz(int row, int col) {
-    constexpr int NCH = W / 8;
-    static_assert(NCH == 8 || NCH == 16, "tile width");
-    int f;
-    if constexpr (NCH == 16) {
-        f = 4 * (row & 3) + ((row >> 2) & 3);
-    } else {          // two rows per 64 banks
-        const int h = row >> 1;
-        f = 4 * (h & 1) + ((h >> 1) & 3);
-    }
-    return row * W + (((col >> 3) ^ f) << 3) + (col & 7);
-}
-
-__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& u) { return __builtin_bit_cast(bf16x8, u); }
-
-__device__ __forceinline__ u32x4 lds_read16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-
-__device__ __forceinline__ u32x2 lds_read8(const uint16_t* p) { return *reinterpret_cast<const u32x2*>(p); }
-
-__device__ __forceinline__ bf16x8 join8(const u32x2& a, const u32x2& b) {
-    u32x4 u = {a[0], a[1], b[0], b[1]};
-    return as_bf16x8(u);
-}
-
-// Transpose read of a swizzled W-wide tile.  Lane L = 4e + q of each 16-lane
-// group points at row r0 + e, columns col(q) .. col(q) + 3; lane i of the group
-// receives rows r0 .. r0+3 of column col(i / 4) + i % 4.
-template <int W>
-__device__ __forceinline__ u32x2 tr_read(const uint16_t* tile, int r0, int col_q) {
-    const int L = threadIdx.x & 15;
-    const uint16_t* p = tile + swz<W>(r0 + (L >> 2), col_q);
-    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-    bf16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((TTT_LDS bf16x4_t*)(p));
-    return __builtin_bit_cast(u32x2, x);
-}
-
-// 8 consecutive tokens (r0 .. r0+7) as one MFMA operand; see tr_read for col_q
-template <int W>
-__device__ __forceinline__ u32x4 tr_read8(const uint16_t* tile, int r0, int col_q) {
-    const u32x2 a = tr_read<W>(tile, r0, col_q);
-    const u32x2 b = tr_read<W>(tile, r0 + 4, col_q);
-    return u32x4{a[0], a[1], b[0], b[1]};
-}
-
 // bf16x8 built from two D tiles (4 floats each): elements 0..3 from x, 4..7 from y
 __device__ __forceinline__ bf16x8 pack8(const f32x4& x, const f32x4& y) {
     u32x4 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
                pack_bf16x2(y[2], y[3])};
     return as_bf16x8(u);
-}
-
-// scale 8 packed bf16 by 8 fp32 weights and re-round to bf16
-__device__ __forceinline__ bf16x8 scale8(const u32x4& raw, const float* w) {
-    u32x4 u;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        float lo = __uint_as_float(raw[p] << 16) * w[2 * p];
-        float hi = __uint_as_float(raw[p] & 0xffff0000u) * w[2 * p + 1];
-        u[p] = pack_bf16x2(lo, hi);
-    }
-    return as_bf16x8(u);
-}
-
-// Momentum coefficient tables by a wavefront prefix scan (one wave):
-//   bp[r] = beta^r (prefix product), cc[r] = sum_{u<=r} beta^u (prefix sum), r = 0..C
-template <int C>
-__device__ void coefficient_scan(float beta, float* cc, float* bp) {
-    const int lane = threadIdx.x & 63;
-    float base_p = 1.0f, base_c = 0.0f;
-    for (int r0 = 0; r0 <= C; r0 += 64) {
-        float p = (lane == 0) ? 1.0f : beta;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            float o = __shfl_up(p, d, 64);
-            if (lane >= d) p *= o;
-        }
-        float s = p;   // p = beta^lane; now the prefix sum of p
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            float o = __shfl_up(s, d, 64);
-            if (lane >= d) s += o;
-        }
-        const int r = r0 + lane;
-        if (r <= C) {
-            bp[r] = base_p * p;
-            cc[r] = base_c + base_p * s;
-        }
-        const float p63 = __shfl(p, 63, 64), s63 = __shfl(s, 63, 64);
-        base_c = base_c + base_p * s63;
-        base_p = base_p * p63 * beta;
-    }
 }
 
 // LDS layout of one workgroup (bf16 elements, then floats).  The staged tiles
@@ -576,7 +478,7 @@ chunk_kernel(ChunkParams p) {
             if (t0 > t_begin) intra_and_store(buf ^ 1, n_prev, row_prev);
             if constexpr (SWIGLU) {
                 features(buf, true, true);
-                __syncthreads();
+                lds_barrier();
             }
             scores(buf, n);
             readout(buf, t_scale, true);
@@ -599,7 +501,7 @@ chunk_kernel(ChunkParams p) {
             if (t0 + CH < t_end) fetch(pf, t0 + CH, false, true, true, true);
             if constexpr (SWIGLU) {
                 features(buf, false, true);
-                __syncthreads();
+                lds_barrier();
             }
             read_vt(buf);
             update(buf, n);
@@ -625,7 +527,7 @@ chunk_kernel(ChunkParams p) {
             if (t0 + CH < t_end) fetch(pf, t0 + CH, false, true, true, true);
             if constexpr (SWIGLU) {
                 features(buf, false, true);
-                __syncthreads();
+                lds_barrier();
             }
             read_vt(buf);
             update(buf, n);
@@ -652,7 +554,7 @@ chunk_kernel(ChunkParams p) {
             if (t0 + CH < t_end) fetch(pf, t0 + CH, true, false, false, false);
             if constexpr (SWIGLU) {
                 features(buf, true, false);
-                __syncthreads();
+                lds_barrier();
             }
             readout(buf, 1.0f, false);
 #pragma unroll
@@ -725,8 +627,34 @@ bool fast_supported(const Shape& s, int chunk) {
     return chunk == 0 || chunk == 64 || chunk == 128;
 }
 
-FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split) {
+FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split, bool single_launch) {
     FastPlan p{};
+    if (wide_supported(s) && value_split != 2) {
+        // one workgroup of four waves per sequence segment (chunk_wide.hip)
+        p.wide = true;
+        p.chunk = CH;
+        p.nwaves = 4;
+        p.dvt = 2;
+        p.dv_split = 1;
+        p.phi_split = 1;
+        const int n_chunks = (s.T + CH - 1) / CH;
+        int S = 1;
+        if (segments > 0) {
+            S = std::min(std::min(segments, n_chunks), wide_max_segments());
+        } else {
+            while ((long)s.n_seq() * S < 256 && n_chunks >= 8 * S && 2 * S <= wide_max_segments()) S *= 2;
+        }
+        const int seg_chunks = (n_chunks + S - 1) / S;
+        p.seg_len = seg_chunks * CH;
+        p.segments = (n_chunks + seg_chunks - 1) / seg_chunks;
+        p.summary_bytes = wide_summary_bytes(s, p.segments);
+        p.partial_bytes = 0;
+        p.zero_bytes = wide_zero_bytes(s);
+        // one launch, on request, when every workgroup of the grid can be resident at once
+        const long grid = ((long)s.n_seq() * p.segments + 7) / 8 * 8;
+        p.fused = single_launch && p.segments > 1 && grid <= wide_fused_capacity();
+        return p;
+    }
     // The chunk length is a tiling choice (results differ only by rounding);
     // this path always tiles at 64 tokens.
     p.chunk = CH;
@@ -811,6 +739,7 @@ hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, b
 
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
                        hipEvent_t ev_end, int* n_kernels) {
+    if (p.wide) return launch_wide(s, p, workspace, a, ev_begin, ev_end, n_kernels);
     ChunkParams cp{};
     cp.q = static_cast<const uint16_t*>(a.q);
     cp.k = static_cast<const uint16_t*>(a.k);

@@ -1,0 +1,877 @@
+// Wide-tile bf16 MFMA chunk kernels for gfx950: the TTT forward for the
+// identity feature map with d_k = d_v = 128 (Variants 3-5 of Table 2 on the
+// thelatestinai.com page), one workgroup of four waves per sequence segment.
+//
+// Same chunk algebra as the 16x16 kernels (chunk_mfma.hip): within a chunk of
+// n tokens entered with the carried state (T, M), T = S + beta/(1-beta) M,
+//   o_i = T q_i - beta^{i+2}/(1-beta) M q_i + sum_{j<=i} eta_j c_{i-j} (q_i . k_j) v_j
+//   T  <- T + sum_j eta_j v_j k_j^T / (1 - beta)
+//   M  <- beta^n M + sum_j eta_j beta^{n-1-j} v_j k_j^T
+// with c_r = sum_{u<=r} beta^u: dense causal blocks inside the chunk and a
+// fixed-size fp32 state between chunks, the parallel evaluation of the
+// outer-product accumulation that the kualia.ai blog ("The Linear Attention
+// Equivalence") identifies with linear attention.
+//
+// Why a second kernel family.  On gfx950 the LDS delivers about 128 bytes per
+// clock per CU to 16-byte reads and less to transpose reads, while one
+// v_mfma_f32_16x16x32_bf16 consumes 2 KiB of operands per 16 K flops.  With
+// v_mfma_f32_32x32x16_bf16 the same operand bytes feed twice the flops, and a
+// wave owning 32 value rows of the state reads each staged q and k row once
+// per 32 rows instead of once per 16.  Each of the four waves keeps T and M for
+// its 32 value columns (4 tiles of 32 features x 32 values each, 128 fp32
+// registers) and issues the readout, the update and its share of the score
+// tiles; the workgroup needs one barrier per chunk.
+//
+// Register layouts of v_mfma_f32_32x32x16_bf16 (lane l, n = l % 32, h = l / 32):
+//   A operand  lane holds A[m = n][k = 8h .. 8h+7]
+//   B operand  lane holds B[k = 8h .. 8h+7][n]
+//   D result   lane holds D[m = 8(r/4) + 4h + r%4][n], r = 0..15
+// The state is kept as D tiles of T^T (features x values).  The A-operand rows
+// of the update (features) are permuted by sigma(m) = 16(q/2) + 8h + 4(q%2) + r'
+// for m = 8q + 4h + r', so that accumulator registers 8k .. 8k+7 of a tile
+// hold 8 consecutive features: the state feeds the readout directly as an A
+// operand whose B operand is one 16-byte row read of q.  The value columns
+// (the n index of the update, taken from the transpose read of v) are permuted
+// by pi(m) = 16h + 4q + r', so that after the readout each lane holds 16
+// consecutive output columns of one token (two 16-byte stores).  Inside a
+// 16-token contraction block the lanes of half h take tokens 4h .. 4h+3 and
+// 8+4h .. 8+4h+3, which is exactly how a 32x32 score tile S^T = K Q^T leaves
+// them in its accumulators; the scaled score tiles therefore go to LDS as ready
+// B-operand fragments (16 bytes per lane, no swizzle) and come back with
+// conflict-free 16-byte reads.
+
+#include <algorithm>
+#include <cmath>
+
+#include "device_common.h"
+#include "internal.h"
+#include "lds_tiles.h"
+
+namespace ttt {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+enum WideKind : int { W_OUTPUT = 0, W_SUMMARY = 1, W_BIDIR = 2, W_FUSED = 3 };
+
+constexpr int WC = 64;     // tokens per chunk
+constexpr int WD = 128;    // features (d_k = d_phi) and values (d_v)
+constexpr int WNW = 4;     // waves per workgroup; wave w owns value columns 32w .. 32w+31
+constexpr int WNT = WNW * 64;
+constexpr int WFT = WD / 32;    // feature tiles of the state per wave
+constexpr int WKB = WC / 16;    // 16-token contraction blocks per chunk
+
+struct WideParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* eta;
+    uint16_t* o;
+    float* state;        // segment summaries / entry states
+    const uint16_t* zeros;   // 16 zero bytes, read for rows past the end of a chunk
+    float eta_scalar;
+    float beta;
+    int eta_kind;
+    int T;
+    int seg_count, seg_len;
+    float beta_seg;      // beta^seg_len
+    int n_units;
+    // cooperative (fused) launch only: per-sequence arrival counters (two per
+    // sequence), this launch's epoch, a bound on each wait, and a flag set when a
+    // wait gave up
+    unsigned* counters;
+    unsigned epoch;
+    unsigned spin_limit;
+    unsigned* wait_failed;
+};
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// accumulator registers 8 kh .. 8 kh + 7 of a 32x32 tile as one bf16 operand
+__device__ __forceinline__ bf16x8 pack_half(const f32x16& x, int kh) {
+    const int b = 8 * kh;
+    u32x4 u = {pack_bf16x2(x[b + 0], x[b + 1]), pack_bf16x2(x[b + 2], x[b + 3]),
+               pack_bf16x2(x[b + 4], x[b + 5]), pack_bf16x2(x[b + 6], x[b + 7])};
+    return as_bf16x8(u);
+}
+
+// LDS of one workgroup.  Stage buffers hold the 64 x 128 bf16 tiles of one
+// chunk (XOR-swizzled rows): q, k, v for the output pass, k, v for the
+// summary pass and the first pass of the bidirectional kernel, q for its
+// second pass.  The output pass keeps three buffers (the copy of chunk c + 2
+// is in flight while chunk c is computed), the others four (copies three
+// chunks ahead).  Each buffer is a separate __shared__ object and the chunk
+// loop is unrolled over the ring, so that in every step the buffer being
+// filled by global_load_lds and the buffers being read are distinct objects:
+// the compiler then knows that the transpose reads cannot alias the copies in
+// flight and does not make them wait.  Besides: the score fragments of the
+// current chunk (3 tiles x 2 halves x 64 lanes x 16 bytes) and floats: the
+// per-token weights of every buffer, c_r, beta^r, and the score coefficients
+// k0 c_d at index 64 + d (zero for d < 0).
+struct WideLds {
+    static constexpr int TILE = WC * WD;
+    static constexpr int P_FRAG = 3 * 2 * 64 * 8;
+    static constexpr int N_F32 = 4 * 2 * WC + 2 * (WC + 1) + 2 + 2 * WC;
+};
+template <int KIND>
+struct WideRing {
+    static constexpr bool QKV = KIND == W_OUTPUT || KIND == W_FUSED;
+    static constexpr int NB = QKV ? 3 : 4;                        // buffers
+    static constexpr int TILES = QKV ? 3 : 2;                     // tiles per buffer
+    static constexpr int SIZE = TILES * WideLds::TILE;
+    static constexpr int K_OFF = QKV ? WideLds::TILE : 0;
+    static constexpr int V_OFF = QKV ? 2 * WideLds::TILE : WideLds::TILE;
+    static constexpr int BYTES = 2 * NB * SIZE + 2 * WideLds::P_FRAG + 4 * WideLds::N_F32;
+};
+static_assert(WideRing<W_OUTPUT>::BYTES <= 160 * 1024 && WideRing<W_SUMMARY>::BYTES <= 160 * 1024, "LDS budget");
+
+// s_waitcnt immediate for vmcnt(k) alone (gfx9 encoding: vmcnt in bits 3:0 and 15:14)
+constexpr int vmcnt_imm(int k) { return (k & 15) | ((k >> 4) << 14) | 0x0F70; }
+
+// Arrival barrier of the workgroups of one sequence (W_FUSED only; the
+// cooperative launch makes them co-resident).  Every workgroup adds 1 to
+// *counter and waits until it reaches target = epoch x workgroups per
+// sequence; counters only grow, so nothing is reset between launches.  The
+// release makes this workgroup's global writes visible device-wide before it
+// arrives.  Polling uses relaxed atomic loads (an acquire on every poll would
+// invalidate the caches the other workgroups of the XCD are using); one
+// acquire fence follows the last poll.  The wait is bounded: after spin_limit
+// polls it sets *failed and returns, so the kernel always terminates.
+__device__ __forceinline__ void seq_sync(unsigned* counter, unsigned target, unsigned spin_limit, unsigned* failed) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned polls = 0;
+        while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++polls > spin_limit) {
+                __hip_atomic_store(failed, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+template <bool MOM, bool ETAV, int KIND>
+__global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
+    using L = WideLds;
+    using R = WideRing<KIND>;
+    __shared__ __attribute__((aligned(16))) uint16_t stage_a[R::SIZE];
+    __shared__ __attribute__((aligned(16))) uint16_t stage_b[R::SIZE];
+    __shared__ __attribute__((aligned(16))) uint16_t stage_c[R::SIZE];
+    __shared__ __attribute__((aligned(16))) uint16_t stage_d[R::NB > 3 ? R::SIZE : 8];
+    __shared__ __attribute__((aligned(16))) uint16_t pfrag[R::QKV ? L::P_FRAG : 8];
+    __shared__ __attribute__((aligned(16))) float sF[L::N_F32];
+    float* const w_a = sF;               // per-token weights of the chunk in stage_a
+    float* const w_b = sF + 2 * WC;      // ... stage_b
+    float* const w_c = sF + 4 * WC;      // ... stage_c
+    float* const w_d = sF + 6 * WC;      // ... stage_d
+    float* sC = sF + 8 * WC;             // c_r, r = 0..WC
+    float* sBP = sC + WC + 1;            // beta^r, r = 0..WC
+    float* sK = sBP + WC + 1 + 2;        // k0 c_{x - 64} for x >= 64, 0 below (x = 0..127)
+    auto tq = [](uint16_t* st) { return st; };
+    auto tk = [](uint16_t* st) { return st + R::K_OFF; };
+    auto tv = [](uint16_t* st) { return st + R::V_OFF; };
+    auto s_wt = [](float* w) { return w; };          // eta_j / (1 - beta)
+    auto s_wm = [](float* w) { return w + WC; };     // eta_j beta^{n-1-j}
+    u32x4* const P_lds = reinterpret_cast<u32x4*>(pfrag);
+
+    // ---- unit of work (XCD-aware: consecutive units land on one XCD) --------
+    const int G = gridDim.x;
+    const int u = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (u >= p.n_units) return;
+    const int nseg = (KIND == W_SUMMARY) ? p.seg_count - 1 : (KIND == W_BIDIR ? 1 : p.seg_count);
+    // the workgroups of one sequence must be co-resident for W_FUSED; the launch guarantees it
+    const int seg = u % nseg;
+    const int seq = u / nseg;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n32 = lane & 31, hh = lane >> 5;
+    const int g16 = (lane >> 4) & 1;     // which half of n the lane's 16-lane group covers
+    const int q4 = lane & 3;             // column quartet a lane points at in a transpose read
+    const float beta = p.beta;
+    const float inv1mb = 1.0f / (1.0f - beta);
+    const float t_scale = ETAV ? 1.0f : p.eta_scalar * inv1mb;
+
+    const int t_begin = (KIND == W_BIDIR) ? 0 : seg * p.seg_len;
+    const int t_end = (KIND == W_BIDIR) ? p.T : min(p.T, t_begin + p.seg_len);
+    const size_t seq_row = (size_t)seq * p.T;
+
+    if (wave == 0) coefficient_scan<WC>(beta, sC, sBP);
+
+    // ---- state: T^T and M^T tiles (features x this wave's 32 value columns) --
+    f32x16 Ts[WFT], Ms[MOM ? WFT : 1];
+#pragma unroll
+    for (int ft = 0; ft < WFT; ++ft) Ts[ft] = f32x16{};
+#pragma unroll
+    for (int ft = 0; ft < (MOM ? WFT : 1); ++ft) Ms[ft] = f32x16{};
+
+    // workspace slots: [slot][T | M][wave][ft][r4][lane] f32x4 (16 floats per lane per tile)
+    constexpr size_t TILE_F4 = 4 * 64;
+    constexpr size_t HALF_F4 = (size_t)WNW * WFT * TILE_F4;
+    auto slot_ptr = [&](int s) {
+        return reinterpret_cast<f32x4*>(p.state) + ((size_t)seq * (p.seg_count - 1) + s) * 2 * HALF_F4;
+    };
+
+    // transpose-read columns: value columns in pi order, feature columns in sigma order
+    const int col_v = 32 * wave + 16 * (q4 & 1) + 8 * g16 + 4 * (q4 >> 1);
+    auto col_k = [&](int ft) { return 32 * ft + 16 * g16 + 8 * (q4 & 1) + 4 * (q4 >> 1); };
+
+    // Asynchronous staging (global_load_lds, 16 bytes per lane).  Wave w copies
+    // the row groups 4g .. 4g+3 with g = w, w+4, w+8, w+12 of each tile: one
+    // instruction fills 1 KiB of LDS, lane L landing at byte 16 L = row L / 16,
+    // physical piece L % 16, so the lane reads the logical piece
+    // (L % 16) ^ f(row) of its row; f(row) = 4 (row % 4) + (row / 4) % 4 is
+    // 4 (L / 16) + w for every group this wave copies.  Rows at or past the end
+    // of the chunk read a zeroed page instead.
+    const int lane_row = lane >> 4;
+    const int lane_col = 8 * ((lane & 15) ^ (4 * lane_row + wave));
+    auto stage = [&](uint16_t* st, int t0, bool want_q, bool want_k, bool want_v) {
+        const int n = min(WC, t_end - t0);
+        const size_t row0 = seq_row + t0;
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi) {
+            const int grp = wave + 4 * gi;
+            const int r = 4 * grp + lane_row;
+            const size_t off = (row0 + r) * WD + lane_col;
+            const bool in = r < n;
+            if (want_q) {
+                const uint16_t* src = in ? p.q + off : p.zeros;
+                __builtin_amdgcn_global_load_lds((TTT_GLOBAL const void*)src, (TTT_LDS void*)(tq(st) + grp * 4 * WD), 16, 0, 0);
+            }
+            if (want_k) {
+                const uint16_t* src = in ? p.k + off : p.zeros;
+                __builtin_amdgcn_global_load_lds((TTT_GLOBAL const void*)src, (TTT_LDS void*)(tk(st) + grp * 4 * WD), 16, 0, 0);
+            }
+            if (want_v) {
+                const uint16_t* src = in ? p.v + off : p.zeros;
+                __builtin_amdgcn_global_load_lds((TTT_GLOBAL const void*)src, (TTT_LDS void*)(tv(st) + grp * 4 * WD), 16, 0, 0);
+            }
+        }
+    };
+    // rate of this thread's token of the chunk at t0 (threads 0..63)
+    auto load_eta = [&](int t0) {
+        const int n = min(WC, t_end - t0);
+        float et = p.eta_scalar;
+        if (ETAV) et = tid < n ? p.eta[seq_row + t0 + tid] : 0.0f;
+        return et;
+    };
+    // per-token weights of a chunk of n tokens
+    auto put_weights = [&](float* w, float et, int n) {
+        if (tid < WC) {
+            if (ETAV && p.eta_kind == ETA_SOFTPLUS) et = softplus_f32(et);
+            if (tid >= n) et = 0.0f;
+            s_wt(w)[tid] = et * inv1mb;
+            s_wm(w)[tid] = tid < n ? et * sBP[n - 1 - tid] : 0.0f;
+        }
+    };
+    // the stage copies this wave issued have landed (the barrier that follows publishes them)
+    auto wait_stage = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+
+    // per-token weights of contraction block b in this lane's token order
+    auto weights8 = [&](const float* w, int b, float* out) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(w + 16 * b + 4 * hh);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(w + 16 * b + 8 + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            out[e] = a[e];
+            out[4 + e] = c[e];
+        }
+    };
+
+    // v fragments: lane holds v[16b + slot(h, e)][32 wave + pi(n)]
+    u32x4 vf[WKB];
+    auto read_v = [&](uint16_t* st) {
+#pragma unroll
+        for (int b = 0; b < WKB; ++b) {
+            const u32x2 lo = tr_read<WD>(tv(st), 16 * b + 4 * hh, col_v);
+            const u32x2 hi = tr_read<WD>(tv(st), 16 * b + 8 + 4 * hh, col_v);
+            vf[b] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+
+    // T-part value operands w_T v (the raw fragments for a scalar rate)
+    u32x4 bT[WKB];
+    auto value_weights = [&](float* w) {
+#pragma unroll
+        for (int b = 0; b < WKB; ++b) {
+            if constexpr (ETAV) {
+                float x[8];
+                weights8(s_wt(w), b, x);
+                bT[b] = __builtin_bit_cast(u32x4, scale8(vf[b], x));
+            } else {
+                bT[b] = vf[b];
+            }
+        }
+    };
+
+    // update with the chunk in st (after read_v, value_weights):
+    // T += K^T (w_T v), M = beta^n M + K^T (w_M v)
+    auto update = [&](uint16_t* st, float* w, int n) {
+        if constexpr (MOM) {
+            const float bn = sBP[n];
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft) Ms[ft] *= bn;
+        }
+        const uint16_t* K = tk(st);
+#pragma unroll
+        for (int b = 0; b < WKB; ++b) {
+            bf16x8 bM;
+            if constexpr (MOM) {
+                float x[8];
+                weights8(s_wm(w), b, x);
+                bM = scale8(vf[b], x);
+            }
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft) {
+                const u32x2 lo = tr_read<WD>(K, 16 * b + 4 * hh, col_k(ft));
+                const u32x2 hi = tr_read<WD>(K, 16 * b + 8 + 4 * hh, col_k(ft));
+                const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                Ts[ft] = mfma32(a, as_bf16x8(bT[b]), Ts[ft]);
+                if constexpr (MOM) Ms[ft] = mfma32(a, bM, Ms[ft]);
+            }
+        }
+    };
+
+    // q fragment: B operand Q^T[feature 16 kb + 8h + e][token 32 I + n]
+    auto q_frag = [&](uint16_t* st, int I, int kb) {
+        return as_bf16x8(lds_read16(tq(st) + swz<WD>(32 * I + n32, 16 * kb + 8 * hh)));
+    };
+
+    // readout of the chunk's queries from the state entering it
+    auto readout = [&](uint16_t* st, f32x16* oT, f32x16* oM, bool with_m) {
+#pragma unroll
+        for (int I = 0; I < 2; ++I) {
+            oT[I] = f32x16{};
+            if constexpr (MOM) oM[I] = f32x16{};
+        }
+#pragma unroll
+        for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh) {
+                const bf16x8 b0 = q_frag(st, 0, 2 * ft + kh);
+                const bf16x8 b1 = q_frag(st, 1, 2 * ft + kh);
+                const bf16x8 aT = pack_half(Ts[ft], kh);
+                oT[0] = mfma32(aT, b0, oT[0]);
+                oT[1] = mfma32(aT, b1, oT[1]);
+                if constexpr (MOM) {
+                    if (with_m) {
+                        const bf16x8 aM = pack_half(Ms[ft], kh);
+                        oM[0] = mfma32(aM, b0, oM[0]);
+                        oM[1] = mfma32(aM, b1, oM[1]);
+                    }
+                }
+            }
+    };
+
+    // one output tile: lane holds o[i = 32I + n][32 wave + 16h + r], r = 0..15
+    auto store = [&](const f32x16& o, int I, int n, size_t row0) {
+        const int i = 32 * I + n32;
+        if (i < n) {
+            uint16_t* dst = p.o + (row0 + i) * WD + 32 * wave + 16 * hh;
+            const u32x4 lo = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                              pack_bf16x2(o[6], o[7])};
+            const u32x4 hi = {pack_bf16x2(o[8], o[9]), pack_bf16x2(o[10], o[11]), pack_bf16x2(o[12], o[13]),
+                              pack_bf16x2(o[14], o[15])};
+            *reinterpret_cast<u32x4*>(dst) = lo;
+            *reinterpret_cast<u32x4*>(dst + 8) = hi;
+        }
+    };
+
+    __syncthreads();   // coefficient tables
+
+    // ---- output pass over the segment from its entry state (slot seg - 1) ----
+    auto output_pass = [&]() {
+        // score coefficients: c_{i-j} times (1 - beta) when the rate is folded into
+        // the value operand, else times the scalar rate; 0 above the diagonal
+        const float k0 = ETAV ? (1.0f - beta) : p.eta_scalar;
+        if (tid < 2 * WC) sK[tid] = tid >= WC ? k0 * sC[tid - WC] : 0.0f;
+        // score tile of waves 0..2: (J, I) = (0,0), (0,1), (1,1); the fourth wave has none.
+        // Register r holds j = 32 sJ + 8 (r / 4) + 4h + r % 4 of token i = 32 sI + n.
+        const int sJ = (wave == 2) ? 1 : 0;
+        const int sI = (wave == 0) ? 0 : 1;
+        const float* coef = sK + WC + 32 * (sI - sJ) + n32 - 4 * hh;   // coef[-off_r]
+        // M readout weight of token i: -beta^{i+2} / (1 - beta)
+        float gam[2];
+#pragma unroll
+        for (int I = 0; I < 2; ++I) gam[I] = MOM ? -beta * beta * sBP[32 * I + n32] * inv1mb : 0.0f;
+
+        // prologue: chunks 0 and 1 in flight, then the entry state
+        const bool two = t_begin + WC < t_end;
+        stage(stage_a, t_begin, true, true, true);
+        if (two) stage(stage_b, t_begin + WC, true, true, true);
+        const float et0 = load_eta(t_begin);
+        if (seg > 0) {
+            const f32x4* src = slot_ptr(seg - 1);
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const f32x4 t = src[(((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) Ts[ft][4 * r4 + e] = t[e];
+                    if constexpr (MOM) {
+                        const f32x4 m = src[HALF_F4 + (((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) Ms[ft][4 * r4 + e] = m[e];
+                    }
+                }
+        }
+        put_weights(w_a, et0, min(WC, t_end - t_begin));
+        if (two) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); else wait_stage();   // chunk 0 landed
+        lds_barrier();
+
+        // Chunk c, staged in cur with weights wc.  Chunk c + 1 is in flight (weights
+        // go to wn at the end); the copy of chunk c + 2 into far starts mid-step.
+        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) -> bool {
+            const int n = min(WC, t_end - t0);
+            const size_t row0 = seq_row + t0;
+            const bool has_next = t0 + WC < t_end;
+            const bool has_far = t0 + 2 * WC < t_end;
+            float cf[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) cf[r] = coef[-(8 * (r >> 2) + (r & 3))];
+            const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
+
+            // score tile S^T = K Q^T of this wave, scaled, to LDS as B fragments
+            if (wave < 3) {
+                f32x16 acc = f32x16{};
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    const bf16x8 a = as_bf16x8(lds_read16(tk(cur) + swz<WD>(32 * sJ + n32, 16 * kb + 8 * hh)));
+                    acc = mfma32(a, q_frag(cur, sI, kb), acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] *= cf[r];
+#pragma unroll
+                for (int kh = 0; kh < 2; ++kh)
+                    P_lds[(wave * 2 + kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack_half(acc, kh));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+
+            // readout from the entering state, combined: t_scale T q - beta^{i+2}/(1-beta) M q
+            f32x16 o[2];
+            {
+                f32x16 oT[2], oM[2];
+                readout(cur, oT, oM, true);
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        float x = oT[I][r] * t_scale;
+                        if constexpr (MOM) x = fmaf(gam[I], oM[I][r], x);
+                        o[I][r] = x;
+                    }
+                }
+            }
+            lds_barrier();   // every wave's score fragments
+
+            // intra-chunk term with the weighted value fragments, then the store
+            read_v(cur);
+            value_weights(wc);
+#pragma unroll
+            for (int I = 0; I < 2; ++I) {
+                // blocks 0, 1 from tile (0, I); blocks 2, 3 from tile (1, 1)
+#pragma unroll
+                for (int b = 0; b < 2 * (I + 1); ++b) {
+                    const int tile = (b < 2) ? I : 2;
+                    const bf16x8 pb = as_bf16x8(P_lds[(tile * 2 + (b & 1)) * 64 + lane]);
+                    o[I] = mfma32(as_bf16x8(bT[b]), pb, o[I]);
+                }
+                store(o[I], I, n, row0);
+            }
+            if (has_far) stage(far, t0 + 2 * WC, true, true, true);
+            __builtin_amdgcn_sched_barrier(0);
+            update(cur, wc, n);
+            if (!has_next) return false;
+            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
+            // chunk c + 1 landed; the 12 copies of chunk c + 2 may still be in flight
+            if (has_far) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); else wait_stage();
+            lds_barrier();
+            return true;
+        };
+        for (int t0 = t_begin;; t0 += 3 * WC) {
+            if (!step(stage_a, w_a, w_b, stage_c, t0)) break;
+            if (!step(stage_b, w_b, w_c, stage_a, t0 + WC)) break;
+            if (!step(stage_c, w_c, w_a, stage_b, t0 + 2 * WC)) break;
+        }
+    };
+
+    // ---- summary pass of the fused kernel: three q, k, v buffers, k, v copied two ahead ----
+    auto fused_summary_pass = [&]() {
+        auto issue_kv = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, false, true, true); };
+        auto wait_kv = [&](int t0) {
+            if (t0 + 2 * WC < t_end) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); else wait_stage();
+        };
+        issue_kv(stage_a, t_begin);
+        issue_kv(stage_b, t_begin + WC);
+        put_weights(w_a, load_eta(t_begin), min(WC, t_end - t_begin));
+        wait_kv(t_begin - WC);
+        lds_barrier();
+        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) -> bool {
+            const int n = min(WC, t_end - t0);
+            const bool has_next = t0 + WC < t_end;
+            const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
+            issue_kv(far, t0 + 2 * WC);
+            read_v(cur);
+            value_weights(wc);
+            update(cur, wc, n);
+            if (!has_next) return false;
+            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
+            wait_kv(t0);
+            lds_barrier();
+            return true;
+        };
+        for (int t0 = t_begin;; t0 += 3 * WC) {
+            if (!step(stage_a, w_a, w_b, stage_c, t0)) break;
+            if (!step(stage_b, w_b, w_c, stage_a, t0 + WC)) break;
+            if (!step(stage_c, w_c, w_a, stage_b, t0 + 2 * WC)) break;
+        }
+    };
+
+    auto write_summary = [&](f32x4* dst) {
+#pragma unroll
+        for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                dst[(((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane] =
+                    f32x4{Ts[ft][4 * r4], Ts[ft][4 * r4 + 1], Ts[ft][4 * r4 + 2], Ts[ft][4 * r4 + 3]};
+                if constexpr (MOM)
+                    dst[HALF_F4 + (((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane] =
+                        f32x4{Ms[ft][4 * r4], Ms[ft][4 * r4 + 1], Ms[ft][4 * r4 + 2], Ms[ft][4 * r4 + 3]};
+            }
+    };
+
+    if constexpr (KIND == W_OUTPUT) {
+        output_pass();
+    } else if constexpr (KIND == W_FUSED) {
+        // 1. zero-entry summary of this segment (every segment but the last)
+        if (seg < p.seg_count - 1) {
+            fused_summary_pass();
+            write_summary(slot_ptr(seg));
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft) Ts[ft] = f32x16{};
+#pragma unroll
+            for (int ft = 0; ft < (MOM ? WFT : 1); ++ft) Ms[ft] = f32x16{};
+        }
+        // 2. the sequence's summaries are written: scan them, each workgroup one slice
+        unsigned* cnt = p.counters + 2 * (size_t)seq;
+        const unsigned target = p.epoch * (unsigned)p.seg_count;
+        seq_sync(cnt, target, p.spin_limit, p.wait_failed);
+        {
+            // this workgroup's slice of the float4s of a slot (T, then M with momentum),
+            // every step's summary loaded before the first add: at most 32 loads per thread
+            const int steps = p.seg_count - 1;
+            const int total = (MOM ? 2 : 1) * (int)HALF_F4;
+            const int per = (total + p.seg_count - 1) / p.seg_count;
+            const int e0 = seg * per, e1 = min(total, e0 + per);
+            const int n_el = (e1 - e0 + WNT - 1) / WNT;          // elements per thread
+            const float bL = p.beta_seg;
+            f32x4* base = reinterpret_cast<f32x4*>(p.state) + (size_t)seq * steps * 2 * HALF_F4;
+            constexpr int MAXL = 32;
+            const int batch = max(1, MAXL / steps);               // elements per round of loads
+            for (int eb = 0; eb < n_el; eb += batch) {
+            f32x4 d[MAXL];
+#pragma unroll
+            for (int j = 0; j < MAXL; ++j) {
+                const int ei = eb + j / steps, st = j % steps;
+                const int e = e0 + tid + ei * WNT;
+                if (j / steps < batch && ei < n_el && e < e1) d[j] = base[(size_t)st * 2 * HALF_F4 + e];
+            }
+#pragma unroll
+            for (int j = 0; j < MAXL; ++j) {
+                const int ei = eb + j / steps, st = j % steps;
+                const int e = e0 + tid + ei * WNT;
+                if (j / steps < batch && ei < n_el && e < e1) {
+                    // running prefix of element ei lives in d[j]: add the previous step's
+                    if (st > 0) {
+                        if (e >= (int)HALF_F4) {
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) d[j][r] = fmaf(bL, d[j - 1][r], d[j][r]);
+                        } else {
+                            d[j] += d[j - 1];
+                        }
+                    }
+                    base[(size_t)st * 2 * HALF_F4 + e] = d[j];
+                }
+            }
+            }
+        }
+        // 3. entry states are complete: the output pass
+        seq_sync(cnt + 1, target, p.spin_limit, p.wait_failed);
+        output_pass();
+    } else {
+        // SUMMARY: zero-entry state change of the segment.  BIDIR: the same over
+        // the whole sequence, then every query reads S = t_scale T - kappa M.
+        // Four buffers of k, v: copies run three chunks ahead (8 per chunk and wave).
+        auto issue_kv = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, false, true, true); };
+        // wait until the copies of the chunk at t0 landed, with those of later chunks in flight
+        auto wait_kv = [&](int t0) {
+            const int later = t0 + 3 * WC < t_end ? 2 : (t0 + 2 * WC < t_end ? 1 : 0);
+            if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+            else wait_stage();
+        };
+        issue_kv(stage_a, t_begin);
+        issue_kv(stage_b, t_begin + WC);
+        issue_kv(stage_c, t_begin + 2 * WC);
+        put_weights(w_a, load_eta(t_begin), min(WC, t_end - t_begin));
+        wait_kv(t_begin - WC);
+        lds_barrier();
+        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) -> bool {
+            const int n = min(WC, t_end - t0);
+            const bool has_next = t0 + WC < t_end;
+            const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
+            issue_kv(far, t0 + 3 * WC);
+            read_v(cur);
+            value_weights(wc);
+            update(cur, wc, n);
+            if (!has_next) return false;
+            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
+            wait_kv(t0);
+            lds_barrier();
+            return true;
+        };
+        for (int t0 = t_begin;; t0 += 4 * WC) {
+            if (!step(stage_a, w_a, w_b, stage_d, t0)) break;
+            if (!step(stage_b, w_b, w_c, stage_a, t0 + WC)) break;
+            if (!step(stage_c, w_c, w_d, stage_b, t0 + 2 * WC)) break;
+            if (!step(stage_d, w_d, w_a, stage_c, t0 + 3 * WC)) break;
+        }
+        if constexpr (KIND == W_SUMMARY) {
+            f32x4* dst = slot_ptr(seg);
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    dst[(((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane] =
+                        f32x4{Ts[ft][4 * r4], Ts[ft][4 * r4 + 1], Ts[ft][4 * r4 + 2], Ts[ft][4 * r4 + 3]};
+                    if constexpr (MOM)
+                        dst[HALF_F4 + (((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane] =
+                            f32x4{Ms[ft][4 * r4], Ms[ft][4 * r4 + 1], Ms[ft][4 * r4 + 2], Ms[ft][4 * r4 + 3]};
+                }
+        } else {
+            const float kappa = beta * inv1mb;
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float x = Ts[ft][r] * t_scale;
+                    if constexpr (MOM) x = fmaf(-kappa, Ms[ft][r], x);
+                    Ts[ft][r] = x;
+                }
+            __syncthreads();   // every wave is done with the stage buffers
+            // queries: four buffers, copies three chunks ahead (4 per chunk and wave)
+            auto issue_q = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, true, false, false); };
+            auto wait_q = [&](int t0) {
+                const int later = t0 + 3 * WC < t_end ? 2 : (t0 + 2 * WC < t_end ? 1 : 0);
+                if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+                else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+                else wait_stage();
+            };
+            issue_q(stage_a, 0);
+            issue_q(stage_b, WC);
+            issue_q(stage_c, 2 * WC);
+            wait_q(-WC);
+            lds_barrier();
+            auto qstep = [&](uint16_t* cur, uint16_t* far, int t0) -> bool {
+                const int n = min(WC, t_end - t0);
+                const size_t row0 = seq_row + t0;
+                const bool has_next = t0 + WC < t_end;
+                issue_q(far, t0 + 3 * WC);
+                f32x16 oT[2], oM[2];
+                readout(cur, oT, oM, false);
+#pragma unroll
+                for (int I = 0; I < 2; ++I) store(oT[I], I, n, row0);
+                if (!has_next) return false;
+                wait_q(t0);
+                lds_barrier();
+                return true;
+            };
+            for (int t0 = 0;; t0 += 4 * WC) {
+                if (!qstep(stage_a, stage_d, t0)) break;
+                if (!qstep(stage_b, stage_a, t0 + WC)) break;
+                if (!qstep(stage_c, stage_b, t0 + 2 * WC)) break;
+                if (!qstep(stage_d, stage_c, t0 + 3 * WC)) break;
+            }
+        }
+    }
+}
+
+// Composes segment summaries into entry states, in place:
+//   T <- T + dT_s,  M <- beta^L M + dM_s,  slot s <- (T, M) = entry state of segment s + 1.
+// One thread per float4 of one sequence's state; all summaries are loaded
+// before the first store so that the loads overlap.
+template <int MAXS>
+__global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_steps, float bL, int mom) {
+    constexpr int HALF = WNW * WFT * 4 * 64;       // float4s of T (and of M) per slot
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)n_seq * HALF) return;
+    const size_t seqi = idx / HALF, e = idx % HALF;
+    f32x4* base = reinterpret_cast<f32x4*>(state) + seqi * n_steps * 2 * HALF + e;
+    f32x4 dT[MAXS], dM[MAXS];
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+        if (s < n_steps) {
+            dT[s] = base[(size_t)s * 2 * HALF];
+            if (mom) dM[s] = base[(size_t)s * 2 * HALF + HALF];
+        }
+    }
+    f32x4 T = {0.f, 0.f, 0.f, 0.f}, M = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+        if (s < n_steps) {
+            T += dT[s];
+            base[(size_t)s * 2 * HALF] = T;
+            if (mom) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) M[r] = fmaf(bL, M[r], dM[s][r]);
+                base[(size_t)s * 2 * HALF + HALF] = M;
+            }
+        }
+    }
+}
+
+template <bool MOM, bool ETAV, int KIND>
+hipError_t launch_wide_one(const WideParams& wp, hipStream_t st) {
+    const int grid = (wp.n_units + 7) / 8 * 8;
+    hipLaunchKernelGGL((wide_kernel<MOM, ETAV, KIND>), dim3(grid), dim3(WNT), 0, st, wp);
+    return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_wide_kind(bool mom, bool etav, const WideParams& wp, hipStream_t st) {
+    if (mom) return etav ? launch_wide_one<true, true, KIND>(wp, st) : launch_wide_one<true, false, KIND>(wp, st);
+    return etav ? launch_wide_one<false, true, KIND>(wp, st) : launch_wide_one<false, false, KIND>(wp, st);
+}
+
+}  // namespace
+
+int wide_fused_capacity() {
+    static int cached = -1;
+    if (cached >= 0) return cached;
+    int dev = 0, coop = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, wide_kernel<true, true, W_FUSED>, WNT, 0) !=
+            hipSuccess) {
+        (void)hipGetLastError();
+        return cached = 0;
+    }
+    return cached = coop ? per_cu * cus : 0;
+}
+
+size_t wide_zero_bytes(const Shape& s) {
+    // zero page, then two counters per sequence and the wait-failed flag
+    return 256 + ((size_t)(2 * s.n_seq() + 1) * sizeof(unsigned) + 255) / 256 * 256;
+}
+
+size_t wide_flag_offset(const Shape& s, const FastPlan& p) {
+    return p.summary_bytes + 256 + (size_t)2 * s.n_seq() * sizeof(unsigned);
+}
+
+bool wide_supported(const Shape& s) {
+    return s.bf16 && !s.swiglu && s.d_k == WD && s.d_v == WD && s.d_phi == WD;
+}
+
+size_t wide_summary_bytes(const Shape& s, int segments) {
+    if (segments <= 1) return 0;
+    return (size_t)s.n_seq() * (segments - 1) * 2 * WD * WD * sizeof(float);
+}
+
+int wide_max_segments() { return 16; }
+
+hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
+                       hipEvent_t ev_end, int* n_kernels) {
+    WideParams wp{};
+    wp.q = static_cast<const uint16_t*>(a.q);
+    wp.k = static_cast<const uint16_t*>(a.k);
+    wp.v = static_cast<const uint16_t*>(a.v);
+    wp.eta = a.eta;
+    wp.o = static_cast<uint16_t*>(a.o);
+    wp.state = static_cast<float*>(workspace);
+    wp.zeros = reinterpret_cast<const uint16_t*>(static_cast<const char*>(workspace) + p.summary_bytes);
+    wp.eta_scalar = a.eta_scalar;
+    wp.beta = a.beta;
+    wp.eta_kind = a.eta_kind;
+    wp.T = s.T;
+    const bool mom = a.beta != 0.0f;
+    const bool etav = a.eta_kind != ETA_SCALAR;
+    wp.beta_seg = (float)std::pow((double)a.beta, (double)p.seg_len);
+    hipStream_t st = a.stream;
+    hipError_t e = hipSuccess;
+    int nk = 0;
+    if (!a.bidirectional && p.fused) {
+        char* z = static_cast<char*>(workspace) + p.summary_bytes + 256;
+        wp.seg_count = p.segments;
+        wp.seg_len = p.seg_len;
+        wp.n_units = s.n_seq() * p.segments;
+        wp.counters = reinterpret_cast<unsigned*>(z);
+        wp.wait_failed = wp.counters + 2 * s.n_seq();
+        wp.epoch = a.epoch;
+        wp.spin_limit = 1u << 20;
+        const int grid = (wp.n_units + 7) / 8 * 8;
+        void* args[] = {&wp};
+        const void* fn = mom ? (etav ? (const void*)wide_kernel<true, true, W_FUSED>
+                                     : (const void*)wide_kernel<true, false, W_FUSED>)
+                             : (etav ? (const void*)wide_kernel<false, true, W_FUSED>
+                                     : (const void*)wide_kernel<false, false, W_FUSED>);
+        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+        e = hipLaunchCooperativeKernel(fn, dim3(grid), dim3(WNT), args, 0, st);
+        if (e == hipSuccess) {
+            if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+            if (n_kernels) *n_kernels = 1;
+            return hipSuccess;
+        }
+        // the grid cannot be made resident right now; the caller takes the three-kernel
+        // path and does not advance the epoch (no workgroup of this launch ran)
+        (void)hipGetLastError();
+        return hipErrorCooperativeLaunchTooLarge;
+    }
+    if (a.bidirectional) {
+        wp.seg_count = 1;
+        wp.seg_len = s.T;
+        wp.n_units = s.n_seq();
+        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+        if ((e = launch_wide_kind<W_BIDIR>(mom, etav, wp, st)) != hipSuccess) return e;
+        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        ++nk;
+    } else {
+        wp.seg_count = p.segments;
+        wp.seg_len = p.seg_len;
+        if (p.segments > 1) {
+            wp.n_units = s.n_seq() * (p.segments - 1);
+            if ((e = launch_wide_kind<W_SUMMARY>(mom, etav, wp, st)) != hipSuccess) return e;
+            ++nk;
+            if (p.segments > 2) {
+                constexpr int HALF = WNW * WFT * 4 * 64;
+                const size_t n_threads = (size_t)s.n_seq() * HALF;
+                const float bL = (float)std::pow((double)a.beta, (double)p.seg_len);
+                const dim3 grid((unsigned)((n_threads + 255) / 256));
+                if (p.segments - 1 <= 7)
+                    hipLaunchKernelGGL(wide_scan<7>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments - 1, bL,
+                                       mom ? 1 : 0);
+                else
+                    hipLaunchKernelGGL(wide_scan<15>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments - 1,
+                                       bL, mom ? 1 : 0);
+                if ((e = hipGetLastError()) != hipSuccess) return e;
+                ++nk;
+            }
+        }
+        wp.n_units = s.n_seq() * p.segments;
+        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+        if ((e = launch_wide_kind<W_OUTPUT>(mom, etav, wp, st)) != hipSuccess) return e;
+        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        ++nk;
+    }
+    if (n_kernels) *n_kernels = nk;
+    return hipSuccess;
+}
+
+}  // namespace ttt

@@ -22,6 +22,7 @@ struct FwdArgs {
     bool bidirectional;
     void* o;
     hipStream_t stream;
+    unsigned epoch;    // 1, 2, 3, ... per forward of a handle whose plan is fused
 };
 
 // Shape of one layer (copied from the descriptor).
@@ -50,10 +51,27 @@ struct FastPlan {
     int seg_len;      // tokens per segment (multiple of chunk)
     size_t summary_bytes;   // segment summaries / entry states
     size_t partial_bytes;   // fp32 partial outputs when phi_split > 1
+    bool wide;              // 32x32-tile kernels (chunk_wide.hip)
+    bool fused;             // wide causal path as one cooperative launch (summary, scan, output)
+    size_t zero_bytes;      // zeroed tail of the workspace (cleared once at create): a page read
+                            // for rows past a chunk end, then the fused path's counters
 };
 
 bool fast_supported(const Shape& s, int chunk);
-FastPlan fast_plan(const Shape& s, int chunk, int segments, int value_split);
+FastPlan fast_plan(const Shape& s, int chunk, int segments, int value_split, bool single_launch);
+// 32x32-tile kernels: identity map, d_k = d_v = 128, bf16
+bool wide_supported(const Shape& s);
+size_t wide_summary_bytes(const Shape& s, int segments);
+int wide_max_segments();
+// workgroups the fused cooperative kernel can keep resident at once (0 if the
+// device cannot launch cooperatively)
+int wide_fused_capacity();
+size_t wide_zero_bytes(const Shape& s);
+// offset of the fused path's wait-failed flag inside the workspace
+size_t wide_flag_offset(const Shape& s, const FastPlan& p);
+hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
+                       hipEvent_t ev_end, int* n_kernels);
+
 // Enqueues the whole forward (all kernels).  If ev_begin/ev_end are non-null
 // they are recorded around the output kernel.
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a,
