@@ -76,7 +76,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
     tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs], verbose)
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

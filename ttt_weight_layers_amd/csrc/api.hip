@@ -189,7 +189,7 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
             return e == hipErrorOutOfMemory ? TTT_LA_ERR_OOM : TTT_LA_ERR_HIP;
         }
         if (h->fast && h->fp.zero_bytes) {
-            // the zeroed page is read, never written, by the kernels
+            // counters of the single-launch path: they start at zero and only grow
             char* zp = static_cast<char*>(h->workspace) + h->fp.summary_bytes + h->fp.partial_bytes;
             if (hipMemset(zp, 0, h->fp.zero_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
                 (void)hipGetLastError();

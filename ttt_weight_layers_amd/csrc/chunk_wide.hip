@@ -68,7 +68,6 @@ struct WideParams {
     const float* eta;
     uint16_t* o;
     float* state;        // segment summaries / entry states
-    const uint16_t* zeros;   // 16 zero bytes, read for rows past the end of a chunk
     float eta_scalar;
     float beta;
     int eta_kind;
@@ -100,9 +99,8 @@ __device__ __forceinline__ bf16x8 pack_half(const f32x16& x, int kh) {
 // LDS of one workgroup.  Stage buffers hold the 64 x 128 bf16 tiles of one
 // chunk (XOR-swizzled rows): q, k, v for the output pass, k, v for the
 // summary pass and the first pass of the bidirectional kernel, q for its
-// second pass.  The output pass keeps three buffers (the copy of chunk c + 2
-// is in flight while chunk c is computed), the others four (copies three
-// chunks ahead).  Each buffer is a separate __shared__ object and the chunk
+// second pass.  Three buffers: the copy of chunk c + 2 is in flight while
+// chunk c is computed.  Each buffer is a separate __shared__ object and the chunk
 // loop is unrolled over the ring, so that in every step the buffer being
 // filled by global_load_lds and the buffers being read are distinct objects:
 // the compiler then knows that the transpose reads cannot alias the copies in
@@ -118,7 +116,7 @@ struct WideLds {
 template <int KIND>
 struct WideRing {
     static constexpr bool QKV = KIND == W_OUTPUT || KIND == W_FUSED;
-    static constexpr int NB = QKV ? 3 : 4;                        // buffers
+    static constexpr int NB = 3;                                  // buffers
     static constexpr int TILES = QKV ? 3 : 2;                     // tiles per buffer
     static constexpr int SIZE = TILES * WideLds::TILE;
     static constexpr int K_OFF = QKV ? WideLds::TILE : 0;
@@ -163,13 +161,11 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t stage_a[R::SIZE];
     __shared__ __attribute__((aligned(16))) uint16_t stage_b[R::SIZE];
     __shared__ __attribute__((aligned(16))) uint16_t stage_c[R::SIZE];
-    __shared__ __attribute__((aligned(16))) uint16_t stage_d[R::NB > 3 ? R::SIZE : 8];
     __shared__ __attribute__((aligned(16))) uint16_t pfrag[R::QKV ? L::P_FRAG : 8];
     __shared__ __attribute__((aligned(16))) float sF[L::N_F32];
     float* const w_a = sF;               // per-token weights of the chunk in stage_a
     float* const w_b = sF + 2 * WC;      // ... stage_b
     float* const w_c = sF + 4 * WC;      // ... stage_c
-    float* const w_d = sF + 6 * WC;      // ... stage_d
     float* sC = sF + 8 * WC;             // c_r, r = 0..WC
     float* sBP = sC + WC + 1;            // beta^r, r = 0..WC
     float* sK = sBP + WC + 1 + 2;        // k0 c_{x - 64} for x >= 64, 0 below (x = 0..127)
@@ -222,37 +218,44 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     const int col_v = 32 * wave + 16 * (q4 & 1) + 8 * g16 + 4 * (q4 >> 1);
     auto col_k = [&](int ft) { return 32 * ft + 16 * g16 + 8 * (q4 & 1) + 4 * (q4 >> 1); };
 
-    // Asynchronous staging (global_load_lds, 16 bytes per lane).  Wave w copies
-    // the row groups 4g .. 4g+3 with g = w, w+4, w+8, w+12 of each tile: one
-    // instruction fills 1 KiB of LDS, lane L landing at byte 16 L = row L / 16,
-    // physical piece L % 16, so the lane reads the logical piece
+    // Asynchronous staging: buffer loads straight into LDS, 16 bytes per lane.
+    // Wave w copies the row groups 4g .. 4g+3 with g = w, w+4, w+8, w+12 of each
+    // tile: one instruction fills 1 KiB of LDS, lane L landing at byte 16 L =
+    // row L / 16, physical piece L % 16, so the lane reads the logical piece
     // (L % 16) ^ f(row) of its row; f(row) = 4 (row % 4) + (row / 4) % 4 is
-    // 4 (L / 16) + w for every group this wave copies.  Rows at or past the end
-    // of the chunk read a zeroed page instead.
+    // 4 (L / 16) + w for every group this wave copies.  Each copy goes through a
+    // buffer resource spanning exactly the chunk's n valid rows: rows past the
+    // end of the sequence read as zero (range check), and the lane offsets are
+    // the same for every chunk (four registers).
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const int lane_row = lane >> 4;
     const int lane_col = 8 * ((lane & 15) ^ (4 * lane_row + wave));
-    auto stage = [&](uint16_t* st, int t0, bool want_q, bool want_k, bool want_v) {
+    int voff[4];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) voff[gi] = 2 * ((4 * (wave + 4 * gi) + lane_row) * WD + lane_col);
+    auto chunk_rsrc = [&](const uint16_t* tensor, size_t row0, int n) {
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(tensor + row0 * WD), (short)0, n * WD * 2, 0x00020000);
+    };
+    // copies of row group gi of this wave (one instruction per tensor)
+    // (the resources are bound to locals before use: passed as temporaries straight
+    // into the builtin they make the host pass drop the kernels without a diagnostic)
+    auto stage_group = [&](uint16_t* st, int t0, int gi, bool want_q, bool want_k, bool want_v) {
         const int n = min(WC, t_end - t0);
         const size_t row0 = seq_row + t0;
+        const int grp = wave_s + 4 * gi;
+        const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(p.q, row0, n);
+        const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(p.k, row0, n);
+        const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(p.v, row0, n);
+        if (want_q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (TTT_LDS void*)(tq(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
+        if (want_k)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (TTT_LDS void*)(tk(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
+        if (want_v)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (TTT_LDS void*)(tv(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
+    };
+    auto stage = [&](uint16_t* st, int t0, bool want_q, bool want_k, bool want_v) {
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) {
-            const int grp = wave + 4 * gi;
-            const int r = 4 * grp + lane_row;
-            const size_t off = (row0 + r) * WD + lane_col;
-            const bool in = r < n;
-            if (want_q) {
-                const uint16_t* src = in ? p.q + off : p.zeros;
-                __builtin_amdgcn_global_load_lds((TTT_GLOBAL const void*)src, (TTT_LDS void*)(tq(st) + grp * 4 * WD), 16, 0, 0);
-            }
-            if (want_k) {
-                const uint16_t* src = in ? p.k + off : p.zeros;
-                __builtin_amdgcn_global_load_lds((TTT_GLOBAL const void*)src, (TTT_LDS void*)(tk(st) + grp * 4 * WD), 16, 0, 0);
-            }
-            if (want_v) {
-                const uint16_t* src = in ? p.v + off : p.zeros;
-                __builtin_amdgcn_global_load_lds((TTT_GLOBAL const void*)src, (TTT_LDS void*)(tv(st) + grp * 4 * WD), 16, 0, 0);
-            }
-        }
+        for (int gi = 0; gi < 4; ++gi) stage_group(st, t0, gi, want_q, want_k, want_v);
     };
     // rate of this thread's token of the chunk at t0 (threads 0..63)
     auto load_eta = [&](int t0) {
@@ -311,16 +314,26 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     };
 
     // update with the chunk in st (after read_v, value_weights):
-    // T += K^T (w_T v), M = beta^n M + K^T (w_M v)
-    auto update = [&](uint16_t* st, float* w, int n) {
-        if constexpr (MOM) {
-            const float bn = sBP[n];
-#pragma unroll
-            for (int ft = 0; ft < WFT; ++ft) Ms[ft] *= bn;
-        }
+    // T += K^T (w_T v), M = beta^n M + K^T (w_M v).  The K fragments of block b + 1
+    // are read while block b's products run; if far is set, the copy of the chunk
+    // at t_far into far is issued a row group per block, between the products.
+    auto update = [&](uint16_t* st, float* w, int n, uint16_t* far, int t_far, bool far_q) {
         const uint16_t* K = tk(st);
+        const float bn = MOM ? sBP[n] : 1.0f;
+        u32x4 kf[2][WFT];
+        auto load_k = [&](int b, u32x4* dst) {
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft) {
+                const u32x2 lo = tr_read<WD>(K, 16 * b + 4 * hh, col_k(ft));
+                const u32x2 hi = tr_read<WD>(K, 16 * b + 8 + 4 * hh, col_k(ft));
+                dst[ft] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        };
+        load_k(0, kf[0]);
 #pragma unroll
         for (int b = 0; b < WKB; ++b) {
+            if (b + 1 < WKB) load_k(b + 1, kf[(b + 1) & 1]);
+            if (far) stage_group(far, t_far, b, far_q, true, true);
             bf16x8 bM;
             if constexpr (MOM) {
                 float x[8];
@@ -329,11 +342,12 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             }
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft) {
-                const u32x2 lo = tr_read<WD>(K, 16 * b + 4 * hh, col_k(ft));
-                const u32x2 hi = tr_read<WD>(K, 16 * b + 8 + 4 * hh, col_k(ft));
-                const bf16x8 a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+                const bf16x8 a = as_bf16x8(kf[b & 1][ft]);
                 Ts[ft] = mfma32(a, as_bf16x8(bT[b]), Ts[ft]);
-                if constexpr (MOM) Ms[ft] = mfma32(a, bM, Ms[ft]);
+                if constexpr (MOM) {
+                    if (b == 0) Ms[ft] *= bn;
+                    Ms[ft] = mfma32(a, bM, Ms[ft]);
+                }
             }
         }
     };
@@ -485,9 +499,8 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 }
                 store(o[I], I, n, row0);
             }
-            if (has_far) stage(far, t0 + 2 * WC, true, true, true);
             __builtin_amdgcn_sched_barrier(0);
-            update(cur, wc, n);
+            update(cur, wc, n, has_far ? far : nullptr, t0 + 2 * WC, true);
             if (!has_next) return false;
             put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
             // chunk c + 1 landed; the 12 copies of chunk c + 2 may still be in flight
@@ -502,8 +515,8 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         }
     };
 
-    // ---- summary pass of the fused kernel: three q, k, v buffers, k, v copied two ahead ----
-    auto fused_summary_pass = [&]() {
+    // ---- summary pass: three stage buffers, k, v copied two chunks ahead ----
+    auto summary_pass = [&]() {
         auto issue_kv = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, false, true, true); };
         auto wait_kv = [&](int t0) {
             if (t0 + 2 * WC < t_end) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); else wait_stage();
@@ -517,10 +530,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             const int n = min(WC, t_end - t0);
             const bool has_next = t0 + WC < t_end;
             const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
-            issue_kv(far, t0 + 2 * WC);
             read_v(cur);
             value_weights(wc);
-            update(cur, wc, n);
+            update(cur, wc, n, t0 + 2 * WC < t_end ? far : nullptr, t0 + 2 * WC, false);
             if (!has_next) return false;
             put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
             wait_kv(t0);
@@ -552,7 +564,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     } else if constexpr (KIND == W_FUSED) {
         // 1. zero-entry summary of this segment (every segment but the last)
         if (seg < p.seg_count - 1) {
-            fused_summary_pass();
+            summary_pass();
             write_summary(slot_ptr(seg));
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft) Ts[ft] = f32x16{};
@@ -608,41 +620,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     } else {
         // SUMMARY: zero-entry state change of the segment.  BIDIR: the same over
         // the whole sequence, then every query reads S = t_scale T - kappa M.
-        // Four buffers of k, v: copies run three chunks ahead (8 per chunk and wave).
-        auto issue_kv = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, false, true, true); };
-        // wait until the copies of the chunk at t0 landed, with those of later chunks in flight
-        auto wait_kv = [&](int t0) {
-            const int later = t0 + 3 * WC < t_end ? 2 : (t0 + 2 * WC < t_end ? 1 : 0);
-            if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
-            else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-            else wait_stage();
-        };
-        issue_kv(stage_a, t_begin);
-        issue_kv(stage_b, t_begin + WC);
-        issue_kv(stage_c, t_begin + 2 * WC);
-        put_weights(w_a, load_eta(t_begin), min(WC, t_end - t_begin));
-        wait_kv(t_begin - WC);
-        lds_barrier();
-        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) -> bool {
-            const int n = min(WC, t_end - t0);
-            const bool has_next = t0 + WC < t_end;
-            const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
-            issue_kv(far, t0 + 3 * WC);
-            read_v(cur);
-            value_weights(wc);
-            update(cur, wc, n);
-            if (!has_next) return false;
-            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
-            wait_kv(t0);
-            lds_barrier();
-            return true;
-        };
-        for (int t0 = t_begin;; t0 += 4 * WC) {
-            if (!step(stage_a, w_a, w_b, stage_d, t0)) break;
-            if (!step(stage_b, w_b, w_c, stage_a, t0 + WC)) break;
-            if (!step(stage_c, w_c, w_d, stage_b, t0 + 2 * WC)) break;
-            if (!step(stage_d, w_d, w_a, stage_c, t0 + 3 * WC)) break;
-        }
+        summary_pass();
         if constexpr (KIND == W_SUMMARY) {
             f32x4* dst = slot_ptr(seg);
 #pragma unroll
@@ -666,24 +644,20 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                     Ts[ft][r] = x;
                 }
             __syncthreads();   // every wave is done with the stage buffers
-            // queries: four buffers, copies three chunks ahead (4 per chunk and wave)
+            // queries: three buffers, copies two chunks ahead (4 per chunk and wave)
             auto issue_q = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, true, false, false); };
             auto wait_q = [&](int t0) {
-                const int later = t0 + 3 * WC < t_end ? 2 : (t0 + 2 * WC < t_end ? 1 : 0);
-                if (later == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-                else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-                else wait_stage();
+                if (t0 + 2 * WC < t_end) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); else wait_stage();
             };
             issue_q(stage_a, 0);
             issue_q(stage_b, WC);
-            issue_q(stage_c, 2 * WC);
             wait_q(-WC);
             lds_barrier();
             auto qstep = [&](uint16_t* cur, uint16_t* far, int t0) -> bool {
                 const int n = min(WC, t_end - t0);
                 const size_t row0 = seq_row + t0;
                 const bool has_next = t0 + WC < t_end;
-                issue_q(far, t0 + 3 * WC);
+                issue_q(far, t0 + 2 * WC);
                 f32x16 oT[2], oM[2];
                 readout(cur, oT, oM, false);
 #pragma unroll
@@ -693,11 +667,10 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 lds_barrier();
                 return true;
             };
-            for (int t0 = 0;; t0 += 4 * WC) {
-                if (!qstep(stage_a, stage_d, t0)) break;
+            for (int t0 = 0;; t0 += 3 * WC) {
+                if (!qstep(stage_a, stage_c, t0)) break;
                 if (!qstep(stage_b, stage_a, t0 + WC)) break;
                 if (!qstep(stage_c, stage_b, t0 + 2 * WC)) break;
-                if (!qstep(stage_d, stage_c, t0 + 3 * WC)) break;
             }
         }
     }
@@ -768,12 +741,12 @@ int wide_fused_capacity() {
 }
 
 size_t wide_zero_bytes(const Shape& s) {
-    // zero page, then two counters per sequence and the wait-failed flag
-    return 256 + ((size_t)(2 * s.n_seq() + 1) * sizeof(unsigned) + 255) / 256 * 256;
+    // two counters per sequence and the wait-failed flag
+    return ((size_t)(2 * s.n_seq() + 1) * sizeof(unsigned) + 255) / 256 * 256;
 }
 
 size_t wide_flag_offset(const Shape& s, const FastPlan& p) {
-    return p.summary_bytes + 256 + (size_t)2 * s.n_seq() * sizeof(unsigned);
+    return p.summary_bytes + (size_t)2 * s.n_seq() * sizeof(unsigned);
 }
 
 bool wide_supported(const Shape& s) {
@@ -796,7 +769,6 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
     wp.eta = a.eta;
     wp.o = static_cast<uint16_t*>(a.o);
     wp.state = static_cast<float*>(workspace);
-    wp.zeros = reinterpret_cast<const uint16_t*>(static_cast<const char*>(workspace) + p.summary_bytes);
     wp.eta_scalar = a.eta_scalar;
     wp.beta = a.beta;
     wp.eta_kind = a.eta_kind;
@@ -808,7 +780,7 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
     hipError_t e = hipSuccess;
     int nk = 0;
     if (!a.bidirectional && p.fused) {
-        char* z = static_cast<char*>(workspace) + p.summary_bytes + 256;
+        char* z = static_cast<char*>(workspace) + p.summary_bytes;
         wp.seg_count = p.segments;
         wp.seg_len = p.seg_len;
         wp.n_units = s.n_seq() * p.segments;

@@ -53,8 +53,8 @@ struct FastPlan {
     size_t partial_bytes;   // fp32 partial outputs when phi_split > 1
     bool wide;              // 32x32-tile kernels (chunk_wide.hip)
     bool fused;             // wide causal path as one cooperative launch (summary, scan, output)
-    size_t zero_bytes;      // zeroed tail of the workspace (cleared once at create): a page read
-                            // for rows past a chunk end, then the fused path's counters
+    size_t zero_bytes;      // zeroed tail of the workspace (cleared once at create): the
+                            // counters of the single-launch path
 };
 
 bool fast_supported(const Shape& s, int chunk);
