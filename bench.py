@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--value-split", type=int, default=0, help="plan override: workgroups per value width")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
+    ap.add_argument("--launch", default="auto", choices=["auto", "separate", "single", "prefix"],
+                    help="how a segmented causal forward is launched")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device copy of MIB mebibytes (counter calibration) and exit")
     return ap.parse_args()
@@ -189,7 +191,7 @@ def main():
 
     layer = tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi,
                                    chunk=w.chunk, segments=args.segments, w1=w1, w3=w3,
-                                   value_split=args.value_split)
+                                   value_split=args.value_split, launch=args.launch)
     plan = layer.plan()
     stream = torch.cuda.current_stream()
     mode = tla.mode_bits(w.eta_mode, w.causal)
@@ -271,7 +273,8 @@ def main():
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "d_phi": w.d_phi,
             "phi": w.phi, "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar, "beta": w.beta,
             "causal": w.causal, "chunk": plan.chunk, "segments": plan.segments, "dv_split": plan.dv_split,
-            "phi_split": plan.phi_split, "kernels_per_step": plan.n_kernels, "input_sets": n_sets,
+            "phi_split": plan.phi_split, "launch": args.launch, "kernels_per_step": plan.n_kernels,
+            "input_sets": n_sets,
             "head_tokens_per_s": round(w.head_tokens / (ms_per_step * 1e-3), 1),
         },
         "roofline": roof,

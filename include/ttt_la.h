@@ -79,9 +79,12 @@ enum {
 enum {
     TTT_LA_LAUNCH_AUTO = 0,      /* the library's choice (currently: separate kernels) */
     TTT_LA_LAUNCH_SEPARATE = 1,  /* segment summaries, their scan and the outputs as three kernels */
-    TTT_LA_LAUNCH_SINGLE = 2     /* one cooperative kernel whose workgroups exchange the segment
+    TTT_LA_LAUNCH_SINGLE = 2,    /* one cooperative kernel whose workgroups exchange the segment
                                     summaries through device memory, when the device can keep the
                                     whole grid resident (32x32-tile path only); else as SEPARATE */
+    TTT_LA_LAUNCH_PREFIX = 3     /* one kernel, no exchange: the workgroup of each segment first
+                                    rebuilds its entry state from the keys and values of all earlier
+                                    tokens (32x32-tile path only; else as SEPARATE) */
 };
 
 typedef struct {

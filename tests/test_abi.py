@@ -70,7 +70,7 @@ def test_query_may_alias_key():
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", 0), ("T", -5), ("d_k", 0),
                                          ("d_v", -1), ("dtype", 7), ("phi", 3), ("chunk", -1),
-                                         ("segments", -2), ("value_split", 3), ("launch", 3),
+                                         ("segments", -2), ("value_split", 3), ("launch", 4),
                                          ("launch", -1)])
 def test_bad_descriptor_fields(field, value):
     d = desc()

@@ -160,6 +160,23 @@ def test_single_and_three_launch_paths(eta_mode, beta, segments):
     assert oracle.rel_err(select_heads(got, w, heads), ref) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("eta_mode,beta,segments", [("scalar", 0.9, 8), ("softplus", 0.9, 5), ("per_token", 0.0, 16)])
+def test_prefix_launch(eta_mode, beta, segments):
+    # one kernel: each segment's workgroup rebuilds its entry state from the earlier
+    # tokens; a ragged last chunk and segment counts that do not divide the chunks
+    w = small("v4_momentum_4x8x2048_d128", T=2048 - 37).with_settings(eta_mode=eta_mode, beta=beta)
+    say(f"[prefix launch] segments={segments} {eta_mode} beta={beta}")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d, segments=segments, launch="prefix")
+    plan = lay.plan()
+    assert plan.path == 2 and plan.n_kernels == 1 and plan.workspace_bytes == 0
+    heads = [0, 13, 31]
+    got = run_gpu(w, d, layer=lay)
+    ref = run_oracle(w, x, heads=heads)
+    assert oracle.rel_err(select_heads(got, w, heads), ref) <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("d_k,d_v", [(64, 128), (128, 64), (64, 64)])
 def test_mixed_widths(d_k, d_v):
     w = small("v3_softplus_8x16x4096_d128", B=1, H=2, T=140).with_settings(d_k=d_k, d_v=d_v, d_phi=d_k)

@@ -29,7 +29,9 @@ TTT_LA_PHI_SWIGLU = 1
 TTT_LA_LAUNCH_AUTO = 0
 TTT_LA_LAUNCH_SEPARATE = 1
 TTT_LA_LAUNCH_SINGLE = 2
-_LAUNCH = {"auto": TTT_LA_LAUNCH_AUTO, "separate": TTT_LA_LAUNCH_SEPARATE, "single": TTT_LA_LAUNCH_SINGLE}
+TTT_LA_LAUNCH_PREFIX = 3
+_LAUNCH = {"auto": TTT_LA_LAUNCH_AUTO, "separate": TTT_LA_LAUNCH_SEPARATE, "single": TTT_LA_LAUNCH_SINGLE,
+           "prefix": TTT_LA_LAUNCH_PREFIX}
 
 TTT_LA_CAUSAL = 0
 TTT_LA_BIDIRECTIONAL = 1 << 0

@@ -52,7 +52,7 @@ int check_desc(const ttt_la_desc* d) {
     if (d->phi != TTT_LA_PHI_IDENTITY && d->phi != TTT_LA_PHI_SWIGLU) return TTT_LA_ERR_INVALID_ARG;
     if (d->chunk < 0 || d->segments < 0) return TTT_LA_ERR_INVALID_ARG;
     if (d->value_split < 0 || d->value_split > 2) return TTT_LA_ERR_INVALID_ARG;
-    if (d->launch < TTT_LA_LAUNCH_AUTO || d->launch > TTT_LA_LAUNCH_SINGLE) return TTT_LA_ERR_INVALID_ARG;
+    if (d->launch < TTT_LA_LAUNCH_AUTO || d->launch > TTT_LA_LAUNCH_PREFIX) return TTT_LA_ERR_INVALID_ARG;
     if (d->phi == TTT_LA_PHI_SWIGLU) {
         if (!d->w1 || !d->w3) return TTT_LA_ERR_INVALID_ARG;
         if (!aligned(d->w1, 16) || !aligned(d->w3, 16)) return TTT_LA_ERR_INVALID_ARG;
@@ -169,8 +169,7 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     h->fast = desc->dtype == TTT_LA_BF16 && ttt::fast_supported(h->shape, desc->chunk);
     h->n_kernels = 1;
     if (h->fast) {
-        h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments, desc->value_split,
-                               desc->launch == TTT_LA_LAUNCH_SINGLE);
+        h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments, desc->value_split, desc->launch);
         h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes + h->fp.zero_bytes;
     }
     if (hipGetDevice(&h->device) != hipSuccess) {
@@ -271,7 +270,7 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
         plan->dv_split = h->fp.dv_split;
         plan->phi_split = h->fp.phi_split;
         plan->grid_main = s.n_seq() * h->fp.dv_split * h->fp.phi_split * h->fp.segments;
-        plan->n_kernels = h->fp.fused ? 1
+        plan->n_kernels = (h->fp.fused || h->fp.prefix) ? 1
                                       : 1 + (h->fp.segments > 1 ? 1 : 0) + (h->fp.segments > 2 ? 1 : 0) +
                                             (h->fp.phi_split > 1 ? 1 : 0);
     } else {

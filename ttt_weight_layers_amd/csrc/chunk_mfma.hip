@@ -627,7 +627,7 @@ bool fast_supported(const Shape& s, int chunk) {
     return chunk == 0 || chunk == 64 || chunk == 128;
 }
 
-FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split, bool single_launch) {
+FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split, int launch) {
     FastPlan p{};
     if (wide_supported(s) && value_split != 2) {
         // one workgroup of four waves per sequence segment (chunk_wide.hip)
@@ -647,12 +647,19 @@ FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split,
         const int seg_chunks = (n_chunks + S - 1) / S;
         p.seg_len = seg_chunks * CH;
         p.segments = (n_chunks + seg_chunks - 1) / seg_chunks;
-        p.summary_bytes = wide_summary_bytes(s, p.segments);
         p.partial_bytes = 0;
         p.zero_bytes = wide_zero_bytes(s);
+        if (launch == TTT_LA_LAUNCH_PREFIX) {
+            p.prefix = true;
+            wide_prefix_bounds(s.T, p.segments, p.bounds);
+            p.summary_bytes = 0;
+            p.zero_bytes = 0;
+            return p;
+        }
+        p.summary_bytes = wide_summary_bytes(s, p.segments);
         // one launch, on request, when every workgroup of the grid can be resident at once
         const long grid = ((long)s.n_seq() * p.segments + 7) / 8 * 8;
-        p.fused = single_launch && p.segments > 1 && grid <= wide_fused_capacity();
+        p.fused = launch == TTT_LA_LAUNCH_SINGLE && p.segments > 1 && grid <= wide_fused_capacity();
         return p;
     }
     // The chunk length is a tiling choice (results differ only by rounding);

@@ -47,12 +47,16 @@
 #include "internal.h"
 #include "lds_tiles.h"
 
+// every helper lambda of the kernels is inlined: a lambda left as a call keeps the
+// state it captures by reference in scratch memory
+#define TTT_INLINE __attribute__((always_inline))
+
 namespace ttt {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum WideKind : int { W_OUTPUT = 0, W_SUMMARY = 1, W_BIDIR = 2, W_FUSED = 3 };
+enum WideKind : int { W_OUTPUT = 0, W_SUMMARY = 1, W_BIDIR = 2, W_FUSED = 3, W_PREFIX = 4 };
 
 constexpr int WC = 64;     // tokens per chunk
 constexpr int WD = 128;    // features (d_k = d_phi) and values (d_v)
@@ -82,6 +86,8 @@ struct WideParams {
     unsigned epoch;
     unsigned spin_limit;
     unsigned* wait_failed;
+    // W_PREFIX: first token of each segment, bounds[seg_count] = T
+    int bounds[17];
 };
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -115,7 +121,7 @@ struct WideLds {
 };
 template <int KIND>
 struct WideRing {
-    static constexpr bool QKV = KIND == W_OUTPUT || KIND == W_FUSED;
+    static constexpr bool QKV = KIND == W_OUTPUT || KIND == W_FUSED || KIND == W_PREFIX;
     static constexpr int NB = 3;                                  // buffers
     static constexpr int TILES = QKV ? 3 : 2;                     // tiles per buffer
     static constexpr int SIZE = TILES * WideLds::TILE;
@@ -169,11 +175,11 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     float* sC = sF + 8 * WC;             // c_r, r = 0..WC
     float* sBP = sC + WC + 1;            // beta^r, r = 0..WC
     float* sK = sBP + WC + 1 + 2;        // k0 c_{x - 64} for x >= 64, 0 below (x = 0..127)
-    auto tq = [](uint16_t* st) { return st; };
-    auto tk = [](uint16_t* st) { return st + R::K_OFF; };
-    auto tv = [](uint16_t* st) { return st + R::V_OFF; };
-    auto s_wt = [](float* w) { return w; };          // eta_j / (1 - beta)
-    auto s_wm = [](float* w) { return w + WC; };     // eta_j beta^{n-1-j}
+    auto tq = [](uint16_t* st) TTT_INLINE { return st; };
+    auto tk = [](uint16_t* st) TTT_INLINE { return st + R::K_OFF; };
+    auto tv = [](uint16_t* st) TTT_INLINE { return st + R::V_OFF; };
+    auto s_wt = [](float* w) TTT_INLINE { return w; };          // eta_j / (1 - beta)
+    auto s_wm = [](float* w) TTT_INLINE { return w + WC; };     // eta_j beta^{n-1-j}
     u32x4* const P_lds = reinterpret_cast<u32x4*>(pfrag);
 
     // ---- unit of work (XCD-aware: consecutive units land on one XCD) --------
@@ -194,8 +200,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     const float inv1mb = 1.0f / (1.0f - beta);
     const float t_scale = ETAV ? 1.0f : p.eta_scalar * inv1mb;
 
-    const int t_begin = (KIND == W_BIDIR) ? 0 : seg * p.seg_len;
-    const int t_end = (KIND == W_BIDIR) ? p.T : min(p.T, t_begin + p.seg_len);
+    // token range of the pass being run (the prefix kernel runs two passes)
+    int t_begin = (KIND == W_BIDIR) ? 0 : (KIND == W_PREFIX ? p.bounds[seg] : seg * p.seg_len);
+    int t_end = (KIND == W_BIDIR) ? p.T : (KIND == W_PREFIX ? p.bounds[seg + 1] : min(p.T, t_begin + p.seg_len));
     const size_t seq_row = (size_t)seq * p.T;
 
     if (wave == 0) coefficient_scan<WC>(beta, sC, sBP);
@@ -206,17 +213,29 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     for (int ft = 0; ft < WFT; ++ft) Ts[ft] = f32x16{};
 #pragma unroll
     for (int ft = 0; ft < (MOM ? WFT : 1); ++ft) Ms[ft] = f32x16{};
+    // The momentum is M = rho Ms with a workgroup-uniform scale rho: the decay
+    // beta^n of a chunk multiplies rho instead of the 64 accumulator registers, and
+    // the chunk's M weights are divided by the new rho.  Ms absorbs rho (one pass
+    // over the registers) only when rho would fall below RHO_MIN; so rho stays in
+    // [RHO_MIN, 1] and the weights within a factor 1 / RHO_MIN of their value.
+    constexpr float RHO_MIN = 0x1p-60f;
+    float rho = 1.0f;
+    // rho after a chunk of n tokens (without renormalisation if it stays >= RHO_MIN)
+    auto rho_after = [&](int n) TTT_INLINE {
+        const float r = rho * sBP[n];
+        return r < RHO_MIN ? 1.0f : r;
+    };
 
     // workspace slots: [slot][T | M][wave][ft][r4][lane] f32x4 (16 floats per lane per tile)
     constexpr size_t TILE_F4 = 4 * 64;
     constexpr size_t HALF_F4 = (size_t)WNW * WFT * TILE_F4;
-    auto slot_ptr = [&](int s) {
+    auto slot_ptr = [&](int s) TTT_INLINE {
         return reinterpret_cast<f32x4*>(p.state) + ((size_t)seq * (p.seg_count - 1) + s) * 2 * HALF_F4;
     };
 
     // transpose-read columns: value columns in pi order, feature columns in sigma order
     const int col_v = 32 * wave + 16 * (q4 & 1) + 8 * g16 + 4 * (q4 >> 1);
-    auto col_k = [&](int ft) { return 32 * ft + 16 * g16 + 8 * (q4 & 1) + 4 * (q4 >> 1); };
+    auto col_k = [&](int ft) TTT_INLINE { return 32 * ft + 16 * g16 + 8 * (q4 & 1) + 4 * (q4 >> 1); };
 
     // Asynchronous staging: buffer loads straight into LDS, 16 bytes per lane.
     // Wave w copies the row groups 4g .. 4g+3 with g = w, w+4, w+8, w+12 of each
@@ -233,19 +252,24 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     int voff[4];
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) voff[gi] = 2 * ((4 * (wave + 4 * gi) + lane_row) * WD + lane_col);
-    auto chunk_rsrc = [&](const uint16_t* tensor, size_t row0, int n) {
+    auto chunk_rsrc = [&](const uint16_t* tensor, size_t row0, int n) TTT_INLINE {
         return __builtin_amdgcn_make_buffer_rsrc((void*)(tensor + row0 * WD), (short)0, n * WD * 2, 0x00020000);
     };
     // copies of row group gi of this wave (one instruction per tensor)
     // (the resources are bound to locals before use: passed as temporaries straight
     // into the builtin they make the host pass drop the kernels without a diagnostic)
-    auto stage_group = [&](uint16_t* st, int t0, int gi, bool want_q, bool want_k, bool want_v) {
+    // Every step issues the same number of copies, so that the waits can count them:
+    // a copy of a chunk past the end of the range reads only the range's last row
+    // (the other lanes are out of range) into a buffer nobody reads.  t0 < t_end.
+    // (The resources are bound to locals: passed as temporaries straight into the
+    // copy builtin they make the host pass drop the kernels without a diagnostic.)
+    auto stage_group = [&](uint16_t* st, int t0, int gi, bool want_q, bool want_k, bool want_v) TTT_INLINE {
         const int n = min(WC, t_end - t0);
         const size_t row0 = seq_row + t0;
-        const int grp = wave_s + 4 * gi;
         const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(p.q, row0, n);
         const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(p.k, row0, n);
         const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(p.v, row0, n);
+        const int grp = wave_s + 4 * gi;
         if (want_q)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (TTT_LDS void*)(tq(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
         if (want_k)
@@ -253,31 +277,33 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         if (want_v)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (TTT_LDS void*)(tv(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
     };
-    auto stage = [&](uint16_t* st, int t0, bool want_q, bool want_k, bool want_v) {
+    // first row of a copy that starts at t (t_end - 1 past the end of the range)
+    auto copy_start = [&](int t) TTT_INLINE { return t < t_end ? t : t_end - 1; };
+    auto stage = [&](uint16_t* st, int t0, bool want_q, bool want_k, bool want_v) TTT_INLINE {
 #pragma unroll
-        for (int gi = 0; gi < 4; ++gi) stage_group(st, t0, gi, want_q, want_k, want_v);
+        for (int gi = 0; gi < 4; ++gi) stage_group(st, copy_start(t0), gi, want_q, want_k, want_v);
     };
     // rate of this thread's token of the chunk at t0 (threads 0..63)
-    auto load_eta = [&](int t0) {
+    auto load_eta = [&](int t0) TTT_INLINE {
         const int n = min(WC, t_end - t0);
         float et = p.eta_scalar;
         if (ETAV) et = tid < n ? p.eta[seq_row + t0 + tid] : 0.0f;
         return et;
     };
     // per-token weights of a chunk of n tokens
-    auto put_weights = [&](float* w, float et, int n) {
+    auto put_weights = [&](float* w, float et, int n) TTT_INLINE {
         if (tid < WC) {
             if (ETAV && p.eta_kind == ETA_SOFTPLUS) et = softplus_f32(et);
             if (tid >= n) et = 0.0f;
             s_wt(w)[tid] = et * inv1mb;
-            s_wm(w)[tid] = tid < n ? et * sBP[n - 1 - tid] : 0.0f;
+            if constexpr (MOM) s_wm(w)[tid] = tid < n ? et * sBP[n - 1 - tid] / rho_after(n) : 0.0f;
         }
     };
     // the stage copies this wave issued have landed (the barrier that follows publishes them)
-    auto wait_stage = [&]() { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
+    auto wait_stage = [&]() TTT_INLINE { __builtin_amdgcn_s_waitcnt(0x0F70); };   // vmcnt(0)
 
     // per-token weights of contraction block b in this lane's token order
-    auto weights8 = [&](const float* w, int b, float* out) {
+    auto weights8 = [&](const float* w, int b, float* out) TTT_INLINE {
         const f32x4 a = *reinterpret_cast<const f32x4*>(w + 16 * b + 4 * hh);
         const f32x4 c = *reinterpret_cast<const f32x4*>(w + 16 * b + 8 + 4 * hh);
 #pragma unroll
@@ -289,7 +315,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 
     // v fragments: lane holds v[16b + slot(h, e)][32 wave + pi(n)]
     u32x4 vf[WKB];
-    auto read_v = [&](uint16_t* st) {
+    auto read_v = [&](uint16_t* st) TTT_INLINE {
 #pragma unroll
         for (int b = 0; b < WKB; ++b) {
             const u32x2 lo = tr_read<WD>(tv(st), 16 * b + 4 * hh, col_v);
@@ -300,7 +326,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 
     // T-part value operands w_T v (the raw fragments for a scalar rate)
     u32x4 bT[WKB];
-    auto value_weights = [&](float* w) {
+    auto value_weights = [&](float* w) TTT_INLINE {
 #pragma unroll
         for (int b = 0; b < WKB; ++b) {
             if constexpr (ETAV) {
@@ -314,14 +340,27 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     };
 
     // update with the chunk in st (after read_v, value_weights):
-    // T += K^T (w_T v), M = beta^n M + K^T (w_M v).  The K fragments of block b + 1
-    // are read while block b's products run; if far is set, the copy of the chunk
-    // at t_far into far is issued a row group per block, between the products.
-    auto update = [&](uint16_t* st, float* w, int n, uint16_t* far, int t_far, bool far_q) {
+    // T += K^T (w_T v), M = beta^n M + K^T (w_M v), as a software pipeline over the
+    // four 16-token blocks: while block b's eight products run, the K fragments and
+    // the M-weighted value operand of block b + 1 are prepared and a quarter of the
+    // copy of the chunk at t_far into far is issued.  The copy is issued in every
+    // step (far is always a free buffer); rows past the end of the segment have a
+    // zero-length range and read nothing.
+    auto update = [&](uint16_t* st, float* w, int n, uint16_t* far, int t_far, bool far_q) TTT_INLINE {
+        if constexpr (MOM) {
+            const float r = rho * sBP[n];
+            if (r < RHO_MIN) {
+#pragma unroll
+                for (int ft = 0; ft < WFT; ++ft) Ms[ft] *= r;
+                rho = 1.0f;
+            } else {
+                rho = r;
+            }
+        }
         const uint16_t* K = tk(st);
-        const float bn = MOM ? sBP[n] : 1.0f;
         u32x4 kf[2][WFT];
-        auto load_k = [&](int b, u32x4* dst) {
+        bf16x8 bm[2];
+        auto load_k = [&](int b, u32x4* dst) TTT_INLINE {
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft) {
                 const u32x2 lo = tr_read<WD>(K, 16 * b + 4 * hh, col_k(ft));
@@ -329,36 +368,49 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 dst[ft] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         };
+        auto m_operand = [&](int b) TTT_INLINE {
+            float x[8];
+            weights8(s_wm(w), b, x);
+            return scale8(vf[b], x);
+        };
+        const int t_src = copy_start(t_far);
         load_k(0, kf[0]);
+        if constexpr (MOM) bm[0] = m_operand(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int b = 0; b < WKB; ++b) {
-            if (b + 1 < WKB) load_k(b + 1, kf[(b + 1) & 1]);
-            if (far) stage_group(far, t_far, b, far_q, true, true);
-            bf16x8 bM;
-            if constexpr (MOM) {
-                float x[8];
-                weights8(s_wm(w), b, x);
-                bM = scale8(vf[b], x);
+            if (b + 1 < WKB) {
+                load_k(b + 1, kf[(b + 1) & 1]);
+                if constexpr (MOM) bm[(b + 1) & 1] = m_operand(b + 1);
             }
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft) {
                 const bf16x8 a = as_bf16x8(kf[b & 1][ft]);
                 Ts[ft] = mfma32(a, as_bf16x8(bT[b]), Ts[ft]);
-                if constexpr (MOM) {
-                    if (b == 0) Ms[ft] *= bn;
-                    Ms[ft] = mfma32(a, bM, Ms[ft]);
+                if constexpr (MOM) Ms[ft] = mfma32(a, bm[b & 1], Ms[ft]);
+            }
+            // interleave: each product followed by LDS reads and vector work of the next block
+            if (b + 1 < WKB) {
+#pragma unroll
+                for (int i = 0; i < (MOM ? 8 : 4); ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, MOM ? 2 : 3, 0);   // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, MOM ? 3 : 1, 0);   // VALU
                 }
             }
+            // the copy instructions end a scheduling region: issue them after the block
+            stage_group(far, t_src, b, far_q, true, true);
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
     // q fragment: B operand Q^T[feature 16 kb + 8h + e][token 32 I + n]
-    auto q_frag = [&](uint16_t* st, int I, int kb) {
+    auto q_frag = [&](uint16_t* st, int I, int kb) TTT_INLINE {
         return as_bf16x8(lds_read16(tq(st) + swz<WD>(32 * I + n32, 16 * kb + 8 * hh)));
     };
 
     // readout of the chunk's queries from the state entering it
-    auto readout = [&](uint16_t* st, f32x16* oT, f32x16* oM, bool with_m) {
+    auto readout = [&](uint16_t* st, f32x16* oT, f32x16* oM, bool with_m) TTT_INLINE {
 #pragma unroll
         for (int I = 0; I < 2; ++I) {
             oT[I] = f32x16{};
@@ -384,7 +436,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     };
 
     // one output tile: lane holds o[i = 32I + n][32 wave + 16h + r], r = 0..15
-    auto store = [&](const f32x16& o, int I, int n, size_t row0) {
+    auto store = [&](const f32x16& o, int I, int n, size_t row0) TTT_INLINE {
         const int i = 32 * I + n32;
         if (i < n) {
             uint16_t* dst = p.o + (row0 + i) * WD + 32 * wave + 16 * hh;
@@ -400,7 +452,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     __syncthreads();   // coefficient tables
 
     // ---- output pass over the segment from its entry state (slot seg - 1) ----
-    auto output_pass = [&]() {
+    auto output_pass = [&]() TTT_INLINE {
         // score coefficients: c_{i-j} times (1 - beta) when the rate is folded into
         // the value operand, else times the scalar rate; 0 above the diagonal
         const float k0 = ETAV ? (1.0f - beta) : p.eta_scalar;
@@ -420,7 +472,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         stage(stage_a, t_begin, true, true, true);
         if (two) stage(stage_b, t_begin + WC, true, true, true);
         const float et0 = load_eta(t_begin);
-        if (seg > 0) {
+        if (KIND != W_PREFIX && seg > 0) {
             const f32x4* src = slot_ptr(seg - 1);
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft)
@@ -442,7 +494,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 
         // Chunk c, staged in cur with weights wc.  Chunk c + 1 is in flight (weights
         // go to wn at the end); the copy of chunk c + 2 into far starts mid-step.
-        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) -> bool {
+        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) TTT_INLINE -> bool {
             const int n = min(WC, t_end - t0);
             const size_t row0 = seq_row + t0;
             const bool has_next = t0 + WC < t_end;
@@ -475,10 +527,11 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 readout(cur, oT, oM, true);
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
+                    const float gI = gam[I] * rho;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         float x = oT[I][r] * t_scale;
-                        if constexpr (MOM) x = fmaf(gam[I], oM[I][r], x);
+                        if constexpr (MOM) x = fmaf(gI, oM[I][r], x);
                         o[I][r] = x;
                     }
                 }
@@ -500,11 +553,11 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 store(o[I], I, n, row0);
             }
             __builtin_amdgcn_sched_barrier(0);
-            update(cur, wc, n, has_far ? far : nullptr, t0 + 2 * WC, true);
+            update(cur, wc, n, far, t0 + 2 * WC, true);
             if (!has_next) return false;
             put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
             // chunk c + 1 landed; the 12 copies of chunk c + 2 may still be in flight
-            if (has_far) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); else wait_stage();
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
             lds_barrier();
             return true;
         };
@@ -513,29 +566,30 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             if (!step(stage_b, w_b, w_c, stage_a, t0 + WC)) break;
             if (!step(stage_c, w_c, w_a, stage_b, t0 + 2 * WC)) break;
         }
+        wait_stage();   // the last (empty) copies
     };
 
     // ---- summary pass: three stage buffers, k, v copied two chunks ahead ----
-    auto summary_pass = [&]() {
-        auto issue_kv = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, false, true, true); };
-        auto wait_kv = [&](int t0) {
-            if (t0 + 2 * WC < t_end) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); else wait_stage();
-        };
+    auto summary_pass = [&]() TTT_INLINE {
+        auto issue_kv = [&](uint16_t* st, int t0) TTT_INLINE { stage(st, t0, false, true, true); };   // 8 copies
+        // chunk t0 + WC landed; the copies of chunk t0 + 2 WC (8, some possibly empty) may
+        // still be in flight
+        auto wait_kv = [&]() TTT_INLINE { __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); };
         issue_kv(stage_a, t_begin);
         issue_kv(stage_b, t_begin + WC);
         put_weights(w_a, load_eta(t_begin), min(WC, t_end - t_begin));
-        wait_kv(t_begin - WC);
+        wait_kv();
         lds_barrier();
-        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) -> bool {
+        auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) TTT_INLINE -> bool {
             const int n = min(WC, t_end - t0);
             const bool has_next = t0 + WC < t_end;
             const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
             read_v(cur);
             value_weights(wc);
-            update(cur, wc, n, t0 + 2 * WC < t_end ? far : nullptr, t0 + 2 * WC, false);
+            update(cur, wc, n, far, t0 + 2 * WC, false);
             if (!has_next) return false;
             put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
-            wait_kv(t0);
+            wait_kv();
             lds_barrier();
             return true;
         };
@@ -544,9 +598,10 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             if (!step(stage_b, w_b, w_c, stage_a, t0 + WC)) break;
             if (!step(stage_c, w_c, w_a, stage_b, t0 + 2 * WC)) break;
         }
+        wait_stage();   // the last (empty) copies
     };
 
-    auto write_summary = [&](f32x4* dst) {
+    auto write_summary = [&](f32x4* dst) TTT_INLINE {
 #pragma unroll
         for (int ft = 0; ft < WFT; ++ft)
 #pragma unroll
@@ -555,11 +610,25 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                     f32x4{Ts[ft][4 * r4], Ts[ft][4 * r4 + 1], Ts[ft][4 * r4 + 2], Ts[ft][4 * r4 + 3]};
                 if constexpr (MOM)
                     dst[HALF_F4 + (((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane] =
-                        f32x4{Ms[ft][4 * r4], Ms[ft][4 * r4 + 1], Ms[ft][4 * r4 + 2], Ms[ft][4 * r4 + 3]};
+                        f32x4{rho * Ms[ft][4 * r4], rho * Ms[ft][4 * r4 + 1], rho * Ms[ft][4 * r4 + 2],
+                              rho * Ms[ft][4 * r4 + 3]};
             }
     };
 
     if constexpr (KIND == W_OUTPUT) {
+        output_pass();
+    } else if constexpr (KIND == W_PREFIX) {
+        // entry state from zero over all earlier tokens (an update-only pass), then
+        // the segment's outputs
+        const int s0 = t_begin, s1 = t_end;
+        if (s0 > 0) {
+            t_begin = 0;
+            t_end = s0;
+            summary_pass();
+            __syncthreads();   // every wave is done with the stage buffers and weights
+            t_begin = s0;
+            t_end = s1;
+        }
         output_pass();
     } else if constexpr (KIND == W_FUSED) {
         // 1. zero-entry summary of this segment (every segment but the last)
@@ -570,6 +639,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             for (int ft = 0; ft < WFT; ++ft) Ts[ft] = f32x16{};
 #pragma unroll
             for (int ft = 0; ft < (MOM ? WFT : 1); ++ft) Ms[ft] = f32x16{};
+            rho = 1.0f;
         }
         // 2. the sequence's summaries are written: scan them, each workgroup one slice
         unsigned* cnt = p.counters + 2 * (size_t)seq;
@@ -631,10 +701,11 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                         f32x4{Ts[ft][4 * r4], Ts[ft][4 * r4 + 1], Ts[ft][4 * r4 + 2], Ts[ft][4 * r4 + 3]};
                     if constexpr (MOM)
                         dst[HALF_F4 + (((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane] =
-                            f32x4{Ms[ft][4 * r4], Ms[ft][4 * r4 + 1], Ms[ft][4 * r4 + 2], Ms[ft][4 * r4 + 3]};
+                            f32x4{rho * Ms[ft][4 * r4], rho * Ms[ft][4 * r4 + 1], rho * Ms[ft][4 * r4 + 2],
+                                  rho * Ms[ft][4 * r4 + 3]};
                 }
         } else {
-            const float kappa = beta * inv1mb;
+            const float kappa = beta * inv1mb * rho;
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft)
 #pragma unroll
@@ -645,15 +716,15 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 }
             __syncthreads();   // every wave is done with the stage buffers
             // queries: three buffers, copies two chunks ahead (4 per chunk and wave)
-            auto issue_q = [&](uint16_t* st, int t0) { if (t0 < t_end) stage(st, t0, true, false, false); };
-            auto wait_q = [&](int t0) {
+            auto issue_q = [&](uint16_t* st, int t0) TTT_INLINE { if (t0 < t_end) stage(st, t0, true, false, false); };
+            auto wait_q = [&](int t0) TTT_INLINE {
                 if (t0 + 2 * WC < t_end) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4)); else wait_stage();
             };
             issue_q(stage_a, 0);
             issue_q(stage_b, WC);
             wait_q(-WC);
             lds_barrier();
-            auto qstep = [&](uint16_t* cur, uint16_t* far, int t0) -> bool {
+            auto qstep = [&](uint16_t* cur, uint16_t* far, int t0) TTT_INLINE -> bool {
                 const int n = min(WC, t_end - t0);
                 const size_t row0 = seq_row + t0;
                 const bool has_next = t0 + WC < t_end;
@@ -760,6 +831,13 @@ size_t wide_summary_bytes(const Shape& s, int segments) {
 
 int wide_max_segments() { return 16; }
 
+void wide_prefix_bounds(int T, int S, int* bounds) {
+    // equal chunk-aligned segments
+    const int n_chunks = (T + WC - 1) / WC;
+    const int per = (n_chunks + S - 1) / S;
+    for (int i = 0; i <= S; ++i) bounds[i] = std::min(T, i * per * WC);
+}
+
 hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
                        hipEvent_t ev_end, int* n_kernels) {
     WideParams wp{};
@@ -805,6 +883,17 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
         // path and does not advance the epoch (no workgroup of this launch ran)
         (void)hipGetLastError();
         return hipErrorCooperativeLaunchTooLarge;
+    }
+    if (!a.bidirectional && p.prefix) {
+        wp.seg_count = p.segments;
+        wp.seg_len = p.seg_len;
+        for (int i = 0; i <= p.segments; ++i) wp.bounds[i] = p.bounds[i];
+        wp.n_units = s.n_seq() * p.segments;
+        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
+        if ((e = launch_wide_kind<W_PREFIX>(mom, etav, wp, st)) != hipSuccess) return e;
+        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        if (n_kernels) *n_kernels = 1;
+        return hipSuccess;
     }
     if (a.bidirectional) {
         wp.seg_count = 1;

@@ -55,14 +55,20 @@ struct FastPlan {
     bool fused;             // wide causal path as one cooperative launch (summary, scan, output)
     size_t zero_bytes;      // zeroed tail of the workspace (cleared once at create): the
                             // counters of the single-launch path
+    bool prefix;            // wide causal path as one kernel whose segments rebuild their
+                            // entry states from the earlier tokens
+    int bounds[17];         // prefix path: first token of each segment, bounds[segments] = T
 };
 
 bool fast_supported(const Shape& s, int chunk);
-FastPlan fast_plan(const Shape& s, int chunk, int segments, int value_split, bool single_launch);
+// launch: TTT_LA_LAUNCH_*
+FastPlan fast_plan(const Shape& s, int chunk, int segments, int value_split, int launch);
 // 32x32-tile kernels: identity map, d_k = d_v = 128, bf16
 bool wide_supported(const Shape& s);
 size_t wide_summary_bytes(const Shape& s, int segments);
 int wide_max_segments();
+// prefix path: chunk-aligned segment starts for T tokens and S segments, bounds[S] = T
+void wide_prefix_bounds(int T, int S, int* bounds);
 // workgroups the fused cooperative kernel can keep resident at once (0 if the
 // device cannot launch cooperatively)
 int wide_fused_capacity();
