@@ -368,9 +368,22 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 dst[ft] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         };
+        // the M weights of all four blocks are read up front (one LDS wait)
+        f32x4 wm[MOM ? WKB : 1][2];
+        if constexpr (MOM) {
+#pragma unroll
+            for (int b = 0; b < WKB; ++b) {
+                wm[b][0] = *reinterpret_cast<const f32x4*>(s_wm(w) + 16 * b + 4 * hh);
+                wm[b][1] = *reinterpret_cast<const f32x4*>(s_wm(w) + 16 * b + 8 + 4 * hh);
+            }
+        }
         auto m_operand = [&](int b) TTT_INLINE {
             float x[8];
-            weights8(s_wm(w), b, x);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = wm[b][0][e];
+                x[4 + e] = wm[b][1][e];
+            }
             return scale8(vf[b], x);
         };
         const int t_src = copy_start(t_far);
@@ -457,9 +470,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         // the value operand, else times the scalar rate; 0 above the diagonal
         const float k0 = ETAV ? (1.0f - beta) : p.eta_scalar;
         if (tid < 2 * WC) sK[tid] = tid >= WC ? k0 * sC[tid - WC] : 0.0f;
-        // score tile of waves 0..2: (J, I) = (0,0), (0,1), (1,1); the fourth wave has none.
+        // score tile of waves 0..2: (J, I) = (0,0), (0,1), (1,1); the fourth wave repeats (1,1).
         // Register r holds j = 32 sJ + 8 (r / 4) + 4h + r % 4 of token i = 32 sI + n.
-        const int sJ = (wave == 2) ? 1 : 0;
+        const int sJ = (wave >= 2) ? 1 : 0;
         const int sI = (wave == 0) ? 0 : 1;
         const float* coef = sK + WC + 32 * (sI - sJ) + n32 - 4 * hh;   // coef[-off_r]
         // M readout weight of token i: -beta^{i+2} / (1 - beta)
@@ -467,10 +480,10 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 #pragma unroll
         for (int I = 0; I < 2; ++I) gam[I] = MOM ? -beta * beta * sBP[32 * I + n32] * inv1mb : 0.0f;
 
-        // prologue: chunks 0 and 1 in flight, then the entry state
+        // prologue: chunk 0, the entry state, then chunk 1 (the first step waits for
+        // everything but chunk 1)
         const bool two = t_begin + WC < t_end;
         stage(stage_a, t_begin, true, true, true);
-        if (two) stage(stage_b, t_begin + WC, true, true, true);
         const float et0 = load_eta(t_begin);
         if (KIND != W_PREFIX && seg > 0) {
             const f32x4* src = slot_ptr(seg - 1);
@@ -488,6 +501,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                     }
                 }
         }
+        if (two) stage(stage_b, t_begin + WC, true, true, true);
         put_weights(w_a, et0, min(WC, t_end - t_begin));
         if (two) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); else wait_stage();   // chunk 0 landed
         lds_barrier();
@@ -504,27 +518,47 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             for (int r = 0; r < 16; ++r) cf[r] = coef[-(8 * (r >> 2) + (r & 3))];
             const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
 
-            // score tile S^T = K Q^T of this wave, scaled, to LDS as B fragments
-            if (wave < 3) {
-                f32x16 acc = f32x16{};
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    const bf16x8 a = as_bf16x8(lds_read16(tk(cur) + swz<WD>(32 * sJ + n32, 16 * kb + 8 * hh)));
-                    acc = mfma32(a, q_frag(cur, sI, kb), acc);
-                }
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[r] *= cf[r];
-#pragma unroll
-                for (int kh = 0; kh < 2; ++kh)
-                    P_lds[(wave * 2 + kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack_half(acc, kh));
-            }
-            __builtin_amdgcn_sched_barrier(0);
-
-            // readout from the entering state, combined: t_scale T q - beta^{i+2}/(1-beta) M q
+            // Score tile S^T = K Q^T of this wave and the readout from the entering
+            // state, in one loop: the score products (a chain on one accumulator) are
+            // spread between the 32 independent readout products.  The fourth wave
+            // computes the third wave's tile too (it would wait at the barrier
+            // anyway) and does not write it.
             f32x16 o[2];
             {
-                f32x16 oT[2], oM[2];
-                readout(cur, oT, oM, true);
+                f32x16 oT[2], oM[2], acc = f32x16{};
+#pragma unroll
+                for (int I = 0; I < 2; ++I) {
+                    oT[I] = f32x16{};
+                    if constexpr (MOM) oM[I] = f32x16{};
+                }
+#pragma unroll
+                for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh) {
+                        const int kb = 2 * ft + kh;
+                        const bf16x8 b0 = q_frag(cur, 0, kb);
+                        const bf16x8 b1 = q_frag(cur, 1, kb);
+                        const bf16x8 bs = q_frag(cur, sI, kb);
+                        const bf16x8 ks = as_bf16x8(lds_read16(tk(cur) + swz<WD>(32 * sJ + n32, 16 * kb + 8 * hh)));
+                        const bf16x8 aT = pack_half(Ts[ft], kh);
+                        oT[0] = mfma32(aT, b0, oT[0]);
+                        oT[1] = mfma32(aT, b1, oT[1]);
+                        acc = mfma32(ks, bs, acc);
+                        if constexpr (MOM) {
+                            const bf16x8 aM = pack_half(Ms[ft], kh);
+                            oM[0] = mfma32(aM, b0, oM[0]);
+                            oM[1] = mfma32(aM, b1, oM[1]);
+                        }
+                    }
+                // scaled score fragments to LDS; readout combined:
+                // t_scale T q - beta^{i+2}/(1-beta) M q
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[r] *= cf[r];
+                if (wave < 3) {
+#pragma unroll
+                    for (int kh = 0; kh < 2; ++kh)
+                        P_lds[(wave * 2 + kh) * 64 + lane] = __builtin_bit_cast(u32x4, pack_half(acc, kh));
+                }
 #pragma unroll
                 for (int I = 0; I < 2; ++I) {
                     const float gI = gam[I] * rho;
@@ -536,19 +570,24 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                     }
                 }
             }
-            lds_barrier();   // every wave's score fragments
-
-            // intra-chunk term with the weighted value fragments, then the store
+            // the weighted value fragments do not depend on the scores
             read_v(cur);
             value_weights(wc);
+            lds_barrier();   // every wave's score fragments
+
+            // intra-chunk term with the weighted value fragments (every score
+            // fragment read first), then the store
+            u32x4 pf[6];
+#pragma unroll
+            for (int f = 0; f < 6; ++f) pf[f] = P_lds[f * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int I = 0; I < 2; ++I) {
                 // blocks 0, 1 from tile (0, I); blocks 2, 3 from tile (1, 1)
 #pragma unroll
                 for (int b = 0; b < 2 * (I + 1); ++b) {
                     const int tile = (b < 2) ? I : 2;
-                    const bf16x8 pb = as_bf16x8(P_lds[(tile * 2 + (b & 1)) * 64 + lane]);
-                    o[I] = mfma32(as_bf16x8(bT[b]), pb, o[I]);
+                    o[I] = mfma32(as_bf16x8(bT[b]), as_bf16x8(pf[tile * 2 + (b & 1)]), o[I]);
                 }
                 store(o[I], I, n, row0);
             }
