@@ -83,16 +83,16 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the output kernel from the committed counter runs,
-    or None if they were taken on different kernel sources."""
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of the timed kernel from the committed counter runs,
+    or None if they were taken on another kernel or on different kernel sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
         return None
     return e.get("bytes_per_launch")
 
@@ -237,8 +237,14 @@ def main():
         achieved = w.head_tokens * flops_ht / (k_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = measured_traffic(w.name)
-    roof["kernel"] = "chunk_kernel<OUTPUT>"
+    if plan.path == 2:
+        kind = "BIDIR" if not w.causal else ("PREFIX" if args.launch == "prefix" else "OUTPUT")
+        roof["kernel"] = f"wide_kernel<{kind}>"
+    elif plan.path == 1:
+        roof["kernel"] = "chunk_kernel<BIDIR>" if not w.causal else "chunk_kernel<OUTPUT>"
+    else:
+        roof["kernel"] = "generic_kernel"
+    roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     roof["kernel_ms"] = round(k_avg_ms, 5)
 
     # parity of the first input set's output against the oracle on the sampled heads

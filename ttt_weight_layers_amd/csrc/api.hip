@@ -242,9 +242,7 @@ int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, cons
         }
         h->n_kernels = nk;
     } else {
-        if (eb && hipEventRecord(eb, a.stream) != hipSuccess) return TTT_LA_ERR_HIP;
-        e = ttt::launch_generic(h->shape, a);
-        if (e == hipSuccess && ee && hipEventRecord(ee, a.stream) != hipSuccess) return TTT_LA_ERR_HIP;
+        e = ttt::launch_generic(h->shape, a, eb, ee);
         h->n_kernels = 1;
     }
     return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;

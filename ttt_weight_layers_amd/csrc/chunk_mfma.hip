@@ -59,6 +59,8 @@
 #include <algorithm>
 #include <cmath>
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 #include "lds_tiles.h"
@@ -695,51 +697,60 @@ FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split,
 
 namespace {
 
+// With events, the launch carries them (hipExtLaunchKernel): they take their
+// timestamps at the start and end of the kernel itself, not around its dispatch.
 template <int D, int DK, int DV, int NW, bool MOM, bool ETAV, bool SW, int KIND>
-hipError_t launch_one(const ChunkParams& cp, hipStream_t st) {
+hipError_t launch_one(const ChunkParams& cp, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
     const int grid = (cp.n_units + 7) / 8 * 8;
+    if (eb || ee) {
+        ChunkParams a = cp;
+        void* args[] = {&a};
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(chunk_kernel<D, DK, DV, NW, 1, MOM, ETAV, SW, KIND>),
+                                  dim3(grid), dim3(NW * 64), args, 0, st, eb, ee, 0);
+    }
     hipLaunchKernelGGL((chunk_kernel<D, DK, DV, NW, 1, MOM, ETAV, SW, KIND>), dim3(grid), dim3(NW * 64), 0, st,
                        cp);
     return hipGetLastError();
 }
 
 template <int D, int DK, int DV, int NW, bool MOM, bool ETAV, bool SW>
-hipError_t launch_k(int kind, const ChunkParams& cp, hipStream_t st) {
-    if (kind == K_OUTPUT) return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_OUTPUT>(cp, st);
-    if (kind == K_SUMMARY) return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_SUMMARY>(cp, st);
-    return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_BIDIR>(cp, st);
+hipError_t launch_k(int kind, const ChunkParams& cp, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
+    if (kind == K_OUTPUT) return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_OUTPUT>(cp, st, eb, ee);
+    if (kind == K_SUMMARY) return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_SUMMARY>(cp, st, eb, ee);
+    return launch_one<D, DK, DV, NW, MOM, ETAV, SW, K_BIDIR>(cp, st, eb, ee);
 }
 
 template <int D, int DK, int DV, int NW, bool SW>
-hipError_t launch_kind(int kind, bool mom, bool etav, const ChunkParams& cp, hipStream_t st) {
+hipError_t launch_kind(int kind, bool mom, bool etav, const ChunkParams& cp, hipStream_t st, hipEvent_t eb,
+                       hipEvent_t ee) {
     if (mom) {
-        return etav ? launch_k<D, DK, DV, NW, true, true, SW>(kind, cp, st)
-                    : launch_k<D, DK, DV, NW, true, false, SW>(kind, cp, st);
+        return etav ? launch_k<D, DK, DV, NW, true, true, SW>(kind, cp, st, eb, ee)
+                    : launch_k<D, DK, DV, NW, true, false, SW>(kind, cp, st, eb, ee);
     }
-    return etav ? launch_k<D, DK, DV, NW, false, true, SW>(kind, cp, st)
-                : launch_k<D, DK, DV, NW, false, false, SW>(kind, cp, st);
+    return etav ? launch_k<D, DK, DV, NW, false, true, SW>(kind, cp, st, eb, ee)
+                : launch_k<D, DK, DV, NW, false, false, SW>(kind, cp, st, eb, ee);
 }
 
 // one wave per 16 value columns of the workgroup; DV / (16 NW) workgroups per sequence
 hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, bool etav, const ChunkParams& cp,
-                        hipStream_t st) {
+                        hipStream_t st, hipEvent_t eb = nullptr, hipEvent_t ee = nullptr) {
     if (!s.swiglu) {
         if (s.d_k == 128) {
             if (s.d_v == 128) {
-                return p.nwaves == 8 ? launch_kind<128, 128, 128, 8, false>(kind, mom, etav, cp, st)
-                                     : launch_kind<128, 128, 128, 4, false>(kind, mom, etav, cp, st);
+                return p.nwaves == 8 ? launch_kind<128, 128, 128, 8, false>(kind, mom, etav, cp, st, eb, ee)
+                                     : launch_kind<128, 128, 128, 4, false>(kind, mom, etav, cp, st, eb, ee);
             }
-            return launch_kind<128, 128, 64, 4, false>(kind, mom, etav, cp, st);
+            return launch_kind<128, 128, 64, 4, false>(kind, mom, etav, cp, st, eb, ee);
         }
-        return s.d_v == 128 ? launch_kind<64, 64, 128, 8, false>(kind, mom, etav, cp, st)
-                            : launch_kind<64, 64, 64, 4, false>(kind, mom, etav, cp, st);
+        return s.d_v == 128 ? launch_kind<64, 64, 128, 8, false>(kind, mom, etav, cp, st, eb, ee)
+                            : launch_kind<64, 64, 64, 4, false>(kind, mom, etav, cp, st, eb, ee);
     }
     if (s.d_k == 128) {
-        return s.d_v == 128 ? launch_kind<128, 128, 128, 8, true>(kind, mom, etav, cp, st)
-                            : launch_kind<128, 128, 64, 4, true>(kind, mom, etav, cp, st);
+        return s.d_v == 128 ? launch_kind<128, 128, 128, 8, true>(kind, mom, etav, cp, st, eb, ee)
+                            : launch_kind<128, 128, 64, 4, true>(kind, mom, etav, cp, st, eb, ee);
     }
-    return s.d_v == 128 ? launch_kind<128, 64, 128, 8, true>(kind, mom, etav, cp, st)
-                        : launch_kind<128, 64, 64, 4, true>(kind, mom, etav, cp, st);
+    return s.d_v == 128 ? launch_kind<128, 64, 128, 8, true>(kind, mom, etav, cp, st, eb, ee)
+                        : launch_kind<128, 64, 64, 4, true>(kind, mom, etav, cp, st, eb, ee);
 }
 
 }  // namespace
@@ -779,9 +790,7 @@ hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const
         cp.seg_count = 1;
         cp.seg_len = s.T;
         cp.n_units = s.n_seq() * slice_units;
-        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_chunk(s, p, K_BIDIR, mom, etav, cp, st)) != hipSuccess) return e;
-        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        if ((e = launch_chunk(s, p, K_BIDIR, mom, etav, cp, st, ev_begin, ev_end)) != hipSuccess) return e;
         ++nk;
     } else {
         cp.seg_count = p.segments;
@@ -804,9 +813,7 @@ hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const
             }
         }
         cp.n_units = s.n_seq() * p.segments * slice_units;
-        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_chunk(s, p, K_OUTPUT, mom, etav, cp, st)) != hipSuccess) return e;
-        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        if ((e = launch_chunk(s, p, K_OUTPUT, mom, etav, cp, st, ev_begin, ev_end)) != hipSuccess) return e;
         ++nk;
     }
     if (p.phi_split > 1) {

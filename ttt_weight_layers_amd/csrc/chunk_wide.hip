@@ -40,6 +40,8 @@
 // B-operand fragments (16 bytes per lane, no swizzle) and come back with
 // conflict-free 16-byte reads.
 
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 #include <cmath>
 
@@ -820,17 +822,29 @@ __global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_
     }
 }
 
+// With events, the launch carries them (hipExtLaunchKernel): they take their
+// timestamps at the start and end of the kernel itself, not around its dispatch.
 template <bool MOM, bool ETAV, int KIND>
-hipError_t launch_wide_one(const WideParams& wp, hipStream_t st) {
+hipError_t launch_wide_one(const WideParams& wp, hipStream_t st, hipEvent_t ev_begin, hipEvent_t ev_end) {
     const int grid = (wp.n_units + 7) / 8 * 8;
+    if (ev_begin || ev_end) {
+        WideParams a = wp;
+        void* args[] = {&a};
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(wide_kernel<MOM, ETAV, KIND>), dim3(grid), dim3(WNT),
+                                  args, 0, st, ev_begin, ev_end, 0);
+    }
     hipLaunchKernelGGL((wide_kernel<MOM, ETAV, KIND>), dim3(grid), dim3(WNT), 0, st, wp);
     return hipGetLastError();
 }
 
 template <int KIND>
-hipError_t launch_wide_kind(bool mom, bool etav, const WideParams& wp, hipStream_t st) {
-    if (mom) return etav ? launch_wide_one<true, true, KIND>(wp, st) : launch_wide_one<true, false, KIND>(wp, st);
-    return etav ? launch_wide_one<false, true, KIND>(wp, st) : launch_wide_one<false, false, KIND>(wp, st);
+hipError_t launch_wide_kind(bool mom, bool etav, const WideParams& wp, hipStream_t st, hipEvent_t ev_begin = nullptr,
+                            hipEvent_t ev_end = nullptr) {
+    if (mom)
+        return etav ? launch_wide_one<true, true, KIND>(wp, st, ev_begin, ev_end)
+                    : launch_wide_one<true, false, KIND>(wp, st, ev_begin, ev_end);
+    return etav ? launch_wide_one<false, true, KIND>(wp, st, ev_begin, ev_end)
+                : launch_wide_one<false, false, KIND>(wp, st, ev_begin, ev_end);
 }
 
 }  // namespace
@@ -928,9 +942,7 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
         wp.seg_len = p.seg_len;
         for (int i = 0; i <= p.segments; ++i) wp.bounds[i] = p.bounds[i];
         wp.n_units = s.n_seq() * p.segments;
-        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_wide_kind<W_PREFIX>(mom, etav, wp, st)) != hipSuccess) return e;
-        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        if ((e = launch_wide_kind<W_PREFIX>(mom, etav, wp, st, ev_begin, ev_end)) != hipSuccess) return e;
         if (n_kernels) *n_kernels = 1;
         return hipSuccess;
     }
@@ -938,9 +950,7 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
         wp.seg_count = 1;
         wp.seg_len = s.T;
         wp.n_units = s.n_seq();
-        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_wide_kind<W_BIDIR>(mom, etav, wp, st)) != hipSuccess) return e;
-        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        if ((e = launch_wide_kind<W_BIDIR>(mom, etav, wp, st, ev_begin, ev_end)) != hipSuccess) return e;
         ++nk;
     } else {
         wp.seg_count = p.segments;
@@ -965,9 +975,7 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
             }
         }
         wp.n_units = s.n_seq() * p.segments;
-        if (ev_begin && (e = hipEventRecord(ev_begin, st)) != hipSuccess) return e;
-        if ((e = launch_wide_kind<W_OUTPUT>(mom, etav, wp, st)) != hipSuccess) return e;
-        if (ev_end && (e = hipEventRecord(ev_end, st)) != hipSuccess) return e;
+        if ((e = launch_wide_kind<W_OUTPUT>(mom, etav, wp, st, ev_begin, ev_end)) != hipSuccess) return e;
         ++nk;
     }
     if (n_kernels) *n_kernels = nk;

@@ -19,6 +19,8 @@
 // meet an fp32 error budget) and any shape the MFMA path does not cover.
 // It is plain vector-ALU code: correctness first, adequate speed.
 
+#include <hip/hip_ext.h>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -240,7 +242,7 @@ size_t generic_smem_bytes(const Shape& s) {
     return generic_smem_floats(s.d_k, s.d_phi, s.swiglu) * sizeof(float);
 }
 
-hipError_t launch_generic(const Shape& s, const FwdArgs& a) {
+hipError_t launch_generic(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end) {
     GenericParams p;
     p.q = a.q;
     p.k = a.k;
@@ -266,6 +268,11 @@ hipError_t launch_generic(const Shape& s, const FwdArgs& a) {
         e = hipFuncSetAttribute((const void*)generic_forward<TI, SW>,                                   \
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);                 \
         if (e != hipSuccess) return e;                                                                  \
+        if (ev_begin || ev_end) {                                                                       \
+            void* args[] = {&p};                                                                        \
+            return hipExtLaunchKernel(reinterpret_cast<const void*>(generic_forward<TI, SW>), grid, block, \
+                                      args, smem, a.stream, ev_begin, ev_end, 0);                       \
+        }                                                                                               \
         hipLaunchKernelGGL((generic_forward<TI, SW>), grid, block, smem, a.stream, p);                  \
     } while (0)
     if (s.bf16) {

@@ -38,7 +38,8 @@ struct Shape {
 // ---- generic path: fp32 arithmetic on the vector ALUs ----------
 // Handles every supported shape and mode, fp32 or bf16 inputs.
 size_t generic_smem_bytes(const Shape& s);
-hipError_t launch_generic(const Shape& s, const FwdArgs& a);
+// ev_begin/ev_end (may be null) take the kernel's start and end timestamps
+hipError_t launch_generic(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 // ---- bf16 MFMA path --------------------------------------------------------
 struct FastPlan {
@@ -79,7 +80,7 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
                        hipEvent_t ev_end, int* n_kernels);
 
 // Enqueues the whole forward (all kernels).  If ev_begin/ev_end are non-null
-// they are recorded around the output kernel.
+// they take the start and end timestamps of the output kernel.
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a,
                        hipEvent_t ev_begin, hipEvent_t ev_end, int* n_kernels);
 
