@@ -149,15 +149,18 @@ def _flatten(x, d):
 def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
             beta: float = 0.0, causal: bool = True, phi: str = "identity",
             w1=None, w3=None, ascent: bool = False, inner_steps: int = 1,
-            return_state: bool = False):
+            return_state: bool = False, S0=None, M0=None):
     """Recurrent TTT forward, fp64, one gradient step per token.
 
     q, k: [B, H, T, d_k]; v: [B, H, T, d_v]; eta / a: [B, H, T] (per_token /
     softplus modes); w1, w3: [H, d_phi, d_k] for the SwiGLU feature map.
     Returns o: [B, H, T, d_v] (and the final (S, M) if ``return_state``).
+    ``S0``, ``M0`` ([B, H, d_v, d_phi], causal only) replace the reset state:
+    the recurrent form carries (S, M) from one call to the next (Table 2 lists
+    a recurrent implementation of every variant); None reads as zero.
 
     For every sequence (b, h) independently:
-      S = 0, M = 0                                   (reset per sequence)
+      S = S0 or 0, M = M0 or 0                       (reset per sequence)
       for t = 0 .. T-1:
         G   = grad_S l_t(S)  = -v_t phi(k_t)^T        (explicit gradient)
         M   = beta M - eta_t G      (ascent: + eta_t G)
@@ -189,8 +192,10 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
         raise ValueError("inner_steps > 1 is defined here for beta == 0 only")
     sign = 1.0 if ascent else -1.0
 
-    S = np.zeros((N, d_v, d_phi))
-    M = np.zeros((N, d_v, d_phi))
+    if (S0 is not None or M0 is not None) and not causal:
+        raise ValueError("an entry state is defined for the causal mode only")
+    S = np.zeros((N, d_v, d_phi)) if S0 is None else np.array(S0, dtype=np.float64).reshape(N, d_v, d_phi)
+    M = np.zeros((N, d_v, d_phi)) if M0 is None else np.array(M0, dtype=np.float64).reshape(N, d_v, d_phi)
     o = np.zeros((N, T, d_v))
     for t in range(T):
         for _ in range(inner_steps):
@@ -205,6 +210,46 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
     if return_state:
         return o, S.reshape(B, H, d_v, d_phi), M.reshape(B, H, d_v, d_phi)
     return o
+
+
+def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
+         beta: float = 0.0, phi: str = "identity", w1=None, w3=None):
+    """One recurrent step (decode) for every sequence: the token q1, k1, v1
+    ([B, H, d]) with rate eta ([B, H], per_token / softplus modes) updates the
+    carried state (S, M) ([B, H, d_v, d_phi]) and is read out after its update:
+
+      M' = beta M + eta v phi(k)^T,   S' = S + M',   o = S' phi(q).
+
+    Returns (o [B, H, d_v], S', M').  The step is written out on its own (it is
+    the loop body of ``forward``); the tests check T steps against ``forward``.
+    """
+    q1 = np.asarray(q1, dtype=np.float64)
+    B, H, d_k = q1.shape
+    N = B * H
+    v1 = np.asarray(v1, dtype=np.float64).reshape(N, -1)
+    if phi == "swiglu":
+        w1n = np.broadcast_to(np.asarray(w1, np.float64)[None], (B,) + np.shape(w1)).reshape(N, -1, d_k)
+        w3n = np.broadcast_to(np.asarray(w3, np.float64)[None], (B,) + np.shape(w3)).reshape(N, -1, d_k)
+        pq = features(q1.reshape(N, 1, d_k), phi, w1n, w3n)[:, 0]
+        pk = features(np.asarray(k1, np.float64).reshape(N, 1, d_k), phi, w1n, w3n)[:, 0]
+    else:
+        pq = q1.reshape(N, d_k)
+        pk = np.asarray(k1, np.float64).reshape(N, d_k)
+    if eta_mode == "scalar":
+        e = np.full(N, float(eta_scalar))
+    elif eta_mode == "per_token":
+        e = np.asarray(eta, np.float64).reshape(N)
+    elif eta_mode == "softplus":
+        e = softplus(np.asarray(eta, np.float64).reshape(N))
+    else:
+        raise ValueError(eta_mode)
+    d_v, d_phi = v1.shape[1], pk.shape[1]
+    S = np.asarray(S, np.float64).reshape(N, d_v, d_phi)
+    M = np.asarray(M, np.float64).reshape(N, d_v, d_phi)
+    M_new = beta * M + e[:, None, None] * v1[:, :, None] * pk[:, None, :]
+    S_new = S + M_new
+    o = np.einsum("nvf,nf->nv", S_new, pq)
+    return o.reshape(B, H, d_v), S_new.reshape(B, H, d_v, d_phi), M_new.reshape(B, H, d_v, d_phi)
 
 
 # ----------------------------------------------------------------------------
