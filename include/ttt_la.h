@@ -131,6 +131,42 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out);
 int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
                    float eta_scalar, float beta, uint32_t mode, void* o, void* hip_stream);
 
+/* Causal forward from a carried state.  Table 2 of the thelatestinai.com page
+ * lists a recurrent implementation of every variant beside the parallel one:
+ * the recurrent form keeps the fast weight (S, M) from one call to the next.
+ * Same as ttt_la_forward in the causal mode, except that the state before the
+ * first token is (S0, M0) instead of zero, and that the state after the last
+ * token is written to (S_T, M_T):
+ *   S0, M0, S_T, M_T  device fp32 [B, H, d_v, d_phi] (row r = value column r
+ *            of the fast weight, column = feature), C-contiguous, 16-byte
+ *            aligned.  Any may be NULL: a NULL S0 or M0 reads as zero, a NULL
+ *            S_T or M_T is not written.  S_T may be S0 and M_T may be M0 (the
+ *            state is then updated in place); apart from that the outputs must
+ *            not overlap each other or any input, and S0, M0 must not overlap
+ *            q, k, v, eta or o.
+ * Errors: as ttt_la_forward, and TTT_LA_ERR_INVALID_ARG for the bidirectional
+ * mode bit or a misaligned or overlapping state pointer.
+ * TTT_LA_ERR_UNSUPPORTED for a handle created with TTT_LA_LAUNCH_PREFIX on the
+ * 32x32-tile plan (that plan has no workspace for the entry state). */
+int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
+                         float eta_scalar, float beta, uint32_t mode, const float* S0, const float* M0,
+                         void* o, float* S_T, float* M_T, void* hip_stream);
+
+/* One recurrent step (decode) for every (b, h), the recurrent implementation
+ * of Table 2 applied to a single new token:
+ *   M <- beta M + eta v phi(k)^T,   S <- S + M,   o = S phi(q)
+ *   q, k     device [B, H, 1, d_k] in dtype; v, o: [B, H, 1, d_v] in dtype.
+ *   eta      NULL for TTT_LA_ETA_SCALAR, else device [B, H] fp32 (the rate or
+ *            the softplus argument of this token).
+ *   S, M     device fp32 [B, H, d_v, d_phi] as in ttt_la_forward_state,
+ *            updated in place; they must not overlap each other or any other
+ *            argument.
+ *   mode     rate bits only (TTT_LA_BIDIRECTIONAL is invalid here).
+ * The handle's T is ignored; its B, H, widths, dtype and feature map (W1, W3)
+ * apply.  Allocates nothing, does not synchronise; errors as ttt_la_forward. */
+int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                float beta, uint32_t mode, float* S, float* M, void* o, void* hip_stream);
+
 /* Releases the workspace and the handle.  NULL-safe. */
 void ttt_la_destroy(ttt_la_t h);
 
@@ -144,6 +180,14 @@ const char* ttt_la_status_string(int status);
  * for these arguments before touching the device. */
 int ttt_la_check(const ttt_la_desc* desc, const void* q, const void* k, const void* v,
                  const float* eta, float eta_scalar, float beta, uint32_t mode, const void* o);
+
+/* The same for the state-carrying calls: call = 0 checks the arguments of
+ * ttt_la_forward_state (s_in = S0, m_in = M0, s_out = S_T, m_out = M_T),
+ * call = 1 those of ttt_la_step (s_in = s_out = S, m_in = m_out = M).  The
+ * descriptor is checked first; q must not be NULL. */
+int ttt_la_check_state(const ttt_la_desc* desc, int32_t call, const void* q, const void* k, const void* v,
+                       const float* eta, float eta_scalar, float beta, uint32_t mode, const float* s_in,
+                       const float* m_in, const void* o, const float* s_out, const float* m_out);
 
 /* Kernel plan chosen at create, for tests and measurement. */
 typedef struct {
@@ -169,9 +213,11 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan);
  * 0; always 0 for other plans.  Synchronises with the device (a blocking copy). */
 int ttt_la_wait_status(ttt_la_t h, int32_t* failed);
 
-/* Measurement hook.  When n_slots > 0, every following ttt_la_forward records
- * a pair of HIP events (created here, not device memory) on its stream around
- * the output kernel, cycling through n_slots pairs; ttt_la_kernel_times then
+/* Measurement hook.  When n_slots > 0, every following ttt_la_forward,
+ * ttt_la_forward_state or ttt_la_step passes a pair of HIP events (created
+ * here, not device memory) to the launch of its output kernel (the step
+ * kernel for ttt_la_step), which takes the kernel's start and end timestamps,
+ * cycling through n_slots pairs; ttt_la_kernel_times then
  * returns the elapsed milliseconds of the last min(calls, n_slots) pairs
  * (oldest first) after synchronising on them.  n_slots = 0 turns it off. */
 int ttt_la_enable_kernel_timing(ttt_la_t h, int32_t n_slots);

@@ -174,3 +174,72 @@ def test_binding_refuses_missing_library(tmp_path):
             _binding.load_library(str(tmp_path / "nope.so"))
     finally:
         _binding._lib = saved
+
+
+# ----------------------------------------------------------------------------
+# state-carrying calls: ttt_la_forward_state (call 0) and ttt_la_step (call 1)
+# ----------------------------------------------------------------------------
+
+S0, M0, ST, MT = (0x10000000 * (i + 8) for i in range(4))
+SB = 2 * 3 * 128 * 128 * 4                          # bytes of one fp32 state [B, H, d_v, d_phi]
+
+
+def check_fs(d=None, q=Q, k=K, v=V, eta=None, eta_scalar=0.5, beta=0.9, mode=0, s0=S0, m0=M0, o=O, st=ST, mt=MT):
+    return tla.ttt_la_check_state(d or desc(), 0, q, k, v, eta, eta_scalar, beta, mode, s0, m0, o, st, mt)
+
+
+def check_step(d=None, q=Q, k=K, v=V, eta=None, eta_scalar=0.5, beta=0.9, mode=0, s=S0, m=M0, o=O):
+    return tla.ttt_la_check_state(d or desc(), 1, q, k, v, eta, eta_scalar, beta, mode, s, m, o, s, m)
+
+
+def test_forward_state_valid_arguments():
+    assert check_fs() == tla.TTT_LA_OK
+    assert check_fs(s0=None, m0=None) == tla.TTT_LA_OK               # zero entry state
+    assert check_fs(st=None, mt=None) == tla.TTT_LA_OK               # no final state
+    assert check_fs(st=S0, mt=M0) == tla.TTT_LA_OK                   # in place
+    assert check_fs(eta=ETA, mode=tla.TTT_LA_ETA_SOFTPLUS) == tla.TTT_LA_OK
+    assert check_fs(d=desc(dtype="f32", d_k=64, d_v=64)) == tla.TTT_LA_OK
+
+
+def test_forward_state_rejections():
+    bad = tla.TTT_LA_ERR_INVALID_ARG
+    assert check_fs(mode=tla.TTT_LA_BIDIRECTIONAL) == bad           # causal only
+    assert check_fs(s0=S0 + 8) == bad                                # misaligned
+    assert check_fs(mt=MT + 4) == bad
+    assert check_fs(st=MT) == bad                                    # S_T and M_T overlap
+    assert check_fs(st=S0 + 16) == bad                               # partial overlap with S0
+    assert check_fs(st=M0) == bad                                    # S_T over M0
+    assert check_fs(mt=S0) == bad
+    assert check_fs(s0=Q) == bad                                     # state over an input
+    assert check_fs(st=O + 16) == bad                                # state over the output
+    assert check_fs(st=ST + SB, mt=MT) == tla.TTT_LA_OK              # disjoint elsewhere
+    assert check_fs(beta=1.0) == bad
+    assert check_fs(q=None) == bad
+
+
+def test_step_arguments():
+    bad = tla.TTT_LA_ERR_INVALID_ARG
+    assert check_step() == tla.TTT_LA_OK
+    assert check_step(eta=ETA, mode=tla.TTT_LA_ETA_PER_TOKEN) == tla.TTT_LA_OK
+    assert check_step(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=W3)) == tla.TTT_LA_OK
+    assert check_step(s=None) == bad
+    assert check_step(m=None) == bad
+    assert check_step(s=S0 + 4) == bad
+    assert check_step(m=S0 + 256) == bad                             # S and M overlap
+    assert check_step(mode=tla.TTT_LA_BIDIRECTIONAL) == bad
+    assert check_step(mode=tla.TTT_LA_ETA_SOFTPLUS) == bad           # rate pointer missing
+    assert check_step(eta=ETA) == bad                                # pointer without a mode bit
+    assert check_step(o=Q) == bad
+    assert check_step(s=O) == bad
+    # step and forward_state check different extents: one token per (b, h)
+    assert check_step(o=V + 2 * 3 * 128 * 2) == tla.TTT_LA_OK
+    # call 1 requires the state outputs to be the inputs; unknown call numbers fail
+    assert tla.ttt_la_check_state(desc(), 1, Q, K, V, None, 0.5, 0.9, 0, S0, M0, O, ST, MT) == bad
+    assert tla.ttt_la_check_state(desc(), 2, Q, K, V, None, 0.5, 0.9, 0, S0, M0, O, S0, M0) == bad
+
+
+def test_state_calls_with_null_handle():
+    lib = tla.load_library()
+    assert lib.ttt_la_forward_state(None, Q, K, V, None, 1.0, 0.0, 0, S0, M0, O, ST, MT, None) == \
+        tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_step(None, Q, K, V, None, 1.0, 0.0, 0, S0, M0, O, None) == tla.TTT_LA_ERR_INVALID_ARG

@@ -59,9 +59,9 @@ class ttt_la_plan(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_destroy", "ttt_la_status_string",
-           "ttt_la_check", "ttt_la_get_plan", "ttt_la_wait_status", "ttt_la_enable_kernel_timing",
-           "ttt_la_kernel_times")
+EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_forward_state", "ttt_la_step", "ttt_la_destroy",
+           "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_get_plan",
+           "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -81,6 +81,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_create.restype = ctypes.c_int
     lib.ttt_la_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp]
     lib.ttt_la_forward.restype = ctypes.c_int
+    lib.ttt_la_forward_state.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp]
+    lib.ttt_la_forward_state.restype = ctypes.c_int
+    lib.ttt_la_step.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp]
+    lib.ttt_la_step.restype = ctypes.c_int
+    lib.ttt_la_check_state.argtypes = [ctypes.POINTER(ttt_la_desc), i32, vp, vp, vp, vp, f32, f32, u32, vp, vp,
+                                       vp, vp, vp]
+    lib.ttt_la_check_state.restype = ctypes.c_int
     lib.ttt_la_destroy.argtypes = [vp]
     lib.ttt_la_destroy.restype = None
     lib.ttt_la_status_string.argtypes = [ctypes.c_int]
@@ -120,6 +127,25 @@ def ttt_la_forward(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: fl
                    mode: int, o: int, stream: Optional[int]) -> int:
     return load_library().ttt_la_forward(h, q, k, v, eta, float(eta_scalar), float(beta),
                                          int(mode), o, stream)
+
+
+def ttt_la_forward_state(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float,
+                         mode: int, S0: Optional[int], M0: Optional[int], o: int, S_T: Optional[int],
+                         M_T: Optional[int], stream: Optional[int]) -> int:
+    return load_library().ttt_la_forward_state(h, q, k, v, eta, float(eta_scalar), float(beta), int(mode),
+                                               S0, M0, o, S_T, M_T, stream)
+
+
+def ttt_la_step(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float, mode: int,
+                S: int, M: int, o: int, stream: Optional[int]) -> int:
+    return load_library().ttt_la_step(h, q, k, v, eta, float(eta_scalar), float(beta), int(mode), S, M, o,
+                                      stream)
+
+
+def ttt_la_check_state(desc: ttt_la_desc, call: int, q=None, k=None, v=None, eta=None, eta_scalar=1.0,
+                       beta=0.0, mode=0, s_in=None, m_in=None, o=None, s_out=None, m_out=None) -> int:
+    return load_library().ttt_la_check_state(ctypes.byref(desc), int(call), q, k, v, eta, float(eta_scalar),
+                                             float(beta), int(mode), s_in, m_in, o, s_out, m_out)
 
 
 def ttt_la_destroy(h) -> None:
@@ -251,4 +277,45 @@ class TTTLinearAttention:
                             mode_bits(eta_mode, causal), _ptr(out), s)
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_forward")
+        return out
+
+    def _stream(self, t, stream):
+        import torch
+        return torch.cuda.current_stream(t.device).cuda_stream if stream is None else int(stream)
+
+    @staticmethod
+    def _check(*named):
+        import torch
+        for name, t in named:
+            if t is None:
+                continue
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if t.device.type != "cuda":
+                raise ValueError(f"{name} must be a device tensor")
+        return torch
+
+    def forward_state(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", S0=None, M0=None,
+                      out=None, S_T=None, M_T=None, stream=None):
+        """Causal forward from the carried state (S0, M0) (None = zero); writes the state
+        after the last token to S_T, M_T when given (fp32 [B, H, d_v, d_phi])."""
+        torch = self._check(("q", q), ("k", k), ("v", v), ("S0", S0), ("M0", M0), ("S_T", S_T), ("M_T", M_T))
+        if out is None:
+            out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
+        st = ttt_la_forward_state(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta,
+                                  mode_bits(eta_mode, True), _ptr(S0), _ptr(M0), _ptr(out), _ptr(S_T), _ptr(M_T),
+                                  self._stream(q, stream))
+        if st != TTT_LA_OK:
+            raise TTTError(st, "ttt_la_forward_state")
+        return out
+
+    def step(self, q, k, v, S, M, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", out=None, stream=None):
+        """One recurrent step: q, k, v [B, H, 1, d]; S, M fp32 [B, H, d_v, d_phi] updated in place."""
+        torch = self._check(("q", q), ("k", k), ("v", v), ("S", S), ("M", M))
+        if out is None:
+            out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
+        st = ttt_la_step(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta,
+                         mode_bits(eta_mode, True), _ptr(S), _ptr(M), _ptr(out), self._stream(q, stream))
+        if st != TTT_LA_OK:
+            raise TTTError(st, "ttt_la_step")
         return out

@@ -100,6 +100,77 @@ int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void
     return TTT_LA_OK;
 }
 
+bool state_ok(const void* p) { return !p || aligned(p, 16); }
+
+// ttt_la_forward_state: forward checks, causal only, state pointers aligned, outputs
+// disjoint from everything except (in place) their own input
+int check_forward_state(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                        float eta_scalar, float beta, uint32_t mode, const float* S0, const float* M0, const void* o,
+                        const float* S_T, const float* M_T) {
+    int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, o);
+    if (st != TTT_LA_OK) return st;
+    if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
+    if (!state_ok(S0) || !state_ok(M0) || !state_ok(S_T) || !state_ok(M_T)) return TTT_LA_ERR_INVALID_ARG;
+    const size_t eb = elem_bytes(d->dtype);
+    const size_t nt = (size_t)d->B * d->H * d->T;
+    const size_t sb = (size_t)d->B * d->H * d->d_v * d->d_phi * sizeof(float);
+    const size_t qk_bytes = nt * d->d_k * eb, v_bytes = nt * d->d_v * eb;
+    const size_t eta_bytes = eta ? nt * sizeof(float) : 0;
+    const size_t w_bytes = d->phi == TTT_LA_PHI_SWIGLU ? (size_t)d->H * d->d_phi * d->d_k * eb : 0;
+    const void* states[4] = {S0, M0, S_T, M_T};
+    for (const void* x : states) {
+        if (overlaps(x, sb, q, qk_bytes) || overlaps(x, sb, k, qk_bytes) || overlaps(x, sb, v, v_bytes) ||
+            overlaps(x, sb, eta, eta_bytes) || overlaps(x, sb, o, v_bytes) || overlaps(x, sb, d->w1, w_bytes) ||
+            overlaps(x, sb, d->w3, w_bytes))
+            return TTT_LA_ERR_INVALID_ARG;
+    }
+    if (overlaps(S_T, sb, M_T, sb)) return TTT_LA_ERR_INVALID_ARG;
+    if (S_T != S0 && overlaps(S_T, sb, S0, sb)) return TTT_LA_ERR_INVALID_ARG;
+    if (M_T != M0 && overlaps(M_T, sb, M0, sb)) return TTT_LA_ERR_INVALID_ARG;
+    if (overlaps(S_T, sb, M0, sb) || overlaps(M_T, sb, S0, sb)) return TTT_LA_ERR_INVALID_ARG;
+    return TTT_LA_OK;
+}
+
+// ttt_la_step: one token per (b, h); S, M required, disjoint from each other and
+// from every other argument
+int check_step(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
+               float eta_scalar, float beta, uint32_t mode, const float* S, const float* M, const void* o) {
+    if (!q || !k || !v || !o || !S || !M) return TTT_LA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return TTT_LA_ERR_INVALID_ARG;
+    if (!aligned(S, 16) || !aligned(M, 16)) return TTT_LA_ERR_INVALID_ARG;
+    if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
+    if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
+    const bool per_tok = (mode & TTT_LA_ETA_PER_TOKEN) != 0;
+    const bool softp = (mode & TTT_LA_ETA_SOFTPLUS) != 0;
+    if (per_tok && softp) return TTT_LA_ERR_INVALID_ARG;
+    if (per_tok || softp) {
+        if (!eta || !aligned(eta, 4)) return TTT_LA_ERR_INVALID_ARG;
+    } else {
+        if (eta) return TTT_LA_ERR_INVALID_ARG;
+        if (!std::isfinite(eta_scalar)) return TTT_LA_ERR_INVALID_ARG;
+    }
+    if (!(beta >= 0.0f && beta < 1.0f)) return TTT_LA_ERR_INVALID_ARG;
+    const size_t eb = elem_bytes(d->dtype);
+    const size_t n = (size_t)d->B * d->H;
+    const size_t qk_bytes = n * d->d_k * eb, v_bytes = n * d->d_v * eb;
+    const size_t eta_bytes = eta ? n * sizeof(float) : 0;
+    const size_t sb = n * d->d_v * d->d_phi * sizeof(float);
+    const size_t w_bytes = d->phi == TTT_LA_PHI_SWIGLU ? (size_t)d->H * d->d_phi * d->d_k * eb : 0;
+    if (overlaps(o, v_bytes, q, qk_bytes) || overlaps(o, v_bytes, k, qk_bytes) || overlaps(o, v_bytes, v, v_bytes) ||
+        overlaps(o, v_bytes, eta, eta_bytes) || overlaps(o, v_bytes, d->w1, w_bytes) ||
+        overlaps(o, v_bytes, d->w3, w_bytes))
+        return TTT_LA_ERR_INVALID_ARG;
+    if (overlaps(S, sb, M, sb)) return TTT_LA_ERR_INVALID_ARG;
+    const void* states[2] = {S, M};
+    for (const void* x : states) {
+        if (overlaps(x, sb, q, qk_bytes) || overlaps(x, sb, k, qk_bytes) || overlaps(x, sb, v, v_bytes) ||
+            overlaps(x, sb, eta, eta_bytes) || overlaps(x, sb, o, v_bytes) || overlaps(x, sb, d->w1, w_bytes) ||
+            overlaps(x, sb, d->w3, w_bytes))
+            return TTT_LA_ERR_INVALID_ARG;
+    }
+    return TTT_LA_OK;
+}
+
 Shape shape_of(const ttt_la_desc& d) {
     Shape s;
     s.B = d.B;
@@ -152,6 +223,20 @@ int ttt_la_check(const ttt_la_desc* desc, const void* q, const void* k, const vo
     return check_forward(desc, q, k, v, eta, eta_scalar, beta, mode, o);
 }
 
+int ttt_la_check_state(const ttt_la_desc* desc, int32_t call, const void* q, const void* k, const void* v,
+                       const float* eta, float eta_scalar, float beta, uint32_t mode, const float* s_in,
+                       const float* m_in, const void* o, const float* s_out, const float* m_out) {
+    int st = check_desc(desc);
+    if (st != TTT_LA_OK) return st;
+    if (call == 0)
+        return check_forward_state(desc, q, k, v, eta, eta_scalar, beta, mode, s_in, m_in, o, s_out, m_out);
+    if (call == 1) {
+        if (s_in != s_out || m_in != m_out) return TTT_LA_ERR_INVALID_ARG;
+        return check_step(desc, q, k, v, eta, eta_scalar, beta, mode, s_in, m_in, o);
+    }
+    return TTT_LA_ERR_INVALID_ARG;
+}
+
 int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     if (!out) return TTT_LA_ERR_INVALID_ARG;
     *out = nullptr;
@@ -202,12 +287,24 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     return TTT_LA_OK;
 }
 
-int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
-                   float beta, uint32_t mode, void* o, void* hip_stream) {
-    if (!h) return TTT_LA_ERR_INVALID_ARG;
-    int st = check_forward(&h->desc, q, k, v, eta, eta_scalar, beta, mode, o);
-    if (st != TTT_LA_OK) return st;
+}  // extern "C"
 
+namespace {
+
+// the timing events of the next launch (null when the hook is off)
+void next_events(ttt_la_s* h, hipEvent_t* eb, hipEvent_t* ee) {
+    *eb = *ee = nullptr;
+    if (!h->ev_begin.empty()) {
+        const size_t slot = (size_t)h->calls % h->ev_begin.size();
+        *eb = h->ev_begin[slot];
+        *ee = h->ev_end[slot];
+        h->calls++;
+    }
+}
+
+int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                    float beta, uint32_t mode, const float* S0, const float* M0, void* o, float* S_T, float* M_T,
+                    void* hip_stream) {
     ttt::FwdArgs a{};
     a.q = q;
     a.k = k;
@@ -219,32 +316,81 @@ int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, cons
     a.bidirectional = (mode & TTT_LA_BIDIRECTIONAL) != 0;
     a.o = o;
     a.stream = static_cast<hipStream_t>(hip_stream);
+    a.S0 = S0;
+    a.M0 = M0;
+    a.S_T = S_T;
+    a.M_T = M_T;
+    const bool state_io = S0 || M0 || S_T || M_T;
 
-    hipEvent_t eb = nullptr, ee = nullptr;
-    if (!h->ev_begin.empty()) {
-        const size_t slot = (size_t)h->calls % h->ev_begin.size();
-        eb = h->ev_begin[slot];
-        ee = h->ev_end[slot];
-        h->calls++;
-    }
+    hipEvent_t eb, ee;
+    next_events(h, &eb, &ee);
     hipError_t e;
-    if (h->fast) {
+    if (h->fast && (h->fp.wide || !state_io)) {
         int nk = 0;
         a.epoch = h->epoch + 1;
         e = ttt::launch_fast(h->shape, h->fp, h->workspace, a, eb, ee, &nk);
-        if (e == hipErrorCooperativeLaunchTooLarge && h->fp.fused) {
+        const bool fused_ran = h->fp.fused && !a.bidirectional && !state_io;
+        if (e == hipErrorCooperativeLaunchTooLarge && fused_ran) {
             // the fused grid cannot be resident right now: same result in three launches
             ttt::FastPlan p3 = h->fp;
             p3.fused = false;
             e = ttt::launch_fast(h->shape, p3, h->workspace, a, eb, ee, &nk);
-        } else if (e == hipSuccess && h->fp.fused && !a.bidirectional) {
+        } else if (e == hipSuccess && fused_ran) {
             h->epoch++;
         }
         h->n_kernels = nk;
     } else {
+        // fp32 inputs, and the carried-state calls of the 16x16-tile shapes
         e = ttt::launch_generic(h->shape, a, eb, ee);
         h->n_kernels = 1;
     }
+    return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                   float beta, uint32_t mode, void* o, void* hip_stream) {
+    if (!h) return TTT_LA_ERR_INVALID_ARG;
+    int st = check_forward(&h->desc, q, k, v, eta, eta_scalar, beta, mode, o);
+    if (st != TTT_LA_OK) return st;
+    return enqueue_forward(h, q, k, v, eta, eta_scalar, beta, mode, nullptr, nullptr, o, nullptr, nullptr,
+                           hip_stream);
+}
+
+int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
+                         float eta_scalar, float beta, uint32_t mode, const float* S0, const float* M0, void* o,
+                         float* S_T, float* M_T, void* hip_stream) {
+    if (!h) return TTT_LA_ERR_INVALID_ARG;
+    int st = check_forward_state(&h->desc, q, k, v, eta, eta_scalar, beta, mode, S0, M0, o, S_T, M_T);
+    if (st != TTT_LA_OK) return st;
+    // the prefix plan of the 32x32-tile kernels has no workspace for the entry state
+    if (h->fast && h->fp.wide && h->fp.prefix) return TTT_LA_ERR_UNSUPPORTED;
+    return enqueue_forward(h, q, k, v, eta, eta_scalar, beta, mode, S0, M0, o, S_T, M_T, hip_stream);
+}
+
+int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                float beta, uint32_t mode, float* S, float* M, void* o, void* hip_stream) {
+    if (!h) return TTT_LA_ERR_INVALID_ARG;
+    int st = check_step(&h->desc, q, k, v, eta, eta_scalar, beta, mode, S, M, o);
+    if (st != TTT_LA_OK) return st;
+    ttt::StepArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.eta = eta;
+    a.eta_scalar = eta_scalar;
+    a.beta = beta;
+    a.eta_kind = eta_kind_of(mode);
+    a.S = S;
+    a.M = M;
+    a.o = o;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    hipEvent_t eb, ee;
+    next_events(h, &eb, &ee);
+    const hipError_t e = ttt::launch_step(h->shape, a, eb, ee);
     return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
 

@@ -90,7 +90,26 @@ struct WideParams {
     unsigned* wait_failed;
     // W_PREFIX: first token of each segment, bounds[seg_count] = T
     int bounds[17];
+    // carried state in the caller's layout, fp32 [seq][d_v][d_phi] (W_OUTPUT):
+    // the entry state of segment 0 (has_init; with several segments the scan
+    // copies it into slot 0 first) and the state after the last token (either
+    // output may be null)
+    const float* S0;
+    const float* M0;
+    float* S_T;
+    float* M_T;
+    int has_init;
 };
+
+// The caller's state layout [seq][d_v][d_phi] against the register tiles: lane l
+// of wave w holds value column vcol(w, l) of the fast weight, and the f32x4 group
+// r4 of feature tile ft holds the four consecutive features user_f0(ft, r4, l).
+__device__ __forceinline__ int user_vcol(int w, int l) {
+    return 32 * w + 16 * ((l >> 2) & 1) + 8 * ((l >> 4) & 1) + 4 * ((l >> 3) & 1) + (l & 3);
+}
+__device__ __forceinline__ int user_f0(int ft, int r4, int l) {
+    return 32 * ft + 16 * (r4 >> 1) + 8 * (l >> 5) + 4 * (r4 & 1);
+}
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -231,8 +250,11 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     // workspace slots: [slot][T | M][wave][ft][r4][lane] f32x4 (16 floats per lane per tile)
     constexpr size_t TILE_F4 = 4 * 64;
     constexpr size_t HALF_F4 = (size_t)WNW * WFT * TILE_F4;
+    // seg_count slots per sequence: slot j (j >= 1) receives the summary of segment
+    // j - 1 and, after the scan, holds the entry state of segment j; slot 0 holds
+    // the carried entry state of segment 0 (when the call has one)
     auto slot_ptr = [&](int s) TTT_INLINE {
-        return reinterpret_cast<f32x4*>(p.state) + ((size_t)seq * (p.seg_count - 1) + s) * 2 * HALF_F4;
+        return reinterpret_cast<f32x4*>(p.state) + ((size_t)seq * p.seg_count + s) * 2 * HALF_F4;
     };
 
     // transpose-read columns: value columns in pi order, feature columns in sigma order
@@ -289,7 +311,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     auto load_eta = [&](int t0) TTT_INLINE {
         const int n = min(WC, t_end - t0);
         float et = p.eta_scalar;
-        if (ETAV) et = tid < n ? p.eta[seq_row + t0 + tid] : 0.0f;
+        if (ETAV) et = tid < n ? (p.eta ? p.eta[seq_row + t0 + tid] : p.eta_scalar) : 0.0f;
         return et;
     };
     // per-token weights of a chunk of n tokens
@@ -487,8 +509,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         const bool two = t_begin + WC < t_end;
         stage(stage_a, t_begin, true, true, true);
         const float et0 = load_eta(t_begin);
-        if (KIND != W_PREFIX && seg > 0) {
-            const f32x4* src = slot_ptr(seg - 1);
+        const bool slot_entry = KIND != W_PREFIX && (seg > 0 || (p.has_init && p.seg_count > 1));
+        if (slot_entry) {
+            const f32x4* src = slot_ptr(seg);
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft)
 #pragma unroll
@@ -500,6 +523,26 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                         const f32x4 m = src[HALF_F4 + (((size_t)wave * WFT + ft) * 4 + r4) * 64 + lane];
 #pragma unroll
                         for (int e = 0; e < 4; ++e) Ms[ft][4 * r4 + e] = m[e];
+                    }
+                }
+        } else if (KIND == W_OUTPUT && p.has_init) {
+            // one segment: the entry state straight from the caller's layout,
+            // T = S0 + kappa M0 (the carried-state calls use the per-token weights
+            // of the value operand, t_scale = 1)
+            const float kappa = beta * inv1mb;
+            const float* s0 = p.S0 ? p.S0 + (size_t)seq * WD * WD + (size_t)user_vcol(wave, lane) * WD : nullptr;
+            const float* m0 = p.M0 ? p.M0 + (size_t)seq * WD * WD + (size_t)user_vcol(wave, lane) * WD : nullptr;
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int f0 = user_f0(ft, r4, lane);
+                    const f32x4 sv = s0 ? *reinterpret_cast<const f32x4*>(s0 + f0) : f32x4{0.f, 0.f, 0.f, 0.f};
+                    const f32x4 mv = m0 ? *reinterpret_cast<const f32x4*>(m0 + f0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        Ts[ft][4 * r4 + e] = fmaf(kappa, mv[e], sv[e]);
+                        if constexpr (MOM) Ms[ft][4 * r4 + e] = mv[e];
                     }
                 }
         }
@@ -658,6 +701,26 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 
     if constexpr (KIND == W_OUTPUT) {
         output_pass();
+        if (seg == p.seg_count - 1 && (p.S_T || p.M_T)) {
+            // the state after the last token in the caller's layout:
+            // S = t_scale T - kappa M, M = rho Ms
+            const float kappa = beta * inv1mb;
+            const size_t row = (size_t)seq * WD * WD + (size_t)user_vcol(wave, lane) * WD;
+#pragma unroll
+            for (int ft = 0; ft < WFT; ++ft)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const int f0 = user_f0(ft, r4, lane);
+                    f32x4 sv, mv;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        mv[e] = MOM ? rho * Ms[ft][4 * r4 + e] : 0.0f;
+                        sv[e] = fmaf(-kappa, mv[e], t_scale * Ts[ft][4 * r4 + e]);
+                    }
+                    if (p.S_T) *reinterpret_cast<f32x4*>(p.S_T + row + f0) = sv;
+                    if (p.M_T) *reinterpret_cast<f32x4*>(p.M_T + row + f0) = mv;
+                }
+        }
     } else if constexpr (KIND == W_PREFIX) {
         // entry state from zero over all earlier tokens (an update-only pass), then
         // the segment's outputs
@@ -675,7 +738,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         // 1. zero-entry summary of this segment (every segment but the last)
         if (seg < p.seg_count - 1) {
             summary_pass();
-            write_summary(slot_ptr(seg));
+            write_summary(slot_ptr(seg + 1));
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft) Ts[ft] = f32x16{};
 #pragma unroll
@@ -695,7 +758,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             const int e0 = seg * per, e1 = min(total, e0 + per);
             const int n_el = (e1 - e0 + WNT - 1) / WNT;          // elements per thread
             const float bL = p.beta_seg;
-            f32x4* base = reinterpret_cast<f32x4*>(p.state) + (size_t)seq * steps * 2 * HALF_F4;
+            f32x4* base = slot_ptr(1);
             constexpr int MAXL = 32;
             const int batch = max(1, MAXL / steps);               // elements per round of loads
             for (int eb = 0; eb < n_el; eb += batch) {
@@ -733,7 +796,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         // the whole sequence, then every query reads S = t_scale T - kappa M.
         summary_pass();
         if constexpr (KIND == W_SUMMARY) {
-            f32x4* dst = slot_ptr(seg);
+            f32x4* dst = slot_ptr(seg + 1);
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft)
 #pragma unroll
@@ -788,35 +851,54 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     }
 }
 
-// Composes segment summaries into entry states, in place:
-//   T <- T + dT_s,  M <- beta^L M + dM_s,  slot s <- (T, M) = entry state of segment s + 1.
-// One thread per float4 of one sequence's state; all summaries are loaded
-// before the first store so that the loads overlap.
+// Composes segment summaries into entry states, in place, per sequence:
+//   (T, M) = entry state of segment 0 (the carried state if has_init, else 0),
+//   then for s = 1 .. n_slots - 1:  T <- T + dT,  M <- beta^L M + dM,
+//   slot s <- (T, M) = entry state of segment s.
+// With has_init the carried state is read from the caller's layout, put in the
+// T-form T = S0 + kappa M0 and also written to slot 0 (so that the output kernel
+// never reads S0, M0: they may be the buffers the final state goes to).  One
+// thread per float4 of one sequence's state; all summaries are loaded before
+// the first store so that the loads overlap.
 template <int MAXS>
-__global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_steps, float bL, int mom) {
+__global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_slots, float bL, int mom,
+                                                 const float* S0, const float* M0, float kappa, int has_init) {
     constexpr int HALF = WNW * WFT * 4 * 64;       // float4s of T (and of M) per slot
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)n_seq * HALF) return;
-    const size_t seqi = idx / HALF, e = idx % HALF;
-    f32x4* base = reinterpret_cast<f32x4*>(state) + seqi * n_steps * 2 * HALF + e;
+    const size_t seqi = idx / HALF;
+    const int e = (int)(idx % HALF);
+    f32x4* base = reinterpret_cast<f32x4*>(state) + seqi * n_slots * 2 * HALF + e;
+    const int n_steps = n_slots - 1;
     f32x4 dT[MAXS], dM[MAXS];
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
         if (s < n_steps) {
-            dT[s] = base[(size_t)s * 2 * HALF];
-            if (mom) dM[s] = base[(size_t)s * 2 * HALF + HALF];
+            dT[s] = base[(size_t)(s + 1) * 2 * HALF];
+            if (mom) dM[s] = base[(size_t)(s + 1) * 2 * HALF + HALF];
         }
     }
     f32x4 T = {0.f, 0.f, 0.f, 0.f}, M = {0.f, 0.f, 0.f, 0.f};
+    if (has_init) {
+        // element e = ((wave * WFT + ft) * 4 + r4) * 64 + lane of the register tiles
+        const int lane = e & 63, r4 = (e >> 6) & 3, ft = (e >> 8) % WFT, w = (e >> 8) / WFT;
+        const size_t off = seqi * WD * WD + (size_t)user_vcol(w, lane) * WD + user_f0(ft, r4, lane);
+        const f32x4 sv = S0 ? *reinterpret_cast<const f32x4*>(S0 + off) : f32x4{0.f, 0.f, 0.f, 0.f};
+        if (M0) M = *reinterpret_cast<const f32x4*>(M0 + off);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) T[r] = fmaf(kappa, M[r], sv[r]);
+        base[0] = T;
+        if (mom) base[HALF] = M;
+    }
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
         if (s < n_steps) {
             T += dT[s];
-            base[(size_t)s * 2 * HALF] = T;
+            base[(size_t)(s + 1) * 2 * HALF] = T;
             if (mom) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) M[r] = fmaf(bL, M[r], dM[s][r]);
-                base[(size_t)s * 2 * HALF + HALF] = M;
+                base[(size_t)(s + 1) * 2 * HALF + HALF] = M;
             }
         }
     }
@@ -878,8 +960,10 @@ bool wide_supported(const Shape& s) {
 }
 
 size_t wide_summary_bytes(const Shape& s, int segments) {
+    // one slot per segment: the summaries of segments 0 .. S-2 (then the entry
+    // states of segments 1 .. S-1) and the carried entry state of segment 0
     if (segments <= 1) return 0;
-    return (size_t)s.n_seq() * (segments - 1) * 2 * WD * WD * sizeof(float);
+    return (size_t)s.n_seq() * segments * 2 * WD * WD * sizeof(float);
 }
 
 int wide_max_segments() { return 16; }
@@ -904,13 +988,22 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
     wp.beta = a.beta;
     wp.eta_kind = a.eta_kind;
     wp.T = s.T;
-    const bool mom = a.beta != 0.0f;
-    const bool etav = a.eta_kind != ETA_SCALAR;
+    // A carried state (in or out) takes the kernels with per-token value weights
+    // (a scalar rate is then read as a constant per-token rate, so that the state
+    // needs no 1 / eta), and the momentum kernels whenever M_T is asked for.
+    const bool state_io = a.S0 || a.M0 || a.S_T || a.M_T;
+    const bool mom = a.beta != 0.0f || a.M_T;
+    const bool etav = a.eta_kind != ETA_SCALAR || state_io;
+    wp.S0 = a.S0;
+    wp.M0 = a.M0;
+    wp.S_T = a.S_T;
+    wp.M_T = a.M_T;
+    wp.has_init = (a.S0 || a.M0) ? 1 : 0;
     wp.beta_seg = (float)std::pow((double)a.beta, (double)p.seg_len);
     hipStream_t st = a.stream;
     hipError_t e = hipSuccess;
     int nk = 0;
-    if (!a.bidirectional && p.fused) {
+    if (!a.bidirectional && p.fused && !state_io) {
         char* z = static_cast<char*>(workspace) + p.summary_bytes;
         wp.seg_count = p.segments;
         wp.seg_len = p.seg_len;
@@ -937,7 +1030,7 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
         (void)hipGetLastError();
         return hipErrorCooperativeLaunchTooLarge;
     }
-    if (!a.bidirectional && p.prefix) {
+    if (!a.bidirectional && p.prefix && !state_io) {
         wp.seg_count = p.segments;
         wp.seg_len = p.seg_len;
         for (int i = 0; i <= p.segments; ++i) wp.bounds[i] = p.bounds[i];
@@ -959,17 +1052,20 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
             wp.n_units = s.n_seq() * (p.segments - 1);
             if ((e = launch_wide_kind<W_SUMMARY>(mom, etav, wp, st)) != hipSuccess) return e;
             ++nk;
-            if (p.segments > 2) {
+            // with two segments and no carried state the one summary already is the
+            // entry state of segment 1
+            if (p.segments > 2 || wp.has_init) {
                 constexpr int HALF = WNW * WFT * 4 * 64;
                 const size_t n_threads = (size_t)s.n_seq() * HALF;
                 const float bL = (float)std::pow((double)a.beta, (double)p.seg_len);
+                const float kappa = a.beta / (1.0f - a.beta);
                 const dim3 grid((unsigned)((n_threads + 255) / 256));
                 if (p.segments - 1 <= 7)
-                    hipLaunchKernelGGL(wide_scan<7>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments - 1, bL,
-                                       mom ? 1 : 0);
+                    hipLaunchKernelGGL(wide_scan<7>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments, bL,
+                                       mom ? 1 : 0, a.S0, a.M0, kappa, wp.has_init);
                 else
-                    hipLaunchKernelGGL(wide_scan<15>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments - 1,
-                                       bL, mom ? 1 : 0);
+                    hipLaunchKernelGGL(wide_scan<15>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments, bL,
+                                       mom ? 1 : 0, a.S0, a.M0, kappa, wp.has_init);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 ++nk;
             }

@@ -44,6 +44,13 @@ struct GenericParams {
     int eta_kind;
     int T, H, d_k, d_v, d_phi;
     int n_dvblk;
+    // carried state, fp32 [seq][d_v][d_phi] (causal only; null: zero entry state /
+    // final state not written).  A workgroup reads and writes only its own 16
+    // value rows, so the final state may overwrite the entry state in place.
+    const float* S0;
+    const float* M0;
+    float* S_T;
+    float* M_T;
 };
 
 // LDS layout (floats):
@@ -131,9 +138,13 @@ __global__ void __launch_bounds__(GTHREADS) generic_forward(GenericParams p) {
         }
         sBP[GC] = bp;
     }
-    for (int idx = tid; idx < d_phi * GDV; idx += GTHREADS) {
-        sS[idx] = 0.0f;
-        sM[idx] = 0.0f;
+    {
+        const size_t sbase = ((size_t)seq * p.d_v + dv0) * d_phi;
+        for (int idx = tid; idx < d_phi * GDV; idx += GTHREADS) {
+            const int f = idx / GDV, e = idx % GDV;
+            sS[idx] = p.S0 ? p.S0[sbase + (size_t)e * d_phi + f] : 0.0f;
+            sM[idx] = p.M0 ? p.M0[sbase + (size_t)e * d_phi + f] : 0.0f;
+        }
     }
     __syncthreads();
 
@@ -216,7 +227,17 @@ __global__ void __launch_bounds__(GTHREADS) generic_forward(GenericParams p) {
         __syncthreads();
     }
 
-    if (causal) return;
+    if (causal) {
+        if (p.S_T || p.M_T) {
+            const size_t sbase = ((size_t)seq * p.d_v + dv0) * d_phi;
+            for (int idx = tid; idx < d_phi * GDV; idx += GTHREADS) {
+                const int e = idx / d_phi, f = idx % d_phi;   // coalesced along the features
+                if (p.S_T) p.S_T[sbase + idx] = sS[f * GDV + e];
+                if (p.M_T) p.M_T[sbase + idx] = sM[f * GDV + e];
+            }
+        }
+        return;
+    }
 
     // ---- pass 2 (bidirectional): every query reads the final state ---------
     for (int ch = 0; ch < n_chunks; ++ch) {
@@ -260,6 +281,10 @@ hipError_t launch_generic(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin,
     p.d_v = s.d_v;
     p.d_phi = s.d_phi;
     p.n_dvblk = s.d_v / GDV;
+    p.S0 = a.S0;
+    p.M0 = a.M0;
+    p.S_T = a.S_T;
+    p.M_T = a.M_T;
     const size_t smem = generic_smem_bytes(s);
     dim3 grid((unsigned)(s.n_seq() * p.n_dvblk)), block(GTHREADS);
     hipError_t e = hipSuccess;

@@ -23,6 +23,12 @@ struct FwdArgs {
     void* o;
     hipStream_t stream;
     unsigned epoch;    // 1, 2, 3, ... per forward of a handle whose plan is fused
+    // carried state, fp32 [B, H, d_v, d_phi] in the caller's layout (null: zero
+    // entry state / final state not written)
+    const float* S0 = nullptr;
+    const float* M0 = nullptr;
+    float* S_T = nullptr;
+    float* M_T = nullptr;
 };
 
 // Shape of one layer (copied from the descriptor).
@@ -78,6 +84,24 @@ size_t wide_zero_bytes(const Shape& s);
 size_t wide_flag_offset(const Shape& s, const FastPlan& p);
 hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
                        hipEvent_t ev_end, int* n_kernels);
+
+// ---- recurrent step (decode.hip) ----------------------------------------------
+struct StepArgs {
+    const void* q;       // [B, H, d_k]
+    const void* k;
+    const void* v;       // [B, H, d_v]
+    const float* eta;    // [B, H] or null
+    float eta_scalar;
+    float beta;
+    int eta_kind;        // EtaKind
+    float* S;            // fp32 [B, H, d_v, d_phi], updated in place
+    float* M;
+    void* o;             // [B, H, d_v]
+    hipStream_t stream;
+};
+size_t step_smem_bytes(const Shape& s);
+// ev_begin/ev_end (may be null) take the step kernel's start and end timestamps
+hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 // Enqueues the whole forward (all kernels).  If ev_begin/ev_end are non-null
 // they take the start and end timestamps of the output kernel.
