@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--launch", default="auto", choices=["auto", "separate", "single", "prefix"],
                     help="how a segmented causal forward is launched")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the one-token recurrent step (ttt_la_step) at the workload's B, H and widths "
+                         "instead of the forward; prints its own JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device copy of MIB mebibytes (counter calibration) and exit")
     return ap.parse_args()
@@ -141,6 +144,91 @@ def cpu_baseline(w, x, seconds: float):
     }, o, heads
 
 
+def step_bytes(w) -> int:
+    """Algorithmic bytes of one recurrent step: S and M read and written once (fp32),
+    q, k, v read and o written for one token per (b, h) (+4 B of rate)."""
+    e = 4 if w.dtype == "f32" else 2
+    n = w.B * w.H
+    b = n * (2 * 2 * w.d_v * w.d_phi * 4 + (2 * w.d_k + 2 * w.d_v) * e)
+    if w.eta_mode != "scalar":
+        b += n * 4
+    return b
+
+
+def run_decode(args, w):
+    """K one-token steps of every (b, h) of workload w, the fp32 state resident in
+    HBM; the states are rotated over enough sets to exceed the last-level cache."""
+    import numpy as np
+    import torch
+
+    import ttt_weight_layers_amd as tla
+    from ttt_workloads import make_inputs
+
+    n_tok = 16
+    x = make_inputs(w.with_shape(T=n_tok))
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).to(dev)
+
+    q, k, v = up(x.q_dev), up(x.k_dev), up(x.v_dev)
+    toks = [(q[:, :, t:t + 1].contiguous(), k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous(),
+             None if x.a32 is None else torch.from_numpy(x.a32[:, :, t].copy()).to(dev)) for t in range(n_tok)]
+    w1 = up(x.w1_dev) if x.w1_dev is not None else None
+    w3 = up(x.w3_dev) if x.w3_dev is not None else None
+    lay = tla.TTTLinearAttention(w.B, w.H, 1, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi, w1=w1, w3=w3)
+    state_bytes = 2 * w.B * w.H * w.d_v * w.d_phi * 4
+    n_sets = max(1, min(64, -(-2 * MALL_BYTES // state_bytes)))
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    states = [(torch.randn((w.B, w.H, w.d_v, w.d_phi), generator=g, device=dev) * 0.05,
+               torch.randn((w.B, w.H, w.d_v, w.d_phi), generator=g, device=dev) * 0.05) for _ in range(n_sets)]
+    outs = [torch.empty((w.B, w.H, 1, w.d_v), dtype=v.dtype, device=dev) for _ in range(n_tok)]
+    stream = torch.cuda.current_stream()
+    mode = tla.mode_bits(w.eta_mode, True)
+
+    def step(i):
+        qt, kt, vt, et = toks[i % n_tok]
+        S, M = states[i % n_sets]
+        st = tla.ttt_la_step(lay.handle, qt.data_ptr(), kt.data_ptr(), vt.data_ptr(),
+                             None if et is None else et.data_ptr(), w.eta_scalar, w.beta, mode,
+                             S.data_ptr(), M.data_ptr(), outs[i % n_tok].data_ptr(), stream.cuda_stream)
+        if st != 0:
+            raise tla.TTTError(st, "ttt_la_step")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if tla.ttt_la_enable_kernel_timing(lay.handle, args.steps) != 0:
+        raise RuntimeError("could not create timing events")
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    kms = float(np.mean(tla.ttt_la_kernel_times(lay.handle, args.steps)))
+    tla.ttt_la_enable_kernel_timing(lay.handle, 0)
+    nbytes = step_bytes(w)
+    achieved = nbytes / (kms * 1e-3) / 1e9
+    return {
+        "metric": "TTT-layer decode tokens/sec (1 GPU, one recurrent step per token) + % HBM roofline",
+        "value": round(w.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32 state, " + w.dtype + " tokens", "data": "synthetic",
+        "config": {"workload": w.name + " (decode)", "B": w.B, "H": w.H, "d_k": w.d_k, "d_v": w.d_v,
+                   "d_phi": w.d_phi, "phi": w.phi, "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar,
+                   "beta": w.beta, "state_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "step_kernel",
+                     "kernel_ms": round(kms, 5), "bytes_per_step": nbytes},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -168,6 +256,9 @@ def main():
 
     tla.load_library()
     w = WORKLOADS[args.workload]
+    if args.decode:
+        print(json.dumps(run_decode(args, w)))
+        return
     x = make_inputs(w)
     dev = torch.device("cuda:0")
 

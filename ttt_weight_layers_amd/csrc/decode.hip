@@ -10,9 +10,9 @@
 //
 // The step reads and writes the whole fp32 state once and does under half a
 // flop per byte of it: it is bound by HBM bandwidth.  One workgroup of four waves owns 16
-// value rows of one sequence's S and M; each wave walks four rows, its 64 lanes
-// covering consecutive features (8 bytes a lane, 512 bytes a wave access), and
-// reduces the readout of each row across the wave.  The features
+// value rows of one sequence's S and M; each wave takes four rows at once, its 64
+// lanes covering consecutive features (8 bytes a lane, 512 bytes a wave access),
+// and reduces the readout of each row across the wave.  The features
 // phi(q), phi(k) of the token are formed once per workgroup in LDS (the SwiGLU
 // map as two fp32 dot products per feature against the frozen W1, W3 rows).
 
@@ -43,6 +43,21 @@ struct StepParams {
     int H, d_k, d_v, d_phi;
     int n_rblk;                 // row blocks per sequence (d_v / SR)
 };
+
+// 16 bytes of a row (8 bf16 or 4 fp32) as fp32
+__device__ __forceinline__ void load16_as_f32(const uint16_t* p, float* out) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(u[i] << 16);
+        out[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load16_as_f32(const float* p, float* out) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = u[i];
+}
 
 template <typename TI, bool SWIGLU>
 __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
@@ -75,16 +90,24 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
             sXk[d] = load_as_f32(k, d);
         }
         __syncthreads();
-        // phi(x)_f = silu(W1_f . x) (W3_f . x)
+        // phi(x)_f = silu(W1_f . x) (W3_f . x): one thread per feature, its rows of
+        // W1 and W3 read 16 bytes at a time
         for (int f = tid; f < d_phi; f += STHREADS) {
             float uq = 0.f, gq = 0.f, uk = 0.f, gk = 0.f;
-            for (int d = 0; d < d_k; ++d) {
-                const float a = load_as_f32(w1, (size_t)f * d_k + d);
-                const float b = load_as_f32(w3, (size_t)f * d_k + d);
-                uq = fmaf(a, sXq[d], uq);
-                gq = fmaf(b, sXq[d], gq);
-                uk = fmaf(a, sXk[d], uk);
-                gk = fmaf(b, sXk[d], gk);
+            const TI* a = w1 + (size_t)f * d_k;
+            const TI* b = w3 + (size_t)f * d_k;
+            constexpr int VE = 16 / sizeof(TI);     // elements per 16-byte load
+            for (int d0 = 0; d0 < d_k; d0 += VE) {
+                float av[VE], bv[VE];
+                load16_as_f32(a + d0, av);
+                load16_as_f32(b + d0, bv);
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    uq = fmaf(av[e], sXq[d0 + e], uq);
+                    gq = fmaf(bv[e], sXq[d0 + e], gq);
+                    uk = fmaf(av[e], sXk[d0 + e], uk);
+                    gk = fmaf(bv[e], sXk[d0 + e], gk);
+                }
             }
             sPq[f] = silu_f32(uq) * gq;
             sPk[f] = silu_f32(uk) * gk;
@@ -95,29 +118,44 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
     const float et = eta_at(p.eta_kind, p.eta, p.eta_scalar, (size_t)seq);
     const float beta = p.beta;
     const int lane = tid & 63, wave = tid >> 6;
-    for (int rr = 0; rr < SR / 4; ++rr) {
-        const int row = r0 + 4 * wave + rr;
-        const float ev = et * load_as_f32(v, row);
-        float* Sr = p.S + ((size_t)seq * p.d_v + row) * d_phi;
-        float* Mr = p.M + ((size_t)seq * p.d_v + row) * d_phi;
-        float acc = 0.0f;
-        // two consecutive features a lane, 512 bytes a wave access (d_phi is a
-        // multiple of 64: every pair is whole)
-        for (int c = 2 * lane; c < d_phi; c += 128) {
-            f32x2 m = *reinterpret_cast<const f32x2*>(Mr + c);
-            f32x2 s = *reinterpret_cast<const f32x2*>(Sr + c);
+    constexpr int RW = SR / 4;      // rows of this wave
+    const int row0 = r0 + RW * wave;
+    float* __restrict__ S = p.S + ((size_t)seq * p.d_v + row0) * d_phi;
+    float* __restrict__ M = p.M + ((size_t)seq * p.d_v + row0) * d_phi;
+    float ev[RW], acc[RW];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                m[e] = fmaf(beta, m[e], ev * sPk[c + e]);
-                s[e] += m[e];
-                acc = fmaf(s[e], sPq[c + e], acc);
-            }
-            *reinterpret_cast<f32x2*>(Mr + c) = m;
-            *reinterpret_cast<f32x2*>(Sr + c) = s;
+    for (int rr = 0; rr < RW; ++rr) {
+        ev[rr] = et * load_as_f32(v, row0 + rr);
+        acc[rr] = 0.0f;
+    }
+    // two consecutive features a lane, 512 bytes a wave access (d_phi is a
+    // multiple of 64: every pair is whole); the four rows' loads are issued
+    // together
+    for (int c = 2 * lane; c < d_phi; c += 128) {
+        f32x2 m[RW], sv[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            m[rr] = *reinterpret_cast<const f32x2*>(M + (size_t)rr * d_phi + c);
+            sv[rr] = *reinterpret_cast<const f32x2*>(S + (size_t)rr * d_phi + c);
         }
+        const float pk0 = sPk[c], pk1 = sPk[c + 1], pq0 = sPq[c], pq1 = sPq[c + 1];
 #pragma unroll
-        for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (lane == 0) store_from_f32(o, row, acc);
+        for (int rr = 0; rr < RW; ++rr) {
+            m[rr][0] = fmaf(beta, m[rr][0], ev[rr] * pk0);
+            m[rr][1] = fmaf(beta, m[rr][1], ev[rr] * pk1);
+            sv[rr][0] += m[rr][0];
+            sv[rr][1] += m[rr][1];
+            acc[rr] = fmaf(sv[rr][0], pq0, fmaf(sv[rr][1], pq1, acc[rr]));
+            *reinterpret_cast<f32x2*>(M + (size_t)rr * d_phi + c) = m[rr];
+            *reinterpret_cast<f32x2*>(S + (size_t)rr * d_phi + c) = sv[rr];
+        }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        float a = acc[rr];
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
+        if (lane == 0) store_from_f32(o, row0 + rr, a);
     }
 }
 
