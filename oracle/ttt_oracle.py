@@ -252,6 +252,66 @@ def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: fl
     return o.reshape(B, H, d_v), S_new.reshape(B, H, d_v, d_phi), M_new.reshape(B, H, d_v, d_phi)
 
 
+def backward(q, k, v, dO, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
+             beta: float = 0.0, causal: bool = True):
+    """Gradients of sum(o * dO) for the identity feature map, fp64.
+
+    The plain reverse-mode derivative of ``forward`` (backpropagation through
+    the token loop).  With G_t = dL/dS_t and H_t = dL/dM_t:
+      causal:   G_t = dO_t q_t^T + G_{t+1},         G_T = 0
+      bidir.:   G_t = sum_s dO_s q_s^T  for every t (only S_{T-1} is read)
+                H_t = G_t + beta H_{t+1},           H_T = 0
+      dq_t = S_t^T dO_t   (bidirectional: S_{T-1}^T dO_t)
+      dv_t = eta_t H_t k_t,  dk_t = eta_t H_t^T v_t,  deta_t = v_t^T H_t k_t
+    The rate gradient is returned per token for the per_token mode, as d a_t =
+    deta_t * sigmoid(a_t) for softplus, and summed over every token for the
+    scalar mode.  Returns (dq, dk, dv, deta).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, d_k = q.shape
+    d_v = np.shape(v)[-1]
+    N = B * H
+    qf, kf, vf = _flatten(q, d_k), _flatten(k, d_k), _flatten(v, d_v)
+    gf = _flatten(dO, d_v)
+    lr = learning_rates(eta_mode, T, N, eta, eta_scalar)
+    # forward states S_t (the readout needs them)
+    S = np.zeros((N, d_v, d_k))
+    M = np.zeros((N, d_v, d_k))
+    S_all = np.zeros((T, N, d_v, d_k))
+    for t in range(T):
+        M = beta * M + lr[:, t, None, None] * vf[:, t, :, None] * kf[:, t, None, :]
+        S = S + M
+        S_all[t] = S
+    dq = np.zeros_like(qf)
+    dk = np.zeros_like(kf)
+    dv = np.zeros_like(vf)
+    de = np.zeros((N, T))
+    G = np.zeros((N, d_v, d_k))
+    if not causal:
+        G = np.einsum("ntv,ntf->nvf", gf, qf)
+    Hm = np.zeros((N, d_v, d_k))
+    for t in range(T - 1, -1, -1):
+        if causal:
+            G = G + gf[:, t, :, None] * qf[:, t, None, :]
+            dq[:, t] = np.einsum("nvf,nv->nf", S_all[t], gf[:, t])
+        else:
+            dq[:, t] = np.einsum("nvf,nv->nf", S_all[T - 1], gf[:, t])
+        Hm = G + beta * Hm
+        Hk = np.einsum("nvf,nf->nv", Hm, kf[:, t])
+        dv[:, t] = lr[:, t, None] * Hk
+        dk[:, t] = lr[:, t, None] * np.einsum("nvf,nv->nf", Hm, vf[:, t])
+        de[:, t] = np.einsum("nv,nv->n", vf[:, t], Hk)
+    shape = lambda x, d: x.reshape(B, H, T, d)
+    if eta_mode == "per_token":
+        deta = de.reshape(B, H, T)
+    elif eta_mode == "softplus":
+        a = np.asarray(eta, np.float64).reshape(N, T)
+        deta = (de / (1.0 + np.exp(-a))).reshape(B, H, T)
+    else:
+        deta = float(de.sum())
+    return shape(dq, d_k), shape(dk, d_k), shape(dv, d_v), deta
+
+
 # ----------------------------------------------------------------------------
 # parallel forms (used by tests to check the equivalence the pages state)
 # ----------------------------------------------------------------------------

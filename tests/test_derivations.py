@@ -102,3 +102,57 @@ def test_t_form_is_not_the_plain_state():
     ref = _ref(q, k, v, eta, beta, causal=False)
     _, Tst, _ = _chunk_step(np.zeros((3, 4)), np.zeros((3, 4)), q, k, v, eta, beta)
     assert np.max(np.abs(q @ Tst.T - ref)) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# backward as forward passes on permuted, time-reversed operands (the library
+# computes the gradients this way); checked in fp64 against the oracle backward
+# ----------------------------------------------------------------------------
+
+def _rev(x):
+    return x[:, :, ::-1]
+
+
+@pytest.mark.parametrize("eta_mode", ["scalar", "per_token", "softplus"])
+@pytest.mark.parametrize("beta", [0.0, 0.8])
+def test_backward_as_reversed_forwards_causal(eta_mode, beta):
+    rng = np.random.default_rng(31)
+    B, H, T, d = 1, 2, 11, 4
+    q, k, v, dO = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    a = rng.standard_normal((B, H, T))
+    eta = None if eta_mode == "scalar" else a
+    kw = dict(eta_mode=eta_mode, eta=eta, eta_scalar=0.6, beta=beta)
+    dq, dk, dv, de = oracle.backward(q, k, v, dO, **kw)
+    e = oracle.learning_rates(eta_mode, T, B * H, eta, 0.6).reshape(B, H, T)
+    # dq: the causal forward with (q, k, v) -> (dO, v, k)
+    np.testing.assert_allclose(oracle.forward(dO, v, k, **kw), dq, rtol=1e-10, atol=1e-10)
+    # dv, dk, deta: unit-rate forwards over the reversed sequence
+    u = _rev(oracle.forward(_rev(k), _rev(q), _rev(dO), eta_scalar=1.0, beta=beta))
+    w = _rev(oracle.forward(_rev(v), _rev(dO), _rev(q), eta_scalar=1.0, beta=beta))
+    np.testing.assert_allclose(e[..., None] * u, dv, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(e[..., None] * w, dk, rtol=1e-10, atol=1e-10)
+    d_eta = np.einsum("bhtd,bhtd->bht", v, u)
+    if eta_mode == "per_token":
+        np.testing.assert_allclose(d_eta, de, rtol=1e-10, atol=1e-10)
+    elif eta_mode == "softplus":
+        np.testing.assert_allclose(d_eta / (1 + np.exp(-a)), de, rtol=1e-10, atol=1e-10)
+    else:
+        assert abs(d_eta.sum() - de) <= 1e-9 * max(1.0, abs(de))
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.8])
+def test_backward_as_forwards_bidirectional(beta):
+    rng = np.random.default_rng(32)
+    B, H, T, d = 1, 2, 9, 4
+    q, k, v, dO = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    a = rng.standard_normal((B, H, T))
+    kw = dict(eta_mode="softplus", eta=a, beta=beta, causal=False)
+    dq, dk, dv, de = oracle.backward(q, k, v, dO, **kw)
+    e = np.log1p(np.exp(a))
+    c = np.array([sum(beta ** r for r in range(T - s)) for s in range(T)])     # c_{T-1-s}
+    np.testing.assert_allclose(oracle.forward(dO, v, k, **kw), dq, rtol=1e-10, atol=1e-10)
+    u = oracle.forward(k, q, dO, eta_scalar=1.0, causal=False)
+    w = oracle.forward(v, dO, q, eta_scalar=1.0, causal=False)
+    np.testing.assert_allclose((e * c)[..., None] * u, dv, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose((e * c)[..., None] * w, dk, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(c * np.einsum("bhtd,bhtd->bht", v, u) / (1 + np.exp(-a)), de, rtol=1e-10, atol=1e-10)
