@@ -167,6 +167,32 @@ int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v
 int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
                 float beta, uint32_t mode, float* S, float* M, void* o, void* hip_stream);
 
+/* Gradients of the forward.  Figure 4 of the thelatestinai.com page trains the
+ * parallel form end to end; with L = sum(o * dO) for the o that ttt_la_forward
+ * returns on the same q, k, v, eta, eta_scalar, beta and mode:
+ *   dO       device [B, H, T, d_v] in dtype (the gradient of L with respect to o).
+ *   dQ, dK   device [B, H, T, d_k] in dtype;  dV: [B, H, T, d_v] in dtype.
+ *   dEta     NULL, or device [B, H, T] fp32: dL/deta_t for TTT_LA_ETA_PER_TOKEN,
+ *            dL/da_t (the softplus argument) for TTT_LA_ETA_SOFTPLUS, and for a
+ *            scalar rate the per-token terms whose sum is dL/deta_scalar.
+ *   workspace, workspace_bytes  caller-owned device memory, 16-byte aligned, at
+ *            least ttt_la_backward_workspace() bytes (may be NULL when that is 0).
+ * Identity feature map with d_k == d_v only (TTT_LA_ERR_UNSUPPORTED otherwise).
+ * Runs three forwards of the layer on permuted operands (two over the sequence
+ * reversed in time, with the handle's own kernels and workspace) and two small
+ * kernels; enqueued on hip_stream, no allocation, no synchronisation.
+ * The outputs must not overlap each other, any input or the workspace.
+ * Errors: as ttt_la_forward, and TTT_LA_ERR_INVALID_ARG for a missing, misaligned,
+ * overlapping or too small buffer. */
+int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                    float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV, float* dEta,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Bytes of workspace ttt_la_backward needs on handle h for the given mode bits
+ * (the time-reversed operands of the causal mode; less for the bidirectional
+ * mode).  Host only; TTT_LA_ERR_UNSUPPORTED if the handle's shape has no backward. */
+int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes);
+
 /* Releases the workspace and the handle.  NULL-safe. */
 void ttt_la_destroy(ttt_la_t h);
 
@@ -188,6 +214,12 @@ int ttt_la_check(const ttt_la_desc* desc, const void* q, const void* k, const vo
 int ttt_la_check_state(const ttt_la_desc* desc, int32_t call, const void* q, const void* k, const void* v,
                        const float* eta, float eta_scalar, float beta, uint32_t mode, const float* s_in,
                        const float* m_in, const void* o, const float* s_out, const float* m_out);
+
+/* The same for ttt_la_backward (the descriptor stands for the handle). */
+int ttt_la_check_backward(const ttt_la_desc* desc, const void* q, const void* k, const void* v, const float* eta,
+                          float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ,
+                          const void* dK, const void* dV, const float* dEta, const void* workspace,
+                          size_t workspace_bytes);
 
 /* Kernel plan chosen at create, for tests and measurement. */
 typedef struct {

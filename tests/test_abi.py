@@ -243,3 +243,43 @@ def test_state_calls_with_null_handle():
     assert lib.ttt_la_forward_state(None, Q, K, V, None, 1.0, 0.0, 0, S0, M0, O, ST, MT, None) == \
         tla.TTT_LA_ERR_INVALID_ARG
     assert lib.ttt_la_step(None, Q, K, V, None, 1.0, 0.0, 0, S0, M0, O, None) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+# ----------------------------------------------------------------------------
+# ttt_la_backward
+# ----------------------------------------------------------------------------
+
+DO, DQ, DK, DV, DE, WS = (0x10000000 * (i + 12) for i in range(6))
+TB = 2 * 3 * 100 * 128 * 2                         # one bf16 [B, H, T, d] tensor
+
+
+def check_bw(d=None, q=Q, k=K, v=V, eta=None, beta=0.9, mode=0, dO=DO, dq=DQ, dk=DK, dv=DV, de=DE, ws=WS,
+             wsb=6 * TB):
+    return tla.ttt_la_check_backward(d or desc(), q, k, v, eta, 0.5, beta, mode, dO, dq, dk, dv, de, ws, wsb)
+
+
+def test_backward_arguments():
+    bad = tla.TTT_LA_ERR_INVALID_ARG
+    assert check_bw() == tla.TTT_LA_OK
+    assert check_bw(de=None) == tla.TTT_LA_OK
+    assert check_bw(mode=tla.TTT_LA_BIDIRECTIONAL, wsb=2 * TB) == tla.TTT_LA_OK   # less workspace
+    assert check_bw(wsb=6 * TB - 16) == bad                                      # too small
+    assert check_bw(ws=None) == bad
+    assert check_bw(ws=WS + 8) == bad
+    assert check_bw(dO=None) == bad
+    assert check_bw(dk=DQ) == bad                                                # outputs overlap
+    assert check_bw(dv=Q) == bad                                                 # output over an input
+    assert check_bw(dq=DO) == bad
+    assert check_bw(ws=DO) == bad                                                # workspace over dO
+    assert check_bw(de=DE + 2) == bad
+    assert check_bw(eta=ETA, mode=tla.TTT_LA_ETA_SOFTPLUS, de=ETA) == bad
+    assert check_bw(d=desc(d_v=64)) == tla.TTT_LA_ERR_UNSUPPORTED                # d_k != d_v
+    assert check_bw(d=desc(phi="swiglu", d_phi=256, w1=W1, w3=W3)) == tla.TTT_LA_ERR_UNSUPPORTED
+
+
+def test_backward_null_handle():
+    lib = tla.load_library()
+    n = ctypes.c_size_t(0)
+    assert lib.ttt_la_backward_workspace(None, 0, ctypes.byref(n)) == tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_backward(None, Q, K, V, None, 1.0, 0.0, 0, DO, DQ, DK, DV, None, WS, 0, None) == \
+        tla.TTT_LA_ERR_INVALID_ARG

@@ -1,0 +1,100 @@
+"""GPU parity of ttt_la_backward against the oracle's adjoint recurrence on the
+same seeded inputs and output gradient (identity feature map, d_k = d_v)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ttt_workloads import WORKLOADS, make_inputs
+from _gpu import TOL, from_device, make_layer, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def small(name, **kw):
+    return WORKLOADS[name].with_shape(**kw)
+
+
+def grad_output(w, seed):
+    """A seeded output gradient, rounded to the workload dtype like the inputs."""
+    import torch
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((w.B, w.H, w.T, w.d_v))
+    t = torch.from_numpy(g).to(torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    g64 = t.to(torch.float64).numpy()
+    return t.to("cuda").contiguous(), g64
+
+
+def run_case(w, segments=0, seed=40):
+    import torch
+    x = make_inputs(w)
+    d = to_device(x)
+    dO, dO64 = grad_output(w, seed)
+    lay = make_layer(w, d, segments=segments)
+    dq, dk, dv, de = lay.backward(d["q"], d["k"], d["v"], dO, eta=d["a"], eta_scalar=w.eta_scalar, beta=w.beta,
+                                  eta_mode=w.eta_mode, causal=w.causal)
+    torch.cuda.synchronize()
+    ref = oracle.backward(x.q64, x.k64, x.v64, dO64, eta_mode=w.eta_mode, eta=x.a32, eta_scalar=w.eta_scalar,
+                          beta=w.beta, causal=w.causal)
+    got = (from_device(dq, w.dtype), from_device(dk, w.dtype), from_device(dv, w.dtype))
+    for name, g, r in zip(("dq", "dk", "dv"), got, ref[:3]):
+        err = oracle.rel_err(g, r)
+        say(f"  {name} rel err {err:.2e}")
+        assert err <= TOL[w.dtype], name
+    de_np = de.cpu().numpy().astype(np.float64)
+    if w.eta_mode == "scalar":
+        assert abs(de_np.sum() - ref[3]) <= TOL[w.dtype] * max(1.0, np.abs(de_np).sum())
+    else:
+        err = oracle.rel_err(de_np, ref[3])
+        say(f"  deta rel err {err:.2e}")
+        assert err <= TOL[w.dtype]
+    return lay
+
+
+@pytest.mark.parametrize("eta_mode,beta,segments", [("scalar", 0.9, 4), ("softplus", 0.9, 2),
+                                                    ("per_token", 0.0, 1)])
+def test_backward_wide_tiles(eta_mode, beta, segments):
+    w = small("v4_momentum_4x8x2048_d128", B=1, H=2, T=64 * 4 + 7).with_settings(eta_mode=eta_mode, beta=beta)
+    say(f"[backward wide] {eta_mode} beta={beta} segments={segments}")
+    lay = run_case(w, segments)
+    assert lay.plan().path == 2
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_backward_bidirectional(beta):
+    w = small("v3_softplus_8x16x4096_d128", B=1, H=2, T=64 * 3 + 5).with_settings(causal=False, beta=beta)
+    say(f"[backward bidir d=128] beta={beta}")
+    run_case(w)
+
+
+@pytest.mark.parametrize("case", ["f32_causal", "f32_bidir", "bf16_d64_causal", "bf16_d64_bidir"])
+def test_backward_other_shapes(case):
+    if case.startswith("f32"):
+        w = small("v5_f32_1x1x256_d64", B=1, H=2, T=70).with_settings(eta_mode="softplus", beta=0.5,
+                                                                       causal=case == "f32_causal")
+    else:
+        w = small("bidir_vit_256x6x196_d64", B=2, H=2, T=90).with_settings(causal=case == "bf16_d64_causal",
+                                                                          beta=0.9, eta_mode="per_token")
+    say(f"[backward {case}]")
+    run_case(w)
+
+
+def test_backward_unsupported_for_swiglu():
+    import torch
+    import ttt_weight_layers_amd as tla
+    w = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=64).with_settings(d_phi=128)
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d)
+    st, _ = tla.ttt_la_backward_workspace(lay.handle, 0)
+    assert st == tla.TTT_LA_ERR_UNSUPPORTED
+    dO = torch.zeros_like(d["v"])
+    with pytest.raises(tla.TTTError) as e:
+        lay.backward(d["q"], d["k"], d["v"], dO, eta=d["a"], eta_mode="softplus", beta=0.9)
+    assert e.value.status == tla.TTT_LA_ERR_UNSUPPORTED

@@ -59,8 +59,9 @@ class ttt_la_plan(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_forward_state", "ttt_la_step", "ttt_la_destroy",
-           "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_get_plan",
+EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_forward_state", "ttt_la_step", "ttt_la_backward",
+           "ttt_la_backward_workspace", "ttt_la_destroy",
+           "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_check_backward", "ttt_la_get_plan",
            "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times")
 
 _lib: Optional[ctypes.CDLL] = None
@@ -88,6 +89,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_check_state.argtypes = [ctypes.POINTER(ttt_la_desc), i32, vp, vp, vp, vp, f32, f32, u32, vp, vp,
                                        vp, vp, vp]
     lib.ttt_la_check_state.restype = ctypes.c_int
+    lib.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.ttt_la_backward.restype = ctypes.c_int
+    lib.ttt_la_check_backward.argtypes = [ctypes.POINTER(ttt_la_desc), vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp,
+                                          vp, vp, ctypes.c_size_t]
+    lib.ttt_la_check_backward.restype = ctypes.c_int
+    lib.ttt_la_backward_workspace.argtypes = [vp, u32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ttt_la_backward_workspace.restype = ctypes.c_int
     lib.ttt_la_destroy.argtypes = [vp]
     lib.ttt_la_destroy.restype = None
     lib.ttt_la_status_string.argtypes = [ctypes.c_int]
@@ -146,6 +154,26 @@ def ttt_la_check_state(desc: ttt_la_desc, call: int, q=None, k=None, v=None, eta
                        beta=0.0, mode=0, s_in=None, m_in=None, o=None, s_out=None, m_out=None) -> int:
     return load_library().ttt_la_check_state(ctypes.byref(desc), int(call), q, k, v, eta, float(eta_scalar),
                                              float(beta), int(mode), s_in, m_in, o, s_out, m_out)
+
+
+def ttt_la_backward(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float, mode: int,
+                    dO: int, dQ: int, dK: int, dV: int, dEta: Optional[int], workspace: Optional[int],
+                    workspace_bytes: int, stream: Optional[int]) -> int:
+    return load_library().ttt_la_backward(h, q, k, v, eta, float(eta_scalar), float(beta), int(mode), dO, dQ, dK,
+                                          dV, dEta, workspace, int(workspace_bytes), stream)
+
+
+def ttt_la_check_backward(desc: ttt_la_desc, q=None, k=None, v=None, eta=None, eta_scalar=1.0, beta=0.0, mode=0,
+                          dO=None, dQ=None, dK=None, dV=None, dEta=None, workspace=None, workspace_bytes=0) -> int:
+    return load_library().ttt_la_check_backward(ctypes.byref(desc), q, k, v, eta, float(eta_scalar), float(beta),
+                                                int(mode), dO, dQ, dK, dV, dEta, workspace, int(workspace_bytes))
+
+
+def ttt_la_backward_workspace(h, mode: int):
+    """Returns (status, bytes)."""
+    n = ctypes.c_size_t(0)
+    st = load_library().ttt_la_backward_workspace(h, int(mode), ctypes.byref(n))
+    return st, n.value
 
 
 def ttt_la_destroy(h) -> None:
@@ -319,3 +347,21 @@ class TTTLinearAttention:
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_step")
         return out
+
+    def backward(self, q, k, v, dO, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
+                 stream=None, want_eta=True):
+        """Gradients (dq, dk, dv, deta) of sum(o * dO); the workspace is a device tensor
+        allocated here (the library itself allocates nothing)."""
+        torch = self._check(("q", q), ("k", k), ("v", v), ("dO", dO))
+        mode = mode_bits(eta_mode, causal)
+        st, nbytes = ttt_la_backward_workspace(self.handle, mode)
+        if st != TTT_LA_OK:
+            raise TTTError(st, "ttt_la_backward_workspace")
+        ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device=q.device)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        de = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if want_eta else None
+        st = ttt_la_backward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode, _ptr(dO),
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(de), _ptr(ws), nbytes, self._stream(q, stream))
+        if st != TTT_LA_OK:
+            raise TTTError(st, "ttt_la_backward")
+        return dq, dk, dv, de

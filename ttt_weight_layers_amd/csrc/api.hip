@@ -304,7 +304,7 @@ void next_events(ttt_la_s* h, hipEvent_t* eb, hipEvent_t* ee) {
 
 int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
                     float beta, uint32_t mode, const float* S0, const float* M0, void* o, float* S_T, float* M_T,
-                    void* hip_stream) {
+                    void* hip_stream, bool timed = true) {
     ttt::FwdArgs a{};
     a.q = q;
     a.k = k;
@@ -322,8 +322,8 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     a.M_T = M_T;
     const bool state_io = S0 || M0 || S_T || M_T;
 
-    hipEvent_t eb, ee;
-    next_events(h, &eb, &ee);
+    hipEvent_t eb = nullptr, ee = nullptr;
+    if (timed) next_events(h, &eb, &ee);
     hipError_t e;
     if (h->fast && (h->fp.wide || !state_io)) {
         int nk = 0;
@@ -347,9 +347,128 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
 
+bool backward_supported(const ttt_la_desc& d) { return d.phi == TTT_LA_PHI_IDENTITY && d.d_k == d.d_v; }
+
+// one [B, H, T, d] tensor in the handle's dtype
+size_t tensor_bytes(const ttt_la_desc& d) { return (size_t)d.B * d.H * d.T * d.d_v * elem_bytes(d.dtype); }
+
+// causal: q, k, v, dO reversed in time, then the two rate-1 forward outputs;
+// bidirectional: the two forward outputs only
+size_t backward_ws_bytes(const ttt_la_desc& d, uint32_t mode) {
+    return ((mode & TTT_LA_BIDIRECTIONAL) ? 2 : 6) * tensor_bytes(d);
+}
+
+int check_backward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                   float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ, const void* dK,
+                   const void* dV, const float* dEta, const void* ws, size_t ws_bytes) {
+    int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, dQ);
+    if (st != TTT_LA_OK) return st;
+    if (!backward_supported(*d)) return TTT_LA_ERR_UNSUPPORTED;
+    if (!dO || !dK || !dV) return TTT_LA_ERR_INVALID_ARG;
+    if (!aligned(dO, 16) || !aligned(dK, 16) || !aligned(dV, 16)) return TTT_LA_ERR_INVALID_ARG;
+    if (dEta && !aligned(dEta, 4)) return TTT_LA_ERR_INVALID_ARG;
+    const size_t need = backward_ws_bytes(*d, mode);
+    if (need && (!ws || !aligned(ws, 16) || ws_bytes < need)) return TTT_LA_ERR_INVALID_ARG;
+    const size_t tb = tensor_bytes(*d);
+    const size_t nt = (size_t)d->B * d->H * d->T;
+    const size_t eta_bytes = eta ? nt * sizeof(float) : 0;
+    const void* outs[4] = {dQ, dK, dV, dEta};
+    const size_t out_bytes[4] = {tb, tb, tb, nt * sizeof(float)};
+    const void* ins[5] = {q, k, v, dO, eta};
+    const size_t in_bytes[5] = {tb, tb, tb, tb, eta_bytes};
+    for (int i = 0; i < 4; ++i) {
+        for (int j = 0; j < 5; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 4; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
+        if (overlaps(outs[i], out_bytes[i], ws, need)) return TTT_LA_ERR_INVALID_ARG;
+    }
+    for (int j = 0; j < 5; ++j)
+        if (overlaps(ws, need, ins[j], in_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
+    return TTT_LA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int ttt_la_check_backward(const ttt_la_desc* desc, const void* q, const void* k, const void* v, const float* eta,
+                          float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ,
+                          const void* dK, const void* dV, const float* dEta, const void* workspace,
+                          size_t workspace_bytes) {
+    int st = check_desc(desc);
+    if (st != TTT_LA_OK) return st;
+    return check_backward(desc, q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, workspace,
+                          workspace_bytes);
+}
+
+int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes) {
+    if (!h || !bytes) return TTT_LA_ERR_INVALID_ARG;
+    *bytes = 0;
+    if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
+    if (!backward_supported(h->desc)) return TTT_LA_ERR_UNSUPPORTED;
+    *bytes = backward_ws_bytes(h->desc, mode);
+    return TTT_LA_OK;
+}
+
+int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
+                    float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV, float* dEta,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+    if (!h) return TTT_LA_ERR_INVALID_ARG;
+    int st = check_backward(&h->desc, q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, workspace,
+                            workspace_bytes);
+    if (st != TTT_LA_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const bool bidir = (mode & TTT_LA_BIDIRECTIONAL) != 0;
+    const size_t tb = tensor_bytes(h->desc);
+    char* ws = static_cast<char*>(workspace);
+    // dq: the forward with (q, k, v) -> (dO, v, k) and the caller's rates
+    st = enqueue_forward(h, dO, v, k, eta, eta_scalar, beta, mode, nullptr, nullptr, dQ, nullptr, nullptr,
+                         hip_stream, false);
+    if (st != TTT_LA_OK) return st;
+    void *U, *W;
+    if (!bidir) {
+        // rate-1 forwards over the reversed sequence: u from (k, q, dO), w from (v, dO, q)
+        char *Rq = ws, *Rk = ws + tb, *Rv = ws + 2 * tb, *RdO = ws + 3 * tb;
+        U = ws + 4 * tb;
+        W = ws + 5 * tb;
+        const void* src[4] = {q, k, v, dO};
+        void* dst[4] = {Rq, Rk, Rv, RdO};
+        if (ttt::launch_reverse(src, dst, 4, (size_t)h->desc.B * h->desc.H, h->desc.T,
+                                h->desc.d_v * elem_bytes(h->desc.dtype), stream) != hipSuccess)
+            return TTT_LA_ERR_HIP;
+        st = enqueue_forward(h, Rk, Rq, RdO, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, U, nullptr,
+                             nullptr, hip_stream, false);
+        if (st != TTT_LA_OK) return st;
+        st = enqueue_forward(h, Rv, RdO, Rq, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, W, nullptr,
+                             nullptr, hip_stream, false);
+        if (st != TTT_LA_OK) return st;
+    } else {
+        // every query reads the final state: rate-1, momentum-free bidirectional forwards
+        U = ws;
+        W = ws + tb;
+        st = enqueue_forward(h, k, q, dO, nullptr, 1.0f, 0.0f, TTT_LA_BIDIRECTIONAL, nullptr, nullptr, U, nullptr,
+                             nullptr, hip_stream, false);
+        if (st != TTT_LA_OK) return st;
+        st = enqueue_forward(h, v, dO, q, nullptr, 1.0f, 0.0f, TTT_LA_BIDIRECTIONAL, nullptr, nullptr, W, nullptr,
+                             nullptr, hip_stream, false);
+        if (st != TTT_LA_OK) return st;
+    }
+    ttt::BackArgs b{};
+    b.u = U;
+    b.w = W;
+    b.v = v;
+    b.eta = eta;
+    b.dk = dK;
+    b.dv = dV;
+    b.deta = dEta;
+    b.eta_scalar = eta_scalar;
+    b.beta = beta;
+    b.eta_kind = eta_kind_of(mode);
+    b.causal = !bidir;
+    b.stream = stream;
+    return ttt::launch_finalize_grads(h->shape, b) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+}
 
 int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
                    float beta, uint32_t mode, void* o, void* hip_stream) {

@@ -103,6 +103,27 @@ size_t step_smem_bytes(const Shape& s);
 // ev_begin/ev_end (may be null) take the step kernel's start and end timestamps
 hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// ---- backward helpers (backward.hip) ----------------------------------------------
+// dst[i][seq, t, :] = src[i][seq, T-1-t, :] for count <= 4 tensors of rows of row_bytes
+// (a multiple of 16)
+hipError_t launch_reverse(const void* const* src, void* const* dst, int count, size_t n_seq, int T, size_t row_bytes,
+                          hipStream_t st);
+struct BackArgs {
+    const void* u;       // rate-1 forward outputs [n_seq, T, d] (time-reversed when causal)
+    const void* w;
+    const void* v;
+    const float* eta;
+    void* dk;
+    void* dv;
+    float* deta;         // [n_seq, T] or null
+    float eta_scalar;
+    float beta;
+    int eta_kind;
+    bool causal;
+    hipStream_t stream;
+};
+hipError_t launch_finalize_grads(const Shape& s, const BackArgs& a);
+
 // Enqueues the whole forward (all kernels).  If ev_begin/ev_end are non-null
 // they take the start and end timestamps of the output kernel.
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a,
