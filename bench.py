@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--decode", action="store_true",
                     help="time the one-token recurrent step (ttt_la_step) at the workload's B, H and widths "
                          "instead of the forward; prints its own JSON line")
+    ap.add_argument("--backward", action="store_true",
+                    help="time ttt_la_backward (gradients of the forward) on the workload instead of the forward; "
+                         "prints its own JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a device copy of MIB mebibytes (counter calibration) and exit")
     return ap.parse_args()
@@ -229,6 +232,82 @@ def run_decode(args, w):
     }
 
 
+def run_backward(args, w):
+    """K backward passes over the workload (inputs and the output gradient resident
+    in HBM, rotated over sets like the forward).  Bytes of the roofline: q, k, v, dO
+    read once and dq, dk, dv written once (+ the rate and its gradient)."""
+    import numpy as np
+    import torch
+
+    import ttt_weight_layers_amd as tla
+    from ttt_workloads import make_inputs
+
+    x = make_inputs(w)
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if w.dtype == "bf16" else t).to(dev)
+
+    q0, k0, v0 = up(x.q_dev), up(x.k_dev), up(x.v_dev)
+    a0 = torch.from_numpy(x.a32).to(dev) if x.a32 is not None else None
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    dO0 = torch.randn(v0.shape, generator=g, device=dev).to(v0.dtype)
+    e = 4 if w.dtype == "f32" else 2
+    nbytes = w.head_tokens * ((2 * w.d_k + 2 * w.d_v) * e + (2 * w.d_k + w.d_v) * e)
+    if w.eta_mode != "scalar":
+        nbytes += w.head_tokens * 8
+    n_sets = max(1, min(8, -(-2 * MALL_BYTES // nbytes)))
+    sets = [dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), dO=dO0.clone(), a=None if a0 is None else a0.clone())
+            for _ in range(n_sets)]
+    lay = tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi, chunk=w.chunk,
+                                 segments=args.segments)
+    mode = tla.mode_bits(w.eta_mode, w.causal)
+    st, ws_bytes = tla.ttt_la_backward_workspace(lay.handle, mode)
+    if st != 0:
+        raise tla.TTTError(st, "ttt_la_backward_workspace")
+    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
+    outs = dict(dq=torch.empty_like(q0), dk=torch.empty_like(k0), dv=torch.empty_like(v0),
+                de=torch.empty(q0.shape[:-1], dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        s_ = sets[i % n_sets]
+        r = tla.ttt_la_backward(lay.handle, s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(),
+                                None if s_["a"] is None else s_["a"].data_ptr(), w.eta_scalar, w.beta, mode,
+                                s_["dO"].data_ptr(), outs["dq"].data_ptr(), outs["dk"].data_ptr(),
+                                outs["dv"].data_ptr(), outs["de"].data_ptr(), ws.data_ptr(), ws_bytes,
+                                stream.cuda_stream)
+        if r != 0:
+            raise tla.TTTError(r, "ttt_la_backward")
+
+    for i in range(args.warmup):
+        step(i)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {
+        "metric": "TTT-layer backward tokens/sec (1 GPU) + % HBM roofline of the whole backward",
+        "value": round(w.tokens / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name + " (backward)", "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v,
+                   "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar, "beta": w.beta,
+                   "causal": w.causal, "segments": lay.plan().segments, "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "whole backward (3 forwards + reversal + finalize)", "bytes_per_step": nbytes},
+        "cpu_baseline": None,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -258,6 +337,9 @@ def main():
     w = WORKLOADS[args.workload]
     if args.decode:
         print(json.dumps(run_decode(args, w)))
+        return
+    if args.backward:
+        print(json.dumps(run_backward(args, w)))
         return
     x = make_inputs(w)
     dev = torch.device("cuda:0")
