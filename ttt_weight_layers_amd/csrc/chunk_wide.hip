@@ -860,9 +860,13 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 // never reads S0, M0: they may be the buffers the final state goes to).  One
 // thread per float4 of one sequence's state; all summaries are loaded before
 // the first store so that the loads overlap.
+// mmode: 0 no momentum; 1 compose M; 2 beta^L is below 2^-30, so the carried
+// term beta^L M is below the fp32 resolution of dM and every entry M is the
+// previous segment's dM, already in its slot (only a carried M0 is written).
 template <int MAXS>
-__global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_slots, float bL, int mom,
+__global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_slots, float bL, int mmode,
                                                  const float* S0, const float* M0, float kappa, int has_init) {
+    const bool mom = mmode == 1;
     constexpr int HALF = WNW * WFT * 4 * 64;       // float4s of T (and of M) per slot
     const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (size_t)n_seq * HALF) return;
@@ -888,7 +892,7 @@ __global__ void __launch_bounds__(256) wide_scan(float* state, int n_seq, int n_
 #pragma unroll
         for (int r = 0; r < 4; ++r) T[r] = fmaf(kappa, M[r], sv[r]);
         base[0] = T;
-        if (mom) base[HALF] = M;
+        if (mmode != 0) base[HALF] = M;
     }
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
@@ -1059,13 +1063,14 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
                 const size_t n_threads = (size_t)s.n_seq() * HALF;
                 const float bL = (float)std::pow((double)a.beta, (double)p.seg_len);
                 const float kappa = a.beta / (1.0f - a.beta);
+                const int mmode = !mom ? 0 : (bL < 0x1p-30f ? 2 : 1);
                 const dim3 grid((unsigned)((n_threads + 255) / 256));
                 if (p.segments - 1 <= 7)
                     hipLaunchKernelGGL(wide_scan<7>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments, bL,
-                                       mom ? 1 : 0, a.S0, a.M0, kappa, wp.has_init);
+                                       mmode, a.S0, a.M0, kappa, wp.has_init);
                 else
                     hipLaunchKernelGGL(wide_scan<15>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments, bL,
-                                       mom ? 1 : 0, a.S0, a.M0, kappa, wp.has_init);
+                                       mmode, a.S0, a.M0, kappa, wp.has_init);
                 if ((e = hipGetLastError()) != hipSuccess) return e;
                 ++nk;
             }
