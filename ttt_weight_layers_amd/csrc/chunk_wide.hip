@@ -241,9 +241,10 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     // [RHO_MIN, 1] and the weights within a factor 1 / RHO_MIN of their value.
     constexpr float RHO_MIN = 0x1p-60f;
     float rho = 1.0f;
-    // rho after a chunk of n tokens (without renormalisation if it stays >= RHO_MIN)
-    auto rho_after = [&](int n) TTT_INLINE {
-        const float r = rho * sBP[n];
+    // rho after a chunk of n tokens entered with rho = r0 (without renormalisation
+    // if it stays >= RHO_MIN); the update takes the same step
+    auto rho_step = [&](float r0, int n) TTT_INLINE {
+        const float r = r0 * sBP[n];
         return r < RHO_MIN ? 1.0f : r;
     };
 
@@ -307,20 +308,24 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
 #pragma unroll
         for (int gi = 0; gi < 4; ++gi) stage_group(st, copy_start(t0), gi, want_q, want_k, want_v);
     };
-    // rate of this thread's token of the chunk at t0 (threads 0..63)
+    // The per-token weights of a chunk are formed by one wave (owner), lane j for
+    // token j: the output pass gives the job to its fourth wave in the middle of
+    // the step (it has no score tile of its own), the summary pass to wave 0.
+    // rate of token `lane` of the chunk at t0
     auto load_eta = [&](int t0) TTT_INLINE {
         const int n = min(WC, t_end - t0);
         float et = p.eta_scalar;
-        if (ETAV) et = tid < n ? (p.eta ? p.eta[seq_row + t0 + tid] : p.eta_scalar) : 0.0f;
+        if (ETAV) et = lane < n ? (p.eta ? p.eta[seq_row + t0 + lane] : p.eta_scalar) : 0.0f;
         return et;
     };
-    // per-token weights of a chunk of n tokens
-    auto put_weights = [&](float* w, float et, int n) TTT_INLINE {
-        if (tid < WC) {
+    // per-token weights of a chunk of n tokens entered with momentum scale r0
+    auto put_weights = [&](float* w, float et, int n, float r0, int owner) TTT_INLINE {
+        if (wave == owner) {
             if (ETAV && p.eta_kind == ETA_SOFTPLUS) et = softplus_f32(et);
-            if (tid >= n) et = 0.0f;
-            s_wt(w)[tid] = et * inv1mb;
-            if constexpr (MOM) s_wm(w)[tid] = tid < n ? et * sBP[n - 1 - tid] / rho_after(n) : 0.0f;
+            if (lane >= n) et = 0.0f;
+            s_wt(w)[lane] = et * inv1mb;
+            if constexpr (MOM)
+                s_wm(w)[lane] = lane < n ? et * sBP[n - 1 - lane] * __builtin_amdgcn_rcpf(rho_step(r0, n)) : 0.0f;
         }
     };
     // the stage copies this wave issued have landed (the barrier that follows publishes them)
@@ -547,7 +552,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
                 }
         }
         if (two) stage(stage_b, t_begin + WC, true, true, true);
-        put_weights(w_a, et0, min(WC, t_end - t_begin));
+        put_weights(w_a, et0, min(WC, t_end - t_begin), rho, 3);
         if (two) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); else wait_stage();   // chunk 0 landed
         lds_barrier();
 
@@ -618,6 +623,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             // the weighted value fragments do not depend on the scores
             read_v(cur);
             value_weights(wc);
+            // the weights of the next chunk (its buffer's previous chunk is long done),
+            // published by the barrier below; rho is taken after this chunk's update
+            if (has_next) put_weights(wn, et_next, min(WC, t_end - (t0 + WC)), rho_step(rho, n), 3);
             lds_barrier();   // every wave's score fragments
 
             // intra-chunk term with the weighted value fragments (every score
@@ -639,7 +647,6 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             __builtin_amdgcn_sched_barrier(0);
             update(cur, wc, n, far, t0 + 2 * WC, true);
             if (!has_next) return false;
-            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
             // chunk c + 1 landed; the 12 copies of chunk c + 2 may still be in flight
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
             lds_barrier();
@@ -661,7 +668,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         auto wait_kv = [&]() TTT_INLINE { __builtin_amdgcn_s_waitcnt(vmcnt_imm(8)); };
         issue_kv(stage_a, t_begin);
         issue_kv(stage_b, t_begin + WC);
-        put_weights(w_a, load_eta(t_begin), min(WC, t_end - t_begin));
+        put_weights(w_a, load_eta(t_begin), min(WC, t_end - t_begin), rho, 0);
         wait_kv();
         lds_barrier();
         auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) TTT_INLINE -> bool {
@@ -672,7 +679,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             value_weights(wc);
             update(cur, wc, n, far, t0 + 2 * WC, false);
             if (!has_next) return false;
-            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)));
+            put_weights(wn, et_next, min(WC, t_end - (t0 + WC)), rho, 0);
             wait_kv();
             lds_barrier();
             return true;

@@ -35,9 +35,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, r);
 }
 
-// softplus(a) = ln(1 + e^a), stable form max(a, 0) + log1p(e^-|a|)
+// softplus(a) = ln(1 + e^a), stable form max(a, 0) + log1p(x), x = e^-|a| in
+// (0, 1].  log1p(x) is taken as ln(u) x / (u - 1) with u = 1 + x rounded (the
+// correction of the rounding of 1 + x from Goldberg, "What every computer
+// scientist should know about floating-point arithmetic", 1991; x itself when u
+// rounds to 1), on the hardware exp2 and log2: a few ulp, without a library call.
 __device__ __forceinline__ float softplus_f32(float a) {
-    return fmaxf(a, 0.0f) + log1pf(__expf(-fabsf(a)));
+    const float x = __builtin_amdgcn_exp2f(-fabsf(a) * 1.4426950408889634f);
+    const float u = 1.0f + x;
+    const float l = u == 1.0f ? x : __builtin_amdgcn_logf(u) * 0.6931471805599453f * (x / (u - 1.0f));
+    return fmaxf(a, 0.0f) + l;
 }
 
 __device__ __forceinline__ float silu_f32(float u) {
