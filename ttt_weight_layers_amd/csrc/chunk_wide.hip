@@ -514,6 +514,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         const bool two = t_begin + WC < t_end;
         stage(stage_a, t_begin, true, true, true);
         const float et0 = load_eta(t_begin);
+        // the rate of chunk c + 1 is loaded a step ahead, before the copies of that
+        // step, so that reading it never waits for a copy in flight
+        float et_ahead = two ? load_eta(t_begin + WC) : 0.0f;
         const bool slot_entry = KIND != W_PREFIX && (seg > 0 || (p.has_init && p.seg_count > 1));
         if (slot_entry) {
             const f32x4* src = slot_ptr(seg);
@@ -566,7 +569,8 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             float cf[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) cf[r] = coef[-(8 * (r >> 2) + (r & 3))];
-            const float et_next = has_next ? load_eta(t0 + WC) : 0.0f;
+            const float et_next = et_ahead;
+            et_ahead = has_far ? load_eta(t0 + 2 * WC) : 0.0f;
 
             // Score tile S^T = K Q^T of this wave and the readout from the entering
             // state, in one loop: the score products (a chain on one accumulator) are
