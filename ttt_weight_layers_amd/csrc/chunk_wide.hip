@@ -321,11 +321,13 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     // per-token weights of a chunk of n tokens entered with momentum scale r0
     auto put_weights = [&](float* w, float et, int n, float r0, int owner) TTT_INLINE {
         if (wave == owner) {
+            // the table reads come before the stores
+            float wm = 0.0f;
+            if constexpr (MOM) wm = sBP[max(n - 1 - lane, 0)] * __builtin_amdgcn_rcpf(rho_step(r0, n));
             if (ETAV && p.eta_kind == ETA_SOFTPLUS) et = softplus_f32(et);
             if (lane >= n) et = 0.0f;
             s_wt(w)[lane] = et * inv1mb;
-            if constexpr (MOM)
-                s_wm(w)[lane] = lane < n ? et * sBP[n - 1 - lane] * __builtin_amdgcn_rcpf(rho_step(r0, n)) : 0.0f;
+            if constexpr (MOM) s_wm(w)[lane] = et * wm;
         }
     };
     // the stage copies this wave issued have landed (the barrier that follows publishes them)
@@ -503,7 +505,10 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         // Register r holds j = 32 sJ + 8 (r / 4) + 4h + r % 4 of token i = 32 sI + n.
         const int sJ = (wave >= 2) ? 1 : 0;
         const int sI = (wave == 0) ? 0 : 1;
-        const float* coef = sK + WC + 32 * (sI - sJ) + n32 - 4 * hh;   // coef[-off_r]
+        // one offset added to the array base: the compiler tags an LDS access with its
+        // array only through a short chain of address steps, and an untagged read has
+        // to wait for every copy in flight
+        const float* coef = sK + (WC + 32 * (sI - sJ) + n32 - 4 * hh);   // coef[-off_r]
         // M readout weight of token i: -beta^{i+2} / (1 - beta)
         float gam[2];
 #pragma unroll
