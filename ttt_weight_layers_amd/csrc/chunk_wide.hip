@@ -783,7 +783,10 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             for (int j = 0; j < MAXL; ++j) {
                 const int ei = eb + j / steps, st = j % steps;
                 const int e = e0 + tid + ei * WNT;
-                if (j / steps < batch && ei < n_el && e < e1) d[j] = base[(size_t)st * 2 * HALF_F4 + e];
+                // unconditional loads (an unused one reads element e0), so that all of
+                // them are in flight together instead of one branch at a time
+                const bool ok = j / steps < batch && ei < n_el && e < e1;
+                d[j] = base[(size_t)st * 2 * HALF_F4 + (ok ? e : e0)];
             }
 #pragma unroll
             for (int j = 0; j < MAXL; ++j) {
