@@ -10,22 +10,29 @@
 //
 // The step reads and writes the whole fp32 state once and does under half a
 // flop per byte of it: it is bound by HBM bandwidth.  One workgroup of four waves owns 16
-// value rows of one sequence's S and M; each wave takes four rows at once, its 64
+// value rows (32 with the SwiGLU map) of one sequence's S and M; each wave takes
+// its rows at once, its 64
 // lanes covering consecutive features (8 bytes a lane, 512 bytes a wave access),
 // and reduces the readout of each row across the wave.  The features
 // phi(q), phi(k) of the token are formed once per workgroup in LDS (the SwiGLU
-// map as two fp32 dot products per feature against the frozen W1, W3 rows).
+// map against the frozen W1, W3 rows: on the matrix cores for bf16, as fp32 dot
+// products otherwise).  The first rows of S and M are requested before the
+// features are formed.
 
 #include <hip/hip_ext.h>
 
 #include "device_common.h"
 #include "internal.h"
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 namespace ttt {
 namespace {
 
-constexpr int SR = 16;          // value rows per workgroup
-constexpr int STHREADS = 256;   // four waves, four rows each
+constexpr int STHREADS = 256;   // four waves
+// value rows per workgroup: 16 (four a wave); 32 with the SwiGLU map, so that
+// fewer workgroups form the same features of a token
+constexpr int SR_PLAIN = 16, SR_SWIGLU = 32;
 
 struct StepParams {
     const void* q;
@@ -41,7 +48,7 @@ struct StepParams {
     float beta;
     int eta_kind;
     int H, d_k, d_v, d_phi;
-    int n_rblk;                 // row blocks per sequence (d_v / SR)
+    int n_rblk;                 // row blocks per sequence (d_v / rows per workgroup)
 };
 
 // 16 bytes of a row (8 bf16 or 4 fp32) as fp32
@@ -59,7 +66,7 @@ __device__ __forceinline__ void load16_as_f32(const float* p, float* out) {
     for (int i = 0; i < 4; ++i) out[i] = u[i];
 }
 
-template <typename TI, bool SWIGLU>
+template <typename TI, bool SWIGLU, int SR>
 __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
     extern __shared__ float smem[];
     const int d_k = p.d_k, d_phi = p.d_phi;
@@ -76,10 +83,71 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
     const TI* v = static_cast<const TI*>(p.v) + (size_t)seq * p.d_v;
     TI* o = static_cast<TI*>(p.o) + (size_t)seq * p.d_v;
 
+    // this wave's rows: the token's value entries, the rate and the first 512-byte
+    // slice of each row of S and M are requested before the features are formed,
+    // so that their latency overlaps that of the token's loads
+    const float et = eta_at(p.eta_kind, p.eta, p.eta_scalar, (size_t)seq);
+    const float beta = p.beta;
+    const int lane = tid & 63, wave = tid >> 6;
+    constexpr int RW = SR / 4;      // rows of this wave
+    const int row0 = r0 + RW * wave;
+    float* __restrict__ S = p.S + ((size_t)seq * p.d_v + row0) * d_phi;
+    float* __restrict__ M = p.M + ((size_t)seq * p.d_v + row0) * d_phi;
+    float ev[RW], acc[RW];
+#pragma unroll
+    for (int rr = 0; rr < RW; ++rr) {
+        ev[rr] = load_as_f32(v, row0 + rr);
+        acc[rr] = 0.0f;
+    }
+    // the first NPRE slices of 128 features of every row (the whole row when
+    // d_phi <= 128 NPRE), loaded at once
+    constexpr int NPRE = SWIGLU ? 4 : 1;
+    const int c0 = 2 * lane;
+    f32x2 m0[NPRE][RW], s0[NPRE][RW];
+#pragma unroll
+    for (int it = 0; it < NPRE; ++it) {
+        const int c = c0 + 128 * it;
+        if (c < d_phi) {
+#pragma unroll
+            for (int rr = 0; rr < RW; ++rr) {
+                m0[it][rr] = *reinterpret_cast<const f32x2*>(M + (size_t)rr * d_phi + c);
+                s0[it][rr] = *reinterpret_cast<const f32x2*>(S + (size_t)rr * d_phi + c);
+            }
+        }
+    }
+
     if constexpr (!SWIGLU) {
         for (int f = tid; f < d_phi; f += STHREADS) {
             sPq[f] = load_as_f32(q, f);
             sPk[f] = load_as_f32(k, f);
+        }
+    } else if constexpr (sizeof(TI) == 2) {
+        // bf16: W1 x and W3 x on the matrix cores, 32 features a product with q in
+        // column 0 and k in column 1 of the B operand (the other 30 columns zero):
+        // lane l supplies W[f0 + l % 32][k0 + 8 (l / 32) ..] and, for l % 32 < 2, the
+        // same eight entries of q or k; D[i][j] lands in lane j + 32 ((i / 4) % 2),
+        // register 4 (i / 8) + i % 4
+        const int h = seq % p.H;
+        const uint16_t* w1 = static_cast<const uint16_t*>(p.w1) + (size_t)h * d_phi * d_k;
+        const uint16_t* w3 = static_cast<const uint16_t*>(p.w3) + (size_t)h * d_phi * d_k;
+        const int j = lane & 31, kh = lane >> 5;
+        const uint16_t* xrow = j == 0 ? q : k;
+        for (int f0 = 32 * wave; f0 < d_phi; f0 += 4 * 32) {
+            f32x16 u1 = {}, u3 = {};
+            for (int k0 = 0; k0 < d_k; k0 += 16) {
+                const u32x4 a1 = *reinterpret_cast<const u32x4*>(w1 + (size_t)(f0 + j) * d_k + k0 + 8 * kh);
+                const u32x4 a3 = *reinterpret_cast<const u32x4*>(w3 + (size_t)(f0 + j) * d_k + k0 + 8 * kh);
+                const u32x4 b = j < 2 ? *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * kh) : u32x4{0u, 0u, 0u, 0u};
+                u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1),
+                                                             __builtin_bit_cast(bf16x8, b), u1, 0, 0, 0);
+                u3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a3),
+                                                             __builtin_bit_cast(bf16x8, b), u3, 0, 0, 0);
+            }
+            if (j < 2) {
+                float* dst = j == 0 ? sPq : sPk;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) dst[f0 + 8 * (r >> 2) + 4 * kh + (r & 3)] = silu_f32(u1[r]) * u3[r];
+            }
         }
     } else {
         const int h = seq % p.H;
@@ -115,29 +183,11 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
     }
     __syncthreads();
 
-    const float et = eta_at(p.eta_kind, p.eta, p.eta_scalar, (size_t)seq);
-    const float beta = p.beta;
-    const int lane = tid & 63, wave = tid >> 6;
-    constexpr int RW = SR / 4;      // rows of this wave
-    const int row0 = r0 + RW * wave;
-    float* __restrict__ S = p.S + ((size_t)seq * p.d_v + row0) * d_phi;
-    float* __restrict__ M = p.M + ((size_t)seq * p.d_v + row0) * d_phi;
-    float ev[RW], acc[RW];
 #pragma unroll
-    for (int rr = 0; rr < RW; ++rr) {
-        ev[rr] = et * load_as_f32(v, row0 + rr);
-        acc[rr] = 0.0f;
-    }
+    for (int rr = 0; rr < RW; ++rr) ev[rr] *= et;
     // two consecutive features a lane, 512 bytes a wave access (d_phi is a
-    // multiple of 64: every pair is whole); the four rows' loads are issued
-    // together
-    for (int c = 2 * lane; c < d_phi; c += 128) {
-        f32x2 m[RW], sv[RW];
-#pragma unroll
-        for (int rr = 0; rr < RW; ++rr) {
-            m[rr] = *reinterpret_cast<const f32x2*>(M + (size_t)rr * d_phi + c);
-            sv[rr] = *reinterpret_cast<const f32x2*>(S + (size_t)rr * d_phi + c);
-        }
+    // multiple of 64: every pair is whole); the rows' loads are issued together
+    auto row_step = [&](int c, f32x2* m, f32x2* sv) {
         const float pk0 = sPk[c], pk1 = sPk[c + 1], pq0 = sPq[c], pq1 = sPq[c + 1];
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) {
@@ -149,6 +199,18 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
             *reinterpret_cast<f32x2*>(M + (size_t)rr * d_phi + c) = m[rr];
             *reinterpret_cast<f32x2*>(S + (size_t)rr * d_phi + c) = sv[rr];
         }
+    };
+#pragma unroll
+    for (int it = 0; it < NPRE; ++it)
+        if (c0 + 128 * it < d_phi) row_step(c0 + 128 * it, m0[it], s0[it]);
+    for (int c = c0 + 128 * NPRE; c < d_phi; c += 128) {
+        f32x2 m[RW], sv[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+            m[rr] = *reinterpret_cast<const f32x2*>(M + (size_t)rr * d_phi + c);
+            sv[rr] = *reinterpret_cast<const f32x2*>(S + (size_t)rr * d_phi + c);
+        }
+        row_step(c, m, sv);
     }
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
@@ -183,12 +245,18 @@ hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, h
     p.d_k = s.d_k;
     p.d_v = s.d_v;
     p.d_phi = s.d_phi;
-    p.n_rblk = s.d_v / SR;
+    const int sr = (s.swiglu && s.d_v % SR_SWIGLU == 0) ? SR_SWIGLU : SR_PLAIN;
+    p.n_rblk = s.d_v / sr;
     const size_t smem = step_smem_bytes(s);
     const dim3 grid((unsigned)(s.n_seq() * p.n_rblk)), block(STHREADS);
     void* args[] = {&p};
-    const void* fn = s.bf16 ? (s.swiglu ? (const void*)step_kernel<uint16_t, true> : (const void*)step_kernel<uint16_t, false>)
-                            : (s.swiglu ? (const void*)step_kernel<float, true> : (const void*)step_kernel<float, false>);
+    const void* fn;
+    if (s.swiglu && sr == SR_SWIGLU)
+        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU> : (const void*)step_kernel<float, true, SR_SWIGLU>;
+    else if (s.swiglu)
+        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN> : (const void*)step_kernel<float, true, SR_PLAIN>;
+    else
+        fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN> : (const void*)step_kernel<float, false, SR_PLAIN>;
     return hipExtLaunchKernel(fn, grid, block, args, smem, a.stream, ev_begin, ev_end, 0);
 }
 
