@@ -62,43 +62,80 @@ struct FinalizeParams {
     size_t n_rows;
 };
 
-// one wave per row (b, h, s)
+// 16 bytes a lane: a row (b, h, s) of d values is d / VE consecutive lanes, a
+// wave 64 VE / d rows (d = 64 or 128)
+template <typename TI>
+__device__ __forceinline__ void load_vec(const TI* p, float* out);
+template <>
+__device__ __forceinline__ void load_vec<uint16_t>(const uint16_t* p, float* out) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        out[2 * i] = __uint_as_float(u[i] << 16);
+        out[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+}
+template <>
+__device__ __forceinline__ void load_vec<float>(const float* p, float* out) {
+    const f32x4 u = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = u[i];
+}
+template <typename TI>
+__device__ __forceinline__ void store_vec(TI* p, const float* x);
+template <>
+__device__ __forceinline__ void store_vec<uint16_t>(uint16_t* p, const float* x) {
+    *reinterpret_cast<u32x4*>(p) = u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                                         pack_bf16x2(x[6], x[7])};
+}
+template <>
+__device__ __forceinline__ void store_vec<float>(float* p, const float* x) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+}
+
 template <typename TI>
 __global__ void __launch_bounds__(256) finalize_grads(FinalizeParams p) {
-    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= p.n_rows) return;
+    constexpr int VE = 16 / sizeof(TI);
+    const int lpr = p.d / VE;                                  // lanes per row: 4 .. 32
     const int lane = threadIdx.x & 63;
-    const size_t seq = row / p.T;
-    const int s = (int)(row % p.T);
+    const size_t row = ((size_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / lpr) + lane / lpr;
+    const bool live = row < p.n_rows;
+    const size_t r = live ? row : 0;
+    const int j0 = (lane % lpr) * VE;
+    const size_t seq = r / p.T;
+    const int s = (int)(r % p.T);
     // the forward outputs of token s: at T-1-s of the reversed sequence (causal)
-    const size_t src = p.causal ? seq * p.T + (p.T - 1 - s) : row;
+    const size_t src = p.causal ? seq * p.T + (p.T - 1 - s) : r;
     float c = 1.0f;
     if (!p.causal && p.beta != 0.0f) {
         // c_{T-1-s} = sum_{r=0}^{T-1-s} beta^r = (1 - beta^{T-s}) / (1 - beta)
         c = (1.0f - powf(p.beta, (float)(p.T - s))) / (1.0f - p.beta);
     }
-    const float e = eta_at(p.eta_kind, p.eta, p.eta_scalar, row);
-    const TI* u = static_cast<const TI*>(p.u) + src * p.d;
-    const TI* w = static_cast<const TI*>(p.w) + src * p.d;
-    const TI* v = static_cast<const TI*>(p.v) + row * p.d;
-    TI* dk = static_cast<TI*>(p.dk) + row * p.d;
-    TI* dv = static_cast<TI*>(p.dv) + row * p.d;
-    float dot = 0.0f;
-    for (int j = lane; j < p.d; j += 64) {
-        const float uj = load_as_f32(u, j), wj = load_as_f32(w, j);
-        store_from_f32(dv, j, e * c * uj);
-        store_from_f32(dk, j, e * c * wj);
-        dot = fmaf(load_as_f32(v, j), uj, dot);
-    }
+    const float e = eta_at(p.eta_kind, p.eta, p.eta_scalar, r);
+    float u[VE], w[VE], v[VE];
+    load_vec(static_cast<const TI*>(p.u) + src * p.d + j0, u);
+    load_vec(static_cast<const TI*>(p.w) + src * p.d + j0, w);
+    load_vec(static_cast<const TI*>(p.v) + r * p.d + j0, v);
+    float dv[VE], dk[VE], dot = 0.0f;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
-    if (lane == 0 && p.deta) {
+    for (int i = 0; i < VE; ++i) {
+        dv[i] = e * c * u[i];
+        dk[i] = e * c * w[i];
+        dot = fmaf(v[i], u[i], dot);
+    }
+    if (live) {
+        store_vec(static_cast<TI*>(p.dv) + r * p.d + j0, dv);
+        store_vec(static_cast<TI*>(p.dk) + r * p.d + j0, dk);
+    }
+    // the row's lanes are consecutive and lpr is a power of two
+    for (int off = lpr / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);
+    if (live && lane % lpr == 0 && p.deta) {
         float g = c * dot;                               // dL/deta_s
         if (p.eta_kind == ETA_SOFTPLUS) {
-            const float a = p.eta[row];
+            const float a = p.eta[r];
             g *= 1.0f / (1.0f + __expf(-a));             // d softplus(a) / da = sigmoid(a)
         }
-        p.deta[row] = g;
+        p.deta[r] = g;
     }
 }
 
@@ -135,7 +172,9 @@ hipError_t launch_finalize_grads(const Shape& s, const BackArgs& a) {
     p.T = s.T;
     p.d = s.d_v;
     p.n_rows = (size_t)s.n_seq() * s.T;
-    const dim3 grid((unsigned)((p.n_rows + 3) / 4));
+    // rows per workgroup: four waves of 64 VE / d rows (VE = 16 / element bytes)
+    const size_t rows_per_wg = 4 * (size_t)(64 * (16 / (s.bf16 ? 2 : 4)) / s.d_v);
+    const dim3 grid((unsigned)((p.n_rows + rows_per_wg - 1) / rows_per_wg));
     if (s.bf16)
         hipLaunchKernelGGL(finalize_grads<uint16_t>, grid, dim3(256), 0, a.stream, p);
     else
