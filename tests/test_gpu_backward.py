@@ -31,12 +31,12 @@ def grad_output(w, seed):
     return t.to("cuda").contiguous(), g64
 
 
-def run_case(w, segments=0, seed=40):
+def run_case(w, segments=0, seed=40, launch=None):
     import torch
     x = make_inputs(w)
     d = to_device(x)
     dO, dO64 = grad_output(w, seed)
-    lay = make_layer(w, d, segments=segments)
+    lay = make_layer(w, d, segments=segments, launch=launch or "auto")
     dq, dk, dv, de = lay.backward(d["q"], d["k"], d["v"], dO, eta=d["a"], eta_scalar=w.eta_scalar, beta=w.beta,
                                   eta_mode=w.eta_mode, causal=w.causal)
     torch.cuda.synchronize()
@@ -63,6 +63,16 @@ def test_backward_wide_tiles(eta_mode, beta, segments):
     w = small("v4_momentum_4x8x2048_d128", B=1, H=2, T=64 * 4 + 7).with_settings(eta_mode=eta_mode, beta=beta)
     say(f"[backward wide] {eta_mode} beta={beta} segments={segments}")
     lay = run_case(w, segments)
+    assert lay.plan().path == 2
+
+
+@pytest.mark.parametrize("launch", ["prefix", "single"])
+def test_backward_wide_other_launches(launch):
+    # these plans take reversed copies of the inputs instead of reading them in
+    # reverse order
+    w = small("v4_momentum_4x8x2048_d128", B=1, H=2, T=64 * 5 + 11).with_settings(eta_mode="softplus", beta=0.9)
+    say(f"[backward wide launch={launch}]")
+    lay = run_case(w, 3, launch=launch)
     assert lay.plan().path == 2
 
 

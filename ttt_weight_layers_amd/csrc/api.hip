@@ -304,8 +304,9 @@ void next_events(ttt_la_s* h, hipEvent_t* eb, hipEvent_t* ee) {
 
 int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
                     float beta, uint32_t mode, const float* S0, const float* M0, void* o, float* S_T, float* M_T,
-                    void* hip_stream, bool timed = true) {
+                    void* hip_stream, bool timed = true, bool reverse = false) {
     ttt::FwdArgs a{};
+    a.reverse = reverse;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -341,6 +342,7 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
         h->n_kernels = nk;
     } else {
         // fp32 inputs, and the carried-state calls of the 16x16-tile shapes
+        if (reverse) return TTT_LA_ERR_INVALID_ARG;
         e = ttt::launch_generic(h->shape, a, eb, ee);
         h->n_kernels = 1;
     }
@@ -427,7 +429,19 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
                          hip_stream, false);
     if (st != TTT_LA_OK) return st;
     void *U, *W;
-    if (!bidir) {
+    // the 32x32-tile kernels of three launches read and write in reverse time order
+    // themselves; the other plans get reversed copies
+    const bool rev_in_kernel = !bidir && h->fast && h->fp.wide && !h->fp.fused && !h->fp.prefix;
+    if (rev_in_kernel) {
+        U = ws;
+        W = ws + tb;
+        st = enqueue_forward(h, k, q, dO, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, U, nullptr, nullptr,
+                             hip_stream, false, true);
+        if (st != TTT_LA_OK) return st;
+        st = enqueue_forward(h, v, dO, q, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, W, nullptr, nullptr,
+                             hip_stream, false, true);
+        if (st != TTT_LA_OK) return st;
+    } else if (!bidir) {
         // rate-1 forwards over the reversed sequence: u from (k, q, dO), w from (v, dO, q)
         char *Rq = ws, *Rk = ws + tb, *Rv = ws + 2 * tb, *RdO = ws + 3 * tb;
         U = ws + 4 * tb;
@@ -466,6 +480,7 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
     b.beta = beta;
     b.eta_kind = eta_kind_of(mode);
     b.causal = !bidir;
+    b.uw_reversed = !bidir && !rev_in_kernel;
     b.stream = stream;
     return ttt::launch_finalize_grads(h->shape, b) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }

@@ -58,6 +58,7 @@ struct FinalizeParams {
     float beta;
     int eta_kind;
     int causal;
+    int uw_reversed;
     int T, d;
     size_t n_rows;
 };
@@ -104,8 +105,8 @@ __global__ void __launch_bounds__(256) finalize_grads(FinalizeParams p) {
     const int j0 = (lane % lpr) * VE;
     const size_t seq = r / p.T;
     const int s = (int)(r % p.T);
-    // the forward outputs of token s: at T-1-s of the reversed sequence (causal)
-    const size_t src = p.causal ? seq * p.T + (p.T - 1 - s) : r;
+    // the forward outputs of token s (at T-1-s when they are stored reversed)
+    const size_t src = p.uw_reversed ? seq * p.T + (p.T - 1 - s) : r;
     float c = 1.0f;
     if (!p.causal && p.beta != 0.0f) {
         // c_{T-1-s} = sum_{r=0}^{T-1-s} beta^r = (1 - beta^{T-s}) / (1 - beta)
@@ -169,6 +170,7 @@ hipError_t launch_finalize_grads(const Shape& s, const BackArgs& a) {
     p.beta = a.beta;
     p.eta_kind = a.eta_kind;
     p.causal = a.causal ? 1 : 0;
+    p.uw_reversed = a.uw_reversed ? 1 : 0;
     p.T = s.T;
     p.d = s.d_v;
     p.n_rows = (size_t)s.n_seq() * s.T;

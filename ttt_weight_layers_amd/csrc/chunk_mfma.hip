@@ -758,6 +758,7 @@ hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, b
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
                        hipEvent_t ev_end, int* n_kernels) {
     if (p.wide) return launch_wide(s, p, workspace, a, ev_begin, ev_end, n_kernels);
+    if (a.reverse) return hipErrorInvalidValue;   // time reversal: 32x32-tile kernels only
     ChunkParams cp{};
     cp.q = static_cast<const uint16_t*>(a.q);
     cp.k = static_cast<const uint16_t*>(a.k);

@@ -99,6 +99,7 @@ struct WideParams {
     float* S_T;
     float* M_T;
     int has_init;
+    int reverse;        // time-reversed rows (see FwdArgs::reverse)
 };
 
 // The caller's state layout [seq][d_v][d_phi] against the register tiles: lane l
@@ -290,17 +291,20 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     // copy builtin they make the host pass drop the kernels without a diagnostic.)
     auto stage_group = [&](uint16_t* st, int t0, int gi, bool want_q, bool want_k, bool want_v) TTT_INLINE {
         const int n = min(WC, t_end - t0);
-        const size_t row0 = seq_row + t0;
+        // reversed: the chunk's rows are tensor rows T-t0-n .. T-t0-1, row r of the
+        // chunk at n-1-r of the range (r >= n wraps far past it and reads zero)
+        const size_t row0 = p.reverse ? seq_row + (p.T - t0 - n) : seq_row + t0;
+        const int vo = p.reverse ? voff[gi] + 2 * (n - 1 - 2 * (4 * (wave_s + 4 * gi) + lane_row)) * WD : voff[gi];
         const __amdgpu_buffer_rsrc_t rq = chunk_rsrc(p.q, row0, n);
         const __amdgpu_buffer_rsrc_t rk = chunk_rsrc(p.k, row0, n);
         const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(p.v, row0, n);
         const int grp = wave_s + 4 * gi;
         if (want_q)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (TTT_LDS void*)(tq(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (TTT_LDS void*)(tq(st) + grp * 4 * WD), 16, vo, 0, 0, 0);
         if (want_k)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (TTT_LDS void*)(tk(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (TTT_LDS void*)(tk(st) + grp * 4 * WD), 16, vo, 0, 0, 0);
         if (want_v)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (TTT_LDS void*)(tv(st) + grp * 4 * WD), 16, voff[gi], 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (TTT_LDS void*)(tv(st) + grp * 4 * WD), 16, vo, 0, 0, 0);
     };
     // first row of a copy that starts at t (t_end - 1 past the end of the range)
     auto copy_start = [&](int t) TTT_INLINE { return t < t_end ? t : t_end - 1; };
@@ -315,7 +319,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     auto load_eta = [&](int t0) TTT_INLINE {
         const int n = min(WC, t_end - t0);
         float et = p.eta_scalar;
-        if (ETAV) et = lane < n ? (p.eta ? p.eta[seq_row + t0 + lane] : p.eta_scalar) : 0.0f;
+        if (ETAV)
+            et = lane < n ? (p.eta ? p.eta[seq_row + (p.reverse ? p.T - 1 - (t0 + lane) : t0 + lane)] : p.eta_scalar)
+                          : 0.0f;
         return et;
     };
     // per-token weights of a chunk of n tokens entered with momentum scale r0
@@ -483,7 +489,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     auto store = [&](const f32x16& o, int I, int n, size_t row0) TTT_INLINE {
         const int i = 32 * I + n32;
         if (i < n) {
-            uint16_t* dst = p.o + (row0 + i) * WD + 32 * wave + 16 * hh;
+            // row0 = seq_row + t0; reversed: tensor row T-1-(t0+i)
+            const size_t orow = p.reverse ? 2 * seq_row + (p.T - 1) - row0 - i : row0 + i;
+            uint16_t* dst = p.o + orow * WD + 32 * wave + 16 * hh;
             const u32x4 lo = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                               pack_bf16x2(o[6], o[7])};
             const u32x4 hi = {pack_bf16x2(o[8], o[9]), pack_bf16x2(o[10], o[11]), pack_bf16x2(o[12], o[13]),
@@ -1022,6 +1030,8 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
     wp.S_T = a.S_T;
     wp.M_T = a.M_T;
     wp.has_init = (a.S0 || a.M0) ? 1 : 0;
+    wp.reverse = a.reverse ? 1 : 0;
+    if (a.reverse && (state_io || a.bidirectional)) return hipErrorInvalidValue;
     wp.beta_seg = (float)std::pow((double)a.beta, (double)p.seg_len);
     hipStream_t st = a.stream;
     hipError_t e = hipSuccess;

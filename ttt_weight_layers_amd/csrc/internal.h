@@ -29,6 +29,10 @@ struct FwdArgs {
     const float* M0 = nullptr;
     float* S_T = nullptr;
     float* M_T = nullptr;
+    // time-reversed causal forward (32x32-tile plans of three launches, no carried
+    // state): step t of the recurrence reads row T-1-t of q, k, v and the rates and
+    // writes row T-1-t of o
+    bool reverse = false;
 };
 
 // Shape of one layer (copied from the descriptor).
@@ -109,8 +113,9 @@ hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, h
 hipError_t launch_reverse(const void* const* src, void* const* dst, int count, size_t n_seq, int T, size_t row_bytes,
                           hipStream_t st);
 struct BackArgs {
-    const void* u;       // rate-1 forward outputs [n_seq, T, d] (time-reversed when causal)
+    const void* u;       // rate-1 forward outputs [n_seq, T, d]
     const void* w;
+    bool uw_reversed;    // causal: u, w are stored reversed in time
     const void* v;
     const float* eta;
     void* dk;
