@@ -255,6 +255,13 @@ int ttt_la_wait_status(ttt_la_t h, int32_t* failed);
 int ttt_la_enable_kernel_timing(ttt_la_t h, int32_t n_slots);
 int ttt_la_kernel_times(ttt_la_t h, float* ms, int32_t capacity, int32_t* count);
 
+/* The same hook on one call in `every` (>= 1): the first following call and
+ * every `every`-th one after it carry the events, the others launch without
+ * them (an event pair around a kernel costs the stream some time of its own).
+ * ttt_la_enable_kernel_timing(h, n) is ttt_la_enable_kernel_timing_every(h, n, 1).
+ * TTT_LA_ERR_INVALID_ARG for a null handle, n_slots < 0 or every < 1. */
+int ttt_la_enable_kernel_timing_every(ttt_la_t h, int32_t n_slots, int32_t every);
+
 #ifdef __cplusplus
 }
 #endif

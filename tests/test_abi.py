@@ -159,6 +159,7 @@ def test_null_handle_calls():
     assert lib.ttt_la_forward(None, Q, K, V, None, 1.0, 0.0, 0, O, None) == tla.TTT_LA_ERR_INVALID_ARG
     assert lib.ttt_la_get_plan(None, None) == tla.TTT_LA_ERR_INVALID_ARG
     assert lib.ttt_la_enable_kernel_timing(None, 4) == tla.TTT_LA_ERR_INVALID_ARG
+    assert lib.ttt_la_enable_kernel_timing_every(None, 4, 2) == tla.TTT_LA_ERR_INVALID_ARG
     n = ctypes.c_int32(0)
     assert lib.ttt_la_kernel_times(None, None, 0, ctypes.byref(n)) == tla.TTT_LA_ERR_INVALID_ARG
     assert lib.ttt_la_create(None, None) == tla.TTT_LA_ERR_INVALID_ARG

@@ -160,6 +160,33 @@ def test_single_and_three_launch_paths(eta_mode, beta, segments):
     assert oracle.rel_err(select_heads(got, w, heads), ref) <= TOL[w.dtype]
 
 
+def test_timing_hook_between_single_launches():
+    # the measurement hook switched on (one call in two) and off between forwards of
+    # the single-launch plan: the arrival counters keep their targets, so every
+    # forward waits as it should and gives the same output
+    import ttt_weight_layers_amd as tla
+    w = small("v4_momentum_4x8x2048_d128", T=1024 + 29)
+    say("[timing hook / single launch]")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d, segments=8, launch="single")
+    assert lay.plan().n_kernels == 1
+    first = run_gpu(w, d, layer=lay)
+    run_gpu(w, d, layer=lay)
+    assert tla.ttt_la_enable_kernel_timing_every(lay.handle, 4, 2) == tla.TTT_LA_OK
+    outs = [run_gpu(w, d, layer=lay) for _ in range(4)]
+    times = tla.ttt_la_kernel_times(lay.handle, 4)
+    assert len(times) == 2 and all(t > 0 for t in times)
+    assert tla.ttt_la_enable_kernel_timing(lay.handle, 0) == tla.TTT_LA_OK
+    outs.append(run_gpu(w, d, layer=lay))
+    assert lay.wait_failed() == 0
+    for o in outs:
+        np.testing.assert_array_equal(o, first)
+    heads = [0, 17, 31]
+    ref = run_oracle(w, x, heads=heads)
+    assert oracle.rel_err(select_heads(first, w, heads), ref) <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("eta_mode,beta,segments", [("scalar", 0.9, 8), ("softplus", 0.9, 5), ("per_token", 0.0, 16)])
 def test_prefix_launch(eta_mode, beta, segments):
     # one kernel: each segment's workgroup rebuilds its entry state from the earlier

@@ -7,6 +7,7 @@ loaded on first use and its absence is an error, never a fallback.
 from ._binding import (  # noqa: F401
     EXPORTS, LIB_PATH, TTTError, TTTLinearAttention, load_library, make_desc, mode_bits,
     ttt_la_check, ttt_la_create, ttt_la_desc, ttt_la_destroy, ttt_la_enable_kernel_timing,
+    ttt_la_enable_kernel_timing_every,
     ttt_la_forward, ttt_la_forward_state, ttt_la_step, ttt_la_check_state, ttt_la_get_plan,
     ttt_la_backward, ttt_la_backward_workspace, ttt_la_check_backward,
     ttt_la_kernel_times, ttt_la_plan, ttt_la_status_string,

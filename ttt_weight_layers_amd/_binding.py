@@ -62,7 +62,8 @@ class ttt_la_plan(ctypes.Structure):
 EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_forward_state", "ttt_la_step", "ttt_la_backward",
            "ttt_la_backward_workspace", "ttt_la_destroy",
            "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_check_backward", "ttt_la_get_plan",
-           "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times")
+           "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times",
+           "ttt_la_enable_kernel_timing_every")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -110,6 +111,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_enable_kernel_timing.restype = ctypes.c_int
     lib.ttt_la_kernel_times.argtypes = [vp, ctypes.POINTER(f32), i32, ctypes.POINTER(i32)]
     lib.ttt_la_kernel_times.restype = ctypes.c_int
+    lib.ttt_la_enable_kernel_timing_every.argtypes = [vp, i32, i32]
+    lib.ttt_la_enable_kernel_timing_every.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -205,6 +208,10 @@ def ttt_la_wait_status(h) -> int:
 
 def ttt_la_enable_kernel_timing(h, n_slots: int) -> int:
     return load_library().ttt_la_enable_kernel_timing(h, int(n_slots))
+
+
+def ttt_la_enable_kernel_timing_every(h, n_slots: int, every: int) -> int:
+    return load_library().ttt_la_enable_kernel_timing_every(h, int(n_slots), int(every))
 
 
 def ttt_la_kernel_times(h, capacity: int):

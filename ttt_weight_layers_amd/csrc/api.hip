@@ -25,7 +25,9 @@ struct ttt_la_s {
     unsigned epoch;      // completed launches of the fused path (its counter targets)
     // measurement hook
     std::vector<hipEvent_t> ev_begin, ev_end;
-    int calls;
+    int calls;           // timed calls so far
+    int every;           // time one call in `every`
+    int seen;            // calls since the timing was set
 };
 
 namespace {
@@ -198,7 +200,7 @@ void release_events(ttt_la_s* h) {
     h->ev_begin.clear();
     h->ev_end.clear();
     h->calls = 0;
-    h->epoch = 0;
+    h->seen = 0;
 }
 
 }  // namespace
@@ -250,6 +252,8 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     h->workspace = nullptr;
     h->workspace_bytes = 0;
     h->calls = 0;
+    h->every = 1;
+    h->seen = 0;
     h->epoch = 0;
     h->fast = desc->dtype == TTT_LA_BF16 && ttt::fast_supported(h->shape, desc->chunk);
     h->n_kernels = 1;
@@ -294,7 +298,7 @@ namespace {
 // the timing events of the next launch (null when the hook is off)
 void next_events(ttt_la_s* h, hipEvent_t* eb, hipEvent_t* ee) {
     *eb = *ee = nullptr;
-    if (!h->ev_begin.empty()) {
+    if (!h->ev_begin.empty() && h->seen++ % h->every == 0) {
         const size_t slot = (size_t)h->calls % h->ev_begin.size();
         *eb = h->ev_begin[slot];
         *ee = h->ev_end[slot];
@@ -578,12 +582,17 @@ int ttt_la_wait_status(ttt_la_t h, int32_t* failed) {
     return TTT_LA_OK;
 }
 
-int ttt_la_enable_kernel_timing(ttt_la_t h, int32_t n_slots) {
-    if (!h || n_slots < 0) return TTT_LA_ERR_INVALID_ARG;
+int ttt_la_enable_kernel_timing(ttt_la_t h, int32_t n_slots) { return ttt_la_enable_kernel_timing_every(h, n_slots, 1); }
+
+int ttt_la_enable_kernel_timing_every(ttt_la_t h, int32_t n_slots, int32_t every) {
+    if (!h || n_slots < 0 || every < 1) return TTT_LA_ERR_INVALID_ARG;
     release_events(h);
+    h->every = every;
     for (int32_t i = 0; i < n_slots; ++i) {
+        // timestamps only: no system-scope fence (an L2 write-back) around the kernel
         hipEvent_t a = nullptr, b = nullptr;
-        if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+        if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess ||
+            hipEventCreateWithFlags(&b, hipEventDisableSystemFence) != hipSuccess) {
             if (a) (void)hipEventDestroy(a);
             release_events(h);
             return TTT_LA_ERR_HIP;
