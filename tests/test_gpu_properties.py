@@ -160,6 +160,24 @@ def test_single_and_three_launch_paths(eta_mode, beta, segments):
     assert oracle.rel_err(select_heads(got, w, heads), ref) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("eta_mode,beta", [("softplus", 0.9), ("per_token", 0.999), ("scalar", 0.0)])
+def test_two_segments_with_split_summary(eta_mode, beta):
+    # two segments of 20 chunks and few sequences: segment 0 is summarised in two
+    # halves and the output kernel of segment 1 combines them (beta^(L/2) M_a + M_b;
+    # with beta = 0.999 that term matters, with 0.9 it is below 2^-30)
+    w = small("v4_momentum_4x8x2048_d128", B=1, H=3, T=64 * 40 - 13).with_settings(eta_mode=eta_mode, beta=beta)
+    say(f"[split summary] {eta_mode} beta={beta}")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d, segments=2)
+    plan = lay.plan()
+    assert plan.path == 2 and plan.segments == 2
+    got = run_gpu(w, d, layer=lay)
+    assert lay.plan().n_kernels == 2
+    ref = run_oracle(w, x)
+    assert oracle.rel_err(got, ref) <= TOL[w.dtype]
+
+
 def test_timing_hook_between_single_launches():
     # the measurement hook switched on (one call in two) and off between forwards of
     # the single-launch plan: the arrival counters keep their targets, so every

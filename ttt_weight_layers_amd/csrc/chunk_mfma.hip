@@ -658,10 +658,16 @@ FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split,
             p.zero_bytes = 0;
             return p;
         }
-        p.summary_bytes = wide_summary_bytes(s, p.segments);
         // one launch, on request, when every workgroup of the grid can be resident at once
         const long grid = ((long)s.n_seq() * p.segments + 7) / 8 * 8;
         p.fused = launch == TTT_LA_LAUNCH_SINGLE && p.segments > 1 && grid <= wide_fused_capacity();
+        // two segments whose one summary would leave half the CUs idle: summarise the
+        // halves of segment 0 (an even number of chunks, at least 8 each)
+        p.sum_split = (!p.fused && p.segments == 2 && 2L * s.n_seq() <= 256 && seg_chunks % 2 == 0 &&
+                       seg_chunks >= 16)
+                          ? 2
+                          : 1;
+        p.summary_bytes = wide_summary_bytes(s, p.segments + (p.sum_split == 2 ? 1 : 0));
         return p;
     }
     // The chunk length is a tiling choice (results differ only by rounding);

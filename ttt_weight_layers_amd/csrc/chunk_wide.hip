@@ -79,6 +79,8 @@ struct WideParams {
     int eta_kind;
     int T;
     int seg_count, seg_len;
+    int slot_count;     // workspace slots per sequence
+    int entry_split;    // summary slots per segment: segment j enters with slot j entry_split
     float beta_seg;      // beta^seg_len
     int n_units;
     // cooperative (fused) launch only: per-sequence arrival counters (two per
@@ -256,7 +258,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
     // j - 1 and, after the scan, holds the entry state of segment j; slot 0 holds
     // the carried entry state of segment 0 (when the call has one)
     auto slot_ptr = [&](int s) TTT_INLINE {
-        return reinterpret_cast<f32x4*>(p.state) + ((size_t)seq * p.seg_count + s) * 2 * HALF_F4;
+        return reinterpret_cast<f32x4*>(p.state) + ((size_t)seq * p.slot_count + s) * 2 * HALF_F4;
     };
 
     // transpose-read columns: value columns in pi order, feature columns in sigma order
@@ -532,7 +534,7 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         float et_ahead = two ? load_eta(t_begin + WC) : 0.0f;
         const bool slot_entry = KIND != W_PREFIX && (seg > 0 || (p.has_init && p.seg_count > 1));
         if (slot_entry) {
-            const f32x4* src = slot_ptr(seg);
+            const f32x4* src = slot_ptr(seg * p.entry_split);
 #pragma unroll
             for (int ft = 0; ft < WFT; ++ft)
 #pragma unroll
@@ -977,6 +979,25 @@ int wide_fused_capacity() {
     return cached = coop ? per_cu * cus : 0;
 }
 
+// The scan over n_slots slots per sequence of summaries of seg_len tokens each
+// (slot 0: the carried state when has_init).
+static hipError_t launch_scan(const Shape& s, float* state, int n_slots, int seg_len, const FwdArgs& a, bool mom,
+                       int has_init, hipStream_t st) {
+    constexpr int HALF = WNW * WFT * 4 * 64;
+    const size_t n_threads = (size_t)s.n_seq() * HALF;
+    const float bL = (float)std::pow((double)a.beta, (double)seg_len);
+    const float kappa = a.beta / (1.0f - a.beta);
+    const int mmode = !mom ? 0 : (bL < 0x1p-30f ? 2 : 1);
+    const dim3 grid((unsigned)((n_threads + 255) / 256));
+    if (n_slots - 1 <= 7)
+        hipLaunchKernelGGL(wide_scan<7>, grid, dim3(256), 0, st, state, s.n_seq(), n_slots, bL, mmode, a.S0, a.M0,
+                           kappa, has_init);
+    else
+        hipLaunchKernelGGL(wide_scan<15>, grid, dim3(256), 0, st, state, s.n_seq(), n_slots, bL, mmode, a.S0, a.M0,
+                           kappa, has_init);
+    return hipGetLastError();
+}
+
 size_t wide_zero_bytes(const Shape& s) {
     // two counters per sequence and the wait-failed flag
     return ((size_t)(2 * s.n_seq() + 1) * sizeof(unsigned) + 255) / 256 * 256;
@@ -1033,6 +1054,8 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
     wp.reverse = a.reverse ? 1 : 0;
     if (a.reverse && (state_io || a.bidirectional)) return hipErrorInvalidValue;
     wp.beta_seg = (float)std::pow((double)a.beta, (double)p.seg_len);
+    wp.slot_count = p.segments;
+    wp.entry_split = 1;
     hipStream_t st = a.stream;
     hipError_t e = hipSuccess;
     int nk = 0;
@@ -1081,26 +1104,29 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
     } else {
         wp.seg_count = p.segments;
         wp.seg_len = p.seg_len;
-        if (p.segments > 1) {
+        if (p.segments == 2 && p.sum_split == 2) {
+            // summaries of the two halves of segment 0 into slots 1 and 2 (three slots
+            // per sequence, slot 0 the carried state), scanned over the half length:
+            // segment 1 enters with slot 2
+            WideParams sp = wp;
+            sp.seg_count = 3;
+            sp.seg_len = p.seg_len / 2;
+            sp.slot_count = 3;
+            sp.n_units = s.n_seq() * 2;
+            if ((e = launch_wide_kind<W_SUMMARY>(mom, etav, sp, st)) != hipSuccess) return e;
+            if ((e = launch_scan(s, wp.state, 3, sp.seg_len, a, mom, wp.has_init, st)) != hipSuccess) return e;
+            nk += 2;
+            wp.slot_count = 3;
+            wp.entry_split = 2;
+        } else if (p.segments > 1) {
             wp.n_units = s.n_seq() * (p.segments - 1);
             if ((e = launch_wide_kind<W_SUMMARY>(mom, etav, wp, st)) != hipSuccess) return e;
             ++nk;
             // with two segments and no carried state the one summary already is the
             // entry state of segment 1
             if (p.segments > 2 || wp.has_init) {
-                constexpr int HALF = WNW * WFT * 4 * 64;
-                const size_t n_threads = (size_t)s.n_seq() * HALF;
-                const float bL = (float)std::pow((double)a.beta, (double)p.seg_len);
-                const float kappa = a.beta / (1.0f - a.beta);
-                const int mmode = !mom ? 0 : (bL < 0x1p-30f ? 2 : 1);
-                const dim3 grid((unsigned)((n_threads + 255) / 256));
-                if (p.segments - 1 <= 7)
-                    hipLaunchKernelGGL(wide_scan<7>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments, bL,
-                                       mmode, a.S0, a.M0, kappa, wp.has_init);
-                else
-                    hipLaunchKernelGGL(wide_scan<15>, grid, dim3(256), 0, st, wp.state, s.n_seq(), p.segments, bL,
-                                       mmode, a.S0, a.M0, kappa, wp.has_init);
-                if ((e = hipGetLastError()) != hipSuccess) return e;
+                if ((e = launch_scan(s, wp.state, p.segments, p.seg_len, a, mom, wp.has_init, st)) != hipSuccess)
+                    return e;
                 ++nk;
             }
         }

@@ -69,6 +69,8 @@ struct FastPlan {
     bool prefix;            // wide causal path as one kernel whose segments rebuild their
                             // entry states from the earlier tokens
     int bounds[17];         // prefix path: first token of each segment, bounds[segments] = T
+    int sum_split;          // two segments: summaries over halves of segment 0 (2) or all
+                            // of it (1); the halves put twice the workgroups on the summary
 };
 
 bool fast_supported(const Shape& s, int chunk);
