@@ -574,8 +574,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
         if (two) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12)); else wait_stage();   // chunk 0 landed
         lds_barrier();
 
-        // Chunk c, staged in cur with weights wc.  Chunk c + 1 is in flight (weights
-        // go to wn at the end); the copy of chunk c + 2 into far starts mid-step.
+        // Chunk c, staged in cur with weights wc.  Chunk c + 1 is in flight (its
+        // weights go to wn before the middle barrier); the copy of chunk c + 2 into
+        // far is issued during the update.
         auto step = [&](uint16_t* cur, float* wc, float* wn, uint16_t* far, int t0) TTT_INLINE -> bool {
             const int n = min(WC, t_end - t0);
             const size_t row0 = seq_row + t0;
@@ -643,7 +644,9 @@ __global__ void __launch_bounds__(WNT, 1) wide_kernel(WideParams p) {
             read_v(cur);
             value_weights(wc);
             // the weights of the next chunk (its buffer's previous chunk is long done),
-            // published by the barrier below; rho is taken after this chunk's update
+            // published by the barrier below; the momentum scale they divide by is rho
+            // after this chunk's update and the next one's, predicted the way the
+            // update takes it
             if (has_next) put_weights(wn, et_next, min(WC, t_end - (t0 + WC)), rho_step(rho, n), 3);
             lds_barrier();   // every wave's score fragments
 
