@@ -244,6 +244,11 @@ chunk_kernel(ChunkParams p) {
     auto fetch = [&](PF& f, int t0, bool want_q, bool want_k, bool want_v, bool want_eta) {
         const int n = min(CH, t_end - t0);
         const size_t row0 = seq_row + t0;
+        // the rate first: its address may have to come back from a register spill,
+        // and waiting for that reload must not mean waiting for the chunk's loads
+        f.eta = 0.0f;
+        if (want_eta && tid < n) f.eta = ETAV ? p.eta[row0 + tid] : p.eta_scalar;
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < PF::PX; ++i) {
             const int idx = tid + i * NT;
@@ -259,8 +264,6 @@ chunk_kernel(ChunkParams p) {
             const size_t off = (row0 + r) * DV + dv_base + 8 * c;
             f.v[i] = (want_v && r < n) ? *reinterpret_cast<const u32x4*>(p.v + off) : u32x4{0u, 0u, 0u, 0u};
         }
-        f.eta = 0.0f;
-        if (want_eta && tid < n) f.eta = ETAV ? p.eta[row0 + tid] : p.eta_scalar;
     };
 
     // write a prefetched chunk into buffer buf of the swizzled LDS tiles (and its token weights)
