@@ -66,6 +66,15 @@ def test_backward_wide_tiles(eta_mode, beta, segments):
     assert lay.plan().path == 2
 
 
+def test_backward_two_segments_split_summary():
+    # two segments of 20 chunks on two sequences: the forwards inside the backward
+    # (two of them reading in reverse time order) summarise segment 0 in two halves
+    w = small("v4_momentum_4x8x2048_d128", B=1, H=2, T=64 * 40 - 13).with_settings(eta_mode="softplus", beta=0.9)
+    say("[backward split summary]")
+    lay = run_case(w, 2)
+    assert lay.plan().path == 2 and lay.plan().segments == 2
+
+
 @pytest.mark.parametrize("launch", ["prefix", "single"])
 def test_backward_wide_other_launches(launch):
     # these plans take reversed copies of the inputs instead of reading them in

@@ -152,12 +152,19 @@ def run_steps(lay, w, d, S, M, t0, t1):
     return np.concatenate([from_device(o, w.dtype) for o in outs], axis=2)
 
 
-@pytest.mark.parametrize("case", ["bf16_d128_momentum", "f32_d64_softplus", "bf16_swiglu_per_token"])
+@pytest.mark.parametrize("case", ["bf16_d128_momentum", "f32_d64_softplus", "bf16_swiglu_per_token",
+                                  "bf16_swiglu_dk64", "f32_swiglu"])
 def test_step_matches_recurrence(case):
     if case == "bf16_d128_momentum":
         w = small("v4_momentum_4x8x2048_d128", B=2, H=2, T=6)
     elif case == "f32_d64_softplus":
         w = small("v5_f32_1x1x256_d64", B=2, H=2, T=6).with_settings(eta_mode="softplus", beta=0.9)
+    elif case == "bf16_swiglu_dk64":
+        # the matrix-core features with four k-steps; d_v = 64 takes 32 rows a workgroup
+        w = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=4).with_settings(d_k=64, d_v=64, d_phi=256)
+    elif case == "f32_swiglu":
+        # fp32 features as dot products
+        w = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=4).with_settings(dtype="f32", d_phi=128)
     else:
         w = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=5).with_settings(eta_mode="per_token")
     say(f"[step {case}]")
