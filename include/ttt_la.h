@@ -179,8 +179,12 @@ int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const f
  *            least ttt_la_backward_workspace() bytes (may be NULL when that is 0).
  * Identity feature map with d_k == d_v only (TTT_LA_ERR_UNSUPPORTED otherwise).
  * Runs three forwards of the layer on permuted operands (two over the sequence
- * reversed in time, with the handle's own kernels and workspace) and two small
- * kernels; enqueued on hip_stream, no allocation, no synchronisation.
+ * reversed in time) and one or two small kernels, enqueued on hip_stream, no
+ * allocation, no synchronisation.  On the bf16 d = 128 plans of three launches
+ * the two reversed forwards read their rows in reverse order and run beside the
+ * first one on two streams of the handle (created on the first call, default
+ * priority), which start after the work already on hip_stream and which
+ * hip_stream waits for; their segment summaries live in the workspace.
  * The outputs must not overlap each other, any input or the workspace.
  * Errors: as ttt_la_forward, and TTT_LA_ERR_INVALID_ARG for a missing, misaligned,
  * overlapping or too small buffer. */
@@ -188,9 +192,11 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
                     float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV, float* dEta,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Bytes of workspace ttt_la_backward needs on handle h for the given mode bits
- * (the time-reversed operands of the causal mode; less for the bidirectional
- * mode).  Host only; TTT_LA_ERR_UNSUPPORTED if the handle's shape has no backward. */
+/* Bytes of workspace ttt_la_backward needs on handle h for the given mode bits:
+ * two [B, H, T, d] tensors (the outputs of the two rate-1 forwards), plus in
+ * causal mode either two segment-summary areas of the handle's plan (bf16 d = 128
+ * plans of three launches) or the four time-reversed operands.  Host only;
+ * TTT_LA_ERR_UNSUPPORTED if the handle's shape has no backward. */
 int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes);
 
 /* Releases the workspace and the handle.  NULL-safe. */

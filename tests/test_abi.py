@@ -263,8 +263,24 @@ def test_backward_arguments():
     bad = tla.TTT_LA_ERR_INVALID_ARG
     assert check_bw() == tla.TTT_LA_OK
     assert check_bw(de=None) == tla.TTT_LA_OK
-    assert check_bw(mode=tla.TTT_LA_BIDIRECTIONAL, wsb=2 * TB) == tla.TTT_LA_OK   # less workspace
-    assert check_bw(wsb=6 * TB - 16) == bad                                      # too small
+    assert check_bw(mode=tla.TTT_LA_BIDIRECTIONAL, wsb=2 * TB) == tla.TTT_LA_OK   # the two outputs
+    # bf16 d = 128, one segment: the two outputs and no summaries
+    assert check_bw(wsb=2 * TB) == tla.TTT_LA_OK
+    assert check_bw(wsb=2 * TB - 16) == bad                                      # too small
+    # two segments of 8 chunks: plus a summary area of 6 sequences x 2 slots x 128 KiB
+    # for each reversed forward
+    d2 = desc(T=1024, segments=2)
+    tb2 = 2 * 3 * 1024 * 128 * 2
+    need2 = 2 * tb2 + 2 * (6 * 2 * 128 * 128 * 2 * 4)
+    assert check_bw(d=d2, wsb=need2) == tla.TTT_LA_OK
+    assert check_bw(d=d2, wsb=need2 - 16) == bad
+    # the single-launch plan and the 16x16-tile shapes take reversed copies of
+    # q, k, v, dO: six tensors
+    assert check_bw(d=desc(launch="single"), wsb=6 * TB - 16) == bad
+    assert check_bw(d=desc(launch="single"), wsb=6 * TB) == tla.TTT_LA_OK
+    tb64 = 2 * 3 * 100 * 64 * 2
+    assert check_bw(d=desc(d_k=64, d_v=64), wsb=6 * tb64 - 16) == bad
+    assert check_bw(d=desc(d_k=64, d_v=64), wsb=6 * tb64) == tla.TTT_LA_OK
     assert check_bw(ws=None) == bad
     assert check_bw(ws=WS + 8) == bad
     assert check_bw(dO=None) == bad

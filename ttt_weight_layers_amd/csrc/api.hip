@@ -28,6 +28,11 @@ struct ttt_la_s {
     int calls;           // timed calls so far
     int every;           // time one call in `every`
     int seen;            // calls since the timing was set
+    // the backward's two time-reversed forwards run beside the first one on their
+    // own streams (created on first use; default priority)
+    hipStream_t aux[2];
+    hipEvent_t fork, join[2];
+    bool aux_ready;
 };
 
 namespace {
@@ -308,7 +313,8 @@ void next_events(ttt_la_s* h, hipEvent_t* eb, hipEvent_t* ee) {
 
 int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
                     float beta, uint32_t mode, const float* S0, const float* M0, void* o, float* S_T, float* M_T,
-                    void* hip_stream, bool timed = true, bool reverse = false) {
+                    void* hip_stream, bool timed = true, bool reverse = false, void* workspace = nullptr) {
+    if (!workspace) workspace = h->workspace;
     ttt::FwdArgs a{};
     a.reverse = reverse;
     a.q = q;
@@ -333,13 +339,13 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     if (h->fast && (h->fp.wide || !state_io)) {
         int nk = 0;
         a.epoch = h->epoch + 1;
-        e = ttt::launch_fast(h->shape, h->fp, h->workspace, a, eb, ee, &nk);
+        e = ttt::launch_fast(h->shape, h->fp, workspace, a, eb, ee, &nk);
         const bool fused_ran = h->fp.fused && !a.bidirectional && !state_io;
         if (e == hipErrorCooperativeLaunchTooLarge && fused_ran) {
             // the fused grid cannot be resident right now: same result in three launches
             ttt::FastPlan p3 = h->fp;
             p3.fused = false;
-            e = ttt::launch_fast(h->shape, p3, h->workspace, a, eb, ee, &nk);
+            e = ttt::launch_fast(h->shape, p3, workspace, a, eb, ee, &nk);
         } else if (e == hipSuccess && fused_ran) {
             h->epoch++;
         }
@@ -358,10 +364,38 @@ bool backward_supported(const ttt_la_desc& d) { return d.phi == TTT_LA_PHI_IDENT
 // one [B, H, T, d] tensor in the handle's dtype
 size_t tensor_bytes(const ttt_la_desc& d) { return (size_t)d.B * d.H * d.T * d.d_v * elem_bytes(d.dtype); }
 
-// causal: q, k, v, dO reversed in time, then the two rate-1 forward outputs;
-// bidirectional: the two forward outputs only
+// The 32x32-tile plans of three launches (decided from the descriptor alone: a
+// single or prefix launch was not asked for) read the time-reversed operands in
+// reverse order themselves.
+bool reversed_in_kernel(const ttt_la_desc& d) {
+    const Shape s = shape_of(d);
+    return d.dtype == TTT_LA_BF16 && ttt::fast_supported(s, d.chunk) && ttt::wide_supported(s) && d.value_split != 2 &&
+           d.launch != TTT_LA_LAUNCH_SINGLE && d.launch != TTT_LA_LAUNCH_PREFIX;
+}
+
+// Workspace of the backward.  Bidirectional: the two forward outputs.  Causal,
+// reversed in the kernels: the two forward outputs, then a segment-summary area
+// for each of the two reversed forwards (they run beside the first one, which uses
+// the handle's).  Causal otherwise: q, k, v, dO reversed in time, then the outputs.
 size_t backward_ws_bytes(const ttt_la_desc& d, uint32_t mode) {
-    return ((mode & TTT_LA_BIDIRECTIONAL) ? 2 : 6) * tensor_bytes(d);
+    if (mode & TTT_LA_BIDIRECTIONAL) return 2 * tensor_bytes(d);
+    if (reversed_in_kernel(d)) {
+        const ttt::FastPlan p = ttt::fast_plan(shape_of(d), d.chunk, d.segments, d.value_split, d.launch);
+        return 2 * tensor_bytes(d) + 2 * p.summary_bytes;
+    }
+    return 6 * tensor_bytes(d);
+}
+
+// streams and events of the concurrent reversed forwards; false if any is missing
+bool ensure_aux(ttt_la_s* h) {
+    if (h->aux_ready) return true;
+    for (int i = 0; i < 2; ++i)
+        if (!h->aux[i] && hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking) != hipSuccess) return false;
+    if (!h->fork && hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess) return false;
+    for (int i = 0; i < 2; ++i)
+        if (!h->join[i] && hipEventCreateWithFlags(&h->join[i], hipEventDisableTiming) != hipSuccess) return false;
+    h->aux_ready = true;
+    return true;
 }
 
 int check_backward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
@@ -428,23 +462,43 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
     const bool bidir = (mode & TTT_LA_BIDIRECTIONAL) != 0;
     const size_t tb = tensor_bytes(h->desc);
     char* ws = static_cast<char*>(workspace);
+    // the 32x32-tile kernels of three launches read and write in reverse time order
+    // themselves; the other plans get reversed copies
+    const bool rev_in_kernel = !bidir && reversed_in_kernel(h->desc);
+    // With in-kernel reversal, u and w (each with its own summary area) run on two
+    // more streams beside dq: they start after everything enqueued so far on
+    // hip_stream, and hip_stream waits for them before the finalize pass (all on
+    // hip_stream if the streams cannot be made).
+    const bool conc = rev_in_kernel && ensure_aux(h);
+    if (conc) {
+        if (hipEventRecord(h->fork, stream) != hipSuccess) return TTT_LA_ERR_HIP;
+        for (int i = 0; i < 2; ++i)
+            if (hipStreamWaitEvent(h->aux[i], h->fork, 0) != hipSuccess) return TTT_LA_ERR_HIP;
+    }
     // dq: the forward with (q, k, v) -> (dO, v, k) and the caller's rates
     st = enqueue_forward(h, dO, v, k, eta, eta_scalar, beta, mode, nullptr, nullptr, dQ, nullptr, nullptr,
                          hip_stream, false);
     if (st != TTT_LA_OK) return st;
     void *U, *W;
-    // the 32x32-tile kernels of three launches read and write in reverse time order
-    // themselves; the other plans get reversed copies
-    const bool rev_in_kernel = !bidir && h->fast && h->fp.wide && !h->fp.fused && !h->fp.prefix;
     if (rev_in_kernel) {
         U = ws;
         W = ws + tb;
+        char* ws_u = ws + 2 * tb;
+        char* ws_w = ws_u + h->fp.summary_bytes;
+        void* su = conc ? static_cast<void*>(h->aux[0]) : hip_stream;
+        void* sw = conc ? static_cast<void*>(h->aux[1]) : hip_stream;
         st = enqueue_forward(h, k, q, dO, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, U, nullptr, nullptr,
-                             hip_stream, false, true);
+                             su, false, true, ws_u);
         if (st != TTT_LA_OK) return st;
         st = enqueue_forward(h, v, dO, q, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, W, nullptr, nullptr,
-                             hip_stream, false, true);
+                             sw, false, true, ws_w);
         if (st != TTT_LA_OK) return st;
+        if (conc) {
+            for (int i = 0; i < 2; ++i) {
+                if (hipEventRecord(h->join[i], h->aux[i]) != hipSuccess) return TTT_LA_ERR_HIP;
+                if (hipStreamWaitEvent(stream, h->join[i], 0) != hipSuccess) return TTT_LA_ERR_HIP;
+            }
+        }
     } else if (!bidir) {
         // rate-1 forwards over the reversed sequence: u from (k, q, dO), w from (v, dO, q)
         char *Rq = ws, *Rk = ws + tb, *Rv = ws + 2 * tb, *RdO = ws + 3 * tb;
@@ -535,6 +589,11 @@ int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const f
 void ttt_la_destroy(ttt_la_t h) {
     if (!h) return;
     release_events(h);
+    for (int i = 0; i < 2; ++i) {
+        if (h->aux[i]) (void)hipStreamDestroy(h->aux[i]);
+        if (h->join[i]) (void)hipEventDestroy(h->join[i]);
+    }
+    if (h->fork) (void)hipEventDestroy(h->fork);
     if (h->workspace) (void)hipFree(h->workspace);
     delete h;
 }
