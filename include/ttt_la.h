@@ -179,12 +179,15 @@ int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const f
  *            least ttt_la_backward_workspace() bytes (may be NULL when that is 0).
  * Identity feature map with d_k == d_v only (TTT_LA_ERR_UNSUPPORTED otherwise).
  * Runs three forwards of the layer on permuted operands (two over the sequence
- * reversed in time) and one or two small kernels, enqueued on hip_stream, no
- * allocation, no synchronisation.  On the bf16 d = 128 plans of three launches
- * the two reversed forwards read their rows in reverse order and run beside the
- * first one on two streams of the handle (created on the first call, default
- * priority), which start after the work already on hip_stream and which
- * hip_stream waits for; their segment summaries live in the workspace.
+ * reversed in time) and one or two small kernels, enqueued on hip_stream; no
+ * device memory is allocated and nothing is synchronised with the host.  On the
+ * bf16 d = 128 plans of three launches the two reversed forwards read their rows
+ * in reverse order and run beside the first one on two streams of the handle,
+ * which start after the work already on hip_stream and which hip_stream waits
+ * for; their segment summaries live in the workspace.  The first such call on a
+ * handle creates those two streams (default priority) and three events; if that
+ * fails, everything runs on hip_stream.  Like the forward, one handle serves one
+ * stream at a time.
  * The outputs must not overlap each other, any input or the workspace.
  * Errors: as ttt_la_forward, and TTT_LA_ERR_INVALID_ARG for a missing, misaligned,
  * overlapping or too small buffer. */
