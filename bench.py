@@ -321,7 +321,7 @@ def run_backward(args, w):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
               f"(the layer shards over (b, h) with no communication)", file=sys.stderr)
         sys.exit(2)
 
