@@ -153,25 +153,66 @@ __global__ void __launch_bounds__(GTHREADS) generic_forward(GenericParams p) {
     const bool causal = !(p.eta_kind & 0x100);   // bit 8 carries the bidirectional flag
     const int eta_kind = p.eta_kind & 0xff;
 
+    // Identity map: the rows of chunk ch + 1 (k, q, this workgroup's v columns, the
+    // rates) are loaded into registers while chunk ch is computed, every load of a
+    // chunk issued before any is waited for.  d_phi = d_k <= 128: at most 8 feature
+    // values of q and of k a thread.
+    constexpr int PL = 8;
+    float rk[PL], rq[PL], rv = 0.0f, re = 0.0f;
+    auto fetch = [&](int ch) {
+        const int t0 = ch * GC;
+        const int n = min(GC, T - t0);
+        const size_t row0 = seq_row0 + t0;
+#pragma unroll
+        for (int u = 0; u < PL; ++u) {
+            const int idx = tid + u * GTHREADS;
+            const int r = idx / d_phi, f = idx - r * d_phi;
+            const bool ok = idx < GC * d_phi && r < n;
+            rk[u] = ok ? load_as_f32(k, (row0 + r) * d_k + f) : 0.0f;
+            rq[u] = ok && causal ? load_as_f32(q, (row0 + r) * d_k + f) : 0.0f;
+        }
+        const int j = tid / GDV, e = tid % GDV;
+        rv = j < n ? load_as_f32(v, (row0 + j) * p.d_v + dv0 + e) : 0.0f;
+        re = tid < n ? eta_at(eta_kind, p.eta, p.eta_scalar, row0 + tid) : 0.0f;
+    };
+    if constexpr (!SWIGLU) {
+        if (n_chunks > 0) fetch(0);
+    }
+
     // ---- pass 1: state updates (causal: interleaved with the readout) -------
     for (int ch = 0; ch < n_chunks; ++ch) {
         const int t0 = ch * GC;
         const int n = min(GC, T - t0);
         const size_t row0 = seq_row0 + t0;
 
-        load_features<TI, SWIGLU>(k, w1, w3, sPk, sXk, row0, n, d_k, d_phi);
-        if (causal) load_features<TI, SWIGLU>(q, w1, w3, sPq, sXq, row0, n, d_k, d_phi);
-        {
-            int j = tid / GDV, e = tid % GDV;
+        float et = 0.0f;
+        if constexpr (SWIGLU) {
+            load_features<TI, SWIGLU>(k, w1, w3, sPk, sXk, row0, n, d_k, d_phi);
+            if (causal) load_features<TI, SWIGLU>(q, w1, w3, sPq, sXq, row0, n, d_k, d_phi);
+            const int j = tid / GDV, e = tid % GDV;
             sV[tid] = j < n ? load_as_f32(v, (row0 + j) * p.d_v + dv0 + e) : 0.0f;
+            et = tid < n ? eta_at(eta_kind, p.eta, p.eta_scalar, row0 + tid) : 0.0f;
+        } else {
+#pragma unroll
+            for (int u = 0; u < PL; ++u) {
+                const int idx = tid + u * GTHREADS;
+                if (idx < GC * d_phi) {
+                    sPk[idx] = rk[u];
+                    if (causal) sPq[idx] = rq[u];
+                }
+            }
+            sV[tid] = rv;
+            et = re;
         }
         if (tid < GC) {
-            float et = tid < n ? eta_at(eta_kind, p.eta, p.eta_scalar, row0 + tid) : 0.0f;
             sEta[tid] = et;
             sWS[tid] = tid < n ? et * sC[n - 1 - tid] : 0.0f;     // eta_j c_{n-1-j}
             sWM[tid] = tid < n ? et * sBP[n - 1 - tid] : 0.0f;    // eta_j beta^{n-1-j}
         }
         __syncthreads();
+        if constexpr (!SWIGLU) {
+            if (ch + 1 < n_chunks) fetch(ch + 1);   // in flight during this chunk
+        }
 
         if (causal) {
             // A_ij = c_{i-j} eta_j phi(q_i).phi(k_j) for j <= i
