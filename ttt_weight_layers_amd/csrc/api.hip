@@ -387,13 +387,20 @@ size_t backward_ws_bytes(const ttt_la_desc& d, uint32_t mode) {
 }
 
 // streams and events of the concurrent reversed forwards; false if any is missing
+// (the failure is cleared from the HIP error state, so that it cannot be reported
+// by a later launch check)
 bool ensure_aux(ttt_la_s* h) {
     if (h->aux_ready) return true;
-    for (int i = 0; i < 2; ++i)
-        if (!h->aux[i] && hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking) != hipSuccess) return false;
-    if (!h->fork && hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess) return false;
-    for (int i = 0; i < 2; ++i)
-        if (!h->join[i] && hipEventCreateWithFlags(&h->join[i], hipEventDisableTiming) != hipSuccess) return false;
+    bool ok = true;
+    for (int i = 0; i < 2 && ok; ++i)
+        if (!h->aux[i] && hipStreamCreateWithFlags(&h->aux[i], hipStreamNonBlocking) != hipSuccess) ok = false;
+    if (ok && !h->fork && hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess) ok = false;
+    for (int i = 0; i < 2 && ok; ++i)
+        if (!h->join[i] && hipEventCreateWithFlags(&h->join[i], hipEventDisableTiming) != hipSuccess) ok = false;
+    if (!ok) {
+        (void)hipGetLastError();
+        return false;
+    }
     h->aux_ready = true;
     return true;
 }
