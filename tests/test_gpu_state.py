@@ -74,6 +74,25 @@ def test_forward_state_wide_tiles(eta_mode, beta, segments):
     assert oracle.rel_err(M_T.cpu().numpy(), M) <= STATE_TOL[w.dtype]
 
 
+def test_forward_state_split_summary():
+    # two segments of 20 chunks on two sequences: segment 0 is summarised in two
+    # halves, the scan starts from the carried state in slot 0
+    w = small("v4_momentum_4x8x2048_d128", B=1, H=2, T=64 * 40 - 13).with_settings(eta_mode="softplus", beta=0.9)
+    say("[state split summary]")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d, segments=2)
+    assert lay.plan().path == 2 and lay.plan().segments == 2
+    S0, M0 = entry_state(w, 9)
+    S_T = dev32(np.zeros_like(S0))
+    M_T = dev32(np.zeros_like(M0))
+    got = forward_state(lay, w, d, dev32(S0), dev32(M0), S_T, M_T)
+    o, S, M = oracle_state(w, x, S0, M0)
+    assert oracle.rel_err(got, o) <= TOL[w.dtype]
+    assert oracle.rel_err(S_T.cpu().numpy(), S) <= STATE_TOL[w.dtype]
+    assert oracle.rel_err(M_T.cpu().numpy(), M) <= STATE_TOL[w.dtype]
+
+
 def test_forward_state_in_place_and_chained():
     # the final state overwrites the entry state; two calls over the halves of a
     # sequence equal one call over all of it

@@ -985,7 +985,7 @@ int wide_fused_capacity() {
 // The scan over n_slots slots per sequence of summaries of seg_len tokens each
 // (slot 0: the carried state when has_init).
 static hipError_t launch_scan(const Shape& s, float* state, int n_slots, int seg_len, const FwdArgs& a, bool mom,
-                       int has_init, hipStream_t st) {
+                              int has_init, hipStream_t st) {
     constexpr int HALF = WNW * WFT * 4 * 64;
     const size_t n_threads = (size_t)s.n_seq() * HALF;
     const float bL = (float)std::pow((double)a.beta, (double)seg_len);
