@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -89,11 +90,34 @@ def algorithmic_flops_per_ht(w, chunk: int) -> int:
     return f
 
 
-def source_hash() -> str:
+def source_hash(kernel: str) -> str:
+    """Hash of the code that compiles into `kernel`: the source file whose
+    __global__ function carries its name, and the headers that file includes,
+    followed through their own includes."""
+    csrc = os.path.dirname(KERNEL_SOURCE)
+    inc = os.path.join(ROOT, "include")
+    base = kernel.split("<")[0]
+    pat = re.compile(r"__global__[^;{]*?\b" + re.escape(base) + r"\s*\(")
+    srcs = [n for n in sorted(os.listdir(csrc)) if n.endswith(".hip")
+            and pat.search(open(os.path.join(csrc, n)).read())]
+    if len(srcs) != 1:
+        return ""
+    todo, seen = [os.path.join(csrc, srcs[0])], []
+    while todo:
+        path = todo.pop()
+        if path in seen:
+            continue
+        seen.append(path)
+        text = open(path).read()
+        for name in re.findall(r'^#include "([^"]+)"', text, re.M):
+            for d in (csrc, inc):
+                if os.path.exists(os.path.join(d, name)):
+                    todo.append(os.path.join(d, name))
+                    break
     h = hashlib.sha256()
-    for name in sorted(os.listdir(os.path.dirname(KERNEL_SOURCE))):
-        with open(os.path.join(os.path.dirname(KERNEL_SOURCE), name), "rb") as f:
-            h.update(name.encode())
+    for path in sorted(seen):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -107,7 +131,7 @@ def measured_traffic(workload: str, kernel: str):
     except (OSError, ValueError):
         return None
     e = t.get(workload)
-    if not e or e.get("source_hash") != source_hash() or e.get("kernel") != kernel:
+    if not e or e.get("source_hash") != source_hash(kernel) or e.get("kernel") != kernel:
         return None
     return e.get("bytes_per_launch")
 
@@ -427,7 +451,7 @@ def main():
     elif plan.path == 1:
         roof["kernel"] = "chunk_kernel<BIDIR>" if not w.causal else "chunk_kernel<OUTPUT>"
     else:
-        roof["kernel"] = "generic_kernel"
+        roof["kernel"] = "generic_forward"
     roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     roof["kernel_ms"] = round(k_avg_ms, 5)
 

@@ -173,7 +173,7 @@ def test_two_segments_with_split_summary(eta_mode, beta):
     plan = lay.plan()
     assert plan.path == 2 and plan.segments == 2
     got = run_gpu(w, d, layer=lay)
-    assert lay.plan().n_kernels == 2
+    assert lay.plan().n_kernels == 3
     ref = run_oracle(w, x)
     assert oracle.rel_err(got, ref) <= TOL[w.dtype]
 

@@ -619,7 +619,8 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
         plan->phi_split = h->fp.phi_split;
         plan->grid_main = s.n_seq() * h->fp.dv_split * h->fp.phi_split * h->fp.segments;
         plan->n_kernels = (h->fp.fused || h->fp.prefix) ? 1
-                                      : 1 + (h->fp.segments > 1 ? 1 : 0) + (h->fp.segments > 2 ? 1 : 0) +
+                                      : 1 + (h->fp.segments > 1 ? 1 : 0) +
+                                            (h->fp.segments > 2 || h->fp.sum_split == 2 ? 1 : 0) +
                                             (h->fp.phi_split > 1 ? 1 : 0);
     } else {
         plan->path = 0;
