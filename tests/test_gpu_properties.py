@@ -115,6 +115,18 @@ def test_bidirectional_with_rates_and_momentum(eta_mode, beta):
     assert oracle.rel_err(got, run_oracle(w, x)) <= TOL[w.dtype]
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 129, 256, 257, 700])
+@pytest.mark.parametrize("eta_mode,beta", [("scalar", 0.0), ("softplus", 0.5)])
+def test_bidirectional_lengths(T, eta_mode, beta):
+    # d = 64: up to 256 tokens every load of a sequence is issued at once (rows past
+    # the end are zeroed when staged); longer sequences stream chunk by chunk
+    w = small("bidir_vit_256x6x196_d64", B=1, H=3, T=T).with_settings(eta_mode=eta_mode, beta=beta)
+    say(f"[bidir lengths] T={T} {eta_mode} beta={beta}")
+    x = make_inputs(w)
+    got = run_gpu(w, to_device(x))
+    assert oracle.rel_err(got, run_oracle(w, x)) <= TOL[w.dtype]
+
+
 @pytest.mark.parametrize("eta_mode", ["scalar", "softplus"])
 @pytest.mark.parametrize("beta", [0.0, 0.9])
 def test_bidirectional_wide_tiles(eta_mode, beta):

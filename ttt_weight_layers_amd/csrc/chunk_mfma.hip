@@ -114,6 +114,20 @@ struct Lds {
     // floats: 2 x (eta, eta/(1-beta), eta beta^{n-1-j}) [CH each], c[CH+1], beta^r[CH+1]
     static constexpr int N_F32 = 6 * CH + 2 * (CH + 1);
     static constexpr int BYTES = 2 * N_BF16 + 4 * N_F32;
+    // The bidirectional kernel stages k (pass 0) and q (pass 1) in the same place,
+    // never both at once, and has no score tiles: its floats follow the staged tiles.
+    static constexpr int stage(bool bidir) { return bidir ? TX + TV : STAGE; }
+    static constexpr int off_phi(bool bidir) { return 2 * stage(bidir); }
+    static constexpr int n_bf16(bool bidir) { return bidir ? off_phi(true) + (SWIGLU ? 2 * CH * D : 0) : N_BF16; }
+    static constexpr int bytes(bool bidir) { return 2 * n_bf16(bidir) + 4 * N_F32; }
+    // workgroups that share a CU (160 KiB of LDS): three for the d = 64
+    // bidirectional kernel without momentum (its registers fit in 168 a lane; four
+    // would leave 128 and spill), otherwise up to two
+    static constexpr int per_cu(bool bidir, bool mom) {
+        constexpr int lds = 160 * 1024;
+        const bool small = bidir && !mom && D == 64 && !SWIGLU;
+        return (small && 3 * bytes(true) <= lds) ? 3 : 2 * bytes(bidir) <= lds ? 2 : 1;
+    }
 };
 
 // Global -> register prefetch of one chunk: each thread owns 16-byte pieces of
@@ -132,7 +146,7 @@ struct Prefetch {
 // width of the layer; DV / (16 NW DVT) workgroups share one sequence segment.
 // ETAV: the step size varies per token (otherwise it is the scalar eta).
 template <int D, int DK, int DV, int NW, int DVT, bool MOM, bool ETAV, bool SWIGLU, int KIND>
-__global__ void __launch_bounds__(NW * 64, (NW == 4 && 2 * Lds<D, DK, NW, SWIGLU>::BYTES <= 160 * 1024) ? 2 : 1)
+__global__ void __launch_bounds__(NW * 64, (NW == 4 ? Lds<D, DK, NW, SWIGLU>::per_cu(KIND == K_BIDIR, MOM) : 1))
 chunk_kernel(ChunkParams p) {
     static_assert(DVT == 1, "one 16-column value tile per wave");
     using L = Lds<D, DK, NW, SWIGLU>;
@@ -144,20 +158,23 @@ chunk_kernel(ChunkParams p) {
     constexpr int NI = CH / 16;           // token blocks per chunk
     constexpr int NJS = CH / 32;          // contraction steps over tokens
 
-    __shared__ __attribute__((aligned(16))) uint16_t smem16[L::N_BF16 + 2 * L::N_F32];
-    float* sF = reinterpret_cast<float*>(smem16 + L::N_BF16);
+    constexpr bool BI = KIND == K_BIDIR;
+    constexpr int NB16 = L::n_bf16(BI);
+    __shared__ __attribute__((aligned(16))) uint16_t smem16[NB16 + 2 * L::N_F32];
+    float* sF = reinterpret_cast<float*>(smem16 + NB16);
     float* sC = sF + 6 * CH;        // c_r, r = 0..CH
     float* sBP = sC + CH + 1;       // beta^r, r = 0..CH
-    auto stage_x = [&](int buf) { return smem16 + buf * L::STAGE; };
-    auto stage_y = [&](int buf) { return smem16 + buf * L::STAGE + L::TX; };
-    auto stage_v = [&](int buf) { return smem16 + buf * L::STAGE + 2 * L::TX; };
+    constexpr int STG = L::stage(BI);
+    auto stage_x = [&](int buf) { return smem16 + buf * STG; };
+    auto stage_y = [&](int buf) { return smem16 + buf * STG + (BI ? 0 : L::TX); };
+    auto stage_v = [&](int buf) { return smem16 + buf * STG + (BI ? 1 : 2) * L::TX; };
     auto tile_a = [&](int buf) { return smem16 + L::OFF_A + buf * CH * CH; };
     auto s_eta = [&](int buf) { return sF + buf * 3 * CH; };
     auto s_wt = [&](int buf) { return sF + buf * 3 * CH + CH; };    // eta_j / (1 - beta)
     auto s_wm = [&](int buf) { return sF + buf * 3 * CH + 2 * CH; }; // eta_j beta^{n-1-j}
     // feature rows read by the contractions: the staged rows (identity) or phi (SwiGLU)
-    auto tile_q = [&](int buf) { return SWIGLU ? smem16 + L::OFF_PHI : stage_x(buf); };
-    auto tile_k = [&](int buf) { return SWIGLU ? smem16 + L::OFF_PHI + CH * D : stage_y(buf); };
+    auto tile_q = [&](int buf) { return SWIGLU ? smem16 + L::off_phi(BI) : stage_x(buf); };
+    auto tile_k = [&](int buf) { return SWIGLU ? smem16 + L::off_phi(BI) + CH * D : stage_y(buf); };
 
     // ---- unit of work (XCD-aware: consecutive units land on one XCD) --------
     const int G = gridDim.x;
@@ -521,7 +538,94 @@ chunk_kernel(ChunkParams p) {
             for (int ft = 0; ft < NFT; ++ft) dst[SLICE_F4 + ((size_t)wave * NFT + ft) * 64 + lane] = M[ft];
         }
     } else {
-        // bidirectional: pass 0 accumulates the state over all tokens ...
+        // bidirectional: pass 0 accumulates the state over all tokens, then every
+        // query reads the final S = t_scale T - kappa M
+        const float kappa = beta * inv1mb;
+        auto final_state = [&]() {
+#pragma unroll
+            for (int ft = 0; ft < NFT; ++ft)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = St[ft][r] * t_scale;
+                    if constexpr (MOM) v = fmaf(-kappa, M[ft][r], v);
+                    St[ft][r] = v;
+                }
+        };
+        // d = 64 sequences of at most NCB chunks (a ViT's patch rows): the loads of
+        // the whole sequence are in flight together, 64 registers a thread.  The
+        // loads take no branch (rows past the end read the last row and are zeroed
+        // when staged), so that none of them waits for another.
+        constexpr int NCB = 4;
+        if constexpr (D == 64 && !SWIGLU) {
+            if (t_end > 0 && t_end <= NCB * CH) {
+                const size_t last = seq_row + t_end - 1;
+                auto fetch_rows = [&](PF& f, int t0, bool kv) {
+                    if (kv) f.eta = ETAV ? p.eta[min(seq_row + t0 + tid, last)] : p.eta_scalar;
+#pragma unroll
+                    for (int i = 0; i < PF::PX; ++i) {
+                        const int idx = tid + i * NT;
+                        const size_t off = min(seq_row + t0 + idx / XCH, last) * WX + 8 * (idx % XCH);
+                        if (kv) f.y[i] = *reinterpret_cast<const u32x4*>(p.k + off);
+                        else f.x[i] = *reinterpret_cast<const u32x4*>(p.q + off);
+                    }
+                    if (kv) {
+#pragma unroll
+                        for (int i = 0; i < PF::PV; ++i) {
+                            const int idx = tid + i * NT;
+                            const size_t off = min(seq_row + t0 + idx / VCH, last) * DV + dv_base + 8 * (idx % VCH);
+                            f.v[i] = *reinterpret_cast<const u32x4*>(p.v + off);
+                        }
+                    }
+                };
+                // stages rows below n, zeros in the rest
+                auto commit_rows = [&](const PF& f, int buf, int n, bool kv) {
+                    PF m;
+                    m.eta = f.eta;
+#pragma unroll
+                    for (int i = 0; i < PF::PX; ++i) {
+                        const bool in = (tid + i * NT) / XCH < n;
+                        m.x[i] = (!kv && in) ? f.x[i] : u32x4{0u, 0u, 0u, 0u};
+                        m.y[i] = (kv && in) ? f.y[i] : u32x4{0u, 0u, 0u, 0u};
+                    }
+#pragma unroll
+                    for (int i = 0; i < PF::PV; ++i)
+                        m.v[i] = (kv && (tid + i * NT) / VCH < n) ? f.v[i] : u32x4{0u, 0u, 0u, 0u};
+                    commit(m, buf, n, !kv, kv, kv, kv);
+                };
+                // k and v of every chunk first; the q loads of a chunk go out once
+                // its k and v are staged, into the registers they leave
+                PF pk[NCB], pq[NCB];
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) fetch_rows(pk[c], c * CH, true);
+                int buf = 0;
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) {
+                    const int n = min(CH, t_end - c * CH);
+                    if (n <= 0) break;
+                    commit_rows(pk[c], buf, n, true);
+                    fetch_rows(pq[c], c * CH, false);
+                    __syncthreads();
+                    read_vt(buf);
+                    update(buf, n);
+                    buf ^= 1;
+                }
+                final_state();
+                __syncthreads();
+                buf = 0;
+#pragma unroll
+                for (int c = 0; c < NCB; ++c) {
+                    const int n = min(CH, t_end - c * CH);
+                    if (n <= 0) break;
+                    commit_rows(pq[c], buf, n, false);
+                    __syncthreads();
+                    readout(buf, 1.0f, false);
+#pragma unroll
+                    for (int I = 0; I < NI; ++I) store(oacc[I], I, n, seq_row + c * CH);
+                    buf ^= 1;
+                }
+                return;
+            }
+        }
         PF pf;
         fetch(pf, 0, false, true, true, true);
         int buf = 0;
@@ -529,7 +633,9 @@ chunk_kernel(ChunkParams p) {
             const int n = min(CH, t_end - t0);
             commit(pf, buf, n, false, true, true, true);
             __syncthreads();
+            // the next chunk's k and v; during the last chunk the first chunk's q
             if (t0 + CH < t_end) fetch(pf, t0 + CH, false, true, true, true);
+            else fetch(pf, 0, true, false, false, false);
             if constexpr (SWIGLU) {
                 features(buf, false, true);
                 lds_barrier();
@@ -538,18 +644,8 @@ chunk_kernel(ChunkParams p) {
             update(buf, n);
             buf ^= 1;
         }
-        // ... then every query reads the final S = t_scale T - kappa M
-        const float kappa = beta * inv1mb;
-#pragma unroll
-        for (int ft = 0; ft < NFT; ++ft)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = St[ft][r] * t_scale;
-                if constexpr (MOM) v = fmaf(-kappa, M[ft][r], v);
-                St[ft][r] = v;
-            }
+        final_state();
         __syncthreads();
-        fetch(pf, 0, true, false, false, false);
         buf = 0;
         for (int t0 = 0; t0 < t_end; t0 += CH) {
             const int n = min(CH, t_end - t0);
