@@ -1,0 +1,77 @@
+"""Seeded sweep over the forward's plan space against the oracle: widths, the
+feature map, ragged lengths, the step-size modes, momentum, causal and
+bidirectional passes, and the plan overrides (segments, value split, launch
+mode).  The case list is drawn once from a fixed seed, so every run checks the
+same cases, and each case's id names its settings."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from ttt_workloads import WORKLOADS, make_inputs
+from _gpu import TOL, make_layer, run_gpu, run_oracle, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=120, seed=20261203):
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        kind = rng.choice(["wide", "wide", "tile", "swiglu", "f32"])
+        c = dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), T=int(rng.integers(1, 900)),
+                 eta_mode=str(rng.choice(["scalar", "per_token", "softplus"])),
+                 beta=float(rng.choice([0.0, 0.5, 0.9, 0.99])), causal=bool(rng.random() < 0.8),
+                 segments=0, value_split=0, launch="auto")
+        if kind == "wide":
+            # d_k = d_v = 128, identity map, bf16: the 32x32-tile kernels
+            c.update(base="v4_momentum_4x8x2048_d128", d_k=128, d_v=128, d_phi=128, phi="identity")
+            c["segments"] = int(rng.choice([0, 1, 2, 3, 4, 8]))
+            if c["causal"]:
+                c["launch"] = str(rng.choice(["auto", "separate", "single", "prefix"]))
+        elif kind == "tile":
+            # the 16x16-tile kernels: d = 64, mixed widths, or a split value width
+            d_k, d_v = [int(x) for x in rng.choice([64, 128], size=2)]
+            c.update(base="bidir_vit_256x6x196_d64", d_k=d_k, d_v=d_v, d_phi=d_k, phi="identity")
+            if d_k == 128 and d_v == 128:
+                c["value_split"] = 2
+            c["segments"] = int(rng.choice([0, 1, 2, 3]))
+        elif kind == "swiglu":
+            d_k, d_v = [int(x) for x in rng.choice([64, 128], size=2)]
+            c.update(base="v2_swiglu_4x16x8192_d128_f512", d_k=d_k, d_v=d_v,
+                     d_phi=int(rng.choice([128, 256])), phi="swiglu", T=int(rng.integers(1, 400)))
+        else:
+            c.update(base="v5_f32_1x1x256_d64", d_k=64, d_v=64, d_phi=64, phi="identity",
+                     T=int(rng.integers(1, 300)))
+        if not c["causal"]:
+            c["segments"] = 0
+            c["launch"] = "auto"
+        cases.append(c)
+    return cases
+
+
+CASES = _cases()
+
+
+def _id(c):
+    return (f"{WORKLOADS[c['base']].dtype}_{c['phi'][:2]}{c['d_k']}x{c['d_v']}f{c['d_phi']}_{c['B']}x{c['H']}x{c['T']}"
+            f"_{c['eta_mode'][:4]}"
+            f"_b{c['beta']}_{'c' if c['causal'] else 'bi'}_s{c['segments']}_v{c['value_split']}_{c['launch']}")
+
+
+@pytest.mark.parametrize("c", CASES, ids=[_id(c) for c in CASES])
+def test_sweep(c):
+    base = WORKLOADS[c["base"]]
+    w = base.with_shape(B=c["B"], H=c["H"], T=c["T"]).with_settings(
+        d_k=c["d_k"], d_v=c["d_v"], d_phi=c["d_phi"], phi=c["phi"], eta_mode=c["eta_mode"], beta=c["beta"],
+        causal=c["causal"], eta_scalar=0.3 if c["eta_mode"] == "scalar" else base.eta_scalar)
+    print(f"[sweep] {_id(c)}", flush=True)
+    sys.stdout.flush()
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d, segments=c["segments"], value_split=c["value_split"], launch=c["launch"])
+    got = run_gpu(w, d, layer=lay)
+    if c["launch"] == "single":
+        assert lay.wait_failed() == 0
+    assert oracle.rel_err(got, run_oracle(w, x)) <= TOL[w.dtype]
