@@ -117,3 +117,36 @@ def test_backward_unsupported_for_swiglu():
     with pytest.raises(tla.TTTError) as e:
         lay.backward(d["q"], d["k"], d["v"], dO, eta=d["a"], eta_mode="softplus", beta=0.9)
     assert e.value.status == tla.TTT_LA_ERR_UNSUPPORTED
+
+
+def _backward_cases(n=40, seed=20261206):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        kind = str(rng.choice(["wide", "wide", "d64", "f32"]))
+        c = dict(kind=kind, B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)),
+                 T=int(rng.integers(1, 500 if kind != "f32" else 150)),
+                 eta_mode=str(rng.choice(["scalar", "per_token", "softplus"])),
+                 beta=float(rng.choice([0.0, 0.5, 0.9])), causal=bool(rng.random() < 0.75),
+                 segments=int(rng.choice([0, 1, 2, 3])) if kind != "f32" else 0, launch="auto")
+        if kind == "wide" and c["causal"]:
+            c["launch"] = str(rng.choice(["auto", "auto", "separate", "single", "prefix"]))
+        cases.append(c)
+    return cases
+
+
+BACKWARD_CASES = _backward_cases()
+
+
+@pytest.mark.parametrize("c", BACKWARD_CASES, ids=[
+    f"{c['kind']}_{c['B']}x{c['H']}x{c['T']}_{c['eta_mode'][:4]}_b{c['beta']}_{'c' if c['causal'] else 'bi'}"
+    f"_s{c['segments']}_{c['launch']}" for c in BACKWARD_CASES])
+def test_backward_sweep(c):
+    # seeded sweep of shapes, modes and plans (the case list is drawn once from a fixed seed)
+    base = {"wide": "v4_momentum_4x8x2048_d128", "d64": "bidir_vit_256x6x196_d64",
+            "f32": "v5_f32_1x1x256_d64"}[c["kind"]]
+    w = small(base, B=c["B"], H=c["H"], T=c["T"]).with_settings(
+        eta_mode=c["eta_mode"], beta=c["beta"], causal=c["causal"],
+        eta_scalar=0.3 if c["eta_mode"] == "scalar" else WORKLOADS[base].eta_scalar)
+    say(f"[backward sweep] {c}")
+    run_case(w, c["segments"], launch=c["launch"])
