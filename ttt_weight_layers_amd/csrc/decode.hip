@@ -132,16 +132,29 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
         const uint16_t* w3 = static_cast<const uint16_t*>(p.w3) + (size_t)h * d_phi * d_k;
         const int j = lane & 31, kh = lane >> 5;
         const uint16_t* xrow = j == 0 ? q : k;
+        // k-steps of 16 (d_k is 64 or 128).  The operands of every step are requested
+        // before the first product, with no branch around a load (a branch made the
+        // compiler wait for each load in turn): steps past d_k re-read the last
+        // step, and their B column is zeroed
+        constexpr int KS = 8;
+        const int ks = d_k / 16;
         for (int f0 = 32 * wave; f0 < d_phi; f0 += 4 * 32) {
+            u32x4 a1[KS], a3[KS], b[KS];
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const int k0 = 16 * min(st, ks - 1) + 8 * kh;
+                a1[st] = *reinterpret_cast<const u32x4*>(w1 + (size_t)(f0 + j) * d_k + k0);
+                a3[st] = *reinterpret_cast<const u32x4*>(w3 + (size_t)(f0 + j) * d_k + k0);
+                b[st] = *reinterpret_cast<const u32x4*>(xrow + k0);
+            }
             f32x16 u1 = {}, u3 = {};
-            for (int k0 = 0; k0 < d_k; k0 += 16) {
-                const u32x4 a1 = *reinterpret_cast<const u32x4*>(w1 + (size_t)(f0 + j) * d_k + k0 + 8 * kh);
-                const u32x4 a3 = *reinterpret_cast<const u32x4*>(w3 + (size_t)(f0 + j) * d_k + k0 + 8 * kh);
-                const u32x4 b = j < 2 ? *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * kh) : u32x4{0u, 0u, 0u, 0u};
-                u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1),
-                                                             __builtin_bit_cast(bf16x8, b), u1, 0, 0, 0);
-                u3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a3),
-                                                             __builtin_bit_cast(bf16x8, b), u3, 0, 0, 0);
+#pragma unroll
+            for (int st = 0; st < KS; ++st) {
+                const u32x4 bs = (j < 2 && st < ks) ? b[st] : u32x4{0u, 0u, 0u, 0u};
+                u1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a1[st]),
+                                                             __builtin_bit_cast(bf16x8, bs), u1, 0, 0, 0);
+                u3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a3[st]),
+                                                             __builtin_bit_cast(bf16x8, bs), u3, 0, 0, 0);
             }
             if (j < 2) {
                 float* dst = j == 0 ? sPq : sPk;
