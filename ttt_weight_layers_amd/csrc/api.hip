@@ -21,7 +21,6 @@ struct ttt_la_s {
     void* workspace;
     size_t workspace_bytes;
     int device;
-    int n_kernels;
     unsigned epoch;      // completed launches of the fused path (its counter targets)
     // measurement hook
     std::vector<hipEvent_t> ev_begin, ev_end;
@@ -261,7 +260,6 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     h->seen = 0;
     h->epoch = 0;
     h->fast = desc->dtype == TTT_LA_BF16 && ttt::fast_supported(h->shape, desc->chunk);
-    h->n_kernels = 1;
     if (h->fast) {
         h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments, desc->value_split, desc->launch);
         h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes + h->fp.zero_bytes;
@@ -337,24 +335,21 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     if (timed) next_events(h, &eb, &ee);
     hipError_t e;
     if (h->fast && (h->fp.wide || !state_io)) {
-        int nk = 0;
         a.epoch = h->epoch + 1;
-        e = ttt::launch_fast(h->shape, h->fp, workspace, a, eb, ee, &nk);
+        e = ttt::launch_fast(h->shape, h->fp, workspace, a, eb, ee, nullptr);
         const bool fused_ran = h->fp.fused && !a.bidirectional && !state_io;
         if (e == hipErrorCooperativeLaunchTooLarge && fused_ran) {
             // the fused grid cannot be resident right now: same result in three launches
             ttt::FastPlan p3 = h->fp;
             p3.fused = false;
-            e = ttt::launch_fast(h->shape, p3, workspace, a, eb, ee, &nk);
+            e = ttt::launch_fast(h->shape, p3, workspace, a, eb, ee, nullptr);
         } else if (e == hipSuccess && fused_ran) {
             h->epoch++;
         }
-        h->n_kernels = nk;
     } else {
         // fp32 inputs, and the carried-state calls of the 16x16-tile shapes
         if (reverse) return TTT_LA_ERR_INVALID_ARG;
         e = ttt::launch_generic(h->shape, a, eb, ee);
-        h->n_kernels = 1;
     }
     return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
