@@ -1,0 +1,73 @@
+"""The causal forward at the largest supported size, B * H * T * d just below
+2^31 elements (one sequence of 2^24 - 37 tokens, d = 128: 4 GiB per bf16
+tensor), checked on sampled outputs against a closed form.
+
+With q = k = e_0 every score phi(k_s) . phi(q_t) is exactly 1, so column j of
+the output is the heavy-ball recurrence of column j of v alone:
+    m_t = beta m_{t-1} + eta v_t[j],   s_t = s_{t-1} + m_t,   o_t[j] = s_t
+(the update rule and readout of the layer with a unit key and query), which an
+IIR filter and a cumulative sum give exactly in fp64 over the whole sequence.
+v repeats with period 5 in t: columns below 64 have zero mean (the state stays
+small, so rounding is small next to every entry and the check is strict),
+columns from 64 on have mean 1 (the state grows with t, so an entry state lost
+at a segment boundary shows as an error of the size of the whole prefix)."""
+import sys
+
+import numpy as np
+import pytest
+from scipy.signal import lfilter
+
+import oracle
+from _gpu import TOL
+
+pytestmark = pytest.mark.gpu
+
+T_MAX = (1 << 24) - 37            # 128 T < 2^31
+COLS = [0, 5, 63, 64, 100, 127]
+
+
+def v_block():
+    r = np.arange(5)[:, None]
+    j = np.arange(128)[None, :]
+    return ((7 * r + j) % 5) - 2 + (j >= 64)
+
+
+def expected(t_rows, eta, beta):
+    t = np.arange(T_MAX)
+    out = np.empty((len(t_rows), len(COLS)))
+    for c, j in enumerate(COLS):
+        vj = (((7 * t + j) % 5) - 2 + (j >= 64)).astype(np.float64)
+        s = np.cumsum(lfilter([eta], [1.0, -beta], vj))
+        out[:, c] = s[t_rows]
+    return out
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.9])
+def test_forward_at_maximum_size(beta):
+    import torch
+    import ttt_weight_layers_amd as tla
+    eta = 0.1
+    print(f"[max size] T={T_MAX} beta={beta}", flush=True)
+    sys.stdout.flush()
+    qk = torch.zeros((1, 1, T_MAX, 128), dtype=torch.bfloat16, device="cuda")
+    qk[..., 0] = 1.0
+    blk = torch.from_numpy(v_block()).to(torch.bfloat16)
+    v = blk.to("cuda").repeat((T_MAX + 4) // 5, 1)[:T_MAX].reshape(1, 1, T_MAX, 128).contiguous()
+    lay = tla.TTTLinearAttention(1, 1, T_MAX, 128, 128, 128, dtype="bf16")
+    plan = lay.plan()
+    assert plan.path == 2
+    o = lay.forward(qk, qk, v, eta_scalar=eta, beta=beta, eta_mode="scalar", causal=True)
+    torch.cuda.synchronize()
+    # rows: both ends, both sides of every segment boundary, and a seeded sample
+    rng = np.random.default_rng(31)
+    rows = [np.arange(256), np.arange(T_MAX - 256, T_MAX), rng.integers(0, T_MAX, 4096)]
+    for b in range(plan.seg_len, T_MAX, plan.seg_len):
+        rows.append(np.arange(b - 70, min(b + 70, T_MAX)))
+    rows = np.unique(np.concatenate(rows))
+    idx = torch.from_numpy(rows).to("cuda")
+    got = o[0, 0].index_select(0, idx)[:, COLS].float().cpu().numpy().astype(np.float64)
+    want = expected(rows, eta, beta)
+    zero_mean = [c for c, j in enumerate(COLS) if j < 64]
+    drift = [c for c, j in enumerate(COLS) if j >= 64]
+    assert oracle.rel_err(got[:, zero_mean], want[:, zero_mean]) <= TOL["bf16"]
+    assert oracle.rel_err(got[:, drift], want[:, drift]) <= TOL["bf16"]
