@@ -71,3 +71,44 @@ def test_forward_at_maximum_size(beta):
     drift = [c for c, j in enumerate(COLS) if j >= 64]
     assert oracle.rel_err(got[:, zero_mean], want[:, zero_mean]) <= TOL["bf16"]
     assert oracle.rel_err(got[:, drift], want[:, drift]) <= TOL["bf16"]
+
+
+def bidir_expected(phase, T, eta, beta, cols):
+    """o_t[j] = s_{T-1}[j] for every t: the recurrence over the whole sequence,
+    rows starting at `phase` of the period-5 pattern (columns >= 32 drift)."""
+    r = phase + np.arange(T)
+    out = []
+    for j in cols:
+        vj = (((7 * r + j) % 5) - 2 + (j >= 32)).astype(np.float64)
+        out.append(np.cumsum(lfilter([eta], [1.0, -beta], vj))[-1])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5])
+def test_bidirectional_at_maximum_size(beta):
+    # 171000 sequences of 196 tokens, d = 64: 2.145e9 elements a tensor (< 2^31)
+    import torch
+    import ttt_weight_layers_amd as tla
+    B, H, T, eta = 171, 1000, 196, 0.1
+    print(f"[max size bidir] {B}x{H}x{T} beta={beta}", flush=True)
+    sys.stdout.flush()
+    n_rows = B * H * T
+    qk = torch.zeros((B, H, T, 64), dtype=torch.bfloat16, device="cuda")
+    qk[..., 0] = 1.0
+    r = np.arange(5)[:, None]
+    j = np.arange(64)[None, :]
+    blk = torch.from_numpy(((7 * r + j) % 5) - 2 + (j >= 32)).to(torch.bfloat16).to("cuda")
+    v = blk.repeat((n_rows + 4) // 5, 1)[:n_rows].reshape(B, H, T, 64).contiguous()
+    lay = tla.TTTLinearAttention(B, H, T, 64, 64, 64, dtype="bf16")
+    o = lay.forward(qk, qk, v, eta_scalar=eta, beta=beta, eta_mode="scalar", causal=False)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(32)
+    seqs = np.unique(np.concatenate([[0, 1, B * H - 2, B * H - 1], rng.integers(0, B * H, 60)]))
+    cols = [0, 7, 31, 32, 50, 63]
+    flat = o.view(B * H, T, 64)
+    got = flat.index_select(0, torch.from_numpy(seqs).to("cuda"))[:, :, cols].float().cpu().numpy()
+    # sequence n starts at row 196 n, phase (196 n) mod 5 = n mod 5
+    want = np.stack([np.broadcast_to(bidir_expected(int(n % 5), T, eta, beta, cols), (T, len(cols)))
+                     for n in seqs])
+    assert oracle.rel_err(got[..., :3].astype(np.float64), want[..., :3]) <= TOL["bf16"]
+    assert oracle.rel_err(got[..., 3:].astype(np.float64), want[..., 3:]) <= TOL["bf16"]
