@@ -4,16 +4,20 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 One step = one full forward of the layer (every kernel of the chunked path:
-segment summaries, segment scan, output pass) over one batch of seeded
-synthetic q, k, v already resident in HBM.  The default workload is the
-momentum variant at B=4, H=8, T=2048, d=128, bf16 (Variant 4 of the ablation
-on the thelatestinai.com page, Table 2).  Input sets are rotated so that the
-working set of the timed loop exceeds the 256 MB last-level cache.
+segment summaries, segment scan, output pass; the SwiGLU feature map where the
+workload has it) over one batch of seeded synthetic q, k, v already resident in
+HBM.  Without --workload every workload of DEFAULT_ORDER is run in turn and
+prints its own JSON line; the last line is the Variant 2 SwiGLU workload
+(B=4, H=16, T=8192, d=128 -> 512 features: the most work per step and the only
+one bound by the matrix cores; thelatestinai.com page, Table 2).  Input sets are
+rotated so that the working set of the timed loop exceeds the 256 MB
+last-level cache.
 
-Prints one JSON line with tokens/s (tokens = B*T positions), the roofline
-fraction of the dominant kernel (its duration measured with HIP events on the
-stream it runs on, during the timed loop) and the CPU oracle's tokens/s on a
-bounded sample of the same workload.
+Each line carries tokens/s (tokens = B*T positions), the roofline of the
+dominant kernel (its duration measured with HIP events on the stream it runs
+on, during the timed loop) and of the whole step (algorithmic work / time per
+step), and the CPU oracle's tokens/s on a bounded sample of the same workload,
+timed over worker processes forked before the first GPU call.
 """
 from __future__ import annotations
 
@@ -33,6 +37,7 @@ METRIC = "TTT-layer fwd tokens/sec (1 GPU) + % MFMA/HBM roofline, Variants 2–5
 DEFAULT_WORKLOAD = "v4_momentum_4x8x2048_d128"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2516.6   # dense bf16, 256 CU x 2.4 GHz x 4096 flop/clk
+F32_PEAK_TFLOPS = 157.3          # fp32 vector (and matrix) peak
 # The output kernel of one timed step in TIMING_EVERY carries a pair of HIP events:
 # an event pair costs the stream a little time of its own, which would otherwise
 # show up in every step of the throughput figure.
@@ -52,11 +57,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--workload", default=None,
+                    help="one workload (default: every workload of DEFAULT_ORDER, one line each, "
+                         "the SwiGLU case last)")
     ap.add_argument("--segments", type=int, default=0, help="plan override: sequence segments (0 = auto)")
     ap.add_argument("--value-split", type=int, default=0, help="plan override: workgroups per value width")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample duration")
     ap.add_argument("--launch", default="auto", choices=["auto", "separate", "single", "prefix"],
                     help="how a segmented causal forward is launched")
     ap.add_argument("--decode", action="store_true",
@@ -136,47 +142,103 @@ def measured_traffic(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, seconds: float):
-    """Times the fp64 oracle on a bounded sample: a few heads at full length."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+# Workloads of the default run, in the order their lines are printed: the
+# Variant 2 SwiGLU case, the one bound by the matrix cores and the most work per
+# step, comes last.
+DEFAULT_ORDER = (
+    "v5_f32_1x1x256_d64",
+    "v4_momentum_4x8x2048_d128",
+    "v3_softplus_8x16x4096_d128",
+    "v5_long_1x16x65536_d128",
+    "v3_long_1x16x65536_d128",
+    "bidir_vit_256x6x196_d64",
+    "v2_swiglu_4x16x8192_d128_f512",
+)
+# Worker processes of the oracle timing: the host cores this process may use,
+# at most 16 (the CPU share of one GPU).
+MAX_ORACLE_WORKERS = 16
 
+
+def oracle_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_ORACLE_WORKERS, n))
+
+
+def make_oracle_pool(n: int):
+    """A pool of n forked worker processes.  Created before the first GPU call
+    of the process (a child forked after it would share the parent's device
+    state); each worker runs the oracle with one BLAS thread."""
+    import multiprocessing as mp
+    return mp.get_context("fork").Pool(processes=n, initializer=_oracle_worker_init)
+
+
+def _oracle_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(limits=1)
+    except Exception:
+        pass
+
+
+def _oracle_task(task):
+    """One sampled sequence in a worker: (workload, q, k, v, a, w1, w3) fp64
+    slices of one (b, h) -> (o [1, 1, T, d_v], seconds)."""
     import oracle
-    # one head first to size the sample
-    with threadpool_limits(limits=1):
-        def run(heads):
-            bs = [h // w.H for h in heads]
-            hs = [h % w.H for h in heads]
-            q = x.q64[bs, hs][:, None]
-            k = x.k64[bs, hs][:, None]
-            v = x.v64[bs, hs][:, None]
-            a = None if x.a32 is None else x.a32[bs, hs][:, None]
-            t0 = time.perf_counter()
-            if w.phi == "swiglu":
-                outs = [oracle.forward(q[i:i + 1], k[i:i + 1], v[i:i + 1], eta_mode=w.eta_mode,
-                                       eta=None if a is None else a[i:i + 1], eta_scalar=w.eta_scalar,
-                                       beta=w.beta, causal=w.causal, phi=w.phi,
-                                       w1=x.w1_64[h:h + 1], w3=x.w3_64[h:h + 1])
-                        for i, h in enumerate(hs)]
-                o = np.concatenate(outs)
-            else:
-                o = oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar,
-                                   beta=w.beta, causal=w.causal)
-            return o, time.perf_counter() - t0
+    w, q, k, v, a, w1, w3 = task
+    t0 = time.perf_counter()
+    o = oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar, beta=w.beta,
+                       causal=w.causal, phi=w.phi, w1=w1, w3=w3)
+    return o, time.perf_counter() - t0
 
-        n_heads = w.B * w.H
-        _, t1 = run([0])
-        n = int(max(1, min(n_heads, seconds / max(t1, 1e-3))))
-        heads = list(range(n))
-        o, dt = run(heads)
-    head_tokens_per_s = n * w.T / dt
+
+def baseline_heads(w, n_workers: int):
+    """The sampled (b, h) sequences at full T: every sequence when there are at
+    most 2 n_workers of them, else n_workers of them (at least 8), always with
+    (0, 0) and (B-1, H-1)."""
+    from ttt_workloads import head_subset
+    total = w.B * w.H
+    if total <= 2 * n_workers:
+        return list(range(total))
+    return head_subset(w, max(8, n_workers))
+
+
+def cpu_baseline(w, x, pool=None, n_workers: int = 1):
+    """Times the fp64 oracle (the recurrence of ``oracle.forward``, untuned) on a
+    bounded sample of the workload: whole sequences at full T, one per worker
+    task, spread over ``n_workers`` processes of ``pool`` (in this process when
+    pool is None).  Returns (baseline dict, oracle outputs [n, 1, T, d_v], heads)."""
+    import numpy as np
+    heads = baseline_heads(w, n_workers if pool is not None else 1)
+    tasks = []
+    for hh in heads:
+        b, h = hh // w.H, hh % w.H
+        sl = lambda t: np.ascontiguousarray(t[b:b + 1, h:h + 1])
+        tasks.append((w, sl(x.q64), sl(x.k64), sl(x.v64),
+                      None if x.a32 is None else np.ascontiguousarray(x.a32[b:b + 1, h:h + 1]),
+                      None if x.w1_64 is None else x.w1_64[h:h + 1],
+                      None if x.w3_64 is None else x.w3_64[h:h + 1]))
+    t0 = time.perf_counter()
+    if pool is None:
+        res = [_oracle_task(t) for t in tasks]
+        cores = 1
+    else:
+        res = pool.map(_oracle_task, tasks, chunksize=1)
+        cores = min(n_workers, len(tasks))
+    wall = time.perf_counter() - t0
+    o = np.concatenate([r[0] for r in res], axis=0)
+    cpu_s = sum(r[1] for r in res)
+    head_tokens_per_s = len(heads) * w.T / wall
     return {
-        "value": head_tokens_per_s / w.H,          # tokens = positions, all heads
+        "value": round(head_tokens_per_s / w.H, 1),   # tokens = positions, all heads
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
-        "sample": f"{n} of {n_heads} (b,h) sequences at full T={w.T}, fp64 numpy recurrence, "
-                  f"{dt:.1f} s; head-tokens/s={head_tokens_per_s:.4g}",
+        "sample": f"{len(heads)} of {w.B * w.H} (b,h) sequences at full T={w.T}, fp64 numpy recurrence, "
+                  f"one sequence per task over {cores} worker processes (one BLAS thread each): "
+                  f"{wall:.1f} s wall, {cpu_s:.1f} s of CPU; head-tokens/s={head_tokens_per_s:.4g}",
     }, o, heads
 
 
@@ -342,39 +404,47 @@ def run_backward(args, w):
     }
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
-              f"(the layer shards over (b, h) with no communication)", file=sys.stderr)
-        sys.exit(2)
+def roofline_of(w, chunk: int, seconds: float):
+    """Roofline object for the algorithmic work of one forward done in `seconds`:
+    bf16 work is priced against the dense bf16 MFMA peak, fp32 work (vector ALU)
+    against the fp32 vector peak; below the ridge of that peak and HBM it is
+    HBM-bound."""
+    bpht = algorithmic_bytes_per_ht(w)
+    flops_ht = algorithmic_flops_per_ht(w, chunk)
+    peak_flops, bound = (MFMA_BF16_PEAK_TFLOPS, "mfma") if w.dtype == "bf16" else (F32_PEAK_TFLOPS, "alu")
+    ridge = peak_flops * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops_ht / bpht < ridge:
+        achieved = w.head_tokens * bpht / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    achieved = w.head_tokens * flops_ht / seconds / 1e12
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak_flops, "unit": "TFLOP/s",
+            "frac": round(achieved / peak_flops, 4)}
 
+
+def timed_kernel_name(plan, w, launch: str) -> str:
+    """The kernel that carries the timing events (the output pass of the plan)."""
+    if plan.path == 3:
+        return "swiglu_kernel<BIDIR>" if not w.causal else "swiglu_kernel<OUTPUT>"
+    if plan.path == 2:
+        if not w.causal:
+            return "wide_kernel<BIDIR>"
+        if plan.n_kernels == 1 and plan.segments > 1:
+            return "wide_kernel<FUSED>" if launch == "single" else "wide_kernel<PREFIX>"
+        return "wide_kernel<OUTPUT>"
+    if plan.path == 1:
+        return "chunk_kernel<BIDIR>" if not w.causal else "chunk_kernel<OUTPUT>"
+    return "generic_forward"
+
+
+def run_forward(args, w, pool=None, n_workers: int = 1):
+    """K timed forwards of workload w; returns the JSON object of its line."""
     import numpy as np
     import torch
 
     import ttt_weight_layers_amd as tla
-    from ttt_workloads import WORKLOADS, make_inputs, bf16_bits_to_f64
+    from ttt_workloads import make_inputs, bf16_bits_to_f64
 
-    if args.calibrate_copy:
-        n = args.calibrate_copy * 2 ** 20
-        # an elementwise kernel that reads n bytes and writes n bytes
-        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
-        return
-
-    tla.load_library()
-    w = WORKLOADS[args.workload]
-    if args.decode:
-        print(json.dumps(run_decode(args, w)))
-        return
-    if args.backward:
-        print(json.dumps(run_backward(args, w)))
-        return
     x = make_inputs(w)
     dev = torch.device("cuda:0")
 
@@ -430,45 +500,36 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     kernel_ms = tla.ttt_la_kernel_times(layer.handle, n_timed)
     tla.ttt_la_enable_kernel_timing(layer.handle, 0)
+    if plan.n_kernels == 1 and plan.segments > 1 and args.launch == "single" and layer.wait_failed():
+        raise RuntimeError("a bounded wait of the single-launch path gave up: its outputs are invalid")
     ms_per_step = total_ms / args.steps
     tokens_per_s = w.tokens / (ms_per_step * 1e-3)
     k_avg_ms = float(np.mean(kernel_ms)) if kernel_ms else float("nan")
 
-    flops_ht = algorithmic_flops_per_ht(w, plan.chunk)
-    ai = flops_ht / bpht
-    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai < ridge:
-        achieved = w.head_tokens * bpht / (k_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    else:
-        achieved = w.head_tokens * flops_ht / (k_avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    if plan.path == 2:
-        kind = "BIDIR" if not w.causal else ("PREFIX" if args.launch == "prefix" else "OUTPUT")
-        roof["kernel"] = f"wide_kernel<{kind}>"
-    elif plan.path == 1:
-        roof["kernel"] = "chunk_kernel<BIDIR>" if not w.causal else "chunk_kernel<OUTPUT>"
-    else:
-        roof["kernel"] = "generic_forward"
+    roof = roofline_of(w, plan.chunk, k_avg_ms * 1e-3)
+    roof["kernel"] = timed_kernel_name(plan, w, args.launch)
     roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     roof["kernel_ms"] = round(k_avg_ms, 5)
+    step_roof = roofline_of(w, plan.chunk, ms_per_step * 1e-3)
+    roof["step_achieved"] = step_roof["achieved"]
+    roof["step_frac"] = step_roof["frac"]
 
     # parity of the first input set's output against the oracle on the sampled heads
     cpu = None
     check = None
     if not args.no_cpu_baseline:
-        # the last forward on set 0 is complete after the synchronize above
         step(0)
         torch.cuda.synchronize()
         o_gpu = sets[0]["o"]
         got = (bf16_bits_to_f64(o_gpu.view(torch.int16).cpu().numpy().view(np.uint16))
                if w.dtype == "bf16" else o_gpu.cpu().numpy().astype(np.float64))
-        cpu, o_ref, heads = cpu_baseline(w, x, args.cpu_seconds)
+        cpu, o_ref, heads = cpu_baseline(w, x, pool, n_workers)
         import oracle
         sel = got[[h // w.H for h in heads], [h % w.H for h in heads]][:, None]
         check = {"rel_err_vs_oracle": float(f"{oracle.rel_err(sel, o_ref):.3e}"), "heads": len(heads)}
+    layer.close()
+    del sets, q0, k0, v0, a0
+    torch.cuda.empty_cache()
 
     out = {
         "metric": METRIC,
@@ -496,8 +557,55 @@ def main():
     }
     if check is not None:
         out["check"] = check
-    print(json.dumps(out), flush=True)
-    layer.close()
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(the layer shards over (b, h) with no communication)", file=sys.stderr)
+        sys.exit(2)
+
+    names = [args.workload] if args.workload else list(DEFAULT_ORDER)
+    forward_run = not (args.calibrate_copy or args.decode or args.backward)
+    # the oracle's worker processes are forked before anything touches the GPU
+    pool, n_workers = None, 1
+    if forward_run and not args.no_cpu_baseline:
+        n_workers = oracle_workers()
+        pool = make_oracle_pool(n_workers)
+
+    import torch
+
+    import ttt_weight_layers_amd as tla
+    from ttt_workloads import WORKLOADS
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy * 2 ** 20
+        # an elementwise kernel that reads n bytes and writes n bytes
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 5}))
+        return
+
+    tla.load_library()
+    if args.decode:
+        print(json.dumps(run_decode(args, WORKLOADS[names[0] if args.workload else DEFAULT_WORKLOAD])))
+        return
+    if args.backward:
+        print(json.dumps(run_backward(args, WORKLOADS[names[0] if args.workload else DEFAULT_WORKLOAD])))
+        return
+    try:
+        for name in names:
+            print(json.dumps(run_forward(args, WORKLOADS[name], pool, n_workers)), flush=True)
+    finally:
+        if pool is not None:
+            pool.terminate()
+            pool.join()
 
 
 if __name__ == "__main__":
