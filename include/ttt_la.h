@@ -75,7 +75,18 @@ enum {
     TTT_LA_ETA_SOFTPLUS = 1u << 2    /* eta_t = softplus(eta[b,h,t]) = ln(1 + e^a) (Table 2, Variant 3) */
 };
 
-/* Launch choice for a causal forward split into segments (ttt_la_desc.launch). */
+typedef struct {
+    int32_t B, H, T;           /* batch, heads, sequence length: B, H, T >= 1 */
+    int32_t d_k, d_v, d_phi;   /* key/query width, value width, feature width */
+    int32_t dtype;             /* ttt_la_dtype of q, k, v, o (and W1, W3) */
+    int32_t phi;               /* ttt_la_phi */
+    int32_t chunk;             /* tile length along T: 0 = auto, else 64 or 128 (bf16); it changes
+                                  the result only by rounding */
+    const void* w1;            /* SWIGLU: device [H, d_phi, d_k] (out x in) in dtype; else NULL */
+    const void* w3;            /* SWIGLU: device [H, d_phi, d_k] in dtype; else NULL */
+} ttt_la_desc;
+
+/* Launch choice for a causal forward split into segments (ttt_la_hints.launch). */
 enum {
     TTT_LA_LAUNCH_AUTO = 0,      /* the library's choice (currently: separate kernels) */
     TTT_LA_LAUNCH_SEPARATE = 1,  /* segment summaries, their scan and the outputs as three kernels */
@@ -87,21 +98,15 @@ enum {
                                     tokens (32x32-tile path only; else as SEPARATE) */
 };
 
+/* Optional kernel-plan hints for ttt_la_create_hinted.  They choose how the
+ * work is tiled and launched, never what is computed: results differ only by
+ * rounding.  All-zero = the library's choice (what ttt_la_create takes). */
 typedef struct {
-    int32_t B, H, T;           /* batch, heads, sequence length: B, H, T >= 1 */
-    int32_t d_k, d_v, d_phi;   /* key/query width, value width, feature width */
-    int32_t dtype;             /* ttt_la_dtype of q, k, v, o (and W1, W3) */
-    int32_t phi;               /* ttt_la_phi */
-    int32_t chunk;             /* tile length along T: 0 = auto, else 64 or 128 (bf16); it changes
-                                  the result only by rounding */
-    int32_t segments;          /* sequence segments scanned in parallel: 0 = auto, else >= 1 (bf16 causal);
-                                  changes the result only by rounding */
+    int32_t segments;          /* sequence segments scanned in parallel: 0 = auto, else >= 1 (bf16 causal) */
     int32_t value_split;       /* workgroups sharing one segment's value columns: 0 = auto, 1 or 2
-                                  (2 is used for d_k = d_v = 128 with the identity map); tiling only */
+                                  (2 is used for d_k = d_v = 128 with the identity map) */
     int32_t launch;            /* TTT_LA_LAUNCH_*: how a segmented causal forward is launched */
-    const void* w1;            /* SWIGLU: device [H, d_phi, d_k] (out x in) in dtype; else NULL */
-    const void* w3;            /* SWIGLU: device [H, d_phi, d_k] in dtype; else NULL */
-} ttt_la_desc;
+} ttt_la_hints;
 
 /* Supported shapes (anything else well-formed returns TTT_LA_ERR_UNSUPPORTED):
  *   d_k, d_v in {64, 128}
@@ -116,6 +121,11 @@ typedef struct {
  * plan for the shape and allocates the workspace (hipMalloc on the current
  * device), once.  On any error *out is set to NULL. */
 int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out);
+
+/* ttt_la_create with kernel-plan hints (hints may be NULL: all automatic).
+ * TTT_LA_ERR_INVALID_ARG for a negative segment count, a value split other
+ * than 0, 1, 2 or an unknown launch value, before any HIP call. */
+int ttt_la_create_hinted(const ttt_la_desc* desc, const ttt_la_hints* hints, ttt_la_t* out);
 
 /* Enqueues one forward pass on hip_stream (a hipStream_t; NULL = the null
  * stream).
@@ -224,8 +234,12 @@ int ttt_la_check_state(const ttt_la_desc* desc, int32_t call, const void* q, con
                        const float* eta, float eta_scalar, float beta, uint32_t mode, const float* s_in,
                        const float* m_in, const void* o, const float* s_out, const float* m_out);
 
-/* The same for ttt_la_backward (the descriptor stands for the handle). */
-int ttt_la_check_backward(const ttt_la_desc* desc, const void* q, const void* k, const void* v, const float* eta,
+/* Host-only validation of plan hints, as ttt_la_create_hinted performs it (NULL is valid). */
+int ttt_la_check_hints(const ttt_la_hints* hints);
+
+/* The same for ttt_la_backward (the descriptor and the hints, NULL = automatic,
+ * stand for the handle: the workspace size depends on the plan). */
+int ttt_la_check_backward(const ttt_la_desc* desc, const ttt_la_hints* hints, const void* q, const void* k, const void* v, const float* eta,
                           float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ,
                           const void* dK, const void* dV, const float* dEta, const void* workspace,
                           size_t workspace_bytes);

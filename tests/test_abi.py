@@ -46,10 +46,22 @@ def test_status_strings():
 
 
 def desc(**kw):
-    base = dict(B=2, H=3, T=100, d_k=128, d_v=128, d_phi=None, dtype="bf16", phi="identity", chunk=0,
-                segments=0)
+    base = dict(B=2, H=3, T=100, d_k=128, d_v=128, d_phi=None, dtype="bf16", phi="identity", chunk=0)
     base.update(kw)
     return tla.make_desc(**base)
+
+
+def test_descriptor_layout_is_the_documented_one():
+    # B, H, T, d_k, d_v, d_phi, dtype, phi, chunk (nine int32), then the two weight pointers
+    names = [f[0] for f in tla.ttt_la_desc._fields_]
+    assert names == ["B", "H", "T", "d_k", "d_v", "d_phi", "dtype", "phi", "chunk", "w1", "w3"]
+    assert tla.ttt_la_desc.w1.offset == 40 and tla.ttt_la_desc.w3.offset == 48
+    assert ctypes.sizeof(tla.ttt_la_desc) == 56
+    text = open(HEADER).read()
+    body = text[text.index("typedef struct {\n    int32_t B, H, T;"):text.index("} ttt_la_desc;")]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"\b(B, H, T|d_k, d_v, d_phi|dtype|phi|chunk|w1|w3);", body)
+    assert fields == ["B, H, T", "d_k, d_v, d_phi", "dtype", "phi", "chunk", "w1", "w3"]
 
 
 def check(d=None, q=Q, k=K, v=V, eta=None, eta_scalar=0.5, beta=0.0, mode=0, o=O):
@@ -69,13 +81,27 @@ def test_query_may_alias_key():
 
 
 @pytest.mark.parametrize("field,value", [("B", 0), ("H", 0), ("T", 0), ("T", -5), ("d_k", 0),
-                                         ("d_v", -1), ("dtype", 7), ("phi", 3), ("chunk", -1),
-                                         ("segments", -2), ("value_split", 3), ("launch", 4),
-                                         ("launch", -1)])
+                                         ("d_v", -1), ("dtype", 7), ("phi", 3), ("chunk", -1)])
 def test_bad_descriptor_fields(field, value):
     d = desc()
     setattr(d, field, value)
     assert check(d=d, q=None) == tla.TTT_LA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("field,value", [("segments", -2), ("value_split", 3), ("value_split", -1),
+                                         ("launch", 4), ("launch", -1)])
+def test_bad_plan_hints(field, value):
+    h = tla.make_hints()
+    setattr(h, field, value)
+    assert tla.ttt_la_check_hints(h) == tla.TTT_LA_ERR_INVALID_ARG
+    # create rejects them before any HIP call
+    st, handle = tla.ttt_la_create_hinted(desc(), h)
+    assert st == tla.TTT_LA_ERR_INVALID_ARG and not handle.value
+
+
+def test_good_plan_hints():
+    assert tla.ttt_la_check_hints(None) == tla.TTT_LA_OK
+    assert tla.ttt_la_check_hints(tla.make_hints(segments=4, value_split=2, launch="prefix")) == tla.TTT_LA_OK
 
 
 @pytest.mark.parametrize("kw", [dict(d_k=96, d_v=128), dict(d_k=128, d_v=32), dict(d_k=256, d_v=128),
@@ -255,8 +281,9 @@ TB = 2 * 3 * 100 * 128 * 2                         # one bf16 [B, H, T, d] tenso
 
 
 def check_bw(d=None, q=Q, k=K, v=V, eta=None, beta=0.9, mode=0, dO=DO, dq=DQ, dk=DK, dv=DV, de=DE, ws=WS,
-             wsb=6 * TB):
-    return tla.ttt_la_check_backward(d or desc(), q, k, v, eta, 0.5, beta, mode, dO, dq, dk, dv, de, ws, wsb)
+             wsb=6 * TB, hints=None):
+    return tla.ttt_la_check_backward(d or desc(), hints, q, k, v, eta, 0.5, beta, mode, dO, dq, dk, dv, de, ws,
+                                     wsb)
 
 
 def test_backward_arguments():
@@ -269,15 +296,16 @@ def test_backward_arguments():
     assert check_bw(wsb=2 * TB - 16) == bad                                      # too small
     # two segments of 8 chunks: plus a summary area of 6 sequences x 2 slots x 128 KiB
     # for each reversed forward
-    d2 = desc(T=1024, segments=2)
+    d2, h2 = desc(T=1024), tla.make_hints(segments=2)
     tb2 = 2 * 3 * 1024 * 128 * 2
     need2 = 2 * tb2 + 2 * (6 * 2 * 128 * 128 * 2 * 4)
-    assert check_bw(d=d2, wsb=need2) == tla.TTT_LA_OK
-    assert check_bw(d=d2, wsb=need2 - 16) == bad
+    assert check_bw(d=d2, hints=h2, wsb=need2) == tla.TTT_LA_OK
+    assert check_bw(d=d2, hints=h2, wsb=need2 - 16) == bad
     # the single-launch plan and the 16x16-tile shapes take reversed copies of
     # q, k, v, dO: six tensors
-    assert check_bw(d=desc(launch="single"), wsb=6 * TB - 16) == bad
-    assert check_bw(d=desc(launch="single"), wsb=6 * TB) == tla.TTT_LA_OK
+    single = tla.make_hints(launch="single")
+    assert check_bw(hints=single, wsb=6 * TB - 16) == bad
+    assert check_bw(hints=single, wsb=6 * TB) == tla.TTT_LA_OK
     tb64 = 2 * 3 * 100 * 64 * 2
     assert check_bw(d=desc(d_k=64, d_v=64), wsb=6 * tb64 - 16) == bad
     assert check_bw(d=desc(d_k=64, d_v=64), wsb=6 * tb64) == tla.TTT_LA_OK

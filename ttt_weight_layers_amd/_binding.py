@@ -45,9 +45,12 @@ class ttt_la_desc(ctypes.Structure):
         ("B", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("d_phi", ctypes.c_int32),
         ("dtype", ctypes.c_int32), ("phi", ctypes.c_int32), ("chunk", ctypes.c_int32),
-        ("segments", ctypes.c_int32), ("value_split", ctypes.c_int32), ("launch", ctypes.c_int32),
         ("w1", ctypes.c_void_p), ("w3", ctypes.c_void_p),
     ]
+
+
+class ttt_la_hints(ctypes.Structure):
+    _fields_ = [("segments", ctypes.c_int32), ("value_split", ctypes.c_int32), ("launch", ctypes.c_int32)]
 
 
 class ttt_la_plan(ctypes.Structure):
@@ -59,7 +62,7 @@ class ttt_la_plan(ctypes.Structure):
     ]
 
 
-EXPORTS = ("ttt_la_create", "ttt_la_forward", "ttt_la_forward_state", "ttt_la_step", "ttt_la_backward",
+EXPORTS = ("ttt_la_create", "ttt_la_create_hinted", "ttt_la_check_hints", "ttt_la_forward", "ttt_la_forward_state", "ttt_la_step", "ttt_la_backward",
            "ttt_la_backward_workspace", "ttt_la_destroy",
            "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_check_backward", "ttt_la_get_plan",
            "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times",
@@ -81,6 +84,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i32, u32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_float
     lib.ttt_la_create.argtypes = [ctypes.POINTER(ttt_la_desc), ctypes.POINTER(vp)]
     lib.ttt_la_create.restype = ctypes.c_int
+    lib.ttt_la_create_hinted.argtypes = [ctypes.POINTER(ttt_la_desc), ctypes.POINTER(ttt_la_hints),
+                                         ctypes.POINTER(vp)]
+    lib.ttt_la_create_hinted.restype = ctypes.c_int
+    lib.ttt_la_check_hints.argtypes = [ctypes.POINTER(ttt_la_hints)]
+    lib.ttt_la_check_hints.restype = ctypes.c_int
     lib.ttt_la_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp]
     lib.ttt_la_forward.restype = ctypes.c_int
     lib.ttt_la_forward_state.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp]
@@ -92,7 +100,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_check_state.restype = ctypes.c_int
     lib.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ttt_la_backward.restype = ctypes.c_int
-    lib.ttt_la_check_backward.argtypes = [ctypes.POINTER(ttt_la_desc), vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp,
+    lib.ttt_la_check_backward.argtypes = [ctypes.POINTER(ttt_la_desc), ctypes.POINTER(ttt_la_hints), vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp,
                                           vp, vp, ctypes.c_size_t]
     lib.ttt_la_check_backward.restype = ctypes.c_int
     lib.ttt_la_backward_workspace.argtypes = [vp, u32, ctypes.POINTER(ctypes.c_size_t)]
@@ -134,6 +142,18 @@ def ttt_la_create(desc: ttt_la_desc):
     return st, h
 
 
+def ttt_la_create_hinted(desc: ttt_la_desc, hints: Optional[ttt_la_hints]):
+    """Returns (status, handle); hints None = all automatic."""
+    h = ctypes.c_void_p()
+    st = load_library().ttt_la_create_hinted(ctypes.byref(desc), None if hints is None else ctypes.byref(hints),
+                                             ctypes.byref(h))
+    return st, h
+
+
+def ttt_la_check_hints(hints: Optional[ttt_la_hints]) -> int:
+    return load_library().ttt_la_check_hints(None if hints is None else ctypes.byref(hints))
+
+
 def ttt_la_forward(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float,
                    mode: int, o: int, stream: Optional[int]) -> int:
     return load_library().ttt_la_forward(h, q, k, v, eta, float(eta_scalar), float(beta),
@@ -166,9 +186,11 @@ def ttt_la_backward(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: f
                                           dV, dEta, workspace, int(workspace_bytes), stream)
 
 
-def ttt_la_check_backward(desc: ttt_la_desc, q=None, k=None, v=None, eta=None, eta_scalar=1.0, beta=0.0, mode=0,
-                          dO=None, dQ=None, dK=None, dV=None, dEta=None, workspace=None, workspace_bytes=0) -> int:
-    return load_library().ttt_la_check_backward(ctypes.byref(desc), q, k, v, eta, float(eta_scalar), float(beta),
+def ttt_la_check_backward(desc: ttt_la_desc, hints: Optional[ttt_la_hints] = None, q=None, k=None, v=None, eta=None,
+                          eta_scalar=1.0, beta=0.0, mode=0, dO=None, dQ=None, dK=None, dV=None, dEta=None,
+                          workspace=None, workspace_bytes=0) -> int:
+    return load_library().ttt_la_check_backward(ctypes.byref(desc), None if hints is None else ctypes.byref(hints),
+                                                q, k, v, eta, float(eta_scalar), float(beta),
                                                 int(mode), dO, dQ, dK, dV, dEta, workspace, int(workspace_bytes))
 
 
@@ -232,20 +254,25 @@ _PHIS = {"identity": TTT_LA_PHI_IDENTITY, "swiglu": TTT_LA_PHI_SWIGLU}
 _ETA = {"scalar": TTT_LA_ETA_SCALAR, "per_token": TTT_LA_ETA_PER_TOKEN, "softplus": TTT_LA_ETA_SOFTPLUS}
 
 
-def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0, segments=0,
-              w1=None, w3=None, value_split=0, launch="auto") -> ttt_la_desc:
+def make_desc(B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0,
+              w1=None, w3=None) -> ttt_la_desc:
     d = ttt_la_desc()
     d.B, d.H, d.T, d.d_k, d.d_v = int(B), int(H), int(T), int(d_k), int(d_v)
     d.d_phi = int(d_k if d_phi is None else d_phi)
     d.dtype = _DTYPES[dtype]
     d.phi = _PHIS[phi]
     d.chunk = int(chunk)
-    d.segments = int(segments)
-    d.value_split = int(value_split)
-    d.launch = _LAUNCH[launch]
     d.w1 = _ptr(w1)
     d.w3 = _ptr(w3)
     return d
+
+
+def make_hints(segments=0, value_split=0, launch="auto") -> ttt_la_hints:
+    h = ttt_la_hints()
+    h.segments = int(segments)
+    h.value_split = int(value_split)
+    h.launch = _LAUNCH[launch] if isinstance(launch, str) else int(launch)
+    return h
 
 
 def _ptr(t) -> Optional[int]:
@@ -270,12 +297,12 @@ class TTTLinearAttention:
     def __init__(self, B, H, T, d_k, d_v, d_phi=None, dtype="bf16", phi="identity", chunk=0,
                  segments=0, w1=None, w3=None, value_split=0, launch="auto"):
         self._keep = (w1, w3)         # W1/W3 are borrowed by the handle
-        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, segments, w1, w3, value_split,
-                              launch)
+        self.desc = make_desc(B, H, T, d_k, d_v, d_phi, dtype, phi, chunk, w1, w3)
+        self.hints = make_hints(segments, value_split, launch)
         self.dtype = dtype
-        st, h = ttt_la_create(self.desc)
+        st, h = ttt_la_create_hinted(self.desc, self.hints)
         if st != TTT_LA_OK:
-            raise TTTError(st, "ttt_la_create")
+            raise TTTError(st, "ttt_la_create_hinted")
         self.handle = h
 
     def close(self):

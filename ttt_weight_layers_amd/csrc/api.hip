@@ -15,6 +15,7 @@
 
 struct ttt_la_s {
     ttt_la_desc desc;
+    ttt_la_hints hints;
     ttt::Shape shape;
     bool fast;
     ttt::FastPlan fp;
@@ -56,9 +57,7 @@ int check_desc(const ttt_la_desc* d) {
     if (d->d_k < 1 || d->d_v < 1 || d->d_phi < 1) return TTT_LA_ERR_INVALID_ARG;
     if (d->dtype != TTT_LA_F32 && d->dtype != TTT_LA_BF16) return TTT_LA_ERR_INVALID_ARG;
     if (d->phi != TTT_LA_PHI_IDENTITY && d->phi != TTT_LA_PHI_SWIGLU) return TTT_LA_ERR_INVALID_ARG;
-    if (d->chunk < 0 || d->segments < 0) return TTT_LA_ERR_INVALID_ARG;
-    if (d->value_split < 0 || d->value_split > 2) return TTT_LA_ERR_INVALID_ARG;
-    if (d->launch < TTT_LA_LAUNCH_AUTO || d->launch > TTT_LA_LAUNCH_PREFIX) return TTT_LA_ERR_INVALID_ARG;
+    if (d->chunk < 0) return TTT_LA_ERR_INVALID_ARG;
     if (d->phi == TTT_LA_PHI_SWIGLU) {
         if (!d->w1 || !d->w3) return TTT_LA_ERR_INVALID_ARG;
         if (!aligned(d->w1, 16) || !aligned(d->w3, 16)) return TTT_LA_ERR_INVALID_ARG;
@@ -74,6 +73,21 @@ int check_desc(const ttt_la_desc* d) {
     const long long widest = std::max(d->d_k, std::max(d->d_v, d->d_phi));
     if ((long long)d->B * d->H * d->T * widest >= (1LL << 31)) return TTT_LA_ERR_UNSUPPORTED;
     return TTT_LA_OK;
+}
+
+// plan hints; null = all automatic
+int check_hints(const ttt_la_hints* h) {
+    if (!h) return TTT_LA_OK;
+    if (h->segments < 0) return TTT_LA_ERR_INVALID_ARG;
+    if (h->value_split < 0 || h->value_split > 2) return TTT_LA_ERR_INVALID_ARG;
+    if (h->launch < TTT_LA_LAUNCH_AUTO || h->launch > TTT_LA_LAUNCH_PREFIX) return TTT_LA_ERR_INVALID_ARG;
+    return TTT_LA_OK;
+}
+
+ttt_la_hints hints_or_auto(const ttt_la_hints* h) {
+    ttt_la_hints r{};
+    if (h) r = *h;
+    return r;
 }
 
 int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
@@ -243,15 +257,21 @@ int ttt_la_check_state(const ttt_la_desc* desc, int32_t call, const void* q, con
     return TTT_LA_ERR_INVALID_ARG;
 }
 
-int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
+int ttt_la_check_hints(const ttt_la_hints* hints) { return check_hints(hints); }
+
+int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) { return ttt_la_create_hinted(desc, nullptr, out); }
+
+int ttt_la_create_hinted(const ttt_la_desc* desc, const ttt_la_hints* hints, ttt_la_t* out) {
     if (!out) return TTT_LA_ERR_INVALID_ARG;
     *out = nullptr;
     int st = check_desc(desc);
     if (st != TTT_LA_OK) return st;
+    if ((st = check_hints(hints)) != TTT_LA_OK) return st;
 
     ttt_la_s* h = new (std::nothrow) ttt_la_s();
     if (!h) return TTT_LA_ERR_OOM;
     h->desc = *desc;
+    h->hints = hints_or_auto(hints);
     h->shape = shape_of(*desc);
     h->workspace = nullptr;
     h->workspace_bytes = 0;
@@ -261,7 +281,7 @@ int ttt_la_create(const ttt_la_desc* desc, ttt_la_t* out) {
     h->epoch = 0;
     h->fast = desc->dtype == TTT_LA_BF16 && ttt::fast_supported(h->shape, desc->chunk);
     if (h->fast) {
-        h->fp = ttt::fast_plan(h->shape, desc->chunk, desc->segments, desc->value_split, desc->launch);
+        h->fp = ttt::fast_plan(h->shape, desc->chunk, h->hints.segments, h->hints.value_split, h->hints.launch);
         h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes + h->fp.zero_bytes;
     }
     if (hipGetDevice(&h->device) != hipSuccess) {
@@ -362,20 +382,20 @@ size_t tensor_bytes(const ttt_la_desc& d) { return (size_t)d.B * d.H * d.T * d.d
 // The 32x32-tile plans of three launches (decided from the descriptor alone: a
 // single or prefix launch was not asked for) read the time-reversed operands in
 // reverse order themselves.
-bool reversed_in_kernel(const ttt_la_desc& d) {
+bool reversed_in_kernel(const ttt_la_desc& d, const ttt_la_hints& hn) {
     const Shape s = shape_of(d);
-    return d.dtype == TTT_LA_BF16 && ttt::fast_supported(s, d.chunk) && ttt::wide_supported(s) && d.value_split != 2 &&
-           d.launch != TTT_LA_LAUNCH_SINGLE && d.launch != TTT_LA_LAUNCH_PREFIX;
+    return d.dtype == TTT_LA_BF16 && ttt::fast_supported(s, d.chunk) && ttt::wide_supported(s) &&
+           hn.value_split != 2 && hn.launch != TTT_LA_LAUNCH_SINGLE && hn.launch != TTT_LA_LAUNCH_PREFIX;
 }
 
 // Workspace of the backward.  Bidirectional: the two forward outputs.  Causal,
 // reversed in the kernels: the two forward outputs, then a segment-summary area
 // for each of the two reversed forwards (they run beside the first one, which uses
 // the handle's).  Causal otherwise: q, k, v, dO reversed in time, then the outputs.
-size_t backward_ws_bytes(const ttt_la_desc& d, uint32_t mode) {
+size_t backward_ws_bytes(const ttt_la_desc& d, const ttt_la_hints& hn, uint32_t mode) {
     if (mode & TTT_LA_BIDIRECTIONAL) return 2 * tensor_bytes(d);
-    if (reversed_in_kernel(d)) {
-        const ttt::FastPlan p = ttt::fast_plan(shape_of(d), d.chunk, d.segments, d.value_split, d.launch);
+    if (reversed_in_kernel(d, hn)) {
+        const ttt::FastPlan p = ttt::fast_plan(shape_of(d), d.chunk, hn.segments, hn.value_split, hn.launch);
         return 2 * tensor_bytes(d) + 2 * p.summary_bytes;
     }
     return 6 * tensor_bytes(d);
@@ -400,7 +420,7 @@ bool ensure_aux(ttt_la_s* h) {
     return true;
 }
 
-int check_backward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
+int check_backward(const ttt_la_desc* d, const ttt_la_hints& hn, const void* q, const void* k, const void* v, const float* eta,
                    float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ, const void* dK,
                    const void* dV, const float* dEta, const void* ws, size_t ws_bytes) {
     int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, dQ);
@@ -409,7 +429,7 @@ int check_backward(const ttt_la_desc* d, const void* q, const void* k, const voi
     if (!dO || !dK || !dV) return TTT_LA_ERR_INVALID_ARG;
     if (!aligned(dO, 16) || !aligned(dK, 16) || !aligned(dV, 16)) return TTT_LA_ERR_INVALID_ARG;
     if (dEta && !aligned(dEta, 4)) return TTT_LA_ERR_INVALID_ARG;
-    const size_t need = backward_ws_bytes(*d, mode);
+    const size_t need = backward_ws_bytes(*d, hn, mode);
     if (need && (!ws || !aligned(ws, 16) || ws_bytes < need)) return TTT_LA_ERR_INVALID_ARG;
     const size_t tb = tensor_bytes(*d);
     const size_t nt = (size_t)d->B * d->H * d->T;
@@ -434,13 +454,14 @@ int check_backward(const ttt_la_desc* d, const void* q, const void* k, const voi
 
 extern "C" {
 
-int ttt_la_check_backward(const ttt_la_desc* desc, const void* q, const void* k, const void* v, const float* eta,
-                          float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ,
-                          const void* dK, const void* dV, const float* dEta, const void* workspace,
-                          size_t workspace_bytes) {
+int ttt_la_check_backward(const ttt_la_desc* desc, const ttt_la_hints* hints, const void* q, const void* k,
+                          const void* v, const float* eta, float eta_scalar, float beta, uint32_t mode,
+                          const void* dO, const void* dQ, const void* dK, const void* dV, const float* dEta,
+                          const void* workspace, size_t workspace_bytes) {
     int st = check_desc(desc);
     if (st != TTT_LA_OK) return st;
-    return check_backward(desc, q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, workspace,
+    if ((st = check_hints(hints)) != TTT_LA_OK) return st;
+    return check_backward(desc, hints_or_auto(hints), q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, workspace,
                           workspace_bytes);
 }
 
@@ -449,7 +470,7 @@ int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes) {
     *bytes = 0;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
     if (!backward_supported(h->desc)) return TTT_LA_ERR_UNSUPPORTED;
-    *bytes = backward_ws_bytes(h->desc, mode);
+    *bytes = backward_ws_bytes(h->desc, h->hints, mode);
     return TTT_LA_OK;
 }
 
@@ -457,7 +478,7 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
                     float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV, float* dEta,
                     void* workspace, size_t workspace_bytes, void* hip_stream) {
     if (!h) return TTT_LA_ERR_INVALID_ARG;
-    int st = check_backward(&h->desc, q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, workspace,
+    int st = check_backward(&h->desc, h->hints, q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, workspace,
                             workspace_bytes);
     if (st != TTT_LA_OK) return st;
     hipStream_t stream = static_cast<hipStream_t>(hip_stream);
@@ -466,7 +487,7 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
     char* ws = static_cast<char*>(workspace);
     // the 32x32-tile kernels of three launches read and write in reverse time order
     // themselves; the other plans get reversed copies
-    const bool rev_in_kernel = !bidir && reversed_in_kernel(h->desc);
+    const bool rev_in_kernel = !bidir && reversed_in_kernel(h->desc, h->hints);
     // With in-kernel reversal, u and w (each with its own summary area) run on two
     // more streams beside dq: they start after everything enqueued so far on
     // hip_stream, and hip_stream waits for them before the finalize pass (all on
