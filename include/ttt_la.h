@@ -264,8 +264,9 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan);
 /* Diagnostic of the single-launch causal path (path 2 with n_kernels == 1):
  * the workgroups of one sequence wait for each other twice per forward, each
  * wait bounded so that a kernel always terminates.  *failed is set to 1 if any
- * wait of any earlier forward on h gave up (its output is then invalid), else
- * 0; always 0 for other plans.  Synchronises with the device (a blocking copy). */
+ * wait of a forward on h since the previous call gave up (that output is then
+ * invalid), else 0; reading a 1 clears the flag.  Always 0 for other plans.
+ * Synchronises with the device (a blocking copy). */
 int ttt_la_wait_status(ttt_la_t h, int32_t* failed);
 
 /* Measurement hook.  When n_slots > 0, every following ttt_la_forward,

@@ -287,6 +287,80 @@ def mode_bits(eta_mode: str = "scalar", causal: bool = True) -> int:
     return _ETA[eta_mode] | (0 if causal else TTT_LA_BIDIRECTIONAL)
 
 
+_TORCH_DTYPES = {"f32": "float32", "bf16": "bfloat16"}
+
+
+def check_tensors(desc: ttt_la_desc, call: str, mode: int, **tensors) -> None:
+    """Host-side check of the torch tensors of one library call against the
+    handle's descriptor, before any pointer reaches the C ABI (which takes raw
+    pointers and cannot see sizes): shape, dtype, contiguity, one CUDA device.
+
+    call: "forward", "forward_state", "step" or "backward".  Tensors that are
+    None are skipped (optional arguments).  Raises ValueError."""
+    import torch
+    B, H, T = desc.B, desc.H, desc.T
+    dk, dv, dphi = desc.d_k, desc.d_v, desc.d_phi
+    io = getattr(torch, _TORCH_DTYPES["f32" if desc.dtype == TTT_LA_F32 else "bf16"])
+    tok = 1 if call == "step" else T
+    per_token = (mode & (TTT_LA_ETA_PER_TOKEN | TTT_LA_ETA_SOFTPLUS)) != 0
+    want = {
+        "q": ((B, H, tok, dk), io), "k": ((B, H, tok, dk), io), "v": ((B, H, tok, dv), io),
+        "out": ((B, H, tok, dv), io), "dO": ((B, H, tok, dv), io),
+        "eta": ((B, H) if call == "step" else (B, H, T), torch.float32),
+    }
+    for name in ("S0", "M0", "S_T", "M_T", "S", "M"):
+        want[name] = ((B, H, dv, dphi), torch.float32)
+    device = None
+    for name, t in tensors.items():
+        if name == "eta" and not per_token:
+            if t is not None:
+                raise ValueError("eta must be None for a scalar rate")
+            continue
+        if t is None:
+            if name == "eta":
+                raise ValueError("a per-token rate needs eta")
+            continue
+        shape, dtype = want[name]
+        if name == "eta" and call == "step" and tuple(t.shape) == (B, H, 1):
+            shape = (B, H, 1)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, the handle expects {shape}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, the handle expects {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    # devices last, once every shape and dtype is known to be right
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if device is None:
+            device = t.device
+        elif t.device != device:
+            raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+
+
+def _launch_stream(t, stream):
+    """(stream handle for the C call, torch stream object or None).  Tensors this
+    binding allocates for a call on another stream are recorded on that stream,
+    so that the caching allocator does not hand their memory out again while the
+    call's kernels may still use it."""
+    import torch
+    cur = torch.cuda.current_stream(t.device)
+    if stream is None or int(stream) == cur.cuda_stream:
+        return cur.cuda_stream, None
+    return int(stream), torch.cuda.ExternalStream(int(stream), device=t.device)
+
+
+def _record(ext, *ts):
+    if ext is None:
+        return
+    for t in ts:
+        if t is not None:
+            t.record_stream(ext)
+
+
 class TTTLinearAttention:
     """One layer shape bound to a library handle.
 
@@ -325,77 +399,75 @@ class TTTLinearAttention:
     def forward(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
                 out=None, stream=None):
         import torch
-        if out is None:
+        mode = mode_bits(eta_mode, causal)
+        check_tensors(self.desc, "forward", mode, q=q, k=k, v=v, eta=eta, out=out)
+        s, ext = _launch_stream(q, stream)
+        fresh = out is None
+        if fresh:
             out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
-        for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-            if t.device.type != "cuda":
-                raise ValueError(f"{name} must be a device tensor")
-        if eta is not None and (eta.dtype != torch.float32 or not eta.is_contiguous()):
-            raise ValueError("eta must be a contiguous float32 device tensor")
-        s = torch.cuda.current_stream(q.device).cuda_stream if stream is None else int(stream)
-        st = ttt_la_forward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta,
-                            mode_bits(eta_mode, causal), _ptr(out), s)
+        st = ttt_la_forward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode, _ptr(out), s)
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_forward")
+        if fresh:
+            _record(ext, out)
         return out
-
-    def _stream(self, t, stream):
-        import torch
-        return torch.cuda.current_stream(t.device).cuda_stream if stream is None else int(stream)
-
-    @staticmethod
-    def _check(*named):
-        import torch
-        for name, t in named:
-            if t is None:
-                continue
-            if not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-            if t.device.type != "cuda":
-                raise ValueError(f"{name} must be a device tensor")
-        return torch
 
     def forward_state(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", S0=None, M0=None,
                       out=None, S_T=None, M_T=None, stream=None):
         """Causal forward from the carried state (S0, M0) (None = zero); writes the state
         after the last token to S_T, M_T when given (fp32 [B, H, d_v, d_phi])."""
-        torch = self._check(("q", q), ("k", k), ("v", v), ("S0", S0), ("M0", M0), ("S_T", S_T), ("M_T", M_T))
-        if out is None:
+        import torch
+        mode = mode_bits(eta_mode, True)
+        check_tensors(self.desc, "forward_state", mode, q=q, k=k, v=v, eta=eta, out=out, S0=S0, M0=M0, S_T=S_T,
+                      M_T=M_T)
+        s, ext = _launch_stream(q, stream)
+        fresh = out is None
+        if fresh:
             out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
-        st = ttt_la_forward_state(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta,
-                                  mode_bits(eta_mode, True), _ptr(S0), _ptr(M0), _ptr(out), _ptr(S_T), _ptr(M_T),
-                                  self._stream(q, stream))
+        st = ttt_la_forward_state(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode,
+                                  _ptr(S0), _ptr(M0), _ptr(out), _ptr(S_T), _ptr(M_T), s)
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_forward_state")
+        if fresh:
+            _record(ext, out)
         return out
 
     def step(self, q, k, v, S, M, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", out=None, stream=None):
         """One recurrent step: q, k, v [B, H, 1, d]; S, M fp32 [B, H, d_v, d_phi] updated in place."""
-        torch = self._check(("q", q), ("k", k), ("v", v), ("S", S), ("M", M))
-        if out is None:
+        import torch
+        mode = mode_bits(eta_mode, True)
+        if S is None or M is None:
+            raise ValueError("the step needs the state S and M")
+        check_tensors(self.desc, "step", mode, q=q, k=k, v=v, eta=eta, out=out, S=S, M=M)
+        s, ext = _launch_stream(q, stream)
+        fresh = out is None
+        if fresh:
             out = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=v.dtype, device=v.device)
-        st = ttt_la_step(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta,
-                         mode_bits(eta_mode, True), _ptr(S), _ptr(M), _ptr(out), self._stream(q, stream))
+        st = ttt_la_step(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode, _ptr(S),
+                         _ptr(M), _ptr(out), s)
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_step")
+        if fresh:
+            _record(ext, out)
         return out
 
     def backward(self, q, k, v, dO, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
                  stream=None, want_eta=True):
         """Gradients (dq, dk, dv, deta) of sum(o * dO); the workspace is a device tensor
         allocated here (the library itself allocates nothing)."""
-        torch = self._check(("q", q), ("k", k), ("v", v), ("dO", dO))
+        import torch
         mode = mode_bits(eta_mode, causal)
+        check_tensors(self.desc, "backward", mode, q=q, k=k, v=v, eta=eta, dO=dO)
         st, nbytes = ttt_la_backward_workspace(self.handle, mode)
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_backward_workspace")
+        s, ext = _launch_stream(q, stream)
         ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device=q.device)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         de = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if want_eta else None
         st = ttt_la_backward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode, _ptr(dO),
-                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(de), _ptr(ws), nbytes, self._stream(q, stream))
+                             _ptr(dq), _ptr(dk), _ptr(dv), _ptr(de), _ptr(ws), nbytes, s)
         if st != TTT_LA_OK:
             raise TTTError(st, "ttt_la_backward")
+        _record(ext, ws, dq, dk, dv, de)
         return dq, dk, dv, de

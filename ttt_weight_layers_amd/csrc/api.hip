@@ -662,6 +662,13 @@ int ttt_la_wait_status(ttt_la_t h, int32_t* failed) {
         return TTT_LA_ERR_HIP;
     }
     *failed = flag != 0;
+    if (flag != 0) {
+        // reported once: the flag covers the forwards since the previous read
+        if (hipMemset(const_cast<char*>(src), 0, sizeof(flag)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+            (void)hipGetLastError();
+            return TTT_LA_ERR_HIP;
+        }
+    }
     return TTT_LA_OK;
 }
 

@@ -1084,10 +1084,11 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
             if (n_kernels) *n_kernels = 1;
             return hipSuccess;
         }
-        // the grid cannot be made resident right now; the caller takes the three-kernel
-        // path and does not advance the epoch (no workgroup of this launch ran)
+        // Only "the grid cannot be made resident right now" sends the caller to the
+        // three-kernel path (it then does not advance the epoch: no workgroup of this
+        // launch ran); any other launch error is the caller's error.
         (void)hipGetLastError();
-        return hipErrorCooperativeLaunchTooLarge;
+        return e;
     }
     if (!a.bidirectional && p.prefix && !state_io) {
         wp.seg_count = p.segments;
