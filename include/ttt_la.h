@@ -247,7 +247,9 @@ int ttt_la_check_backward(const ttt_la_desc* desc, const ttt_la_hints* hints, co
 /* Kernel plan chosen at create, for tests and measurement. */
 typedef struct {
     int32_t path;          /* 0 = generic fp32-accumulate kernels, 1 = bf16 16x16-tile MFMA chunk
-                              kernels, 2 = bf16 32x32-tile MFMA chunk kernels (identity map, d = 128) */
+                              kernels, 2 = bf16 32x32-tile MFMA chunk kernels (identity map, d = 128),
+                              3 = bf16 32x32-tile SwiGLU kernel (d_k = d_v = 128; causal forwards,
+                              bidirectional ones as path 1) */
     int32_t chunk;         /* tokens per chunk */
     int32_t segments;      /* sequence segments per (b, h) scanned in parallel (1 = none) */
     int32_t seg_len;       /* tokens per segment (last one may be shorter) */

@@ -49,7 +49,9 @@ FULL_HEADS = {
 def expected_path(w):
     if w.dtype != "bf16":
         return 0
-    return 2 if (w.phi == "identity" and w.d_k == 128 and w.d_v == 128) else 1
+    if w.d_k == 128 and w.d_v == 128:
+        return 2 if w.phi == "identity" else 3
+    return 1
 
 
 def check(name, got, ref, tol):
@@ -84,8 +86,8 @@ def test_parity_full_shape(name):
     p = lay.plan()
     say(f"  plan: path={p.path} chunk={p.chunk} segments={p.segments} seg_len={p.seg_len} "
         f"dv_split={p.dv_split} phi_split={p.phi_split} grid={p.grid_main}")
-    # bf16 workloads run on an MFMA path (32x32 tiles for the identity map at
-    # d = 128, 16x16 tiles otherwise), fp32 on the fp32-arithmetic path
+    # bf16 workloads run on an MFMA path (32x32 tiles for d = 128: the identity map
+    # and the SwiGLU map; 16x16 tiles otherwise), fp32 on the fp32-arithmetic path
     assert p.path == expected_path(w)
     got = run_gpu(w, d, layer=lay)
     ref = run_oracle(w, x, heads=heads)

@@ -45,6 +45,7 @@ def hipcc() -> str:
 # instead of AGPRs, which would need a copy for every such operation.
 FILE_FLAGS = {
     "chunk_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "swiglu.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

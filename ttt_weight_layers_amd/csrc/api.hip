@@ -627,14 +627,15 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
     const Shape& s = h->shape;
     plan->workspace_bytes = h->workspace_bytes;
     if (h->fast) {
-        plan->path = h->fp.wide ? 2 : 1;
+        plan->path = h->fp.wide ? 2 : (h->fp.swiglu32 ? 3 : 1);
         plan->chunk = h->fp.chunk;
         plan->segments = h->fp.segments;
         plan->seg_len = h->fp.seg_len;
         plan->dv_split = h->fp.dv_split;
         plan->phi_split = h->fp.phi_split;
         plan->grid_main = s.n_seq() * h->fp.dv_split * h->fp.phi_split * h->fp.segments;
-        plan->n_kernels = (h->fp.fused || h->fp.prefix) ? 1
+        plan->n_kernels = h->fp.swiglu32 ? 2
+                          : (h->fp.fused || h->fp.prefix) ? 1
                                       : 1 + (h->fp.segments > 1 ? 1 : 0) +
                                             (h->fp.segments > 2 || h->fp.sum_split == 2 ? 1 : 0) +
                                             (h->fp.phi_split > 1 ? 1 : 0);

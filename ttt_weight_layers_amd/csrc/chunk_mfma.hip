@@ -769,6 +769,22 @@ FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split,
         p.summary_bytes = wide_summary_bytes(s, p.segments + (p.sum_split == 2 ? 1 : 0));
         return p;
     }
+    if (swiglu_supported(s)) {
+        // causal: one workgroup per (sequence, 128-feature slice) over the whole
+        // sequence (swiglu.hip); bidirectional: the 16x16-tile kernel below with the
+        // same slices and the same partial-output area
+        p.swiglu32 = true;
+        p.chunk = CH;
+        p.phi_split = s.d_phi / 128;
+        p.dvt = 1;
+        p.dv_split = 1;
+        p.nwaves = s.d_v / 16;
+        p.segments = 1;
+        p.seg_len = s.T;
+        p.summary_bytes = 0;
+        p.partial_bytes = swiglu_partial_bytes(s);
+        return p;
+    }
     // The chunk length is a tiling choice (results differ only by rounding);
     // this path always tiles at 64 tokens.
     p.chunk = CH;
@@ -863,6 +879,7 @@ hipError_t launch_chunk(const Shape& s, const FastPlan& p, int kind, bool mom, b
 hipError_t launch_fast(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
                        hipEvent_t ev_end, int* n_kernels) {
     if (p.wide) return launch_wide(s, p, workspace, a, ev_begin, ev_end, n_kernels);
+    if (p.swiglu32 && !a.bidirectional) return launch_swiglu(s, workspace, a, ev_begin, ev_end, n_kernels);
     if (a.reverse) return hipErrorInvalidValue;   // time reversal: 32x32-tile kernels only
     ChunkParams cp{};
     cp.q = static_cast<const uint16_t*>(a.q);

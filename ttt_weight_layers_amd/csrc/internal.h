@@ -71,6 +71,9 @@ struct FastPlan {
     int bounds[17];         // prefix path: first token of each segment, bounds[segments] = T
     int sum_split;          // two segments: summaries over halves of segment 0 (2) or all
                             // of it (1); the halves put twice the workgroups on the summary
+    bool swiglu32;          // SwiGLU map, d_k = d_v = 128: causal forwards on the 32x32-tile
+                            // kernel of swiglu.hip (one workgroup per sequence and 128-feature
+                            // slice); bidirectional ones on the 16x16-tile kernels
 };
 
 bool fast_supported(const Shape& s, int chunk);
@@ -90,6 +93,14 @@ size_t wide_zero_bytes(const Shape& s);
 size_t wide_flag_offset(const Shape& s, const FastPlan& p);
 hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const FwdArgs& a, hipEvent_t ev_begin,
                        hipEvent_t ev_end, int* n_kernels);
+
+// ---- SwiGLU feature map on 32x32 tiles (swiglu.hip) ----------------------------
+bool swiglu_supported(const Shape& s);
+// fp32 parts of o of the feature slices: [d_phi / 128][B * H * T][128]
+size_t swiglu_partial_bytes(const Shape& s);
+// causal forward without carried state; ev_begin/ev_end take the feature kernel's timestamps
+hipError_t launch_swiglu(const Shape& s, void* workspace, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end,
+                         int* n_kernels);
 
 // ---- recurrent step (decode.hip) ----------------------------------------------
 struct StepArgs {
