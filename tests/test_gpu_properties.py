@@ -299,3 +299,23 @@ def test_forward_rejects_bad_arguments_without_launching():
     assert st == tla.TTT_LA_ERR_INVALID_ARG
     torch.cuda.synchronize()
     assert torch.all(o == 7.0)
+
+
+@pytest.mark.parametrize("T", [7, 64 * 3 + 11])
+def test_swiglu_workspace_serves_both_modes(T):
+    # one handle, causal then bidirectional calls: the causal kernel keeps each
+    # slice's part as bf16 whole chunks, the bidirectional one as fp32 rows, and
+    # the handle's workspace must hold the larger of the two
+    w = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=T).with_settings(d_phi=256)
+    say(f"[swiglu workspace] T={T}")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d)
+    plan = lay.plan()
+    slices, n_seq, chunks = w.d_phi // 128, w.B * w.H, -(-T // 64)
+    assert plan.path == 3
+    assert plan.workspace_bytes >= max(slices * n_seq * T * 128 * 4, slices * n_seq * chunks * 64 * 128 * 2)
+    for causal in (True, False):
+        wc = w.with_settings(causal=causal)
+        got = run_gpu(wc, d, layer=lay)
+        assert oracle.rel_err(got, run_oracle(wc, x)) <= TOL[w.dtype]

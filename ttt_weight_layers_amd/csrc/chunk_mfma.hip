@@ -782,7 +782,9 @@ FastPlan fast_plan(const Shape& s, int /*chunk*/, int segments, int value_split,
         p.segments = 1;
         p.seg_len = s.T;
         p.summary_bytes = 0;
-        p.partial_bytes = swiglu_partial_bytes(s);
+        // the mode is a per-call choice: room for either kernel's parts (bf16 whole
+        // chunks for the causal kernel, fp32 rows for the bidirectional one)
+        p.partial_bytes = std::max(swiglu_partial_bytes(s), (size_t)p.phi_split * s.n_seq() * s.T * s.d_v * sizeof(float));
         return p;
     }
     // The chunk length is a tiling choice (results differ only by rounding);
