@@ -56,7 +56,9 @@ typedef enum {
     TTT_LA_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size, bad mode bit, beta or eta out of range, overlap */
     TTT_LA_ERR_UNSUPPORTED = -2, /* well-formed request outside the supported shapes */
     TTT_LA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
-    TTT_LA_ERR_OOM = -4          /* workspace allocation failed */
+    TTT_LA_ERR_OOM = -4,         /* workspace allocation failed */
+    TTT_LA_ERR_TOO_LARGE = -5    /* ttt_la_forward_noalloc: the plan needs more scratch than
+                                    TTT_LA_NOALLOC_SCRATCH_BYTES */
 } ttt_la_status;
 
 typedef enum { TTT_LA_F32 = 0, TTT_LA_BF16 = 1 } ttt_la_dtype; /* q, k, v, o, W1, W3 */
@@ -140,6 +142,35 @@ int ttt_la_create_hinted(const ttt_la_desc* desc, const ttt_la_hints* hints, ttt
  * TTT_LA_ERR_HIP if a launch fails. */
 int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
                    float eta_scalar, float beta, uint32_t mode, void* o, void* hip_stream);
+
+/* Size of the static device scratch of ttt_la_forward_noalloc (one copy per
+ * device, held until the process ends). */
+#define TTT_LA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* ttt_la_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  No
+ * handle: the kernel plan is taken from *desc and *hints (hints may be NULL) on
+ * every call, exactly as ttt_la_create_hinted would take it, and the
+ * workspace of that plan (segment summaries, per-slice partial outputs) lives in
+ * a static device array of TTT_LA_NOALLOC_SCRATCH_BYTES instead.  The call makes
+ * no hipMalloc, hipFree or other allocating call; the first call on a device
+ * resolves that device's copy of the array (hipGetSymbolAddress).
+ *   desc, hints  as for ttt_la_create_hinted; q, k, v, eta, eta_scalar, beta,
+ *            mode, o, hip_stream as for ttt_la_forward.  The inputs and o are
+ *            the caller's and stay so.
+ * Results equal those of ttt_la_forward on a handle created from the same desc
+ * and hints.  TTT_LA_LAUNCH_SINGLE runs as three launches here (the single
+ * launch keeps counters from call to call of one handle).
+ * All calls on one device share its scratch and leave their contents in it:
+ * calls that overlap in time on one device (streams that are not ordered with
+ * each other) race and their results are undefined.
+ * Errors: as ttt_la_create_hinted and ttt_la_forward (all before any HIP call),
+ * and TTT_LA_ERR_TOO_LARGE, before any HIP call, when the plan's workspace
+ * exceeds TTT_LA_NOALLOC_SCRATCH_BYTES (for instance B*H*T*d_phi*2 bytes of
+ * SwiGLU partials above 64 MiB; fewer segments shrink the summaries). */
+int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, const void* q, const void* k,
+                           const void* v, const float* eta, float eta_scalar, float beta, uint32_t mode, void* o,
+                           void* hip_stream);
 
 /* Causal forward from a carried state.  Table 2 of the thelatestinai.com page
  * lists a recurrent implementation of every variant beside the parallel one:

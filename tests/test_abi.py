@@ -42,6 +42,7 @@ def test_status_strings():
     assert tla.ttt_la_status_string(-2).startswith("unsupported")
     assert tla.ttt_la_status_string(-3).startswith("HIP")
     assert tla.ttt_la_status_string(-4).startswith("out of")
+    assert "static maximum" in tla.ttt_la_status_string(-5)
     assert tla.ttt_la_status_string(12345) == "unknown status"
 
 

@@ -20,6 +20,8 @@ TTT_LA_ERR_INVALID_ARG = -1
 TTT_LA_ERR_UNSUPPORTED = -2
 TTT_LA_ERR_HIP = -3
 TTT_LA_ERR_OOM = -4
+TTT_LA_ERR_TOO_LARGE = -5
+TTT_LA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 TTT_LA_F32 = 0
 TTT_LA_BF16 = 1
@@ -66,7 +68,7 @@ EXPORTS = ("ttt_la_create", "ttt_la_create_hinted", "ttt_la_check_hints", "ttt_l
            "ttt_la_backward_workspace", "ttt_la_destroy",
            "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_check_backward", "ttt_la_get_plan",
            "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times",
-           "ttt_la_enable_kernel_timing_every")
+           "ttt_la_enable_kernel_timing_every", "ttt_la_forward_noalloc")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -91,6 +93,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_check_hints.restype = ctypes.c_int
     lib.ttt_la_forward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp]
     lib.ttt_la_forward.restype = ctypes.c_int
+    lib.ttt_la_forward_noalloc.argtypes = [ctypes.POINTER(ttt_la_desc), ctypes.POINTER(ttt_la_hints), vp, vp, vp,
+                                           vp, f32, f32, u32, vp, vp]
+    lib.ttt_la_forward_noalloc.restype = ctypes.c_int
     lib.ttt_la_forward_state.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp]
     lib.ttt_la_forward_state.restype = ctypes.c_int
     lib.ttt_la_step.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp]
@@ -152,6 +157,14 @@ def ttt_la_create_hinted(desc: ttt_la_desc, hints: Optional[ttt_la_hints]):
 
 def ttt_la_check_hints(hints: Optional[ttt_la_hints]) -> int:
     return load_library().ttt_la_check_hints(None if hints is None else ctypes.byref(hints))
+
+
+def ttt_la_forward_noalloc(desc: ttt_la_desc, hints: Optional[ttt_la_hints], q: int, k: int, v: int,
+                           eta: Optional[int], eta_scalar: float, beta: float, mode: int, o: int,
+                           stream: Optional[int]) -> int:
+    """The handle-less forward whose workspace is the library's static device scratch."""
+    return load_library().ttt_la_forward_noalloc(ctypes.byref(desc), None if hints is None else ctypes.byref(hints),
+                                                 q, k, v, eta, float(eta_scalar), float(beta), int(mode), o, stream)
 
 
 def ttt_la_forward(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -232,6 +233,7 @@ const char* ttt_la_status_string(int status) {
         case TTT_LA_ERR_UNSUPPORTED: return "unsupported shape or setting";
         case TTT_LA_ERR_HIP: return "HIP runtime error";
         case TTT_LA_ERR_OOM: return "out of device memory";
+        case TTT_LA_ERR_TOO_LARGE: return "needs more scratch memory than the static maximum";
         default: return "unknown status";
     }
 }
@@ -573,6 +575,88 @@ int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, cons
     if (st != TTT_LA_OK) return st;
     return enqueue_forward(h, q, k, v, eta, eta_scalar, beta, mode, nullptr, nullptr, o, nullptr, nullptr,
                            hip_stream);
+}
+
+}  // extern "C"
+
+// ---- forward without allocation: scratch in a static device array ----
+
+namespace {
+
+// One copy per device, allocated by the runtime with the code object and held until
+// the process ends.  In host code `scratch` names a host-side stand-in: only the
+// address hipGetSymbolAddress returns for the current device may reach a kernel.
+static __device__ __align__(256) unsigned char scratch[TTT_LA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// this device's copy of the array, resolved on the first call on the device
+int device_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return TTT_LA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return TTT_LA_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return TTT_LA_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TTT_LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, const void* q, const void* k,
+                           const void* v, const float* eta, float eta_scalar, float beta, uint32_t mode, void* o,
+                           void* hip_stream) {
+    int st = check_desc(desc);
+    if (st != TTT_LA_OK) return st;
+    if ((st = check_hints(hints)) != TTT_LA_OK) return st;
+    if ((st = check_forward(desc, q, k, v, eta, eta_scalar, beta, mode, o)) != TTT_LA_OK) return st;
+    const Shape s = shape_of(*desc);
+    const ttt_la_hints hn = hints_or_auto(hints);
+    ttt::FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.eta = eta;
+    a.eta_scalar = eta_scalar;
+    a.beta = beta;
+    a.eta_kind = eta_kind_of(mode);
+    a.bidirectional = (mode & TTT_LA_BIDIRECTIONAL) != 0;
+    a.o = o;
+    a.stream = static_cast<hipStream_t>(hip_stream);
+    hipError_t e;
+    if (desc->dtype == TTT_LA_BF16 && ttt::fast_supported(s, desc->chunk)) {
+        ttt::FastPlan p = ttt::fast_plan(s, desc->chunk, hn.segments, hn.value_split, hn.launch);
+        // the single-launch form keeps counters that must persist from call to call
+        // of one handle: three launches instead, which compute the same
+        p.fused = false;
+        const size_t need = p.summary_bytes + p.partial_bytes;
+        if (need > TTT_LA_NOALLOC_SCRATCH_BYTES) return TTT_LA_ERR_TOO_LARGE;
+        void* ws = nullptr;
+        if (need && (st = device_scratch(&ws)) != TTT_LA_OK) return st;
+        e = ttt::launch_fast(s, p, ws, a, nullptr, nullptr, nullptr);
+    } else {
+        if (ttt::generic_smem_bytes(s) > 160 * 1024) return TTT_LA_ERR_UNSUPPORTED;
+        e = ttt::launch_generic(s, a, nullptr, nullptr);
+    }
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return TTT_LA_ERR_HIP;
+    }
+    return TTT_LA_OK;
 }
 
 int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
