@@ -12,7 +12,9 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libttt_la.so")
+# TTT_LA_LIBRARY names another build of the same sources (the host-sanitized
+# one of build_sanitized.py, for the host-only tests)
+LIB_PATH = os.environ.get("TTT_LA_LIBRARY") or os.path.join(_PKG, "libttt_la.so")
 
 # status codes
 TTT_LA_OK = 0

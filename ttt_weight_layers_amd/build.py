@@ -61,25 +61,30 @@ def _run(cmd, verbose):
         print(out)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 4, out: str = LIB, build_dir: str = BUILD,
+          host_flags=(), link_flags=("-Wl,--no-undefined",)) -> str:
+    """Compiles every csrc/*.hip into build_dir and links ``out``.  host_flags
+    are added to every compile (for options of the host pass only, each must be
+    preceded by -Xarch_host); link_flags to the link."""
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError("no HIP sources found")
     objs = []
     cmds = []
     for src in sources:
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+        obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj])
+        cmds.append([cc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *host_flags, "-c", src,
+                     "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *link_flags, "-o", tmp, *objs], verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
