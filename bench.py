@@ -425,7 +425,8 @@ def roofline_of(w, chunk: int, seconds: float):
 def timed_kernel_name(plan, w, launch: str) -> str:
     """The kernel that carries the timing events (the output pass of the plan)."""
     if plan.path == 3:
-        return "swiglu_kernel<BIDIR>" if not w.causal else "swiglu_kernel<OUTPUT>"
+        # the bidirectional SwiGLU pass runs on the 16x16-tile kernel
+        return "chunk_kernel<BIDIR>" if not w.causal else "swiglu_kernel<OUTPUT>"
     if plan.path == 2:
         if not w.causal:
             return "wide_kernel<BIDIR>"

@@ -34,14 +34,15 @@ SMALL = {
     "bidir_vit_256x6x196_d64": dict(B=3, H=2, T=196),
 }
 
-# full shapes: how many heads the oracle recomputes at full T
+# full shapes: how many heads the oracle recomputes at full T (a subset always holds
+# the first and the last (b, h))
 FULL_HEADS = {
     "v5_f32_1x1x256_d64": None,             # all
     "v4_momentum_4x8x2048_d128": None,      # all 32
     "v3_softplus_8x16x4096_d128": 8,
-    "v2_swiglu_4x16x8192_d128_f512": 3,
-    "v5_long_1x16x65536_d128": 4,
-    "v3_long_1x16x65536_d128": 4,
+    "v2_swiglu_4x16x8192_d128_f512": 8,
+    "v5_long_1x16x65536_d128": 8,
+    "v3_long_1x16x65536_d128": 8,
     "bidir_vit_256x6x196_d64": 64,
 }
 
