@@ -435,6 +435,8 @@ def timed_kernel_name(plan, w, launch: str) -> str:
         return "wide_kernel<OUTPUT>"
     if plan.path == 1:
         return "chunk_kernel<BIDIR>" if not w.causal else "chunk_kernel<OUTPUT>"
+    if plan.path == 4:
+        return "short_forward"
     return "generic_forward"
 
 

@@ -280,7 +280,9 @@ typedef struct {
     int32_t path;          /* 0 = generic fp32-accumulate kernels, 1 = bf16 16x16-tile MFMA chunk
                               kernels, 2 = bf16 32x32-tile MFMA chunk kernels (identity map, d = 128),
                               3 = bf16 32x32-tile SwiGLU kernel (d_k = d_v = 128; causal forwards,
-                              bidirectional ones as path 1) */
+                              bidirectional ones as path 1), 4 = fp32 one-pass masked T x T product
+                              (identity map, d_k in {64, 128}, d_v a multiple of 64, T <= 1024;
+                              calls with a carried state as path 0) */
     int32_t chunk;         /* tokens per chunk */
     int32_t segments;      /* sequence segments per (b, h) scanned in parallel (1 = none) */
     int32_t seg_len;       /* tokens per segment (last one may be shorter) */

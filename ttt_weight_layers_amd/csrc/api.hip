@@ -371,7 +371,8 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     } else {
         // fp32 inputs, and the carried-state calls of the 16x16-tile shapes
         if (reverse) return TTT_LA_ERR_INVALID_ARG;
-        e = ttt::launch_generic(h->shape, a, eb, ee);
+        if (!state_io && ttt::short_supported(h->shape)) e = ttt::launch_short(h->shape, a, eb, ee);
+        else e = ttt::launch_generic(h->shape, a, eb, ee);
     }
     return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
@@ -649,8 +650,12 @@ int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, c
         if (need && (st = device_scratch(&ws)) != TTT_LA_OK) return st;
         e = ttt::launch_fast(s, p, ws, a, nullptr, nullptr, nullptr);
     } else {
-        if (ttt::generic_smem_bytes(s) > 160 * 1024) return TTT_LA_ERR_UNSUPPORTED;
-        e = ttt::launch_generic(s, a, nullptr, nullptr);
+        if (ttt::short_supported(s)) {
+            e = ttt::launch_short(s, a, nullptr, nullptr);
+        } else {
+            if (ttt::generic_smem_bytes(s) > 160 * 1024) return TTT_LA_ERR_UNSUPPORTED;
+            e = ttt::launch_generic(s, a, nullptr, nullptr);
+        }
     }
     if (e != hipSuccess) {
         (void)hipGetLastError();
@@ -723,6 +728,16 @@ int ttt_la_get_plan(ttt_la_t h, ttt_la_plan* plan) {
                                       : 1 + (h->fp.segments > 1 ? 1 : 0) +
                                             (h->fp.segments > 2 || h->fp.sum_split == 2 ? 1 : 0) +
                                             (h->fp.phi_split > 1 ? 1 : 0);
+    } else if (ttt::short_supported(s)) {
+        // forwards without carried state; the carried-state calls take path 0
+        plan->path = 4;
+        plan->chunk = 64;
+        plan->segments = 1;
+        plan->seg_len = s.T;
+        plan->dv_split = s.d_v / 64;
+        plan->phi_split = 1;
+        plan->grid_main = ttt::short_grid(s);
+        plan->n_kernels = 1;
     } else {
         plan->path = 0;
         plan->chunk = 16;

@@ -95,6 +95,12 @@ hipError_t launch_wide(const Shape& s, const FastPlan& p, void* workspace, const
                        hipEvent_t ev_end, int* n_kernels);
 
 // ---- SwiGLU feature map on 32x32 tiles (swiglu.hip) ----------------------------
+// fp32 one-pass masked product for short sequences (short_f32.hip): identity map,
+// d_k in {64, 128}, d_v a multiple of 64, T <= 1024, no carried state
+bool short_supported(const Shape& s);
+int short_grid(const Shape& s);
+hipError_t launch_short(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
+
 bool swiglu_supported(const Shape& s);
 // fp32 parts of o of the feature slices: [d_phi / 128][B * H * T][128]
 size_t swiglu_partial_bytes(const Shape& s);
