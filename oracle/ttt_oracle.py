@@ -30,6 +30,14 @@ KV Binding Is Secretly Linear Attention"; readings are marked READING):
 * READING: the readout of token t uses the state after token t's own update,
   o_t = S_t phi(q_t).  In the bidirectional (ViT) mode every token updates the
   state first and every query reads the final state.
+* The mean-squared binding loss (``loss="mse"``) is the other inner-loop loss
+  the pages name: the Modular TTT abstract on the mlsanity.com page compares MSE
+  and inner-product losses, and the same page lists "Parallelizing Linear
+  Transformers with the Delta Rule over Sequence Length" among the works the
+  paper builds on.  READING: l_t(S) = 1/2 ||S phi(k_t) - v_t||^2, gradient
+  (S phi(k_t) - v_t) phi(k_t)^T, taken through the same inner loop (rate,
+  momentum, readout after the update).  With beta = 0 a descent step is the
+  delta rule S_t = S_{t-1} - eta_t (S_{t-1} phi(k_t) - v_t) phi(k_t)^T.
 
 ``forward`` is the definition, a token-by-token loop.  ``forward_closed_form``
 and ``forward_chunked`` are the parallel forms the blog says the recurrence can
@@ -48,7 +56,7 @@ import numpy as np
 
 __all__ = [
     "softplus", "silu", "swiglu_features", "features", "learning_rates",
-    "binding_loss", "binding_loss_grad", "forward", "forward_closed_form",
+    "binding_loss", "binding_loss_grad", "mse_loss", "mse_loss_grad", "forward", "forward_closed_form",
     "forward_chunked", "rel_err",
 ]
 
@@ -137,6 +145,22 @@ def binding_loss_grad(S, phik, v):
     return np.broadcast_to(g, np.shape(S)).copy()
 
 
+def mse_loss(S, phik, v):
+    """l(S) = 1/2 ||S phi(k) - v||^2: the mean-squared key->value binding loss.
+
+    S: [..., d_v, d_phi], phik: [..., d_phi], v: [..., d_v].  READING of the MSE
+    inner-loop loss the mlsanity.com page names (Modular TTT abstract).
+    """
+    r = np.einsum("...vf,...f->...v", S, phik) - v
+    return 0.5 * np.einsum("...v,...v->...", r, r)
+
+
+def mse_loss_grad(S, phik, v):
+    """Gradient of ``mse_loss`` with respect to S: (S phi(k) - v) phi(k)^T."""
+    r = np.einsum("...vf,...f->...v", S, phik) - v
+    return np.einsum("...v,...f->...vf", r, phik)
+
+
 # ----------------------------------------------------------------------------
 # the definition: token-by-token recurrence
 # ----------------------------------------------------------------------------
@@ -149,7 +173,7 @@ def _flatten(x, d):
 def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
             beta: float = 0.0, causal: bool = True, phi: str = "identity",
             w1=None, w3=None, ascent: bool = False, inner_steps: int = 1,
-            return_state: bool = False, S0=None, M0=None):
+            return_state: bool = False, S0=None, M0=None, loss: str = "dot"):
     """Recurrent TTT forward, fp64, one gradient step per token.
 
     q, k: [B, H, T, d_k]; v: [B, H, T, d_v]; eta / a: [B, H, T] (per_token /
@@ -162,7 +186,8 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
     For every sequence (b, h) independently:
       S = S0 or 0, M = M0 or 0                       (reset per sequence)
       for t = 0 .. T-1:
-        G   = grad_S l_t(S)  = -v_t phi(k_t)^T        (explicit gradient)
+        G   = grad_S l_t(S)  = -v_t phi(k_t)^T        (explicit gradient; loss="mse":
+                             = (S phi(k_t) - v_t) phi(k_t)^T)
         M   = beta M - eta_t G      (ascent: + eta_t G)
         S   = S + M
         o_t = S phi(q_t)                              (causal readout)
@@ -191,6 +216,9 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
     if inner_steps != 1 and beta != 0.0:
         raise ValueError("inner_steps > 1 is defined here for beta == 0 only")
     sign = 1.0 if ascent else -1.0
+    if loss not in ("dot", "mse"):
+        raise ValueError(f"unknown binding loss {loss!r}")
+    loss_grad = binding_loss_grad if loss == "dot" else mse_loss_grad
 
     if (S0 is not None or M0 is not None) and not causal:
         raise ValueError("an entry state is defined for the causal mode only")
@@ -199,7 +227,7 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
     o = np.zeros((N, T, d_v))
     for t in range(T):
         for _ in range(inner_steps):
-            G = binding_loss_grad(S, pk[:, t], vf[:, t])
+            G = loss_grad(S, pk[:, t], vf[:, t])
             M = beta * M + sign * lr[:, t, None, None] * G
             S = S + M
         if causal:

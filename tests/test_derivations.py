@@ -156,3 +156,47 @@ def test_backward_as_forwards_bidirectional(beta):
     np.testing.assert_allclose((e * c)[..., None] * u, dv, rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose((e * c)[..., None] * w, dk, rtol=1e-10, atol=1e-10)
     np.testing.assert_allclose(c * np.einsum("bhtd,bhtd->bht", v, u) / (1 + np.exp(-a)), de, rtol=1e-10, atol=1e-10)
+
+
+# ----------------------------------------------------------------------------
+# delta rule (mean-squared binding loss, beta = 0): chunk form
+#
+# Within a chunk entered with S0 (d_v x d_k), write the step of token t as
+# S_t = S_{t-1} + u_t k_t^T with u_t = eta_t (v_t - S_{t-1} k_t).  Unrolling S_{t-1}
+# = S0 + sum_{j<t} u_j k_j^T gives, with rows = tokens,
+#   (I + diag(eta) L) U = diag(eta) (V - K S0^T),  L = strictly lower part of K K^T
+# so U = A (V - K S0^T) with A = (I + diag(eta) L)^{-1} diag(eta), and
+#   O = Q S0^T + tril(Q K^T) U,     S_n = S0 + U^T K.
+# ----------------------------------------------------------------------------
+
+def _delta_chunked(q, k, v, eta, chunk):
+    T, dk = k.shape
+    dv = v.shape[1]
+    S = np.zeros((dv, dk))
+    o = np.zeros((T, dv))
+    for c0 in range(0, T, chunk):
+        Q, K, V, e = q[c0:c0 + chunk], k[c0:c0 + chunk], v[c0:c0 + chunk], eta[c0:c0 + chunk]
+        n = len(K)
+        L = np.tril(K @ K.T, -1)
+        # unit lower-triangular inverse by forward substitution, row by row
+        X = np.zeros((n, n))
+        Nm = e[:, None] * L
+        for t in range(n):
+            X[t, t] = 1.0
+            for j in range(t):
+                X[t] -= Nm[t, j] * X[j]
+        A = X * e[None, :]
+        U = A @ (V - K @ S.T)
+        o[c0:c0 + n] = Q @ S.T + np.tril(Q @ K.T) @ U
+        S = S + U.T @ K
+    return o, S
+
+
+@pytest.mark.parametrize("chunk", [1, 5, 16, 64])
+def test_delta_chunk_form_equals_recurrence(chunk):
+    q, k, v, eta = _inputs(150, 8, 6, 31)
+    got, S = _delta_chunked(q, k, v, eta, chunk)
+    ref, Sref, _ = oracle.forward(q[None, None], k[None, None], v[None, None], eta_mode="per_token",
+                                  eta=eta[None, None], loss="mse", return_state=True)
+    np.testing.assert_allclose(got, ref[0, 0], rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(S, Sref[0, 0], rtol=1e-10, atol=1e-10)
