@@ -85,9 +85,17 @@ def algorithmic_bytes_per_ht(w) -> int:
     return b
 
 
+# tokens per chunk of the delta-rule kernel
+DELTA_CHUNK = 32
+
+
 def algorithmic_flops_per_ht(w, chunk: int) -> int:
     """Causal intra-chunk triangle + state readout and update (x2 with momentum)
-    + SwiGLU feature map for q and k."""
+    + SwiGLU feature map for q and k.  Delta rule (loss "mse"): K S^T, Q S^T and
+    the update U^T K (3 d_k d_v multiply-adds) plus the half triangles of K K^T,
+    Q K^T, tril(Q K^T) U and the solve for U (C/2 (2 d_k + 2 d_v))."""
+    if w.loss == "mse":
+        return 2 * (3 * w.d_k * w.d_v + DELTA_CHUNK // 2 * (2 * w.d_k + 2 * w.d_v))
     if not w.causal:
         return 4 * w.d_phi * w.d_v
     f = (chunk + 1) * (w.d_phi + w.d_v) + 4 * w.d_phi * w.d_v * (2 if w.beta != 0.0 else 1)
@@ -152,6 +160,7 @@ DEFAULT_ORDER = (
     "v5_long_1x16x65536_d128",
     "v3_long_1x16x65536_d128",
     "bidir_vit_256x6x196_d64",
+    "v3_delta_8x16x4096_d128",
     "v2_swiglu_4x16x8192_d128_f512",
 )
 # Worker processes of the oracle timing: the host cores this process may use,
@@ -190,7 +199,7 @@ def _oracle_task(task):
     w, q, k, v, a, w1, w3 = task
     t0 = time.perf_counter()
     o = oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar, beta=w.beta,
-                       causal=w.causal, phi=w.phi, w1=w1, w3=w3)
+                       causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss)
     return o, time.perf_counter() - t0
 
 
@@ -424,6 +433,8 @@ def roofline_of(w, chunk: int, seconds: float):
 
 def timed_kernel_name(plan, w, launch: str) -> str:
     """The kernel that carries the timing events (the output pass of the plan)."""
+    if w.loss == "mse":
+        return "delta_forward"
     if plan.path == 3:
         # the bidirectional SwiGLU pass runs on the 16x16-tile kernel
         return "chunk_kernel<BIDIR>" if not w.causal else "swiglu_kernel<OUTPUT>"
@@ -474,7 +485,8 @@ def run_forward(args, w, pool=None, n_workers: int = 1):
                                    value_split=args.value_split, launch=args.launch)
     plan = layer.plan()
     stream = torch.cuda.current_stream()
-    mode = tla.mode_bits(w.eta_mode, w.causal)
+    mode = tla.mode_bits(w.eta_mode, w.causal, w.loss)
+    chunk = DELTA_CHUNK if w.loss == "mse" else plan.chunk
 
     def step(i):
         s = sets[i % n_sets]
@@ -509,11 +521,11 @@ def run_forward(args, w, pool=None, n_workers: int = 1):
     tokens_per_s = w.tokens / (ms_per_step * 1e-3)
     k_avg_ms = float(np.mean(kernel_ms)) if kernel_ms else float("nan")
 
-    roof = roofline_of(w, plan.chunk, k_avg_ms * 1e-3)
+    roof = roofline_of(w, chunk, k_avg_ms * 1e-3)
     roof["kernel"] = timed_kernel_name(plan, w, args.launch)
     roof["traffic"] = measured_traffic(w.name, roof["kernel"])
     roof["kernel_ms"] = round(k_avg_ms, 5)
-    step_roof = roofline_of(w, plan.chunk, ms_per_step * 1e-3)
+    step_roof = roofline_of(w, chunk, ms_per_step * 1e-3)
     roof["step_achieved"] = step_roof["achieved"]
     roof["step_frac"] = step_roof["frac"]
 
@@ -550,8 +562,10 @@ def run_forward(args, w, pool=None, n_workers: int = 1):
         "config": {
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "d_phi": w.d_phi,
             "phi": w.phi, "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar, "beta": w.beta,
-            "causal": w.causal, "chunk": plan.chunk, "segments": plan.segments, "dv_split": plan.dv_split,
-            "phi_split": plan.phi_split, "launch": args.launch, "kernels_per_step": plan.n_kernels,
+            "causal": w.causal, "loss": w.loss, "chunk": chunk,
+            "segments": 1 if w.loss == "mse" else plan.segments, "dv_split": plan.dv_split,
+            "phi_split": plan.phi_split, "launch": args.launch,
+            "kernels_per_step": 1 if w.loss == "mse" else plan.n_kernels,
             "input_sets": n_sets,
             "head_tokens_per_s": round(w.head_tokens / (ms_per_step * 1e-3), 1),
         },

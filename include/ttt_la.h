@@ -74,7 +74,13 @@ enum {
     TTT_LA_BIDIRECTIONAL = 1u << 0,  /* o_t = S_{T-1} phi(q_t): all tokens update before any readout */
     TTT_LA_ETA_SCALAR = 0u,          /* eta_t = eta_scalar; the eta pointer must be NULL */
     TTT_LA_ETA_PER_TOKEN = 1u << 1,  /* eta_t = eta[b,h,t] */
-    TTT_LA_ETA_SOFTPLUS = 1u << 2    /* eta_t = softplus(eta[b,h,t]) = ln(1 + e^a) (Table 2, Variant 3) */
+    TTT_LA_ETA_SOFTPLUS = 1u << 2,   /* eta_t = softplus(eta[b,h,t]) = ln(1 + e^a) (Table 2, Variant 3) */
+    TTT_LA_LOSS_MSE = 1u << 3        /* binding loss 1/2 ||S phi(k_t) - v_t||^2 instead of -<S phi(k_t), v_t>:
+                                        the delta rule S_t = S_{t-1} - eta_t (S_{t-1} k_t - v_t) k_t^T
+                                        (mlsanity.com page: Modular TTT abstract, MSE and inner-product
+                                        losses; "Builds on": the delta-rule parallelisation paper).
+                                        ttt_la_forward only; bf16, identity map, d_k = d_v in {64, 128},
+                                        causal, beta = 0; anything else TTT_LA_ERR_UNSUPPORTED */
 };
 
 typedef struct {

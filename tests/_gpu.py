@@ -65,7 +65,7 @@ def run_gpu(w: Workload, d, chunk=None, segments=0, eta_sign=1.0, q_override=Non
     q = d["q"] if q_override is None else q_override
     v = d["v"] if v_scale is None else (d["v"] * v_scale).contiguous()
     o = lay.forward(q, d["k"], v, eta=eta, eta_scalar=eta_scalar, beta=w.beta, eta_mode=w.eta_mode,
-                    causal=w.causal)
+                    causal=w.causal, loss=w.loss)
     torch.cuda.synchronize()
     return from_device(o, w.dtype)
 
@@ -91,10 +91,10 @@ def run_oracle(w: Workload, x: Inputs, heads=None, q64=None):
                 outs.append(oracle.forward(q[i:i + 1], k[i:i + 1], v[i:i + 1], eta_mode=w.eta_mode,
                                            eta=None if a is None else a[i:i + 1],
                                            eta_scalar=w.eta_scalar, beta=w.beta, causal=w.causal,
-                                           phi=w.phi, w1=w1[h:h + 1], w3=w3[h:h + 1]))
+                                           phi=w.phi, w1=w1[h:h + 1], w3=w3[h:h + 1], loss=w.loss))
             return np.concatenate(outs, axis=0)
     return oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar, beta=w.beta,
-                          causal=w.causal, phi=w.phi, w1=w1, w3=w3)
+                          causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss)
 
 
 def select_heads(o: np.ndarray, w: Workload, heads):

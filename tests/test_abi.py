@@ -329,3 +329,19 @@ def test_backward_null_handle():
     assert lib.ttt_la_backward_workspace(None, 0, ctypes.byref(n)) == tla.TTT_LA_ERR_INVALID_ARG
     assert lib.ttt_la_backward(None, Q, K, V, None, 1.0, 0.0, 0, DO, DQ, DK, DV, None, WS, 0, None) == \
         tla.TTT_LA_ERR_INVALID_ARG
+
+
+def test_mse_loss_mode():
+    # the delta rule: bf16 identity map, d_k = d_v in {64, 128}, causal, beta = 0
+    mse = tla.TTT_LA_LOSS_MSE
+    assert check(mode=mse) == tla.TTT_LA_OK
+    assert check(d=desc(d_k=64, d_v=64), eta=ETA, mode=mse | tla.TTT_LA_ETA_SOFTPLUS) == tla.TTT_LA_OK
+    assert check(mode=mse, beta=0.5) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(mode=mse | tla.TTT_LA_BIDIRECTIONAL) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(dtype="f32", d_k=64, d_v=64), mode=mse) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(d_k=64, d_v=128), mode=mse) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=W3), mode=mse) == tla.TTT_LA_ERR_UNSUPPORTED
+    # no carried-state forward, step or backward for the delta rule
+    assert check_fs(mode=mse, beta=0.0) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check_step(mode=mse, beta=0.0) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert tla.mode_bits("softplus", True, "mse") == tla.TTT_LA_ETA_SOFTPLUS | mse

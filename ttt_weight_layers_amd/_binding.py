@@ -42,6 +42,7 @@ TTT_LA_BIDIRECTIONAL = 1 << 0
 TTT_LA_ETA_SCALAR = 0
 TTT_LA_ETA_PER_TOKEN = 1 << 1
 TTT_LA_ETA_SOFTPLUS = 1 << 2
+TTT_LA_LOSS_MSE = 1 << 3
 
 
 class ttt_la_desc(ctypes.Structure):
@@ -298,8 +299,11 @@ def _ptr(t) -> Optional[int]:
     return int(t.data_ptr())
 
 
-def mode_bits(eta_mode: str = "scalar", causal: bool = True) -> int:
-    return _ETA[eta_mode] | (0 if causal else TTT_LA_BIDIRECTIONAL)
+_LOSS = {"dot": 0, "mse": TTT_LA_LOSS_MSE}
+
+
+def mode_bits(eta_mode: str = "scalar", causal: bool = True, loss: str = "dot") -> int:
+    return _ETA[eta_mode] | (0 if causal else TTT_LA_BIDIRECTIONAL) | _LOSS[loss]
 
 
 _TORCH_DTYPES = {"f32": "float32", "bf16": "bfloat16"}
@@ -412,9 +416,10 @@ class TTTLinearAttention:
         return ttt_la_wait_status(self.handle)
 
     def forward(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
-                out=None, stream=None):
+                out=None, stream=None, loss="dot"):
+        """One forward; loss "mse" runs the delta rule (TTT_LA_LOSS_MSE)."""
         import torch
-        mode = mode_bits(eta_mode, causal)
+        mode = mode_bits(eta_mode, causal, loss)
         check_tensors(self.desc, "forward", mode, q=q, k=k, v=v, eta=eta, out=out)
         s, ext = _launch_stream(q, stream)
         fresh = out is None

@@ -40,7 +40,7 @@ namespace {
 
 using ttt::Shape;
 
-constexpr uint32_t kModeMask = TTT_LA_BIDIRECTIONAL | TTT_LA_ETA_PER_TOKEN | TTT_LA_ETA_SOFTPLUS;
+constexpr uint32_t kModeMask = TTT_LA_BIDIRECTIONAL | TTT_LA_ETA_PER_TOKEN | TTT_LA_ETA_SOFTPLUS | TTT_LA_LOSS_MSE;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -91,6 +91,8 @@ ttt_la_hints hints_or_auto(const ttt_la_hints* h) {
     return r;
 }
 
+Shape shape_of(const ttt_la_desc& d);
+
 int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
                   float eta_scalar, float beta, uint32_t mode, const void* o) {
     if (!q || !k || !v || !o) return TTT_LA_ERR_INVALID_ARG;
@@ -118,6 +120,11 @@ int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void
         if (overlaps(o, v_bytes, d->w1, w_bytes) || overlaps(o, v_bytes, d->w3, w_bytes))
             return TTT_LA_ERR_INVALID_ARG;
     }
+    // the delta rule runs for one configuration (no momentum, causal, bf16 identity map,
+    // square state of width 64 or 128)
+    if ((mode & TTT_LA_LOSS_MSE) &&
+        (beta != 0.0f || (mode & TTT_LA_BIDIRECTIONAL) || !ttt::delta_supported(shape_of(*d))))
+        return TTT_LA_ERR_UNSUPPORTED;
     return TTT_LA_OK;
 }
 
@@ -131,6 +138,7 @@ int check_forward_state(const ttt_la_desc* d, const void* q, const void* k, cons
     int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, o);
     if (st != TTT_LA_OK) return st;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
+    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // the delta rule has no carried state here
     if (!state_ok(S0) || !state_ok(M0) || !state_ok(S_T) || !state_ok(M_T)) return TTT_LA_ERR_INVALID_ARG;
     const size_t eb = elem_bytes(d->dtype);
     const size_t nt = (size_t)d->B * d->H * d->T;
@@ -161,6 +169,7 @@ int check_step(const ttt_la_desc* d, const void* q, const void* k, const void* v
     if (!aligned(S, 16) || !aligned(M, 16)) return TTT_LA_ERR_INVALID_ARG;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
+    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // no delta-rule step
     const bool per_tok = (mode & TTT_LA_ETA_PER_TOKEN) != 0;
     const bool softp = (mode & TTT_LA_ETA_SOFTPLUS) != 0;
     if (per_tok && softp) return TTT_LA_ERR_INVALID_ARG;
@@ -356,7 +365,10 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     hipEvent_t eb = nullptr, ee = nullptr;
     if (timed) next_events(h, &eb, &ee);
     hipError_t e;
-    if (h->fast && (h->fp.wide || !state_io)) {
+    if (mode & TTT_LA_LOSS_MSE) {
+        // validated by check_forward: the delta-rule kernel, no workspace
+        e = ttt::launch_delta(h->shape, a, eb, ee);
+    } else if (h->fast && (h->fp.wide || !state_io)) {
         a.epoch = h->epoch + 1;
         e = ttt::launch_fast(h->shape, h->fp, workspace, a, eb, ee, nullptr);
         const bool fused_ran = h->fp.fused && !a.bidirectional && !state_io;
@@ -427,6 +439,7 @@ int check_backward(const ttt_la_desc* d, const ttt_la_hints& hn, const void* q, 
                    float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ, const void* dK,
                    const void* dV, const float* dEta, const void* ws, size_t ws_bytes) {
     int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, dQ);
+    if (st == TTT_LA_OK && (mode & TTT_LA_LOSS_MSE)) return TTT_LA_ERR_UNSUPPORTED;   // no delta-rule backward
     if (st != TTT_LA_OK) return st;
     if (!backward_supported(*d)) return TTT_LA_ERR_UNSUPPORTED;
     if (!dO || !dK || !dV) return TTT_LA_ERR_INVALID_ARG;
@@ -639,7 +652,9 @@ int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, c
     a.o = o;
     a.stream = static_cast<hipStream_t>(hip_stream);
     hipError_t e;
-    if (desc->dtype == TTT_LA_BF16 && ttt::fast_supported(s, desc->chunk)) {
+    if (mode & TTT_LA_LOSS_MSE) {
+        e = ttt::launch_delta(s, a, nullptr, nullptr);
+    } else if (desc->dtype == TTT_LA_BF16 && ttt::fast_supported(s, desc->chunk)) {
         ttt::FastPlan p = ttt::fast_plan(s, desc->chunk, hn.segments, hn.value_split, hn.launch);
         // the single-launch form keeps counters that must persist from call to call
         // of one handle: three launches instead, which compute the same

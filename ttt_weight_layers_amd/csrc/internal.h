@@ -101,6 +101,11 @@ bool short_supported(const Shape& s);
 int short_grid(const Shape& s);
 hipError_t launch_short(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// delta rule (mean-squared binding loss, no momentum, causal; delta.hip): bf16,
+// identity map, d_k = d_v in {64, 128}
+bool delta_supported(const Shape& s);
+hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
+
 bool swiglu_supported(const Shape& s);
 // fp32 parts of o of the feature slices: [d_phi / 128][B * H * T][128]
 size_t swiglu_partial_bytes(const Shape& s);

@@ -54,6 +54,7 @@ class Workload:
     l2norm: bool          # per-token L2 normalisation of q, k, v
     seed: int
     note: str = ""
+    loss: str = "dot"     # binding loss: "dot" (linear attention) or "mse" (delta rule)
 
     @property
     def n_seq(self) -> int:
@@ -81,7 +82,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The seven synthetic workloads.  Seeds 1001..1007 in this order.
+# The synthetic workloads.  Seeds 1001..1008 in this order.
 WORKLOADS = {
     # Plain causal linear attention (the last row of the ablation, Table 2, with a
     # constant unit step and no momentum), fp32.
@@ -126,6 +127,13 @@ WORKLOADS = {
         dtype="bf16", phi="identity", eta_mode="scalar", eta_scalar=1.0, beta=0.0,
         causal=False, chunk=0, l2norm=False, seed=1007,
         note="bidirectional, eta=1, no momentum"),
+    # The mean-squared binding loss (delta rule) at the Variant-3 shape: per-token rate,
+    # no momentum, L2-normalised tokens (each step is then a contraction along k).
+    "v3_delta_8x16x4096_d128": Workload(
+        "v3_delta_8x16x4096_d128", B=8, H=16, T=4096, d_k=128, d_v=128, d_phi=128,
+        dtype="bf16", phi="identity", eta_mode="softplus", eta_scalar=0.0, beta=0.0,
+        causal=True, chunk=0, l2norm=True, seed=1008,
+        note="delta rule (MSE loss), eta=softplus(a), no momentum", loss="mse"),
 }
 
 
