@@ -13,33 +13,48 @@
 //     u_t = eta_t r_t - sum_{j<t} N_tj u_j,   r_t = v_t - S0 k_t,  N_tj = eta_t (k_t . k_j)
 //     O   = Q S0^T + tril(Q K^T) U,           S_C = S0 + U^T K
 // R = V - K S0^T, the scores and the update are dense products on the matrix cores;
-// the C-step solve for U runs in fp32 with one thread per value column.
+// the C-step solve for U runs in fp32, four lanes per value column.
 //
-// One workgroup (four waves) walks one sequence in chunks of 32 tokens and keeps
-// its fp32 S in registers as 16x16 MFMA result tiles (wave w: value rows
-// 32w .. 32w+31 at d = 128, 16w .. 16w+15 at d = 64).  A bf16 copy of S in LDS
-// serves as the operand of K S0^T and Q S0^T.
+// A workgroup (four waves) walks one sequence in chunks of 32 tokens for 64 of its
+// value columns (the rows of S evolve independently: row i only meets column i of
+// v), keeps those 64 rows of S in fp32 registers as 16x16 MFMA result tiles (wave
+// w: rows 16w .. 16w+15) and a bf16 copy of S^T in LDS as the operand of K S0^T and
+// Q S0^T (written four entries at a time, read back by transpose reads).  The next chunk's rows load into registers while the current one is used;
+// the LDS tiles of q, k, v are double-buffered.  Waves exchange data through LDS only,
+// so the barriers inside the chunk loop wait for LDS traffic alone (lds_barrier), not
+// for the prefetch loads or the output stores in flight.
 //
 // Register layouts of v_mfma_f32_16x16x32_bf16 (lane l, c16 = l % 16, g = l / 16):
 //   A operand  A[m = c16][k = 8g .. 8g+7]      B operand  B[k = 8g .. 8g+7][n = c16]
 //   D result   D[m = 4g .. 4g+3][n = c16]
 // Operands whose contraction runs along the features are 16-byte row reads of the
-// swizzled tiles; those whose contraction runs over tokens (U^T, K, U) are
-// transpose reads.
+// swizzled tiles; those whose contraction runs over tokens (U^T, K, U) or over the
+// rows of the S^T copy are transpose reads.
 
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
 #include "lds_tiles.h"
 
+#define TTT_INLINE __attribute__((always_inline))
+
 namespace ttt {
 namespace {
 
 constexpr int DC = 32;         // tokens per chunk
 constexpr int DTH = 256;       // threads: four waves
+constexpr int DVW = 64;        // value columns per workgroup
 constexpr int NSTR = DC + 4;   // row stride (floats) of N
 constexpr int PSTR = 40;       // row stride (bf16) of the masked scores: 16 rows read at one
                                // column fall on distinct banks
+
+// x of lane OWNER of each group of four lanes, in all four (one DPP move)
+template <int OWNER>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), OWNER | (OWNER << 2) | (OWNER << 4) |
+                                                                               (OWNER << 6),
+                                                      0xF, 0xF, false));
+}
 
 struct DeltaParams {
     const uint16_t* q;
@@ -50,157 +65,203 @@ struct DeltaParams {
     float eta_scalar;
     int eta_kind;
     int T;
+    int n_vsplit;              // workgroups per sequence (value columns DVW each)
 };
 
-template <int D>
+// DK = d_k = d_v.  Rows of the state evolve independently under the delta rule (row i
+// of S only meets v's column i), so a workgroup owns DVW value columns of one sequence.
+template <int DK>
 __global__ void __launch_bounds__(DTH, 1) delta_forward(DeltaParams p) {
-    constexpr int NT = D / 16;                // 16-wide tiles across d
-    constexpr int SRT = D / 64;               // value-row tiles of S per wave
-    constexpr int OTB = NT / 4;               // value tiles of R and O per wave
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[DC * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sK[DC * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[DC * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sU[DC * D];
-    __shared__ __attribute__((aligned(16))) uint16_t sS[D * D];
-    __shared__ __attribute__((aligned(16))) float sR[DC * D];
-    __shared__ __attribute__((aligned(16))) float sN[DC * NSTR];
+    constexpr int NT = DK / 16;                  // 16-wide feature tiles
+    constexpr int QL = DC * DK / 8 / DTH;        // 16-byte loads per thread of a q or k chunk
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][DC * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][DC * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][DC * DVW];
+    __shared__ __attribute__((aligned(16))) uint16_t sU[DC * DVW];
+    __shared__ __attribute__((aligned(16))) uint16_t sST[DK * DVW];  // S^T in bf16: row = feature
+    __shared__ __attribute__((aligned(16))) float sR[DC * DVW];
+    __shared__ __attribute__((aligned(16))) float sN[DC * NSTR];   // N^T: row j holds N[4m + i][j] at 8i + m
     __shared__ __attribute__((aligned(16))) uint16_t sP[DC * PSTR];
-    __shared__ float sE[DC];
+    __shared__ float sE[2][DC];
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4, q4 = lane & 3;
     const int T = p.T;
-    const size_t row0 = (size_t)blockIdx.x * T;
-    const int vr0 = wv * 16 * SRT;            // first value row of this wave's S tiles
+    const int seq = blockIdx.x / p.n_vsplit;
+    const int vc0 = (blockIdx.x % p.n_vsplit) * DVW;   // first value column of the workgroup
+    const size_t row0 = (size_t)seq * T;
+    const int vr0 = 16 * wv;                         // this wave's value rows of S (local)
+    const int dv = DK;                               // row length of v and o
 
-    f32x4 St[SRT][NT];
+    f32x4 St[NT];
 #pragma unroll
-    for (int a = 0; a < SRT; ++a)
+    for (int b = 0; b < NT; ++b) St[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = tid; e < DVW * DK / 8; e += DTH) *reinterpret_cast<u32x4*>(sST + 8 * e) = u32x4{0u, 0u, 0u, 0u};
+
+    // next chunk's rows in registers (zero past T)
+    u32x4 rq[QL], rk[QL], rv;
+    float re = 0.0f;
+    bool re_valid = false;
+    auto fetch = [&](int c) {
+        const int t0 = c * DC, n = min(DC, T - t0);
 #pragma unroll
-        for (int b = 0; b < NT; ++b) St[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int e = tid; e < D * D / 8; e += DTH) *reinterpret_cast<u32x4*>(sS + 8 * e) = u32x4{0u, 0u, 0u, 0u};
+        for (int l = 0; l < QL; ++l) {
+            const int e = tid + l * DTH, r = e / (DK / 8), col = 8 * (e % (DK / 8));
+            rq[l] = rk[l] = u32x4{0u, 0u, 0u, 0u};
+            if (r < n) {
+                rq[l] = *reinterpret_cast<const u32x4*>(p.q + (row0 + t0 + r) * DK + col);
+                rk[l] = *reinterpret_cast<const u32x4*>(p.k + (row0 + t0 + r) * DK + col);
+            }
+        }
+        {
+            const int r = tid / (DVW / 8), col = 8 * (tid % (DVW / 8));
+            rv = r < n ? *reinterpret_cast<const u32x4*>(p.v + (row0 + t0 + r) * dv + vc0 + col)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+        // the raw rate only: its softplus waits until commit, when the load has landed
+        re_valid = tid < n;
+        if (tid < DC) re = re_valid ? (p.eta_kind == ETA_SCALAR ? p.eta_scalar : p.eta[row0 + t0 + tid]) : 0.0f;
+    };
+    auto commit = [&](int b) {
+#pragma unroll
+        for (int l = 0; l < QL; ++l) {
+            const int e = tid + l * DTH, r = e / (DK / 8), col = 8 * (e % (DK / 8));
+            *reinterpret_cast<u32x4*>(sQ[b] + swz<DK>(r, col)) = rq[l];
+            *reinterpret_cast<u32x4*>(sK[b] + swz<DK>(r, col)) = rk[l];
+        }
+        {
+            const int r = tid / (DVW / 8), col = 8 * (tid % (DVW / 8));
+            *reinterpret_cast<u32x4*>(sV[b] + swz<DVW>(r, col)) = rv;
+        }
+        if (tid < DC) sE[b][tid] = !re_valid ? 0.0f : (p.eta_kind == ETA_SOFTPLUS ? softplus_f32(re) : re);
+    };
 
     const int n_chunks = (T + DC - 1) / DC;
+    fetch(0);
+    commit(0);
+    __syncthreads();
     for (int c = 0; c < n_chunks; ++c) {
+        const int b = c & 1;
         const int t0 = c * DC;
         const int n = min(DC, T - t0);
+        const uint16_t* Q = sQ[b];
+        const uint16_t* K = sK[b];
+        const uint16_t* V = sV[b];
+        const float* E = sE[b];
+        if (c + 1 < n_chunks) fetch(c + 1);
 
-        // ---- stage q, k, v rows of the chunk (zero past T) and the rates ----
-        for (int e = tid; e < DC * D / 8; e += DTH) {
-            const int r = e / (D / 8), col = 8 * (e % (D / 8));
-            u32x4 xq = {0u, 0u, 0u, 0u}, xk = xq, xv = xq;
-            if (r < n) {
-                const size_t off = (row0 + t0 + r) * D + col;
-                xq = *reinterpret_cast<const u32x4*>(p.q + off);
-                xk = *reinterpret_cast<const u32x4*>(p.k + off);
-                xv = *reinterpret_cast<const u32x4*>(p.v + off);
-            }
-            const int s = swz<D>(r, col);
-            *reinterpret_cast<u32x4*>(sQ + s) = xq;
-            *reinterpret_cast<u32x4*>(sK + s) = xk;
-            *reinterpret_cast<u32x4*>(sV + s) = xv;
-        }
-        if (tid < DC) sE[tid] = tid < n ? eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + t0 + tid) : 0.0f;
-        __syncthreads();
-
-        // ---- R = V - K S0^T and O = Q S0^T (wave: value tiles OTB w .. OTB w + OTB - 1) ----
-        f32x4 Oacc[2][OTB];
-#pragma unroll
-        for (int ta = 0; ta < 2; ++ta)
-#pragma unroll
-            for (int j = 0; j < OTB; ++j) {
-                const int tb = OTB * wv + j;
-                f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const bf16x8 bS = as_bf16x8(lds_read16(sS + swz<D>(16 * tb + c16, 32 * kk + 8 * g)));
-                    ks = mfma16(as_bf16x8(lds_read16(sK + swz<D>(16 * ta + c16, 32 * kk + 8 * g))), bS, ks);
-                    qs = mfma16(as_bf16x8(lds_read16(sQ + swz<D>(16 * ta + c16, 32 * kk + 8 * g))), bS, qs);
-                }
-                Oacc[ta][j] = qs;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * ta + 4 * g + r, col = 16 * tb + c16;
-                    sR[t * D + col] = bf16_bits_to_f32(sV[swz<D>(t, col)]) - ks[r];
-                }
-            }
-        // ---- N = diag(eta) strictly-lower(K K^T) and P = tril(Q K^T): the 2x2 tiles of 16
-        //      tokens; waves 0..2 take the tiles (0,0), (1,0), (1,1), wave 3 zeroes (0,1) ----
-        {
-            const int ti = wv == 0 ? 0 : 1, tj = wv == 2 ? 1 : 0;
-            if (wv < 3) {
-                f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const bf16x8 bK = as_bf16x8(lds_read16(sK + swz<D>(16 * tj + c16, 32 * kk + 8 * g)));
-                    gk = mfma16(as_bf16x8(lds_read16(sK + swz<D>(16 * ti + c16, 32 * kk + 8 * g))), bK, gk);
-                    gq = mfma16(as_bf16x8(lds_read16(sQ + swz<D>(16 * ti + c16, 32 * kk + 8 * g))), bK, gq);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 16 * ti + 4 * g + r, j = 16 * tj + c16;
-                    sN[t * NSTR + j] = j < t ? sE[t] * gk[r] : 0.0f;
-                    sP[t * PSTR + j] = f32_to_bf16_bits(j <= t ? gq[r] : 0.0f);
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = 4 * g + r, j = 16 + c16;
-                    sN[t * NSTR + j] = 0.0f;
-                    sP[t * PSTR + j] = 0;
-                }
-            }
-        }
-        __syncthreads();
-
-        // ---- U: forward substitution, one thread per value column ----
-        if (tid < D) {
-            float u[DC];
-#pragma unroll
-            for (int t = 0; t < DC; ++t) {
-                float acc = sE[t] * sR[t * D + tid];
-#pragma unroll
-                for (int j4 = 0; j4 < t; j4 += 4) {
-                    const f32x4 nr = *reinterpret_cast<const f32x4*>(sN + t * NSTR + j4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (j4 + e < t) acc = fmaf(-nr[e], u[j4 + e], acc);
-                }
-                u[t] = acc;
-            }
-#pragma unroll
-            for (int t = 0; t < DC; ++t) sU[swz<D>(t, tid)] = f32_to_bf16_bits(u[t]);
-        }
-        __syncthreads();
-
-        // ---- O += tril(Q K^T) U, written out ----
+        // ---- R = V - K S0^T and O = Q S0^T: tiles (token tile ta, value tile wv) ----
+        f32x4 Oacc[2];
 #pragma unroll
         for (int ta = 0; ta < 2; ++ta) {
-            const bf16x8 aP = as_bf16x8(*reinterpret_cast<const u32x4*>(sP + (16 * ta + c16) * PSTR + 8 * g));
+            f32x4 ks = {0.f, 0.f, 0.f, 0.f}, qs = ks;
 #pragma unroll
-            for (int j = 0; j < OTB; ++j) {
-                const int tb = OTB * wv + j;
-                const f32x4 o = mfma16(aP, as_bf16x8(tr_read8<D>(sU, 8 * g, 16 * tb + 4 * q4)), Oacc[ta][j]);
+            for (int kk = 0; kk < DK / 32; ++kk) {
+                const bf16x8 bS = as_bf16x8(tr_read8<DVW>(sST, 32 * kk + 8 * g, 16 * wv + 4 * q4));
+                ks = mfma16(as_bf16x8(lds_read16(K + swz<DK>(16 * ta + c16, 32 * kk + 8 * g))), bS, ks);
+                qs = mfma16(as_bf16x8(lds_read16(Q + swz<DK>(16 * ta + c16, 32 * kk + 8 * g))), bS, qs);
+            }
+            Oacc[ta] = qs;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * ta + 4 * g + r, col = 16 * wv + c16;
+                sR[t * DVW + col] = bf16_bits_to_f32(V[swz<DVW>(t, col)]) - ks[r];
+            }
+        }
+        // ---- N = diag(eta) strictly-lower(K K^T) and P = tril(Q K^T) on the 2x2 tiles of
+        //      16 tokens: waves 0..2 take (0,0), (1,0), (1,1), wave 3 zeroes (0,1) ----
+        {
+            const int ti = wv == 0 ? 0 : 1, tj = wv == 2 ? 1 : 0;
+            f32x4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
+            if (wv < 3) {
+#pragma unroll
+                for (int kk = 0; kk < DK / 32; ++kk) {
+                    const bf16x8 bK = as_bf16x8(lds_read16(K + swz<DK>(16 * tj + c16, 32 * kk + 8 * g)));
+                    gk = mfma16(as_bf16x8(lds_read16(K + swz<DK>(16 * ti + c16, 32 * kk + 8 * g))), bK, gk);
+                    gq = mfma16(as_bf16x8(lds_read16(Q + swz<DK>(16 * ti + c16, 32 * kk + 8 * g))), bK, gq);
+                }
+            }
+            const int i0 = wv < 3 ? 16 * ti : 0, j0 = wv < 3 ? 16 * tj : 16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = i0 + 4 * g + r, j = j0 + c16;
+                const float nv = (wv < 3 && j < t) ? E[t] * gk[r] : 0.0f;
+                sN[j * NSTR + 8 * (t & 3) + (t >> 2)] = nv;
+                sP[t * PSTR + j] = f32_to_bf16_bits((wv < 3 && j <= t) ? gq[r] : 0.0f);
+            }
+        }
+        lds_barrier();
+
+        // ---- (I + N) U = diag(eta) R by forward substitution, column by column of N: lane i
+        //      of a quad keeps the running sums of the tokens t = 4m + i of its value
+        //      column; token j is final once columns 0 .. j-1 are applied, its owner's
+        //      value is broadcast to the quad (DPP) and column j applied to the rest.
+        //      N[t][j] = 0 for t <= j, so finished sums stay untouched. ----
+        {
+            const int col = tid >> 2, i = tid & 3;
+            float acc[DC / 4];
+#pragma unroll
+            for (int m = 0; m < DC / 4; ++m) acc[m] = E[4 * m + i] * sR[(4 * m + i) * DVW + col];
+            // N^T rows of four steps in registers, the next four loading meanwhile
+            f32x4 nb[2][8];
+            auto load_n = [&](int j4, f32x4* dst) TTT_INLINE {
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    dst[2 * s4] = *reinterpret_cast<const f32x4*>(sN + (j4 + s4) * NSTR + 8 * i);
+                    dst[2 * s4 + 1] = *reinterpret_cast<const f32x4*>(sN + (j4 + s4) * NSTR + 8 * i + 4);
+                }
+            };
+            auto apply = [&](const f32x4& n0, const f32x4& n1, float uj) TTT_INLINE {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[m] = fmaf(-n0[m], uj, acc[m]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[4 + m] = fmaf(-n1[m], uj, acc[4 + m]);
+            };
+            load_n(0, nb[0]);
+#pragma unroll
+            for (int j4 = 0; j4 < DC; j4 += 4) {
+                const f32x4* cur = nb[(j4 >> 2) & 1];
+                if (j4 + 4 < DC) load_n(j4 + 4, nb[((j4 >> 2) + 1) & 1]);
+                apply(cur[0], cur[1], quad_bcast<0>(acc[j4 >> 2]));
+                apply(cur[2], cur[3], quad_bcast<1>(acc[j4 >> 2]));
+                apply(cur[4], cur[5], quad_bcast<2>(acc[j4 >> 2]));
+                if (j4 + 3 < DC - 1) apply(cur[6], cur[7], quad_bcast<3>(acc[j4 >> 2]));
+            }
+#pragma unroll
+            for (int m = 0; m < DC / 4; ++m) sU[swz<DVW>(4 * m + i, col)] = f32_to_bf16_bits(acc[m]);
+        }
+        lds_barrier();
+
+        // ---- S += U^T K, and its bf16 copy for the next chunk ----
+        {
+            const bf16x8 aU = as_bf16x8(tr_read8<DVW>(sU, 8 * g, vr0 + 4 * q4));
+#pragma unroll
+            for (int bt = 0; bt < NT; ++bt) {
+                St[bt] = mfma16(aU, as_bf16x8(tr_read8<DK>(K, 8 * g, 16 * bt + 4 * q4)), St[bt]);
+                // lane holds S[vr0 + 4g + r][16 bt + c16], r = 0..3: four consecutive entries of
+                // one row of S^T
+                *reinterpret_cast<u32x2*>(sST + swz<DVW>(16 * bt + c16, vr0 + 4 * g)) =
+                    u32x2{pack_bf16x2(St[bt][0], St[bt][1]), pack_bf16x2(St[bt][2], St[bt][3])};
+            }
+        }
+        // the next chunk's rows go to LDS before this chunk's outputs are stored: the wait
+        // for the loads (vector-memory counter) then does not include the stores
+        if (c + 1 < n_chunks) commit(b ^ 1);
+        // ---- O += tril(Q K^T) U, written out ----
+        {
+            const bf16x8 bU = as_bf16x8(tr_read8<DVW>(sU, 8 * g, 16 * wv + 4 * q4));
+#pragma unroll
+            for (int ta = 0; ta < 2; ++ta) {
+                const bf16x8 aP = as_bf16x8(*reinterpret_cast<const u32x4*>(sP + (16 * ta + c16) * PSTR + 8 * g));
+                const f32x4 o = mfma16(aP, bU, Oacc[ta]);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int t = 16 * ta + 4 * g + r;
-                    if (t < n) p.o[(row0 + t0 + t) * D + 16 * tb + c16] = f32_to_bf16_bits(o[r]);
+                    if (t < n) p.o[(row0 + t0 + t) * dv + vc0 + 16 * wv + c16] = f32_to_bf16_bits(o[r]);
                 }
             }
         }
-        // ---- S += U^T K, and its bf16 copy for the next chunk ----
-#pragma unroll
-        for (int a = 0; a < SRT; ++a) {
-            const bf16x8 aU = as_bf16x8(tr_read8<D>(sU, 8 * g, vr0 + 16 * a + 4 * q4));
-#pragma unroll
-            for (int b = 0; b < NT; ++b) {
-                St[a][b] = mfma16(aU, as_bf16x8(tr_read8<D>(sK, 8 * g, 16 * b + 4 * q4)), St[a][b]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sS[swz<D>(vr0 + 16 * a + 4 * g + r, 16 * b + c16)] = f32_to_bf16_bits(St[a][b][r]);
-            }
-        }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -222,7 +283,8 @@ hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
     p.eta_scalar = a.eta_scalar;
     p.eta_kind = a.eta_kind;
     p.T = s.T;
-    const dim3 grid((unsigned)s.n_seq()), block(DTH);
+    p.n_vsplit = s.d_v / DVW;
+    const dim3 grid((unsigned)(s.n_seq() * p.n_vsplit)), block(DTH);
     const void* fn = s.d_k == 128 ? reinterpret_cast<const void*>(delta_forward<128>)
                                   : reinterpret_cast<const void*>(delta_forward<64>);
     if (ev_begin || ev_end) {
