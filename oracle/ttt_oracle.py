@@ -55,7 +55,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "softplus", "silu", "swiglu_features", "features", "learning_rates",
+    "softplus", "silu", "silu_grad", "swiglu_features", "features", "learning_rates",
     "binding_loss", "binding_loss_grad", "mse_loss", "mse_loss_grad", "forward", "forward_closed_form",
     "forward_chunked", "rel_err",
 ]
@@ -280,9 +280,23 @@ def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: fl
     return o.reshape(B, H, d_v), S_new.reshape(B, H, d_v, d_phi), M_new.reshape(B, H, d_v, d_phi)
 
 
+def silu_grad(u):
+    """d silu(u) / du = sigmoid(u) (1 + u (1 - sigmoid(u)))."""
+    u = np.asarray(u, dtype=np.float64)
+    sg = 1.0 / (1.0 + np.exp(-u))
+    return sg * (1.0 + u * (1.0 - sg))
+
+
 def backward(q, k, v, dO, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
-             beta: float = 0.0, causal: bool = True):
-    """Gradients of sum(o * dO) for the identity feature map, fp64.
+             beta: float = 0.0, causal: bool = True, phi: str = "identity", w1=None, w3=None):
+    """Gradients of sum(o * dO), fp64.
+
+    phi="swiglu": the recurrence below runs on the features phi(q), phi(k)
+    (it gives dphi(q), dphi(k) in place of dq, dk), then the chain rule through
+    phi(x) = silu(u) * g, u = W1 x, g = W3 x:
+      du = dphi * g * silu'(u),  dg = dphi * silu(u)
+      dx = W1^T du + W3^T dg,    dW1[h] = sum over b, t of du x^T (q and k both), dW3 alike.
+    Returns (dq, dk, dv, deta, dW1, dW3) for SwiGLU.
 
     The plain reverse-mode derivative of ``forward`` (backpropagation through
     the token loop).  With G_t = dL/dS_t and H_t = dL/dM_t:
@@ -296,10 +310,19 @@ def backward(q, k, v, dO, *, eta_mode: str = "scalar", eta=None, eta_scalar: flo
     scalar mode.  Returns (dq, dk, dv, deta).
     """
     q = np.asarray(q, dtype=np.float64)
-    B, H, T, d_k = q.shape
+    B, H, T, d_in = q.shape
     d_v = np.shape(v)[-1]
     N = B * H
-    qf, kf, vf = _flatten(q, d_k), _flatten(k, d_k), _flatten(v, d_v)
+    xq, xk, vf = _flatten(q, d_in), _flatten(k, d_in), _flatten(v, d_v)
+    if phi == "swiglu":
+        w1n = np.broadcast_to(np.asarray(w1, np.float64)[None], (B,) + np.shape(w1)).reshape(N, -1, d_in)
+        w3n = np.broadcast_to(np.asarray(w3, np.float64)[None], (B,) + np.shape(w3)).reshape(N, -1, d_in)
+        qf, kf = features(xq, phi, w1n, w3n), features(xk, phi, w1n, w3n)
+    elif phi == "identity":
+        qf, kf = xq, xk
+    else:
+        raise ValueError(f"unknown feature map {phi!r}")
+    d_k = qf.shape[-1]
     gf = _flatten(dO, d_v)
     lr = learning_rates(eta_mode, T, N, eta, eta_scalar)
     # forward states S_t (the readout needs them)
@@ -337,7 +360,21 @@ def backward(q, k, v, dO, *, eta_mode: str = "scalar", eta=None, eta_scalar: flo
         deta = (de / (1.0 + np.exp(-a))).reshape(B, H, T)
     else:
         deta = float(de.sum())
-    return shape(dq, d_k), shape(dk, d_k), shape(dv, d_v), deta
+    if phi != "swiglu":
+        return shape(dq, d_k), shape(dk, d_k), shape(dv, d_v), deta
+    # chain rule through the feature map, for q and for k
+    dW1 = np.zeros(np.shape(w1))
+    dW3 = np.zeros(np.shape(w3))
+    dx = []
+    for x, dphi in ((xq, dq), (xk, dk)):
+        u = np.einsum("nfd,ntd->ntf", w1n, x)
+        g = np.einsum("nfd,ntd->ntf", w3n, x)
+        du = dphi * g * silu_grad(u)
+        dg = dphi * silu(u)
+        dx.append(np.einsum("nfd,ntf->ntd", w1n, du) + np.einsum("nfd,ntf->ntd", w3n, dg))
+        dW1 += np.einsum("ntf,ntd->nfd", du, x).reshape(B, H, -1, d_in).sum(axis=0)
+        dW3 += np.einsum("ntf,ntd->nfd", dg, x).reshape(B, H, -1, d_in).sum(axis=0)
+    return shape(dx[0], d_in), shape(dx[1], d_in), shape(dv, d_v), deta, dW1, dW3
 
 
 # ----------------------------------------------------------------------------

@@ -90,3 +90,71 @@ def test_planted_backward_mistakes_fail_a_pin(monkeypatch, mistake):
     monkeypatch.setattr(oracle, "backward", bad)
     with pytest.raises(AssertionError):
         test_backward_hand_example()
+
+
+# ----------------------------------------------------------------------------
+# SwiGLU feature map (Variant 2): gradients through phi and of W1, W3
+# ----------------------------------------------------------------------------
+
+def test_swiglu_backward_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_swiglu_backward_T1.json")))
+    one = lambda x: np.full((1, 1, 1, 1), float(x))
+    w = lambda x: np.full((1, 1, 1), float(x))
+    o = oracle.forward(one(g["q"]), one(g["k"]), one(g["v"]), eta_mode="per_token", eta=np.full((1, 1, 1), g["eta"]),
+                       phi="swiglu", w1=w(g["w1"]), w3=w(g["w3"]))
+    assert abs(o.item() - g["o"]) <= 1e-12
+    dq, dk, dv, de, dW1, dW3 = oracle.backward(one(g["q"]), one(g["k"]), one(g["v"]), one(g["dO"]),
+                                               eta_mode="per_token", eta=np.full((1, 1, 1), g["eta"]),
+                                               phi="swiglu", w1=w(g["w1"]), w3=w(g["w3"]))
+    for got, name in ((dq, "dq"), (dk, "dk"), (dv, "dv"), (de, "deta"), (dW1, "dW1"), (dW3, "dW3")):
+        assert abs(np.asarray(got).item() - g[name]) <= 1e-12, name
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("eta_mode,beta", [("scalar", 0.0), ("softplus", 0.6), ("per_token", 0.6)])
+def test_swiglu_backward_matches_finite_differences(causal, eta_mode, beta):
+    rng = np.random.default_rng(22)
+    B, H, T, d_in, d_phi, dv_ = 2, 2, 4, 3, 5, 2
+    q = rng.standard_normal((B, H, T, d_in))
+    k = rng.standard_normal((B, H, T, d_in))
+    v = rng.standard_normal((B, H, T, dv_))
+    dO = rng.standard_normal((B, H, T, dv_))
+    a = rng.standard_normal((B, H, T))
+    w1 = rng.standard_normal((H, d_phi, d_in)) * 0.7
+    w3 = rng.standard_normal((H, d_phi, d_in)) * 0.7
+    es = 0.8
+    eta = None if eta_mode == "scalar" else a
+    kw = dict(eta_mode=eta_mode, beta=beta, causal=causal, phi="swiglu")
+
+    def L(q_=q, k_=k, v_=v, a_=eta, w1_=w1, w3_=w3):
+        return float((oracle.forward(q_, k_, v_, eta=a_, eta_scalar=es, w1=w1_, w3=w3_, **kw) * dO).sum())
+
+    dq, dk, dv, de, dW1, dW3 = oracle.backward(q, k, v, dO, eta=eta, eta_scalar=es, w1=w1, w3=w3, **kw)
+    tol = dict(rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(dq, _fd(lambda x: L(q_=x), q), **tol)
+    np.testing.assert_allclose(dk, _fd(lambda x: L(k_=x), k), **tol)
+    np.testing.assert_allclose(dv, _fd(lambda x: L(v_=x), v), **tol)
+    np.testing.assert_allclose(dW1, _fd(lambda x: L(w1_=x), w1), **tol)
+    np.testing.assert_allclose(dW3, _fd(lambda x: L(w3_=x), w3), **tol)
+    if eta_mode != "scalar":
+        np.testing.assert_allclose(de, _fd(lambda x: L(a_=x), a), **tol)
+
+
+@pytest.mark.parametrize("mistake", ["silu_grad_as_sigmoid", "gate_grad_dropped"])
+def test_planted_swiglu_backward_mistakes_fail_a_pin(monkeypatch, mistake):
+    test_swiglu_backward_hand_example()
+    if mistake == "silu_grad_as_sigmoid":
+        monkeypatch.setattr(O, "silu_grad", lambda u: 1.0 / (1.0 + np.exp(-np.asarray(u, float))))
+    else:
+        orig = O.silu
+        # the gate's own gradient dg = dphi * silu(u) lost: silu reads as zero where the
+        # backward calls it
+
+        def silu_only_in_forward(u):
+            import inspect
+            if inspect.stack()[1].function == "backward":
+                return np.zeros_like(np.asarray(u, float))
+            return orig(u)
+        monkeypatch.setattr(O, "silu", silu_only_in_forward)
+    with pytest.raises(AssertionError):
+        test_swiglu_backward_hand_example()
