@@ -242,10 +242,36 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
                     float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV, float* dEta,
                     void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Gradients of a SwiGLU layer (Variant 2 of Table 2 on the thelatestinai.com page:
+ * only the last layer of the fast-weight MLP is updated by the inner loop, so W1
+ * and W3 are slow weights, trained through the outer loop as Figure 4 trains the
+ * parallel form end to end).  With L = sum(o * dO) for the o of ttt_la_forward on
+ * the same arguments:
+ *   dQ, dK, dV, dEta  as for ttt_la_backward (dQ and dK through phi)
+ *   dW1, dW3  device fp32 [H, d_phi, d_k], 16-byte aligned: dL/dW1, dL/dW3 summed
+ *            over the batch (overwritten, not accumulated)
+ *   workspace  caller-owned device memory, 256-byte aligned, at least
+ *            ttt_la_backward_workspace(h, mode) bytes
+ * bf16, d_k = d_v = 128 (TTT_LA_ERR_UNSUPPORTED otherwise, and for
+ * TTT_LA_LOSS_MSE).  Causal and bidirectional.  Runs, on hip_stream: the features
+ * phi(q), phi(k); for each 128-feature slice a forward of the d = 128 identity plan
+ * giving dL/dphi(q) and one (rate 1, over the sequence reversed in time when
+ * causal) giving dL/dphi(k); one SwiGLU forward of (k, q, dO) at rate 1 giving
+ * dV and dEta; the chain rule through phi (du = dphi g silu'(u), dg = dphi silu(u))
+ * and the products dq = W1^T du + W3^T dg, dW1 = sum du x^T, dW3 = sum dg x^T,
+ * with fixed-order sums.  No device memory is allocated.  The outputs must not
+ * overlap each other, any input or the workspace.
+ * Errors: as ttt_la_backward. */
+int ttt_la_backward_swiglu(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
+                           float eta_scalar, float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV,
+                           float* dEta, float* dW1, float* dW3, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
 /* Bytes of workspace ttt_la_backward needs on handle h for the given mode bits:
  * two [B, H, T, d] tensors (the outputs of the two rate-1 forwards), plus in
  * causal mode either two segment-summary areas of the handle's plan (bf16 d = 128
- * plans of three launches) or the four time-reversed operands.  Host only;
+ * plans of three launches) or the four time-reversed operands.  For a SwiGLU
+ * handle: the workspace of ttt_la_backward_swiglu.  Host only;
  * TTT_LA_ERR_UNSUPPORTED if the handle's shape has no backward. */
 int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes);
 

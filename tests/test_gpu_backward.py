@@ -104,18 +104,34 @@ def test_backward_other_shapes(case):
     run_case(w)
 
 
-def test_backward_unsupported_for_swiglu():
+def test_backward_entry_points_for_swiglu():
     import torch
     import ttt_weight_layers_amd as tla
+    # d = 128: the workspace query answers for ttt_la_backward_swiglu; ttt_la_backward itself
+    # (no place for dW1, dW3) refuses a SwiGLU handle
     w = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=64).with_settings(d_phi=128)
     x = make_inputs(w)
     d = to_device(x)
     lay = make_layer(w, d)
-    st, _ = tla.ttt_la_backward_workspace(lay.handle, 0)
-    assert st == tla.TTT_LA_ERR_UNSUPPORTED
+    st, nbytes = tla.ttt_la_backward_workspace(lay.handle, tla.TTT_LA_ETA_SOFTPLUS)
+    assert st == tla.TTT_LA_OK and nbytes > 0
     dO = torch.zeros_like(d["v"])
+    outs = [torch.empty_like(d["q"]) for _ in range(3)]
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    st = tla.ttt_la_backward(lay.handle, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(), d["a"].data_ptr(),
+                             0.0, 0.9, tla.TTT_LA_ETA_SOFTPLUS, dO.data_ptr(), *(o.data_ptr() for o in outs), None,
+                             ws.data_ptr(), nbytes, None)
+    assert st == tla.TTT_LA_ERR_UNSUPPORTED
+    # d = 64: no SwiGLU backward
+    w64 = small("v2_swiglu_4x16x8192_d128_f512", B=1, H=2, T=64).with_settings(d_k=64, d_v=64, d_phi=128)
+    x64 = make_inputs(w64)
+    d64 = to_device(x64)
+    lay64 = make_layer(w64, d64)
+    st, _ = tla.ttt_la_backward_workspace(lay64.handle, 0)
+    assert st == tla.TTT_LA_ERR_UNSUPPORTED
     with pytest.raises(tla.TTTError) as e:
-        lay.backward(d["q"], d["k"], d["v"], dO, eta=d["a"], eta_mode="softplus", beta=0.9)
+        lay64.backward(d64["q"], d64["k"], d64["v"], torch.zeros_like(d64["v"]), eta=d64["a"], eta_mode="softplus",
+                       beta=0.9)
     assert e.value.status == tla.TTT_LA_ERR_UNSUPPORTED
 
 

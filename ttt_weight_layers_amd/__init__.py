@@ -10,7 +10,7 @@ from ._binding import (  # noqa: F401
     ttt_la_check, ttt_la_create, ttt_la_desc, ttt_la_destroy, ttt_la_enable_kernel_timing,
     ttt_la_enable_kernel_timing_every,
     ttt_la_forward, ttt_la_forward_noalloc, ttt_la_forward_state, ttt_la_step, ttt_la_check_state, ttt_la_get_plan,
-    ttt_la_backward, ttt_la_backward_workspace, ttt_la_check_backward,
+    ttt_la_backward, ttt_la_backward_swiglu, ttt_la_backward_workspace, ttt_la_check_backward,
     ttt_la_kernel_times, ttt_la_plan, ttt_la_status_string,
     ttt_la_wait_status,
     TTT_LA_OK, TTT_LA_ERR_INVALID_ARG, TTT_LA_ERR_UNSUPPORTED, TTT_LA_ERR_HIP, TTT_LA_ERR_OOM,

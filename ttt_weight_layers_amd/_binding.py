@@ -71,7 +71,7 @@ EXPORTS = ("ttt_la_create", "ttt_la_create_hinted", "ttt_la_check_hints", "ttt_l
            "ttt_la_backward_workspace", "ttt_la_destroy",
            "ttt_la_status_string", "ttt_la_check", "ttt_la_check_state", "ttt_la_check_backward", "ttt_la_get_plan",
            "ttt_la_wait_status", "ttt_la_enable_kernel_timing", "ttt_la_kernel_times",
-           "ttt_la_enable_kernel_timing_every", "ttt_la_forward_noalloc")
+           "ttt_la_enable_kernel_timing_every", "ttt_la_forward_noalloc", "ttt_la_backward_swiglu")
 
 _lib: Optional[ctypes.CDLL] = None
 
@@ -108,6 +108,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ttt_la_check_state.restype = ctypes.c_int
     lib.ttt_la_backward.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.ttt_la_backward.restype = ctypes.c_int
+    lib.ttt_la_backward_swiglu.argtypes = [vp, vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                           ctypes.c_size_t, vp]
+    lib.ttt_la_backward_swiglu.restype = ctypes.c_int
     lib.ttt_la_check_backward.argtypes = [ctypes.POINTER(ttt_la_desc), ctypes.POINTER(ttt_la_hints), vp, vp, vp, vp, f32, f32, u32, vp, vp, vp, vp,
                                           vp, vp, ctypes.c_size_t]
     lib.ttt_la_check_backward.restype = ctypes.c_int
@@ -208,6 +211,13 @@ def ttt_la_check_backward(desc: ttt_la_desc, hints: Optional[ttt_la_hints] = Non
     return load_library().ttt_la_check_backward(ctypes.byref(desc), None if hints is None else ctypes.byref(hints),
                                                 q, k, v, eta, float(eta_scalar), float(beta),
                                                 int(mode), dO, dQ, dK, dV, dEta, workspace, int(workspace_bytes))
+
+
+def ttt_la_backward_swiglu(h, q: int, k: int, v: int, eta: Optional[int], eta_scalar: float, beta: float,
+                           mode: int, dO: int, dQ: int, dK: int, dV: int, dEta: Optional[int], dW1: int, dW3: int,
+                           workspace: Optional[int], workspace_bytes: int, stream: Optional[int]) -> int:
+    return load_library().ttt_la_backward_swiglu(h, q, k, v, eta, float(eta_scalar), float(beta), int(mode), dO, dQ,
+                                                 dK, dV, dEta, dW1, dW3, workspace, int(workspace_bytes), stream)
 
 
 def ttt_la_backward_workspace(h, mode: int):
@@ -473,8 +483,9 @@ class TTTLinearAttention:
 
     def backward(self, q, k, v, dO, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", causal=True,
                  stream=None, want_eta=True):
-        """Gradients (dq, dk, dv, deta) of sum(o * dO); the workspace is a device tensor
-        allocated here (the library itself allocates nothing)."""
+        """Gradients (dq, dk, dv, deta) of sum(o * dO), and (dW1, dW3) for a SwiGLU layer;
+        the workspace is a device tensor allocated here (the library itself allocates
+        nothing)."""
         import torch
         mode = mode_bits(eta_mode, causal)
         check_tensors(self.desc, "backward", mode, q=q, k=k, v=v, eta=eta, dO=dO)
@@ -485,6 +496,18 @@ class TTTLinearAttention:
         ws = torch.empty(max(1, nbytes), dtype=torch.uint8, device=q.device)
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         de = torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device) if want_eta else None
+        if self.desc.phi == TTT_LA_PHI_SWIGLU:
+            # also the gradients of the feature map's weights (fp32 [H, d_phi, d_k])
+            wshape = (self.desc.H, self.desc.d_phi, self.desc.d_k)
+            dw1 = torch.empty(wshape, dtype=torch.float32, device=q.device)
+            dw3 = torch.empty(wshape, dtype=torch.float32, device=q.device)
+            st = ttt_la_backward_swiglu(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode,
+                                        _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(de), _ptr(dw1), _ptr(dw3),
+                                        _ptr(ws), nbytes, s)
+            if st != TTT_LA_OK:
+                raise TTTError(st, "ttt_la_backward_swiglu")
+            _record(ext, ws, dq, dk, dv, de, dw1, dw3)
+            return dq, dk, dv, de, dw1, dw3
         st = ttt_la_backward(self.handle, _ptr(q), _ptr(k), _ptr(v), _ptr(eta), eta_scalar, beta, mode, _ptr(dO),
                              _ptr(dq), _ptr(dk), _ptr(dv), _ptr(de), _ptr(ws), nbytes, s)
         if st != TTT_LA_OK:

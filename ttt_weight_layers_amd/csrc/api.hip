@@ -466,6 +466,120 @@ int check_backward(const ttt_la_desc* d, const ttt_la_hints& hn, const void* q, 
     return TTT_LA_OK;
 }
 
+// ---- backward through the SwiGLU feature map ----
+
+// Workspace of ttt_la_backward_swiglu (offsets in bytes, each 256-aligned), rows = B H T,
+// P = d_phi / 128 feature slices:
+//   phi_q, phi_k   P x rows x 128 bf16: the features, slice-major
+//   dphi_q         P x rows x 128: dL/dphi(q), slice by slice
+//   w              P x rows x 128: dL/dphi(k) / (eta c), slice by slice
+//   u              rows x 128: the rate-1 forward giving dv and the rate gradient
+//   rq, rk, rdo    rows x 128 each (causal only): q, k, dO reversed in time
+//   dg_q, dg_k     rows x 2 d_phi: [du | dg] of q and of k
+//   wcat           H x 128 x 2 d_phi: [W1 ; W3]^T
+//   sum            segment summaries of the feature-space forwards (d = 128 plan)
+//   part           per-slice partial outputs of the SwiGLU forward
+//   dwpart         fp32 partial sums of dW1, dW3
+struct SwBwdLayout {
+    size_t phi_q, phi_k, dphi_q, w, u, rq, rk, rdo, dg_q, dg_k, wcat, sum, part, dwpart, total;
+};
+
+Shape feature_shape(const Shape& s) {
+    Shape f = s;
+    f.swiglu = false;
+    f.d_k = f.d_v = f.d_phi = 128;
+    f.w1 = f.w3 = nullptr;
+    return f;
+}
+
+SwBwdLayout swiglu_bwd_layout(const ttt_la_desc& d, uint32_t mode) {
+    const Shape s = shape_of(d);
+    const size_t rows = (size_t)s.n_seq() * s.T, P = s.d_phi / 128, E = 2;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) / 256 * 256;
+        return o;
+    };
+    SwBwdLayout L{};
+    L.phi_q = take(P * rows * 128 * E);
+    L.phi_k = take(P * rows * 128 * E);
+    L.dphi_q = take(P * rows * 128 * E);
+    L.w = take(P * rows * 128 * E);
+    L.u = take(rows * 128 * E);
+    if (!(mode & TTT_LA_BIDIRECTIONAL)) {
+        L.rq = take(rows * 128 * E);
+        L.rk = take(rows * 128 * E);
+        L.rdo = take(rows * 128 * E);
+    }
+    L.dg_q = take(rows * 2 * s.d_phi * E);
+    L.dg_k = take(rows * 2 * s.d_phi * E);
+    L.wcat = take((size_t)s.H * 128 * 2 * s.d_phi * E);
+    L.sum = take(ttt::fast_plan(feature_shape(s), 0, 0, 0, 0).summary_bytes);
+    L.part = take(ttt::fast_plan(s, d.chunk, 0, 0, 0).partial_bytes);
+    L.dwpart = take(ttt::swiglu_dw_partial_bytes(s));
+    L.total = off;
+    return L;
+}
+
+bool swiglu_backward_ok(const ttt_la_desc& d) {
+    return d.phi == TTT_LA_PHI_SWIGLU && ttt::swiglu_backward_supported(shape_of(d));
+}
+
+int check_backward_swiglu(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
+                          float eta_scalar, float beta, uint32_t mode, const void* dO, const void* dQ, const void* dK,
+                          const void* dV, const float* dEta, const float* dW1, const float* dW3, const void* ws,
+                          size_t ws_bytes) {
+    int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, dQ);
+    if (st != TTT_LA_OK) return st;
+    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;
+    if (!swiglu_backward_ok(*d)) return TTT_LA_ERR_UNSUPPORTED;
+    if (!dO || !dQ || !dK || !dV || !dW1 || !dW3) return TTT_LA_ERR_INVALID_ARG;
+    if (!aligned(dO, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) || !aligned(dW1, 16) ||
+        !aligned(dW3, 16))
+        return TTT_LA_ERR_INVALID_ARG;
+    if (dEta && !aligned(dEta, 4)) return TTT_LA_ERR_INVALID_ARG;
+    const size_t need = swiglu_bwd_layout(*d, mode).total;
+    if (!ws || !aligned(ws, 256) || ws_bytes < need) return TTT_LA_ERR_INVALID_ARG;
+    const size_t tb = tensor_bytes(*d);
+    const size_t nt = (size_t)d->B * d->H * d->T;
+    const size_t wb = (size_t)d->H * d->d_phi * d->d_k * sizeof(float);
+    const size_t w_in = (size_t)d->H * d->d_phi * d->d_k * 2;
+    const void* outs[6] = {dQ, dK, dV, dEta, dW1, dW3};
+    const size_t out_bytes[6] = {tb, tb, tb, nt * sizeof(float), wb, wb};
+    const void* ins[7] = {q, k, v, dO, eta, d->w1, d->w3};
+    const size_t in_bytes[7] = {tb, tb, tb, tb, eta ? nt * sizeof(float) : 0, w_in, w_in};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 7; ++j)
+            if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
+        if (overlaps(outs[i], out_bytes[i], ws, need)) return TTT_LA_ERR_INVALID_ARG;
+    }
+    for (int j = 0; j < 7; ++j)
+        if (overlaps(ws, need, ins[j], in_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
+    return TTT_LA_OK;
+}
+
+// one forward of the d = 128 identity plan on feature slices (no handle state touched)
+hipError_t feature_forward(const Shape& sf, const ttt::FastPlan& pf, void* ws_sum, const void* q, const void* k,
+                           const void* v, const float* eta, float eta_scalar, float beta, int eta_kind, bool bidir,
+                           bool reverse, void* o, hipStream_t st) {
+    ttt::FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.eta = eta;
+    a.eta_scalar = eta_scalar;
+    a.beta = beta;
+    a.eta_kind = eta_kind;
+    a.bidirectional = bidir;
+    a.reverse = reverse;
+    a.o = o;
+    a.stream = st;
+    return ttt::launch_fast(sf, pf, ws_sum, a, nullptr, nullptr, nullptr);
+}
+
 }  // namespace
 
 extern "C" {
@@ -485,8 +599,107 @@ int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes) {
     if (!h || !bytes) return TTT_LA_ERR_INVALID_ARG;
     *bytes = 0;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
+    if (swiglu_backward_ok(h->desc)) {
+        *bytes = swiglu_bwd_layout(h->desc, mode).total;
+        return TTT_LA_OK;
+    }
     if (!backward_supported(h->desc)) return TTT_LA_ERR_UNSUPPORTED;
     *bytes = backward_ws_bytes(h->desc, h->hints, mode);
+    return TTT_LA_OK;
+}
+
+int ttt_la_backward_swiglu(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
+                           float eta_scalar, float beta, uint32_t mode, const void* dO, void* dQ, void* dK, void* dV,
+                           float* dEta, float* dW1, float* dW3, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+    if (!h) return TTT_LA_ERR_INVALID_ARG;
+    int st = check_backward_swiglu(&h->desc, q, k, v, eta, eta_scalar, beta, mode, dO, dQ, dK, dV, dEta, dW1, dW3,
+                                   workspace, workspace_bytes);
+    if (st != TTT_LA_OK) return st;
+    hipStream_t stream = static_cast<hipStream_t>(hip_stream);
+    const bool bidir = (mode & TTT_LA_BIDIRECTIONAL) != 0;
+    const int kind = eta_kind_of(mode);
+    const Shape& s = h->shape;
+    const Shape sf = feature_shape(s);
+    const ttt::FastPlan pf = ttt::fast_plan(sf, 0, 0, 0, 0);
+    const SwBwdLayout L = swiglu_bwd_layout(h->desc, mode);
+    char* ws = static_cast<char*>(workspace);
+    const size_t rows = (size_t)s.n_seq() * s.T, slice = rows * 128 * 2;
+    const int P = s.d_phi / 128;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+#define TTT_TRY(x)                     \
+    do {                               \
+        if (!ok(x)) {                  \
+            (void)hipGetLastError();   \
+            return TTT_LA_ERR_HIP;     \
+        }                              \
+    } while (0)
+    TTT_TRY(ttt::launch_swiglu_wcat(s, ws + L.wcat, stream));
+    TTT_TRY(ttt::launch_swiglu_gate(s, false, q, ws + L.phi_q, nullptr, nullptr, nullptr, 0.0f, 0.0f, 0, false, bidir,
+                                    stream));
+    TTT_TRY(ttt::launch_swiglu_gate(s, false, k, ws + L.phi_k, nullptr, nullptr, nullptr, 0.0f, 0.0f, 0, false, bidir,
+                                    stream));
+    for (int p = 0; p < P; ++p) {
+        // dL/dphi(q): the forward with (q, k, v) -> (dO, v, phi(k)) and the caller's rates
+        TTT_TRY(feature_forward(sf, pf, ws + L.sum, dO, v, ws + L.phi_k + p * slice, eta, eta_scalar, beta, kind,
+                                bidir, false, ws + L.dphi_q + p * slice, stream));
+        // w: rate-1 forward of (v, dO, phi(q)), over the reversed sequence when causal (the
+        // d = 128 kernels read and write the rows in reverse order themselves)
+        TTT_TRY(feature_forward(sf, pf, ws + L.sum, v, dO, ws + L.phi_q + p * slice, nullptr, 1.0f,
+                                bidir ? 0.0f : beta, 0, bidir, !bidir, ws + L.w + p * slice, stream));
+    }
+    // u: rate-1 SwiGLU forward of (k, q, dO), over reversed copies when causal
+    {
+        ttt::FwdArgs a{};
+        a.eta = nullptr;
+        a.eta_scalar = 1.0f;
+        a.eta_kind = 0;
+        a.bidirectional = bidir;
+        a.beta = bidir ? 0.0f : beta;
+        a.o = ws + L.u;
+        a.stream = stream;
+        if (bidir) {
+            a.q = k;
+            a.k = q;
+            a.v = dO;
+        } else {
+            const void* src[3] = {q, k, dO};
+            void* dst[3] = {ws + L.rq, ws + L.rk, ws + L.rdo};
+            TTT_TRY(ttt::launch_reverse(src, dst, 3, (size_t)s.n_seq(), s.T, 128 * 2, stream));
+            a.q = ws + L.rk;
+            a.k = ws + L.rq;
+            a.v = ws + L.rdo;
+        }
+        TTT_TRY(ttt::launch_fast(s, h->fp, ws + L.part, a, nullptr, nullptr, nullptr));
+    }
+    // dv and the rate gradient from u
+    {
+        ttt::BackArgs b{};
+        b.u = ws + L.u;
+        b.w = ws + L.u;
+        b.v = v;
+        b.eta = eta;
+        b.dk = nullptr;
+        b.dv = dV;
+        b.deta = dEta;
+        b.eta_scalar = eta_scalar;
+        b.beta = beta;
+        b.eta_kind = kind;
+        b.causal = !bidir;
+        b.uw_reversed = !bidir;
+        b.stream = stream;
+        TTT_TRY(ttt::launch_finalize_grads(s, b));
+    }
+    // through phi: [du | dg] of q (dphi as is) and of k (w scaled by eta c), then dq, dk, dW1, dW3
+    TTT_TRY(ttt::launch_swiglu_gate(s, true, q, nullptr, ws + L.dphi_q, ws + L.dg_q, eta, eta_scalar, beta, kind, false,
+                                    bidir, stream));
+    TTT_TRY(ttt::launch_swiglu_gate(s, true, k, nullptr, ws + L.w, ws + L.dg_k, eta, eta_scalar, beta, kind, true,
+                                    bidir, stream));
+    TTT_TRY(ttt::launch_swiglu_dx(s, ws + L.dg_q, ws + L.wcat, dQ, stream));
+    TTT_TRY(ttt::launch_swiglu_dx(s, ws + L.dg_k, ws + L.wcat, dK, stream));
+    TTT_TRY(ttt::launch_swiglu_dw(s, ws + L.dg_q, ws + L.dg_k, q, k, reinterpret_cast<float*>(ws + L.dwpart), dW1, dW3,
+                                  stream));
+#undef TTT_TRY
     return TTT_LA_OK;
 }
 

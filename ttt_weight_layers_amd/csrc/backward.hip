@@ -115,18 +115,19 @@ __global__ void __launch_bounds__(256) finalize_grads(FinalizeParams p) {
     const float e = eta_at(p.eta_kind, p.eta, p.eta_scalar, r);
     float u[VE], w[VE], v[VE];
     load_vec(static_cast<const TI*>(p.u) + src * p.d + j0, u);
-    load_vec(static_cast<const TI*>(p.w) + src * p.d + j0, w);
+    if (p.dk) load_vec(static_cast<const TI*>(p.w) + src * p.d + j0, w);
     load_vec(static_cast<const TI*>(p.v) + r * p.d + j0, v);
     float dv[VE], dk[VE], dot = 0.0f;
 #pragma unroll
     for (int i = 0; i < VE; ++i) {
         dv[i] = e * c * u[i];
-        dk[i] = e * c * w[i];
+        dk[i] = p.dk ? e * c * w[i] : 0.0f;
         dot = fmaf(v[i], u[i], dot);
     }
     if (live) {
         store_vec(static_cast<TI*>(p.dv) + r * p.d + j0, dv);
-        store_vec(static_cast<TI*>(p.dk) + r * p.d + j0, dk);
+        // no dk when the key gradient is formed elsewhere (through the SwiGLU feature map)
+        if (p.dk) store_vec(static_cast<TI*>(p.dk) + r * p.d + j0, dk);
     }
     // the row's lanes are consecutive and lpr is a power of two
     for (int off = lpr / 2; off > 0; off >>= 1) dot += __shfl_xor(dot, off, 64);

@@ -106,6 +106,18 @@ hipError_t launch_short(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
 bool delta_supported(const Shape& s);
 hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// backward through the SwiGLU feature map (swiglu_bwd.hip): d_k = d_v = 128, bf16
+bool swiglu_backward_supported(const Shape& s);
+int swiglu_dw_split(const Shape& s);
+size_t swiglu_dw_partial_bytes(const Shape& s);
+hipError_t launch_swiglu_gate(const Shape& s, bool grads, const void* x, void* phi, const void* dphi, void* dg,
+                              const float* eta, float eta_scalar, float beta, int eta_kind, bool scale_eta,
+                              bool bidir, hipStream_t st);
+hipError_t launch_swiglu_dx(const Shape& s, const void* dg, const void* wcat, void* dx, hipStream_t st);
+hipError_t launch_swiglu_dw(const Shape& s, const void* dg_q, const void* dg_k, const void* x_q, const void* x_k,
+                            float* part, float* dw1, float* dw3, hipStream_t st);
+hipError_t launch_swiglu_wcat(const Shape& s, void* wcat, hipStream_t st);
+
 bool swiglu_supported(const Shape& s);
 // fp32 parts of o of the feature slices: [d_phi / 128][B * H * T][128]
 size_t swiglu_partial_bytes(const Shape& s);
