@@ -224,9 +224,11 @@ int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const f
  *            scalar rate the per-token terms whose sum is dL/deta_scalar.
  *   workspace, workspace_bytes  caller-owned device memory, 16-byte aligned, at
  *            least ttt_la_backward_workspace() bytes (may be NULL when that is 0).
- * Identity feature map with d_k == d_v only (TTT_LA_ERR_UNSUPPORTED otherwise).
+ * Identity feature map (TTT_LA_ERR_UNSUPPORTED for SwiGLU: see ttt_la_backward_swiglu);
+ * d_k and d_v may differ (dQ, dK are d_k wide, dV is d_v wide).
  * Runs three forwards of the layer on permuted operands (two over the sequence
- * reversed in time) and one or two small kernels, enqueued on hip_stream; no
+ * reversed in time; those giving dq and dk have queries and keys of width d_v and
+ * values of width d_k) and one to three small kernels, enqueued on hip_stream; no
  * device memory is allocated and nothing is synchronised with the host.  On the
  * bf16 d = 128 plans of three launches the two reversed forwards read their rows
  * in reverse order and run beside the first one on two streams of the handle,
@@ -268,9 +270,10 @@ int ttt_la_backward_swiglu(ttt_la_t h, const void* q, const void* k, const void*
                            void* hip_stream);
 
 /* Bytes of workspace ttt_la_backward needs on handle h for the given mode bits:
- * two [B, H, T, d] tensors (the outputs of the two rate-1 forwards), plus in
- * causal mode either two segment-summary areas of the handle's plan (bf16 d = 128
- * plans of three launches) or the four time-reversed operands.  For a SwiGLU
+ * the outputs of the two rate-1 forwards ([B, H, T, d_v] and [B, H, T, d_k]),
+ * plus in causal mode either two segment-summary areas of the handle's plan (bf16
+ * d = 128 plans of three launches) or the four time-reversed operands, plus for
+ * d_k != d_v the segment-summary area of the plan with the widths swapped.  For a SwiGLU
  * handle: the workspace of ttt_la_backward_swiglu.  Host only;
  * TTT_LA_ERR_UNSUPPORTED if the handle's shape has no backward. */
 int ttt_la_backward_workspace(ttt_la_t h, uint32_t mode, size_t* bytes);

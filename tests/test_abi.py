@@ -319,7 +319,11 @@ def test_backward_arguments():
     assert check_bw(ws=DO) == bad                                                # workspace over dO
     assert check_bw(de=DE + 2) == bad
     assert check_bw(eta=ETA, mode=tla.TTT_LA_ETA_SOFTPLUS, de=ETA) == bad
-    assert check_bw(d=desc(d_v=64)) == tla.TTT_LA_ERR_UNSUPPORTED                # d_k != d_v
+    # d_k != d_v: reversed q, k (d_k wide) and v, dO (d_v wide), the two rate-1 outputs, then the
+    # swapped plan's summary area
+    kb, vb = 2 * 3 * 100 * 128 * 2, 2 * 3 * 100 * 64 * 2
+    assert check_bw(d=desc(d_v=64), wsb=3 * (kb + vb) - 16) == bad
+    assert check_bw(d=desc(d_v=64), wsb=1 << 30) == tla.TTT_LA_OK
     assert check_bw(d=desc(phi="swiglu", d_phi=256, w1=W1, w3=W3)) == tla.TTT_LA_ERR_UNSUPPORTED
 
 

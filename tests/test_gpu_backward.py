@@ -104,6 +104,22 @@ def test_backward_other_shapes(case):
     run_case(w)
 
 
+@pytest.mark.parametrize("base,d_k,d_v,causal,eta_mode,beta", [
+    ("v3_softplus_8x16x4096_d128", 64, 128, True, "softplus", 0.9),
+    ("v3_softplus_8x16x4096_d128", 128, 64, True, "per_token", 0.0),
+    ("v3_softplus_8x16x4096_d128", 64, 128, False, "scalar", 0.5),
+    ("v3_softplus_8x16x4096_d128", 128, 64, False, "softplus", 0.0),
+    ("v5_f32_1x1x256_d64", 64, 128, True, "softplus", 0.9),
+    ("v5_f32_1x1x256_d64", 128, 64, False, "scalar", 0.0),
+])
+def test_backward_unequal_widths(base, d_k, d_v, causal, eta_mode, beta):
+    # dq and dk come from forwards with queries and keys of width d_v and values of width d_k
+    w = small(base, B=1, H=2, T=150).with_settings(d_k=d_k, d_v=d_v, d_phi=d_k, causal=causal, eta_mode=eta_mode,
+                                                    beta=beta, eta_scalar=0.4 if eta_mode == "scalar" else 0.0)
+    say(f"[backward widths] {w.dtype} d_k={d_k} d_v={d_v} causal={causal} {eta_mode} beta={beta}")
+    run_case(w)
+
+
 def test_backward_entry_points_for_swiglu():
     import torch
     import ttt_weight_layers_amd as tla

@@ -389,10 +389,57 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     return e == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
 
-bool backward_supported(const ttt_la_desc& d) { return d.phi == TTT_LA_PHI_IDENTITY && d.d_k == d.d_v; }
+bool backward_supported(const ttt_la_desc& d) { return d.phi == TTT_LA_PHI_IDENTITY; }
 
-// one [B, H, T, d] tensor in the handle's dtype
+// one [B, H, T, d_v] tensor in the handle's dtype (v, dO, dv); key_bytes: [B, H, T, d_k]
 size_t tensor_bytes(const ttt_la_desc& d) { return (size_t)d.B * d.H * d.T * d.d_v * elem_bytes(d.dtype); }
+size_t key_bytes(const ttt_la_desc& d) { return (size_t)d.B * d.H * d.T * d.d_k * elem_bytes(d.dtype); }
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+// The forwards of the backward that produce dq and dk run with queries and keys of width
+// d_v and values of width d_k: for d_k != d_v that is another shape, with its own plan
+// and segment-summary area in the workspace.
+Shape swapped_shape(const ttt_la_desc& d) {
+    Shape s = shape_of(d);
+    s.d_k = d.d_v;
+    s.d_v = d.d_k;
+    s.d_phi = d.d_v;
+    return s;
+}
+
+size_t swapped_area(const ttt_la_desc& d, const ttt_la_hints& hn) {
+    if (d.d_k == d.d_v) return 0;
+    const Shape ss = swapped_shape(d);
+    if (d.dtype != TTT_LA_BF16 || !ttt::fast_supported(ss, d.chunk)) return 0;
+    const ttt::FastPlan p = ttt::fast_plan(ss, d.chunk, hn.segments, hn.value_split, hn.launch);
+    return align256(p.summary_bytes + p.partial_bytes + p.zero_bytes);
+}
+
+// one forward of the swapped shape (no carried state, not reversed in the kernel)
+hipError_t swapped_forward(const ttt_la_desc& d, const ttt_la_hints& hn, void* area, const void* q, const void* k,
+                           const void* v, const float* eta, float eta_scalar, float beta, uint32_t mode, void* o,
+                           hipStream_t st) {
+    const Shape ss = swapped_shape(d);
+    ttt::FwdArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.eta = eta;
+    a.eta_scalar = eta_scalar;
+    a.beta = beta;
+    a.eta_kind = eta_kind_of(mode);
+    a.bidirectional = (mode & TTT_LA_BIDIRECTIONAL) != 0;
+    a.o = o;
+    a.stream = st;
+    if (d.dtype == TTT_LA_BF16 && ttt::fast_supported(ss, d.chunk)) {
+        ttt::FastPlan p = ttt::fast_plan(ss, d.chunk, hn.segments, hn.value_split, hn.launch);
+        p.fused = false;   // its counters would need a zeroed area of their own
+        return ttt::launch_fast(ss, p, area, a, nullptr, nullptr, nullptr);
+    }
+    if (ttt::short_supported(ss)) return ttt::launch_short(ss, a, nullptr, nullptr);
+    return ttt::launch_generic(ss, a, nullptr, nullptr);
+}
 
 // The 32x32-tile plans of three launches (decided from the descriptor alone: a
 // single or prefix launch was not asked for) read the time-reversed operands in
@@ -408,12 +455,14 @@ bool reversed_in_kernel(const ttt_la_desc& d, const ttt_la_hints& hn) {
 // for each of the two reversed forwards (they run beside the first one, which uses
 // the handle's).  Causal otherwise: q, k, v, dO reversed in time, then the outputs.
 size_t backward_ws_bytes(const ttt_la_desc& d, const ttt_la_hints& hn, uint32_t mode) {
-    if (mode & TTT_LA_BIDIRECTIONAL) return 2 * tensor_bytes(d);
+    const size_t vb = align256(tensor_bytes(d)), kb = align256(key_bytes(d));
+    if (mode & TTT_LA_BIDIRECTIONAL) return vb + kb + swapped_area(d, hn);
     if (reversed_in_kernel(d, hn)) {
         const ttt::FastPlan p = ttt::fast_plan(shape_of(d), d.chunk, hn.segments, hn.value_split, hn.launch);
         return 2 * tensor_bytes(d) + 2 * p.summary_bytes;
     }
-    return 6 * tensor_bytes(d);
+    // reversed q, k, v, dO, then U (d_v wide) and W (d_k wide), then the swapped plan's area
+    return 3 * (kb + vb) + swapped_area(d, hn);
 }
 
 // streams and events of the concurrent reversed forwards; false if any is missing
@@ -447,13 +496,13 @@ int check_backward(const ttt_la_desc* d, const ttt_la_hints& hn, const void* q, 
     if (dEta && !aligned(dEta, 4)) return TTT_LA_ERR_INVALID_ARG;
     const size_t need = backward_ws_bytes(*d, hn, mode);
     if (need && (!ws || !aligned(ws, 16) || ws_bytes < need)) return TTT_LA_ERR_INVALID_ARG;
-    const size_t tb = tensor_bytes(*d);
+    const size_t tb = tensor_bytes(*d), kb = key_bytes(*d);
     const size_t nt = (size_t)d->B * d->H * d->T;
     const size_t eta_bytes = eta ? nt * sizeof(float) : 0;
     const void* outs[4] = {dQ, dK, dV, dEta};
-    const size_t out_bytes[4] = {tb, tb, tb, nt * sizeof(float)};
+    const size_t out_bytes[4] = {kb, kb, tb, nt * sizeof(float)};
     const void* ins[5] = {q, k, v, dO, eta};
-    const size_t in_bytes[5] = {tb, tb, tb, tb, eta_bytes};
+    const size_t in_bytes[5] = {kb, kb, tb, tb, eta_bytes};
     for (int i = 0; i < 4; ++i) {
         for (int j = 0; j < 5; ++j)
             if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j])) return TTT_LA_ERR_INVALID_ARG;
@@ -727,9 +776,22 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
         for (int i = 0; i < 2; ++i)
             if (hipStreamWaitEvent(h->aux[i], h->fork, 0) != hipSuccess) return TTT_LA_ERR_HIP;
     }
-    // dq: the forward with (q, k, v) -> (dO, v, k) and the caller's rates
-    st = enqueue_forward(h, dO, v, k, eta, eta_scalar, beta, mode, nullptr, nullptr, dQ, nullptr, nullptr,
-                         hip_stream, false);
+    const ttt_la_desc& dd = h->desc;
+    const bool swapped = dd.d_k != dd.d_v;
+    const size_t vb = align256(tb), kb = align256(key_bytes(dd));
+    // the swapped shape's summary area sits at the end of the workspace
+    void* sw_area = swapped ? ws + backward_ws_bytes(dd, h->hints, mode) - swapped_area(dd, h->hints) : nullptr;
+    auto fwd_swapped = [&](const void* q_, const void* k_, const void* v_, const float* e_, float es_, float b_,
+                           uint32_t m_, void* o_) {
+        return swapped_forward(dd, h->hints, sw_area, q_, k_, v_, e_, es_, b_, m_, o_, stream) == hipSuccess
+                   ? TTT_LA_OK
+                   : TTT_LA_ERR_HIP;
+    };
+    // dq: the forward with (q, k, v) -> (dO, v, k) and the caller's rates (queries and
+    // keys of width d_v, values of width d_k)
+    st = swapped ? fwd_swapped(dO, v, k, eta, eta_scalar, beta, mode, dQ)
+                 : enqueue_forward(h, dO, v, k, eta, eta_scalar, beta, mode, nullptr, nullptr, dQ, nullptr, nullptr,
+                                   hip_stream, false);
     if (st != TTT_LA_OK) return st;
     void *U, *W;
     if (rev_in_kernel) {
@@ -753,29 +815,34 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
         }
     } else if (!bidir) {
         // rate-1 forwards over the reversed sequence: u from (k, q, dO), w from (v, dO, q)
-        char *Rq = ws, *Rk = ws + tb, *Rv = ws + 2 * tb, *RdO = ws + 3 * tb;
-        U = ws + 4 * tb;
-        W = ws + 5 * tb;
-        const void* src[4] = {q, k, v, dO};
-        void* dst[4] = {Rq, Rk, Rv, RdO};
-        if (ttt::launch_reverse(src, dst, 4, (size_t)h->desc.B * h->desc.H, h->desc.T,
-                                h->desc.d_v * elem_bytes(h->desc.dtype), stream) != hipSuccess)
+        char *Rq = ws, *Rk = ws + kb, *Rv = ws + 2 * kb, *RdO = ws + 2 * kb + vb;
+        U = ws + 2 * kb + 2 * vb;
+        W = ws + 2 * kb + 3 * vb;
+        const void* src_k[2] = {q, k};
+        void* dst_k[2] = {Rq, Rk};
+        const void* src_v[2] = {v, dO};
+        void* dst_v[2] = {Rv, RdO};
+        const size_t eb = elem_bytes(dd.dtype);
+        if (ttt::launch_reverse(src_k, dst_k, 2, (size_t)dd.B * dd.H, dd.T, dd.d_k * eb, stream) != hipSuccess ||
+            ttt::launch_reverse(src_v, dst_v, 2, (size_t)dd.B * dd.H, dd.T, dd.d_v * eb, stream) != hipSuccess)
             return TTT_LA_ERR_HIP;
         st = enqueue_forward(h, Rk, Rq, RdO, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, U, nullptr,
                              nullptr, hip_stream, false);
         if (st != TTT_LA_OK) return st;
-        st = enqueue_forward(h, Rv, RdO, Rq, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, W, nullptr,
-                             nullptr, hip_stream, false);
+        st = swapped ? fwd_swapped(Rv, RdO, Rq, nullptr, 1.0f, beta, TTT_LA_CAUSAL, W)
+                     : enqueue_forward(h, Rv, RdO, Rq, nullptr, 1.0f, beta, TTT_LA_CAUSAL, nullptr, nullptr, W,
+                                       nullptr, nullptr, hip_stream, false);
         if (st != TTT_LA_OK) return st;
     } else {
         // every query reads the final state: rate-1, momentum-free bidirectional forwards
         U = ws;
-        W = ws + tb;
+        W = ws + vb;
         st = enqueue_forward(h, k, q, dO, nullptr, 1.0f, 0.0f, TTT_LA_BIDIRECTIONAL, nullptr, nullptr, U, nullptr,
                              nullptr, hip_stream, false);
         if (st != TTT_LA_OK) return st;
-        st = enqueue_forward(h, v, dO, q, nullptr, 1.0f, 0.0f, TTT_LA_BIDIRECTIONAL, nullptr, nullptr, W, nullptr,
-                             nullptr, hip_stream, false);
+        st = swapped ? fwd_swapped(v, dO, q, nullptr, 1.0f, 0.0f, TTT_LA_BIDIRECTIONAL, W)
+                     : enqueue_forward(h, v, dO, q, nullptr, 1.0f, 0.0f, TTT_LA_BIDIRECTIONAL, nullptr, nullptr, W,
+                                       nullptr, nullptr, hip_stream, false);
         if (st != TTT_LA_OK) return st;
     }
     ttt::BackArgs b{};
@@ -792,7 +859,19 @@ int ttt_la_backward(ttt_la_t h, const void* q, const void* k, const void* v, con
     b.causal = !bidir;
     b.uw_reversed = !bidir && !rev_in_kernel;
     b.stream = stream;
-    return ttt::launch_finalize_grads(h->shape, b) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+    if (!swapped) return ttt::launch_finalize_grads(h->shape, b) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
+    // widths differ: dv and the rate gradient from u (d_v wide), then dk from w (d_k wide)
+    b.dk = nullptr;
+    if (ttt::launch_finalize_grads(h->shape, b) != hipSuccess) return TTT_LA_ERR_HIP;
+    ttt::BackArgs bk = b;
+    bk.u = W;
+    bk.w = W;
+    bk.v = W;           // read for the rate term only, which this pass does not write
+    bk.dv = dK;
+    bk.deta = nullptr;
+    Shape sk = h->shape;
+    sk.d_v = dd.d_k;
+    return ttt::launch_finalize_grads(sk, bk) == hipSuccess ? TTT_LA_OK : TTT_LA_ERR_HIP;
 }
 
 int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,
