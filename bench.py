@@ -365,8 +365,13 @@ def run_backward(args, w):
     n_sets = max(1, min(8, -(-2 * MALL_BYTES // nbytes)))
     sets = [dict(q=q0.clone(), k=k0.clone(), v=v0.clone(), dO=dO0.clone(), a=None if a0 is None else a0.clone())
             for _ in range(n_sets)]
+    w1 = up(x.w1_dev) if x.w1_dev is not None else None
+    w3 = up(x.w3_dev) if x.w3_dev is not None else None
+    swiglu = w.phi == "swiglu"
+    if swiglu:
+        nbytes += 2 * w.H * w.d_phi * w.d_k * (e + 4)     # W1, W3 read, dW1, dW3 written (fp32)
     lay = tla.TTTLinearAttention(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi, chunk=w.chunk,
-                                 segments=args.segments)
+                                 segments=args.segments, w1=w1, w3=w3)
     mode = tla.mode_bits(w.eta_mode, w.causal)
     st, ws_bytes = tla.ttt_la_backward_workspace(lay.handle, mode)
     if st != 0:
@@ -374,15 +379,22 @@ def run_backward(args, w):
     ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     outs = dict(dq=torch.empty_like(q0), dk=torch.empty_like(k0), dv=torch.empty_like(v0),
                 de=torch.empty(q0.shape[:-1], dtype=torch.float32, device=dev))
+    if swiglu:
+        outs["dw1"] = torch.empty((w.H, w.d_phi, w.d_k), dtype=torch.float32, device=dev)
+        outs["dw3"] = torch.empty_like(outs["dw1"])
     stream = torch.cuda.current_stream()
 
     def step(i):
         s_ = sets[i % n_sets]
-        r = tla.ttt_la_backward(lay.handle, s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(),
-                                None if s_["a"] is None else s_["a"].data_ptr(), w.eta_scalar, w.beta, mode,
-                                s_["dO"].data_ptr(), outs["dq"].data_ptr(), outs["dk"].data_ptr(),
-                                outs["dv"].data_ptr(), outs["de"].data_ptr(), ws.data_ptr(), ws_bytes,
-                                stream.cuda_stream)
+        args_ = (lay.handle, s_["q"].data_ptr(), s_["k"].data_ptr(), s_["v"].data_ptr(),
+                 None if s_["a"] is None else s_["a"].data_ptr(), w.eta_scalar, w.beta, mode,
+                 s_["dO"].data_ptr(), outs["dq"].data_ptr(), outs["dk"].data_ptr(),
+                 outs["dv"].data_ptr(), outs["de"].data_ptr())
+        if swiglu:
+            r = tla.ttt_la_backward_swiglu(*args_, outs["dw1"].data_ptr(), outs["dw3"].data_ptr(), ws.data_ptr(),
+                                           ws_bytes, stream.cuda_stream)
+        else:
+            r = tla.ttt_la_backward(*args_, ws.data_ptr(), ws_bytes, stream.cuda_stream)
         if r != 0:
             raise tla.TTTError(r, "ttt_la_backward")
 
@@ -404,11 +416,14 @@ def run_backward(args, w):
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name + " (backward)", "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v,
+                   "d_phi": w.d_phi, "phi": w.phi,
                    "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar, "beta": w.beta,
                    "causal": w.causal, "segments": lay.plan().segments, "input_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "whole backward (3 forwards + reversal + finalize)", "bytes_per_step": nbytes},
+                     "kernel": ("whole backward (features, 2 P + 1 forwards, chain rule through phi, dW)" if swiglu
+                                else "whole backward (3 forwards + reversal + finalize)"),
+                     "bytes_per_step": nbytes},
         "cpu_baseline": None,
     }
 
