@@ -339,3 +339,16 @@ def test_swiglu_workspace_serves_both_modes(T):
         wc = w.with_settings(causal=causal)
         got = run_gpu(wc, d, layer=lay)
         assert oracle.rel_err(got, run_oracle(wc, x)) <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("T,path", [(1024, 4), (1025, 0)])
+def test_fp32_short_kernel_boundary(T, path):
+    # up to 1024 tokens the fp32 forward is one masked product; beyond, the chunked walk
+    w = small("v5_f32_1x1x256_d64", B=1, H=2, T=T).with_settings(eta_mode="softplus", beta=0.9)
+    say(f"[fp32 boundary] T={T}")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d)
+    assert lay.plan().path == path
+    got = run_gpu(w, d, layer=lay)
+    assert oracle.rel_err(got, run_oracle(w, x)) <= TOL[w.dtype]

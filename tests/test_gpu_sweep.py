@@ -19,7 +19,7 @@ def _cases(n=120, seed=20261203):
     rng = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
-        kind = rng.choice(["wide", "wide", "tile", "swiglu", "f32"])
+        kind = rng.choice(["wide", "wide", "tile", "swiglu", "f32", "delta"])
         c = dict(B=int(rng.integers(1, 3)), H=int(rng.integers(1, 4)), T=int(rng.integers(1, 900)),
                  eta_mode=str(rng.choice(["scalar", "per_token", "softplus"])),
                  beta=float(rng.choice([0.0, 0.5, 0.9, 0.99])), causal=bool(rng.random() < 0.8),
@@ -41,9 +41,18 @@ def _cases(n=120, seed=20261203):
             d_k, d_v = [int(x) for x in rng.choice([64, 128], size=2)]
             c.update(base="v2_swiglu_4x16x8192_d128_f512", d_k=d_k, d_v=d_v,
                      d_phi=int(rng.choice([128, 256])), phi="swiglu", T=int(rng.integers(1, 400)))
-        else:
+        elif kind == "f32":
             c.update(base="v5_f32_1x1x256_d64", d_k=64, d_v=64, d_phi=64, phi="identity",
                      T=int(rng.integers(1, 300)))
+        else:
+            # the mean-squared loss: causal, no momentum, d_k = d_v, positive rates only: the raw
+            # per-token rates here are drawn around -2, and with eta < 0 every delta-rule step
+            # multiplies the state by |1 - eta ||k||^2| ~ 3 along k, an exponential growth in
+            # which bf16 rounding grows with it (the scalar rate is 0.3, softplus is positive)
+            d = int(rng.choice([64, 128]))
+            c.update(base="v3_delta_8x16x4096_d128", d_k=d, d_v=d, d_phi=d, phi="identity", beta=0.0,
+                     causal=True, T=int(rng.integers(1, 700)),
+                     eta_mode="softplus" if c["eta_mode"] == "per_token" else c["eta_mode"])
         if not c["causal"]:
             c["segments"] = 0
             c["launch"] = "auto"
@@ -55,7 +64,8 @@ CASES = _cases()
 
 
 def _id(c):
-    return (f"{WORKLOADS[c['base']].dtype}_{c['phi'][:2]}{c['d_k']}x{c['d_v']}f{c['d_phi']}_{c['B']}x{c['H']}x{c['T']}"
+    return (f"{WORKLOADS[c['base']].dtype}_{c['phi'][:2]}{WORKLOADS[c['base']].loss}"
+            f"{c['d_k']}x{c['d_v']}f{c['d_phi']}_{c['B']}x{c['H']}x{c['T']}"
             f"_{c['eta_mode'][:4]}"
             f"_b{c['beta']}_{'c' if c['causal'] else 'bi'}_s{c['segments']}_v{c['value_split']}_{c['launch']}")
 

@@ -66,6 +66,7 @@ struct DeltaParams {
     int eta_kind;
     int T;
     int n_vsplit;              // workgroups per sequence (value columns DVW each)
+    int n_units;               // sequences x n_vsplit (the grid is rounded up to a multiple of 8)
 };
 
 // DK = d_k = d_v.  Rows of the state evolve independently under the delta rule (row i
@@ -87,8 +88,13 @@ __global__ void __launch_bounds__(DTH, 1) delta_forward(DeltaParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4, q4 = lane & 3;
     const int T = p.T;
-    const int seq = blockIdx.x / p.n_vsplit;
-    const int vc0 = (blockIdx.x % p.n_vsplit) * DVW;   // first value column of the workgroup
+    // unit u: the value splits of a sequence are consecutive units, and consecutive units
+    // sit on one XCD (workgroups go to the XCDs in turn), so they share q and k in its L2
+    const int G = gridDim.x;
+    const int u = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (u >= p.n_units) return;
+    const int seq = u / p.n_vsplit;
+    const int vc0 = (u % p.n_vsplit) * DVW;   // first value column of the workgroup
     const size_t row0 = (size_t)seq * T;
     const int vr0 = 16 * wv;                         // this wave's value rows of S (local)
     const int dv = DK;                               // row length of v and o
@@ -284,7 +290,8 @@ hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
     p.eta_kind = a.eta_kind;
     p.T = s.T;
     p.n_vsplit = s.d_v / DVW;
-    const dim3 grid((unsigned)(s.n_seq() * p.n_vsplit)), block(DTH);
+    p.n_units = s.n_seq() * p.n_vsplit;
+    const dim3 grid((unsigned)((p.n_units + 7) / 8 * 8)), block(DTH);
     const void* fn = s.d_k == 128 ? reinterpret_cast<const void*>(delta_forward<128>)
                                   : reinterpret_cast<const void*>(delta_forward<64>);
     if (ev_begin || ev_end) {

@@ -123,22 +123,36 @@ __global__ void __launch_bounds__(GTH) gate_kernel(GateParams p) {
                 G[tb] = mfma16(a, as_bf16x8(lds_read16(sW3 + swz<GW>(16 * tb + c16, 32 * kk + 8 * g))), G[tb]);
             }
         }
+        // results of the tile into LDS (phi or du over the staged x, dg over the staged dphi:
+        // each lane overwrites only entries it alone has read), then 16-byte stores
+        __syncthreads();   // every wave is done reading sX for its products
 #pragma unroll
         for (int tb = 0; tb < 8; ++tb) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = 16 * wv + 4 * g + r, f = 16 * tb + c16;
-                if (t >= n) continue;
                 const float u = U[tb][r], gg = G[tb][r];
                 const float sg = sigmoid_f32(u);
                 if constexpr (MODE == G_FEATURES) {
-                    p.phi[(sl * slice_rows + row0 + t) * GW + f] = f32_to_bf16_bits(u * sg * gg);
+                    sX[swz<GW>(t, f)] = f32_to_bf16_bits(u * sg * gg);
                 } else {
                     const float d = bf16_bits_to_f32(sD[swz<GW>(t, f)]) * sScale[t];
-                    const size_t o = (row0 + t) * (size_t)(2 * p.d_phi) + sl * GW + f;
-                    p.dg[o] = f32_to_bf16_bits(d * gg * sg * (1.0f + u * (1.0f - sg)));
-                    p.dg[o + p.d_phi] = f32_to_bf16_bits(d * u * sg);
+                    sX[swz<GW>(t, f)] = f32_to_bf16_bits(d * gg * sg * (1.0f + u * (1.0f - sg)));
+                    sD[swz<GW>(t, f)] = f32_to_bf16_bits(d * u * sg);
                 }
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < GT * GW / 8; e += GTH) {
+            const int r = e / (GW / 8), col = 8 * (e % (GW / 8));
+            if (r >= n) continue;
+            const u32x4 a = *reinterpret_cast<const u32x4*>(sX + swz<GW>(r, col));
+            if constexpr (MODE == G_FEATURES) {
+                *reinterpret_cast<u32x4*>(p.phi + (sl * slice_rows + row0 + r) * GW + col) = a;
+            } else {
+                const size_t o = (row0 + r) * (size_t)(2 * p.d_phi) + sl * GW + col;
+                *reinterpret_cast<u32x4*>(p.dg + o) = a;
+                *reinterpret_cast<u32x4*>(p.dg + o + p.d_phi) = *reinterpret_cast<const u32x4*>(sD + swz<GW>(r, col));
             }
         }
         __syncthreads();   // the tile's LDS is used up
@@ -158,6 +172,7 @@ constexpr int DXK = 64;      // contraction panel
 __global__ void __launch_bounds__(GTH) dx_kernel(DxParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[GT * DXK];
     __shared__ __attribute__((aligned(16))) uint16_t sB[GW * DXK];
+    __shared__ __attribute__((aligned(16))) uint16_t sO[GT * GW];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4;
     const int tile = blockIdx.x % p.n_tiles;
@@ -196,10 +211,13 @@ __global__ void __launch_bounds__(GTH) dx_kernel(DxParams p) {
 #pragma unroll
     for (int tb = 0; tb < 8; ++tb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = 16 * wv + 4 * g + r;
-            if (t < n) p.dx[(row0 + t) * GW + 16 * tb + c16] = f32_to_bf16_bits(acc[tb][r]);
-        }
+        for (int r = 0; r < 4; ++r) sO[swz<GW>(16 * wv + 4 * g + r, 16 * tb + c16)] = f32_to_bf16_bits(acc[tb][r]);
+    __syncthreads();
+    for (int e = tid; e < GT * GW / 8; e += GTH) {
+        const int r = e / (GW / 8), col = 8 * (e % (GW / 8));
+        if (r < n)
+            *reinterpret_cast<u32x4*>(p.dx + (row0 + r) * GW + col) = *reinterpret_cast<const u32x4*>(sO + swz<GW>(r, col));
+    }
 }
 
 struct DwParams {
