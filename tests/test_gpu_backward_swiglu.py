@@ -25,6 +25,8 @@ def say(*a):
     (256, "scalar", 0.5, False, 2, 1, 100),
     (128, "softplus", 0.9, True, 1, 2, 37),
     (512, "softplus", 0.0, False, 1, 2, 64 * 2 + 5),
+    # dW over several token ranges of 138 tokens (ragged 32-token panels) per sequence
+    (512, "softplus", 0.9, True, 1, 1, 1100),
 ])
 def test_swiglu_backward_parity(d_phi, eta_mode, beta, causal, B, H, T):
     import torch

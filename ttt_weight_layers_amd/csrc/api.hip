@@ -524,13 +524,11 @@ int check_backward(const ttt_la_desc* d, const ttt_la_hints& hn, const void* q, 
 //   w              P x rows x 128: dL/dphi(k) / (eta c), slice by slice
 //   u              rows x 128: the rate-1 forward giving dv and the rate gradient
 //   rq, rk, rdo    rows x 128 each (causal only): q, k, dO reversed in time
-//   dg_q, dg_k     rows x 2 d_phi: [du | dg] of q and of k
-//   wcat           H x 128 x 2 d_phi: [W1 ; W3]^T
 //   sum            segment summaries of the feature-space forwards (d = 128 plan)
 //   part           per-slice partial outputs of the SwiGLU forward
 //   dwpart         fp32 partial sums of dW1, dW3
 struct SwBwdLayout {
-    size_t phi_q, phi_k, dphi_q, w, u, rq, rk, rdo, dg_q, dg_k, wcat, sum, part, dwpart, total;
+    size_t phi_q, phi_k, dphi_q, w, u, rq, rk, rdo, sum, part, dwpart, total;
 };
 
 Shape feature_shape(const Shape& s) {
@@ -561,12 +559,9 @@ SwBwdLayout swiglu_bwd_layout(const ttt_la_desc& d, uint32_t mode) {
         L.rk = take(rows * 128 * E);
         L.rdo = take(rows * 128 * E);
     }
-    L.dg_q = take(rows * 2 * s.d_phi * E);
-    L.dg_k = take(rows * 2 * s.d_phi * E);
-    L.wcat = take((size_t)s.H * 128 * 2 * s.d_phi * E);
     L.sum = take(ttt::fast_plan(feature_shape(s), 0, 0, 0, 0).summary_bytes);
     L.part = take(ttt::fast_plan(s, d.chunk, 0, 0, 0).partial_bytes);
-    L.dwpart = take(ttt::swiglu_dw_partial_bytes(s));
+    L.dwpart = take(ttt::swiglu_chain_dw_partial_bytes(s));
     L.total = off;
     return L;
 }
@@ -683,11 +678,8 @@ int ttt_la_backward_swiglu(ttt_la_t h, const void* q, const void* k, const void*
             return TTT_LA_ERR_HIP;     \
         }                              \
     } while (0)
-    TTT_TRY(ttt::launch_swiglu_wcat(s, ws + L.wcat, stream));
-    TTT_TRY(ttt::launch_swiglu_gate(s, false, q, ws + L.phi_q, nullptr, nullptr, nullptr, 0.0f, 0.0f, 0, false, bidir,
-                                    stream));
-    TTT_TRY(ttt::launch_swiglu_gate(s, false, k, ws + L.phi_k, nullptr, nullptr, nullptr, 0.0f, 0.0f, 0, false, bidir,
-                                    stream));
+    TTT_TRY(ttt::launch_swiglu_features(s, q, ws + L.phi_q, stream));
+    TTT_TRY(ttt::launch_swiglu_features(s, k, ws + L.phi_k, stream));
     for (int p = 0; p < P; ++p) {
         // dL/dphi(q): the forward with (q, k, v) -> (dO, v, phi(k)) and the caller's rates
         TTT_TRY(feature_forward(sf, pf, ws + L.sum, dO, v, ws + L.phi_k + p * slice, eta, eta_scalar, beta, kind,
@@ -739,15 +731,11 @@ int ttt_la_backward_swiglu(ttt_la_t h, const void* q, const void* k, const void*
         b.stream = stream;
         TTT_TRY(ttt::launch_finalize_grads(s, b));
     }
-    // through phi: [du | dg] of q (dphi as is) and of k (w scaled by eta c), then dq, dk, dW1, dW3
-    TTT_TRY(ttt::launch_swiglu_gate(s, true, q, nullptr, ws + L.dphi_q, ws + L.dg_q, eta, eta_scalar, beta, kind, false,
-                                    bidir, stream));
-    TTT_TRY(ttt::launch_swiglu_gate(s, true, k, nullptr, ws + L.w, ws + L.dg_k, eta, eta_scalar, beta, kind, true,
-                                    bidir, stream));
-    TTT_TRY(ttt::launch_swiglu_dx(s, ws + L.dg_q, ws + L.wcat, dQ, stream));
-    TTT_TRY(ttt::launch_swiglu_dx(s, ws + L.dg_k, ws + L.wcat, dK, stream));
-    TTT_TRY(ttt::launch_swiglu_dw(s, ws + L.dg_q, ws + L.dg_k, q, k, reinterpret_cast<float*>(ws + L.dwpart), dW1, dW3,
-                                  stream));
+    // through phi: dq from q and dphi(q), dk from k and w scaled by eta c, then dW1, dW3 from both
+    TTT_TRY(ttt::launch_swiglu_chain_dx(s, q, ws + L.dphi_q, dQ, eta, eta_scalar, beta, kind, false, bidir, stream));
+    TTT_TRY(ttt::launch_swiglu_chain_dx(s, k, ws + L.w, dK, eta, eta_scalar, beta, kind, true, bidir, stream));
+    TTT_TRY(ttt::launch_swiglu_chain_dw(s, q, k, ws + L.dphi_q, ws + L.w, eta, eta_scalar, beta, kind, bidir,
+                                        reinterpret_cast<float*>(ws + L.dwpart), dW1, dW3, stream));
 #undef TTT_TRY
     return TTT_LA_OK;
 }

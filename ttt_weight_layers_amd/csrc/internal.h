@@ -108,15 +108,18 @@ hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
 
 // backward through the SwiGLU feature map (swiglu_bwd.hip): d_k = d_v = 128, bf16
 bool swiglu_backward_supported(const Shape& s);
-int swiglu_dw_split(const Shape& s);
-size_t swiglu_dw_partial_bytes(const Shape& s);
-hipError_t launch_swiglu_gate(const Shape& s, bool grads, const void* x, void* phi, const void* dphi, void* dg,
-                              const float* eta, float eta_scalar, float beta, int eta_kind, bool scale_eta,
-                              bool bidir, hipStream_t st);
-hipError_t launch_swiglu_dx(const Shape& s, const void* dg, const void* wcat, void* dx, hipStream_t st);
-hipError_t launch_swiglu_dw(const Shape& s, const void* dg_q, const void* dg_k, const void* x_q, const void* x_k,
-                            float* part, float* dw1, float* dw3, hipStream_t st);
-hipError_t launch_swiglu_wcat(const Shape& s, void* wcat, hipStream_t st);
+// phi(x) of every 128-feature slice, slice-major [P][B H T][128]
+hipError_t launch_swiglu_features(const Shape& s, const void* x, void* phi, hipStream_t st);
+// the chain rule through phi without [du | dg] in memory: dx of one input, and dW1, dW3
+// from both (the keys' dphi scaled per token when eta is given)
+hipError_t launch_swiglu_chain_dx(const Shape& s, const void* x, const void* dphi, void* dx, const float* eta,
+                                  float eta_scalar, float beta, int eta_kind, bool scale_eta, bool bidir,
+                                  hipStream_t st);
+int swiglu_chain_dw_split(const Shape& s);
+size_t swiglu_chain_dw_partial_bytes(const Shape& s);
+hipError_t launch_swiglu_chain_dw(const Shape& s, const void* x_q, const void* x_k, const void* dphi_q,
+                                  const void* dphi_k, const float* eta, float eta_scalar, float beta, int eta_kind,
+                                  bool bidir, float* part, float* dw1, float* dw3, hipStream_t st);
 
 bool swiglu_supported(const Shape& s);
 // fp32 parts of o of the feature slices: [d_phi / 128][B * H * T][128]
