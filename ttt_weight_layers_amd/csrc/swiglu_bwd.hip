@@ -77,45 +77,61 @@ __global__ void __launch_bounds__(GTH) gate_kernel(GateParams p) {
         *reinterpret_cast<u32x4*>(sW3 + swz<GW>(r, col)) = *reinterpret_cast<const u32x4*>(w3 + r * GW + col);
     }
     const int tile_end = min(p.n_tiles, (grp + 1) * GTPW);
+    // x of a tile: thread tid copies 16-byte pieces tid + 256 i; the next tile's are
+    // loaded while this one is used
+    u32x4 xp[4];
+    auto fetch_x = [&](int tile) {
+        const int t0 = tile * GT, n = min(GT, p.T - t0);
+        const size_t row0 = (size_t)seq * p.T + t0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + GTH * i, r = e >> 4, col = 8 * (e & 15);
+            xp[i] = r < n ? *reinterpret_cast<const u32x4*>(p.x + (row0 + r) * GW + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    if (grp * GTPW < tile_end) fetch_x(grp * GTPW);
     for (int tile = grp * GTPW; tile < tile_end; ++tile) {
         const int t0 = tile * GT;
         const int n = min(GT, p.T - t0);
         const size_t row0 = (size_t)seq * p.T + t0;
-        for (int e = tid; e < GT * GW / 8; e += GTH) {
-            const int r = e / (GW / 8), col = 8 * (e % (GW / 8));
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (r < n) x = *reinterpret_cast<const u32x4*>(p.x + (row0 + r) * GW + col);
-            *reinterpret_cast<u32x4*>(sX + swz<GW>(r, col)) = x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + GTH * i, r = e >> 4, col = 8 * (e & 15);
+            *reinterpret_cast<u32x4*>(sX + swz<GW>(r, col)) = xp[i];
         }
-        __syncthreads();
+        __syncthreads();   // the tile's x (and, the first time, the weights)
+        if (tile + 1 < tile_end) fetch_x(tile + 1);
 
-        // wave wv: tokens 16 wv .. +15, all eight 16-feature tiles of the slice
+        // wave wv: tokens 16 wv .. +15, all eight 16-feature tiles of the slice, as
+        // U^T = W1 X^T and G^T: lane (c16, g) ends with features 16 tb + 4g .. +3 of
+        // token 16 wv + c16
         f32x4 U[8], G[8];
 #pragma unroll
         for (int tb = 0; tb < 8; ++tb) U[tb] = G[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < GW / 32; ++kk) {
-            const bf16x8 a = as_bf16x8(lds_read16(sX + swz<GW>(16 * wv + c16, 32 * kk + 8 * g)));
+            const bf16x8 xb = as_bf16x8(lds_read16(sX + swz<GW>(16 * wv + c16, 32 * kk + 8 * g)));
 #pragma unroll
             for (int tb = 0; tb < 8; ++tb) {
-                U[tb] = mfma16(a, as_bf16x8(lds_read16(sW1 + swz<GW>(16 * tb + c16, 32 * kk + 8 * g))), U[tb]);
-                G[tb] = mfma16(a, as_bf16x8(lds_read16(sW3 + swz<GW>(16 * tb + c16, 32 * kk + 8 * g))), G[tb]);
+                U[tb] = mfma16(as_bf16x8(lds_read16(sW1 + swz<GW>(16 * tb + c16, 32 * kk + 8 * g))), xb, U[tb]);
+                G[tb] = mfma16(as_bf16x8(lds_read16(sW3 + swz<GW>(16 * tb + c16, 32 * kk + 8 * g))), xb, G[tb]);
             }
         }
-        // the features into LDS over the staged x (each lane overwrites only entries it
-        // alone has read), then 16-byte stores
+        // the features into LDS over the staged x (8 bytes a lane and tile), then
+        // 16-byte stores
         __syncthreads();   // every wave is done reading sX for its products
 #pragma unroll
-        for (int tb = 0; tb < 8; ++tb)
+        for (int tb = 0; tb < 8; ++tb) {
+            float ph[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = 16 * wv + 4 * g + r, f = 16 * tb + c16;
-                const float u = U[tb][r];
-                sX[swz<GW>(t, f)] = f32_to_bf16_bits(u * sigmoid_f32(u) * G[tb][r]);
-            }
+            for (int r = 0; r < 4; ++r) ph[r] = U[tb][r] * sigmoid_f32(U[tb][r]) * G[tb][r];
+            *reinterpret_cast<u32x2*>(sX + swz<GW>(16 * wv + c16, 16 * tb + 4 * g)) =
+                u32x2{pack_bf16x2(ph[0], ph[1]), pack_bf16x2(ph[2], ph[3])};
+        }
         __syncthreads();
-        for (int e = tid; e < GT * GW / 8; e += GTH) {
-            const int r = e / (GW / 8), col = 8 * (e % (GW / 8));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = tid + GTH * i, r = e >> 4, col = 8 * (e & 15);
             if (r < n)
                 *reinterpret_cast<u32x4*>(p.phi + (sl * slice_rows + row0 + r) * GW + col) =
                     *reinterpret_cast<const u32x4*>(sX + swz<GW>(r, col));
@@ -224,8 +240,12 @@ __global__ void __launch_bounds__(GTH, 2) chain_dx_kernel(ChainParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t sW[2 * 2 * CF * GW];   // [buffer][W1, W3][32 x 128]
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4, q4 = lane & 3;
-    const int tile = blockIdx.x % p.n_tiles;
-    const int seq = blockIdx.x / p.n_tiles;
+    // XCD-aware: consecutive units (the tiles of one sequence, which read the same W)
+    // share an XCD's L2
+    const int u = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (u >= p.n_seq * p.n_tiles) return;
+    const int tile = u % p.n_tiles;
+    const int seq = u / p.n_tiles;
     const int h = seq % p.H;
     const size_t srow = (size_t)seq * p.T;
     const size_t slice_rows = (size_t)p.n_seq * p.T;
@@ -344,7 +364,10 @@ __global__ void __launch_bounds__(GTH, 2) chain_dw_kernel(ChainParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c16 = lane & 15, g = lane >> 4, q4 = lane & 3;
     const int n_fb = p.d_phi / CF;
-    int blk = blockIdx.x;
+    // XCD-aware: the feature blocks of one (part, head), which read the same x rows and
+    // dphi lines, share an XCD's L2
+    int blk = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (blk >= p.B * p.n_split * p.H * n_fb) return;
     const int fb = blk % n_fb;
     blk /= n_fb;
     const int h = blk % p.H;
@@ -535,7 +558,7 @@ hipError_t launch_swiglu_chain_dx(const Shape& s, const void* x, const void* dph
     p.dphi = static_cast<const uint16_t*>(dphi);
     p.dx = static_cast<uint16_t*>(dx);
     p.n_tiles = (s.T + CT - 1) / CT;
-    hipLaunchKernelGGL(chain_dx_kernel, dim3((unsigned)(s.n_seq() * p.n_tiles)), dim3(GTH), 0, st, p);
+    hipLaunchKernelGGL(chain_dx_kernel, dim3((unsigned)((s.n_seq() * p.n_tiles + 7) / 8 * 8)), dim3(GTH), 0, st, p);
     return hipGetLastError();
 }
 
@@ -563,7 +586,8 @@ hipError_t launch_swiglu_chain_dw(const Shape& s, const void* x_q, const void* x
     p.part = part;
     p.n_split = swiglu_chain_dw_split(s);
     const int n_parts = s.B * p.n_split;
-    hipLaunchKernelGGL(chain_dw_kernel, dim3((unsigned)(n_parts * s.H * (s.d_phi / CF))), dim3(GTH), 0, st, p);
+    hipLaunchKernelGGL(chain_dw_kernel, dim3((unsigned)((n_parts * s.H * (s.d_phi / CF) + 7) / 8 * 8)), dim3(GTH), 0,
+                       st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t per = (size_t)s.H * 2 * s.d_phi * GW;
