@@ -27,6 +27,13 @@ KV Binding Is Secretly Linear Attention"; readings are marked READING):
 * Variant 2 of Table 2 keeps a two-layer MLP fast weight and updates only its
   last layer: the first layer is a frozen feature map.  READING: SwiGLU
   features phi(x) = silu(W1 x) * (W3 x) with silu(u) = u / (1 + e^-u).
+* Variant 1 of Table 2 is Variant 2 with weight normalisation of the updated
+  layer, and has a recurrent implementation only.  The pages do not define the
+  normalisation.  READING (``weight_norm=True``): after every token's update each
+  row of S (one output unit: its weights over the features) is rescaled to the
+  Euclidean norm that row has in the entry state S0, the initial fast weight,
+  which must be given; the momentum buffer is not rescaled.  A row whose entry
+  norm is zero stays zero.
 * READING: the readout of token t uses the state after token t's own update,
   o_t = S_t phi(q_t).  In the bidirectional (ViT) mode every token updates the
   state first and every query reads the final state.
@@ -173,7 +180,7 @@ def _flatten(x, d):
 def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
             beta: float = 0.0, causal: bool = True, phi: str = "identity",
             w1=None, w3=None, ascent: bool = False, inner_steps: int = 1,
-            return_state: bool = False, S0=None, M0=None, loss: str = "dot"):
+            return_state: bool = False, S0=None, M0=None, loss: str = "dot", weight_norm: bool = False):
     """Recurrent TTT forward, fp64, one gradient step per token.
 
     q, k: [B, H, T, d_k]; v: [B, H, T, d_v]; eta / a: [B, H, T] (per_token /
@@ -190,6 +197,7 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
                              = (S phi(k_t) - v_t) phi(k_t)^T)
         M   = beta M - eta_t G      (ascent: + eta_t G)
         S   = S + M
+        weight_norm: S[i, :] *= ||S0[i, :]|| / ||S[i, :]||  (per row; 0 if either is 0)
         o_t = S phi(q_t)                              (causal readout)
       bidirectional: o_t = S_T phi(q_t) for all t.
     ``inner_steps`` > 1 repeats the (momentum-free) step on the same token,
@@ -224,12 +232,21 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
         raise ValueError("an entry state is defined for the causal mode only")
     S = np.zeros((N, d_v, d_phi)) if S0 is None else np.array(S0, dtype=np.float64).reshape(N, d_v, d_phi)
     M = np.zeros((N, d_v, d_phi)) if M0 is None else np.array(M0, dtype=np.float64).reshape(N, d_v, d_phi)
+    if weight_norm:
+        if S0 is None or not causal or loss != "dot":
+            raise ValueError("weight normalisation is defined here for the causal dot-product layer "
+                             "with a given entry state")
+        row_norm0 = np.sqrt(np.sum(S * S, axis=2))          # [N, d_v]
     o = np.zeros((N, T, d_v))
     for t in range(T):
         for _ in range(inner_steps):
             G = loss_grad(S, pk[:, t], vf[:, t])
             M = beta * M + sign * lr[:, t, None, None] * G
             S = S + M
+            if weight_norm:
+                norm = np.sqrt(np.sum(S * S, axis=2))
+                factor = np.divide(row_norm0, norm, out=np.zeros_like(norm), where=norm > 0)
+                S = S * factor[:, :, None]
         if causal:
             o[:, t] = np.einsum("nvf,nf->nv", S, pq[:, t])
     if not causal:
