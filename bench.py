@@ -96,6 +96,10 @@ def algorithmic_flops_per_ht(w, chunk: int) -> int:
     Q K^T, tril(Q K^T) U and the solve for U (C/2 (2 d_k + 2 d_v))."""
     if w.loss == "mse":
         return 2 * (3 * w.d_k * w.d_v + DELTA_CHUNK // 2 * (2 * w.d_k + 2 * w.d_v))
+    if w.weight_norm:
+        # the recurrence: per state entry and token, the momentum and state updates and
+        # the two row sums (norm and readout), four multiply-adds; fp32 vector work
+        return 8 * w.d_v * w.d_phi
     if not w.causal:
         return 4 * w.d_phi * w.d_v
     f = (chunk + 1) * (w.d_phi + w.d_v) + 4 * w.d_phi * w.d_v * (2 if w.beta != 0.0 else 1)
@@ -161,6 +165,7 @@ DEFAULT_ORDER = (
     "v3_long_1x16x65536_d128",
     "bidir_vit_256x6x196_d64",
     "v3_delta_8x16x4096_d128",
+    "v1_weightnorm_4x16x8192_d128_f512",
     "v2_swiglu_4x16x8192_d128_f512",
 )
 # Worker processes of the oracle timing: the host cores this process may use,
@@ -193,13 +198,14 @@ def _oracle_worker_init():
 
 
 def _oracle_task(task):
-    """One sampled sequence in a worker: (workload, q, k, v, a, w1, w3) fp64
+    """One sampled sequence in a worker: (workload, q, k, v, a, w1, w3, S0) fp64
     slices of one (b, h) -> (o [1, 1, T, d_v], seconds)."""
     import oracle
-    w, q, k, v, a, w1, w3 = task
+    w, q, k, v, a, w1, w3, S0 = task
     t0 = time.perf_counter()
+    extra = {"S0": S0, "weight_norm": True} if w.weight_norm else {}
     o = oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar, beta=w.beta,
-                       causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss)
+                       causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss, **extra)
     return o, time.perf_counter() - t0
 
 
@@ -228,7 +234,8 @@ def cpu_baseline(w, x, pool=None, n_workers: int = 1):
         tasks.append((w, sl(x.q64), sl(x.k64), sl(x.v64),
                       None if x.a32 is None else np.ascontiguousarray(x.a32[b:b + 1, h:h + 1]),
                       None if x.w1_64 is None else x.w1_64[h:h + 1],
-                      None if x.w3_64 is None else x.w3_64[h:h + 1]))
+                      None if x.w3_64 is None else x.w3_64[h:h + 1],
+                      None if x.S0 is None else sl(x.S0).astype(np.float64)))
     t0 = time.perf_counter()
     if pool is None:
         res = [_oracle_task(t) for t in tasks]
@@ -435,7 +442,8 @@ def roofline_of(w, chunk: int, seconds: float):
     HBM-bound."""
     bpht = algorithmic_bytes_per_ht(w)
     flops_ht = algorithmic_flops_per_ht(w, chunk)
-    peak_flops, bound = (MFMA_BF16_PEAK_TFLOPS, "mfma") if w.dtype == "bf16" else (F32_PEAK_TFLOPS, "alu")
+    peak_flops, bound = ((MFMA_BF16_PEAK_TFLOPS, "mfma") if w.dtype == "bf16" and not w.weight_norm
+                         else (F32_PEAK_TFLOPS, "alu"))
     ridge = peak_flops * 1e12 / (HBM_PEAK_GBS * 1e9)
     if flops_ht / bpht < ridge:
         achieved = w.head_tokens * bpht / seconds / 1e9
@@ -450,6 +458,8 @@ def timed_kernel_name(plan, w, launch: str) -> str:
     """The kernel that carries the timing events (the output pass of the plan)."""
     if w.loss == "mse":
         return "delta_forward"
+    if w.weight_norm:
+        return "wn_forward"
     if plan.path == 3:
         # the bidirectional SwiGLU pass runs on the 16x16-tile kernel
         return "chunk_kernel<BIDIR>" if not w.causal else "swiglu_kernel<OUTPUT>"
@@ -500,14 +510,21 @@ def run_forward(args, w, pool=None, n_workers: int = 1):
                                    value_split=args.value_split, launch=args.launch)
     plan = layer.plan()
     stream = torch.cuda.current_stream()
-    mode = tla.mode_bits(w.eta_mode, w.causal, w.loss)
+    mode = tla.mode_bits(w.eta_mode, w.causal, w.loss, weight_norm=w.weight_norm)
     chunk = DELTA_CHUNK if w.loss == "mse" else plan.chunk
+    # the weight-normalised recurrence starts from the drawn entry state (no final state)
+    S0 = torch.from_numpy(x.S0).to(dev) if w.weight_norm else None
 
     def step(i):
         s = sets[i % n_sets]
-        st = tla.ttt_la_forward(layer.handle, s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(),
-                                None if s["a"] is None else s["a"].data_ptr(), w.eta_scalar, w.beta, mode,
-                                s["o"].data_ptr(), stream.cuda_stream)
+        a_ptr = None if s["a"] is None else s["a"].data_ptr()
+        if w.weight_norm:
+            st = tla.ttt_la_forward_state(layer.handle, s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(),
+                                          a_ptr, w.eta_scalar, w.beta, mode, S0.data_ptr(), None,
+                                          s["o"].data_ptr(), None, None, stream.cuda_stream)
+        else:
+            st = tla.ttt_la_forward(layer.handle, s["q"].data_ptr(), s["k"].data_ptr(), s["v"].data_ptr(),
+                                    a_ptr, w.eta_scalar, w.beta, mode, s["o"].data_ptr(), stream.cuda_stream)
         if st != 0:
             raise tla.TTTError(st, "ttt_la_forward")
 
@@ -578,9 +595,10 @@ def run_forward(args, w, pool=None, n_workers: int = 1):
             "workload": w.name, "B": w.B, "H": w.H, "T": w.T, "d_k": w.d_k, "d_v": w.d_v, "d_phi": w.d_phi,
             "phi": w.phi, "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar, "beta": w.beta,
             "causal": w.causal, "loss": w.loss, "chunk": chunk,
-            "segments": 1 if w.loss == "mse" else plan.segments, "dv_split": plan.dv_split,
+            "segments": 1 if (w.loss == "mse" or w.weight_norm) else plan.segments, "dv_split": plan.dv_split,
             "phi_split": plan.phi_split, "launch": args.launch,
-            "kernels_per_step": 1 if w.loss == "mse" else plan.n_kernels,
+            "kernels_per_step": 1 if w.loss == "mse" else (3 if w.weight_norm else plan.n_kernels),
+            "weight_norm": w.weight_norm,
             "input_sets": n_sets,
             "head_tokens_per_s": round(w.head_tokens / (ms_per_step * 1e-3), 1),
         },

@@ -75,12 +75,26 @@ enum {
     TTT_LA_ETA_SCALAR = 0u,          /* eta_t = eta_scalar; the eta pointer must be NULL */
     TTT_LA_ETA_PER_TOKEN = 1u << 1,  /* eta_t = eta[b,h,t] */
     TTT_LA_ETA_SOFTPLUS = 1u << 2,   /* eta_t = softplus(eta[b,h,t]) = ln(1 + e^a) (Table 2, Variant 3) */
-    TTT_LA_LOSS_MSE = 1u << 3        /* binding loss 1/2 ||S phi(k_t) - v_t||^2 instead of -<S phi(k_t), v_t>:
+    TTT_LA_LOSS_MSE = 1u << 3,       /* binding loss 1/2 ||S phi(k_t) - v_t||^2 instead of -<S phi(k_t), v_t>:
                                         the delta rule S_t = S_{t-1} - eta_t (S_{t-1} k_t - v_t) k_t^T
                                         (mlsanity.com page: Modular TTT abstract, MSE and inner-product
                                         losses; "Builds on": the delta-rule parallelisation paper).
                                         ttt_la_forward only; bf16, identity map, d_k = d_v in {64, 128},
                                         causal, beta = 0; anything else TTT_LA_ERR_UNSUPPORTED */
+    TTT_LA_WEIGHT_NORM = 1u << 4     /* Variant 1 of Table 2 (thelatestinai.com page): the updated layer
+                                        is weight-normalised, recurrent implementation only.  The pages
+                                        do not define the normalisation; here, after each token's update,
+                                        every row of S (one value column: its weights over the features)
+                                        is rescaled to the Euclidean norm that row has in S0, and M is
+                                        not rescaled (a row with a zero S0 norm stays zero).
+                                        ttt_la_forward_state only, with S0 given (else
+                                        TTT_LA_ERR_INVALID_ARG, as with the bidirectional or MSE bits);
+                                        d_v a multiple of 16, d_phi in {64, 128, 256, 512}, identity map
+                                        (bf16 or fp32, d_k = d_phi) or bf16 SwiGLU map with d_k = 128,
+                                        else TTT_LA_ERR_UNSUPPORTED.  One workgroup per 16 rows of S
+                                        walks the tokens in order; the SwiGLU features of q and k go to
+                                        the handle's workspace first (TTT_LA_ERR_UNSUPPORTED if it is
+                                        smaller than 4 B H T d_phi bytes). */
 };
 
 typedef struct {

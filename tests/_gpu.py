@@ -32,6 +32,7 @@ def to_device(x: Inputs):
     out["a"] = torch.from_numpy(x.a32).to("cuda") if x.a32 is not None else None
     out["w1"] = dev(x.w1_dev) if x.w1_dev is not None else None
     out["w3"] = dev(x.w3_dev) if x.w3_dev is not None else None
+    out["S0"] = torch.from_numpy(x.S0).to("cuda") if x.S0 is not None else None
     return out
 
 
@@ -64,8 +65,12 @@ def run_gpu(w: Workload, d, chunk=None, segments=0, eta_sign=1.0, q_override=Non
             eta = -d["a"]
     q = d["q"] if q_override is None else q_override
     v = d["v"] if v_scale is None else (d["v"] * v_scale).contiguous()
-    o = lay.forward(q, d["k"], v, eta=eta, eta_scalar=eta_scalar, beta=w.beta, eta_mode=w.eta_mode,
-                    causal=w.causal, loss=w.loss)
+    if w.weight_norm:
+        o = lay.forward_state(q, d["k"], v, eta=eta, eta_scalar=eta_scalar, beta=w.beta, eta_mode=w.eta_mode,
+                              S0=d["S0"], weight_norm=True)
+    else:
+        o = lay.forward(q, d["k"], v, eta=eta, eta_scalar=eta_scalar, beta=w.beta, eta_mode=w.eta_mode,
+                        causal=w.causal, loss=w.loss)
     torch.cuda.synchronize()
     return from_device(o, w.dtype)
 
@@ -91,10 +96,24 @@ def run_oracle(w: Workload, x: Inputs, heads=None, q64=None):
                 outs.append(oracle.forward(q[i:i + 1], k[i:i + 1], v[i:i + 1], eta_mode=w.eta_mode,
                                            eta=None if a is None else a[i:i + 1],
                                            eta_scalar=w.eta_scalar, beta=w.beta, causal=w.causal,
-                                           phi=w.phi, w1=w1[h:h + 1], w3=w3[h:h + 1], loss=w.loss))
+                                           phi=w.phi, w1=w1[h:h + 1], w3=w3[h:h + 1], loss=w.loss,
+                                           **_wn(w, x, [bs[i]], [h])))
             return np.concatenate(outs, axis=0)
+        return oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar, beta=w.beta,
+                              causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss, **_wn(w, x, bs, hs))
     return oracle.forward(q, k, v, eta_mode=w.eta_mode, eta=a, eta_scalar=w.eta_scalar, beta=w.beta,
-                          causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss)
+                          causal=w.causal, phi=w.phi, w1=w1, w3=w3, loss=w.loss, **_wn(w, x))
+
+
+def _wn(w: Workload, x: Inputs, bs=None, hs=None):
+    """Oracle arguments of a weight-normalised workload (the entry state of the
+    selected sequences, as [n, 1, d_v, d_phi])."""
+    if not w.weight_norm:
+        return {}
+    S0 = x.S0.astype(np.float64)
+    if bs is not None:
+        S0 = S0[bs, hs][:, None]
+    return {"S0": S0, "weight_norm": True}
 
 
 def select_heads(o: np.ndarray, w: Workload, heads):

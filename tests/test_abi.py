@@ -349,3 +349,25 @@ def test_mse_loss_mode():
     assert check_fs(mode=mse, beta=0.0) == tla.TTT_LA_ERR_UNSUPPORTED
     assert check_step(mode=mse, beta=0.0) == tla.TTT_LA_ERR_UNSUPPORTED
     assert tla.mode_bits("softplus", True, "mse") == tla.TTT_LA_ETA_SOFTPLUS | mse
+
+
+def test_weight_norm_mode():
+    # Variant 1's weight-normalised recurrence: ttt_la_forward_state with an entry state
+    wn = tla.TTT_LA_WEIGHT_NORM
+    assert check_fs(mode=wn) == tla.TTT_LA_OK
+    assert check_fs(mode=wn, m0=None, st=None, mt=None) == tla.TTT_LA_OK
+    assert check_fs(eta=ETA, mode=wn | tla.TTT_LA_ETA_SOFTPLUS) == tla.TTT_LA_OK
+    assert check_fs(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=W3), mode=wn) == tla.TTT_LA_OK
+    assert check_fs(d=desc(dtype="f32", d_k=64, d_v=64), mode=wn) == tla.TTT_LA_OK
+    bad = tla.TTT_LA_ERR_INVALID_ARG
+    assert check_fs(mode=wn, s0=None) == bad                          # the target norms come from S0
+    assert check_fs(mode=wn | tla.TTT_LA_LOSS_MSE, beta=0.0) == bad
+    assert check(mode=wn) == bad                                     # plain forward: no entry state
+    # widths the kernel does not take
+    assert check_fs(d=desc(d_v=120), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check_fs(d=desc(d_k=96, d_v=96), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check_fs(d=desc(d_k=64, phi="swiglu", d_phi=256, w1=W1, w3=W3), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
+    # no weight-normalised step
+    assert check_step(mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert tla.mode_bits("softplus", True, weight_norm=True) == tla.TTT_LA_ETA_SOFTPLUS | wn
+    assert wn == 1 << 4

@@ -33,6 +33,7 @@ SMALL = {
     "v3_long_1x16x65536_d128": dict(B=1, H=2, T=128 * 3 + 50),
     "bidir_vit_256x6x196_d64": dict(B=3, H=2, T=196),
     "v3_delta_8x16x4096_d128": dict(B=2, H=2, T=32 * 9 + 7),
+    "v1_weightnorm_4x16x8192_d128_f512": dict(B=1, H=2, T=16 * 5 + 7),
 }
 
 # full shapes: how many heads the oracle recomputes at full T (a subset always holds
@@ -46,12 +47,13 @@ FULL_HEADS = {
     "v3_long_1x16x65536_d128": 8,
     "bidir_vit_256x6x196_d64": 64,
     "v3_delta_8x16x4096_d128": 8,
+    "v1_weightnorm_4x16x8192_d128_f512": 8,
 }
 
 
 def expected_path(w):
-    if w.loss == "mse":
-        return None   # the plan describes the dot-product forward; the delta rule has its own kernel
+    if w.loss == "mse" or w.weight_norm:
+        return None   # the plan describes the dot-product forward; these have kernels of their own
     if w.dtype != "bf16":
         # fp32: the one-pass masked product for short identity-map sequences
         return 4 if (w.phi == "identity" and w.T <= 1024 and w.d_v % 64 == 0) else 0

@@ -16,6 +16,6 @@ from ._binding import (  # noqa: F401
     TTT_LA_OK, TTT_LA_ERR_INVALID_ARG, TTT_LA_ERR_UNSUPPORTED, TTT_LA_ERR_HIP, TTT_LA_ERR_OOM,
     TTT_LA_ERR_TOO_LARGE, TTT_LA_NOALLOC_SCRATCH_BYTES,
     TTT_LA_F32, TTT_LA_BF16, TTT_LA_PHI_IDENTITY, TTT_LA_PHI_SWIGLU, TTT_LA_CAUSAL,
-    TTT_LA_BIDIRECTIONAL, TTT_LA_ETA_SCALAR, TTT_LA_ETA_PER_TOKEN, TTT_LA_ETA_SOFTPLUS, TTT_LA_LOSS_MSE,
+    TTT_LA_BIDIRECTIONAL, TTT_LA_ETA_SCALAR, TTT_LA_ETA_PER_TOKEN, TTT_LA_ETA_SOFTPLUS, TTT_LA_LOSS_MSE, TTT_LA_WEIGHT_NORM,
     TTT_LA_LAUNCH_AUTO, TTT_LA_LAUNCH_SEPARATE, TTT_LA_LAUNCH_SINGLE, TTT_LA_LAUNCH_PREFIX,
 )

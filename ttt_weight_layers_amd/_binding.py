@@ -43,6 +43,7 @@ TTT_LA_ETA_SCALAR = 0
 TTT_LA_ETA_PER_TOKEN = 1 << 1
 TTT_LA_ETA_SOFTPLUS = 1 << 2
 TTT_LA_LOSS_MSE = 1 << 3
+TTT_LA_WEIGHT_NORM = 1 << 4
 
 
 class ttt_la_desc(ctypes.Structure):
@@ -312,8 +313,9 @@ def _ptr(t) -> Optional[int]:
 _LOSS = {"dot": 0, "mse": TTT_LA_LOSS_MSE}
 
 
-def mode_bits(eta_mode: str = "scalar", causal: bool = True, loss: str = "dot") -> int:
-    return _ETA[eta_mode] | (0 if causal else TTT_LA_BIDIRECTIONAL) | _LOSS[loss]
+def mode_bits(eta_mode: str = "scalar", causal: bool = True, loss: str = "dot", weight_norm: bool = False) -> int:
+    return (_ETA[eta_mode] | (0 if causal else TTT_LA_BIDIRECTIONAL) | _LOSS[loss]
+            | (TTT_LA_WEIGHT_NORM if weight_norm else 0))
 
 
 _TORCH_DTYPES = {"f32": "float32", "bf16": "bfloat16"}
@@ -443,11 +445,12 @@ class TTTLinearAttention:
         return out
 
     def forward_state(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", S0=None, M0=None,
-                      out=None, S_T=None, M_T=None, stream=None):
+                      out=None, S_T=None, M_T=None, stream=None, weight_norm=False):
         """Causal forward from the carried state (S0, M0) (None = zero); writes the state
-        after the last token to S_T, M_T when given (fp32 [B, H, d_v, d_phi])."""
+        after the last token to S_T, M_T when given (fp32 [B, H, d_v, d_phi]).
+        weight_norm: the weight-normalised recurrence (TTT_LA_WEIGHT_NORM; S0 required)."""
         import torch
-        mode = mode_bits(eta_mode, True)
+        mode = mode_bits(eta_mode, True, weight_norm=weight_norm)
         check_tensors(self.desc, "forward_state", mode, q=q, k=k, v=v, eta=eta, out=out, S0=S0, M0=M0, S_T=S_T,
                       M_T=M_T)
         s, ext = _launch_stream(q, stream)

@@ -40,7 +40,8 @@ namespace {
 
 using ttt::Shape;
 
-constexpr uint32_t kModeMask = TTT_LA_BIDIRECTIONAL | TTT_LA_ETA_PER_TOKEN | TTT_LA_ETA_SOFTPLUS | TTT_LA_LOSS_MSE;
+constexpr uint32_t kModeMask =
+    TTT_LA_BIDIRECTIONAL | TTT_LA_ETA_PER_TOKEN | TTT_LA_ETA_SOFTPLUS | TTT_LA_LOSS_MSE | TTT_LA_WEIGHT_NORM;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -94,7 +95,7 @@ ttt_la_hints hints_or_auto(const ttt_la_hints* h) {
 Shape shape_of(const ttt_la_desc& d);
 
 int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
-                  float eta_scalar, float beta, uint32_t mode, const void* o) {
+                  float eta_scalar, float beta, uint32_t mode, const void* o, bool state_call = false) {
     if (!q || !k || !v || !o) return TTT_LA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16)) return TTT_LA_ERR_INVALID_ARG;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
@@ -125,6 +126,11 @@ int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void
     if ((mode & TTT_LA_LOSS_MSE) &&
         (beta != 0.0f || (mode & TTT_LA_BIDIRECTIONAL) || !ttt::delta_supported(shape_of(*d))))
         return TTT_LA_ERR_UNSUPPORTED;
+    // weight normalisation: causal, dot-product loss (and an entry state: forward_state only)
+    if (mode & TTT_LA_WEIGHT_NORM) {
+        if (!state_call || (mode & (TTT_LA_BIDIRECTIONAL | TTT_LA_LOSS_MSE))) return TTT_LA_ERR_INVALID_ARG;
+        if (!ttt::wn_supported(shape_of(*d))) return TTT_LA_ERR_UNSUPPORTED;
+    }
     return TTT_LA_OK;
 }
 
@@ -135,10 +141,11 @@ bool state_ok(const void* p) { return !p || aligned(p, 16); }
 int check_forward_state(const ttt_la_desc* d, const void* q, const void* k, const void* v, const float* eta,
                         float eta_scalar, float beta, uint32_t mode, const float* S0, const float* M0, const void* o,
                         const float* S_T, const float* M_T) {
-    int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, o);
+    int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, o, true);
     if (st != TTT_LA_OK) return st;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
     if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // the delta rule has no carried state here
+    if ((mode & TTT_LA_WEIGHT_NORM) && !S0) return TTT_LA_ERR_INVALID_ARG;   // the target row norms
     if (!state_ok(S0) || !state_ok(M0) || !state_ok(S_T) || !state_ok(M_T)) return TTT_LA_ERR_INVALID_ARG;
     const size_t eb = elem_bytes(d->dtype);
     const size_t nt = (size_t)d->B * d->H * d->T;
@@ -169,7 +176,7 @@ int check_step(const ttt_la_desc* d, const void* q, const void* k, const void* v
     if (!aligned(S, 16) || !aligned(M, 16)) return TTT_LA_ERR_INVALID_ARG;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
-    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // no delta-rule step
+    if (mode & (TTT_LA_LOSS_MSE | TTT_LA_WEIGHT_NORM)) return TTT_LA_ERR_UNSUPPORTED;   // no such step
     const bool per_tok = (mode & TTT_LA_ETA_PER_TOKEN) != 0;
     const bool softp = (mode & TTT_LA_ETA_SOFTPLUS) != 0;
     if (per_tok && softp) return TTT_LA_ERR_INVALID_ARG;
@@ -295,6 +302,10 @@ int ttt_la_create_hinted(const ttt_la_desc* desc, const ttt_la_hints* hints, ttt
         h->fp = ttt::fast_plan(h->shape, desc->chunk, h->hints.segments, h->hints.value_split, h->hints.launch);
         h->workspace_bytes = h->fp.summary_bytes + h->fp.partial_bytes + h->fp.zero_bytes;
     }
+    // the weight-normalised recurrence puts the SwiGLU features of q and k at the start of
+    // the workspace (the plan's areas are not in use during that call)
+    if (ttt::wn_supported(h->shape))
+        h->workspace_bytes = std::max(h->workspace_bytes, ttt::wn_workspace_bytes(h->shape));
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return TTT_LA_ERR_HIP;
@@ -365,7 +376,12 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
     hipEvent_t eb = nullptr, ee = nullptr;
     if (timed) next_events(h, &eb, &ee);
     hipError_t e;
-    if (mode & TTT_LA_LOSS_MSE) {
+    if (mode & TTT_LA_WEIGHT_NORM) {
+        // validated by check_forward_state: the recurrent kernel (the SwiGLU features go
+        // to the handle's workspace first)
+        if (ttt::wn_workspace_bytes(h->shape) > h->workspace_bytes || reverse) return TTT_LA_ERR_UNSUPPORTED;
+        e = ttt::launch_wn(h->shape, h->workspace, a, eb, ee);
+    } else if (mode & TTT_LA_LOSS_MSE) {
         // validated by check_forward: the delta-rule kernel, no workspace
         e = ttt::launch_delta(h->shape, a, eb, ee);
     } else if (h->fast && (h->fp.wide || !state_io)) {

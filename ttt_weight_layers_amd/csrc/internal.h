@@ -106,6 +106,13 @@ hipError_t launch_short(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
 bool delta_supported(const Shape& s);
 hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// weight-normalised recurrent forward (wn.hip): causal, entry state required; bf16 or
+// fp32 identity map (d_k = d_phi), or the bf16 SwiGLU map with d_k = 128; d_v a
+// multiple of 16, d_phi in {64, 128, 256, 512}
+bool wn_supported(const Shape& s);
+size_t wn_workspace_bytes(const Shape& s);
+hipError_t launch_wn(const Shape& s, void* workspace, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
+
 // backward through the SwiGLU feature map (swiglu_bwd.hip): d_k = d_v = 128, bf16
 bool swiglu_backward_supported(const Shape& s);
 // phi(x) of every 128-feature slice, slice-major [P][B H T][128]

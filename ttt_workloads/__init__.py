@@ -22,6 +22,10 @@ Recipe (per workload, numpy PCG64 ``default_rng(seed)``):
      as fp32 (one more ``standard_normal`` draw, shifted by -2).
   5. If the feature map is SwiGLU: W1 then W3 ~ N(0, 1)/sqrt(128), shape
      [H, d_phi, d_k] (out x in), cast like q.
+  6. Workloads with a weight-normalised fast weight (Variant 1): the entry
+     state S0 ~ N(0, 1)/sqrt(d_phi), shape [B, H, d_v, d_phi], fp32 (the
+     stand-in for the learned initial fast weight whose row norms the
+     normalisation keeps).
 """
 from __future__ import annotations
 
@@ -55,6 +59,7 @@ class Workload:
     seed: int
     note: str = ""
     loss: str = "dot"     # binding loss: "dot" (linear attention) or "mse" (delta rule)
+    weight_norm: bool = False   # Variant 1: rows of S kept at their entry-state norms
 
     @property
     def n_seq(self) -> int:
@@ -82,7 +87,7 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
-# The synthetic workloads.  Seeds 1001..1008 in this order.
+# The synthetic workloads.  Seeds 1001..1009 in this order.
 WORKLOADS = {
     # Plain causal linear attention (the last row of the ablation, Table 2, with a
     # constant unit step and no momentum), fp32.
@@ -134,6 +139,13 @@ WORKLOADS = {
         dtype="bf16", phi="identity", eta_mode="softplus", eta_scalar=0.0, beta=0.0,
         causal=True, chunk=0, l2norm=True, seed=1008,
         note="delta rule (MSE loss), eta=softplus(a), no momentum", loss="mse"),
+    # Variant 1: the Variant 2 layer with its updated layer weight-normalised
+    # (recurrent implementation only), from a drawn entry state.
+    "v1_weightnorm_4x16x8192_d128_f512": Workload(
+        "v1_weightnorm_4x16x8192_d128_f512", B=4, H=16, T=8192, d_k=128, d_v=128, d_phi=512,
+        dtype="bf16", phi="swiglu", eta_mode="softplus", eta_scalar=0.0, beta=0.9,
+        causal=True, chunk=0, l2norm=False, seed=1009,
+        note="V1, V2 with weight-normalised rows of S, recurrent", weight_norm=True),
 }
 
 
@@ -157,6 +169,7 @@ class Inputs:
     w3_64: Optional[np.ndarray] = None
     w1_dev: Optional[np.ndarray] = None
     w3_dev: Optional[np.ndarray] = None
+    S0: Optional[np.ndarray] = None         # [B,H,d_v,d_phi] fp32 entry state (weight_norm)
 
 
 def f64_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -209,10 +222,13 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
         s = 1.0 / np.sqrt(128.0)
         w1_dev, w1_64 = round_to_dtype(rng.standard_normal((w.H, w.d_phi, w.d_k)) * s, w.dtype)
         w3_dev, w3_64 = round_to_dtype(rng.standard_normal((w.H, w.d_phi, w.d_k)) * s, w.dtype)
+    S0 = None
+    if w.weight_norm:
+        S0 = (rng.standard_normal((w.B, w.H, w.d_v, w.d_phi)) / np.sqrt(w.d_phi)).astype(np.float32)
     return Inputs(workload=w,
                   q64=raw["q"][1], k64=raw["k"][1], v64=raw["v"][1],
                   q_dev=raw["q"][0], k_dev=raw["k"][0], v_dev=raw["v"][0],
-                  a32=a32, w1_64=w1_64, w3_64=w3_64, w1_dev=w1_dev, w3_dev=w3_dev)
+                  a32=a32, w1_64=w1_64, w3_64=w3_64, w1_dev=w1_dev, w3_dev=w3_dev, S0=S0)
 
 
 def head_subset(w: Workload, n: int = 8, seed: Optional[int] = None):
