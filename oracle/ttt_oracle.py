@@ -258,12 +258,16 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
 
 
 def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
-         beta: float = 0.0, phi: str = "identity", w1=None, w3=None):
+         beta: float = 0.0, phi: str = "identity", w1=None, w3=None, weight_norm: bool = False):
     """One recurrent step (decode) for every sequence: the token q1, k1, v1
     ([B, H, d]) with rate eta ([B, H], per_token / softplus modes) updates the
     carried state (S, M) ([B, H, d_v, d_phi]) and is read out after its update:
 
       M' = beta M + eta v phi(k)^T,   S' = S + M',   o = S' phi(q).
+
+    ``weight_norm``: Variant 1's step (the reading in ``forward``): each row of S'
+    is rescaled to the norm of the same row of S (which a weight-normalised run
+    keeps at its entry-state norm), 0 if either norm is 0.
 
     Returns (o [B, H, d_v], S', M').  The step is written out on its own (it is
     the loop body of ``forward``); the tests check T steps against ``forward``.
@@ -293,6 +297,10 @@ def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: fl
     M = np.asarray(M, np.float64).reshape(N, d_v, d_phi)
     M_new = beta * M + e[:, None, None] * v1[:, :, None] * pk[:, None, :]
     S_new = S + M_new
+    if weight_norm:
+        target = np.sqrt(np.sum(S * S, axis=2))
+        norm = np.sqrt(np.sum(S_new * S_new, axis=2))
+        S_new = S_new * np.divide(target, norm, out=np.zeros_like(norm), where=norm > 0)[:, :, None]
     o = np.einsum("nvf,nf->nv", S_new, pq)
     return o.reshape(B, H, d_v), S_new.reshape(B, H, d_v, d_phi), M_new.reshape(B, H, d_v, d_phi)
 

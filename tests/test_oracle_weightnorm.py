@@ -113,3 +113,19 @@ def test_zero_rows_stay_zero_and_errors():
         oracle.forward(q, k, v, weight_norm=True)
     with pytest.raises(ValueError):
         oracle.forward(q, k, v, S0=S0, causal=False, weight_norm=True)
+
+
+@pytest.mark.parametrize("phi,d_phi", [("identity", None), ("swiglu", 12)])
+def test_steps_give_the_forward(phi, d_phi):
+    # the step rescales to the norms of the state it is given, which a weight-normalised
+    # run keeps at the entry-state norms: T steps are the forward
+    q, k, v, a, S0, M0, kw = _inputs(8, phi=phi, d_phi=d_phi)
+    o_ref, S_ref, M_ref = oracle.forward(q, k, v, eta_mode="softplus", eta=a, beta=0.9, phi=phi, S0=S0, M0=M0,
+                                         return_state=True, weight_norm=True, **kw)
+    S, M = S0.copy(), M0.copy()
+    for t in range(q.shape[2]):
+        o, S, M = oracle.step(q[:, :, t], k[:, :, t], v[:, :, t], S, M, eta_mode="softplus", eta=a[:, :, t],
+                              beta=0.9, phi=phi, weight_norm=True, **kw)
+        np.testing.assert_allclose(o, o_ref[:, :, t], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-11)
+    np.testing.assert_allclose(M, M_ref, rtol=1e-11)
