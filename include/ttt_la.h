@@ -87,8 +87,12 @@ enum {
                                         every row of S (one value column: its weights over the features)
                                         is rescaled to the Euclidean norm that row has in S0, and M is
                                         not rescaled (a row with a zero S0 norm stays zero).
-                                        ttt_la_forward_state only, with S0 given (else
-                                        TTT_LA_ERR_INVALID_ARG, as with the bidirectional or MSE bits);
+                                        ttt_la_forward_state, with S0 given (else
+                                        TTT_LA_ERR_INVALID_ARG, as with the bidirectional or MSE bits),
+                                        and ttt_la_step (each row of the new S rescaled to the norm of
+                                        the same row of the given S, which a weight-normalised run
+                                        keeps at its entry-state norm); ttt_la_forward and the
+                                        backward: TTT_LA_ERR_INVALID_ARG;
                                         d_v a multiple of 16, d_phi in {64, 128, 256, 512}, identity map
                                         (bf16 or fp32, d_k = d_phi) or bf16 SwiGLU map with d_k = 128,
                                         else TTT_LA_ERR_UNSUPPORTED.  One workgroup per 16 rows of S
@@ -222,7 +226,8 @@ int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v
  *   S, M     device fp32 [B, H, d_v, d_phi] as in ttt_la_forward_state,
  *            updated in place; they must not overlap each other or any other
  *            argument.
- *   mode     rate bits only (TTT_LA_BIDIRECTIONAL is invalid here).
+ *   mode     rate bits, and TTT_LA_WEIGHT_NORM (Variant 1's step: see the mode
+ *            bits); TTT_LA_BIDIRECTIONAL is invalid here.
  * The handle's T is ignored; its B, H, widths, dtype and feature map (W1, W3)
  * apply.  Allocates nothing, does not synchronise; errors as ttt_la_forward. */
 int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,

@@ -367,7 +367,8 @@ def test_weight_norm_mode():
     assert check_fs(d=desc(d_v=120), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
     assert check_fs(d=desc(d_k=96, d_v=96), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
     assert check_fs(d=desc(d_k=64, phi="swiglu", d_phi=256, w1=W1, w3=W3), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
-    # no weight-normalised step
-    assert check_step(mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
+    # the weight-normalised step (same widths)
+    assert check_step(mode=wn) == tla.TTT_LA_OK
+    assert check_step(d=desc(phi="swiglu", d_phi=384, w1=W1, w3=W3), mode=wn) == tla.TTT_LA_ERR_UNSUPPORTED
     assert tla.mode_bits("softplus", True, weight_norm=True) == tla.TTT_LA_ETA_SOFTPLUS | wn
     assert wn == 1 << 4

@@ -113,3 +113,35 @@ def test_weight_norm_needs_the_entry_state():
     with pytest.raises(tla.TTTError):
         lay.forward_state(d["q"], d["k"], d["v"], eta_scalar=0.5, weight_norm=True)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("phi,dtype,d_k,d_v,d_phi", [
+    ("identity", "bf16", 128, 128, 128), ("identity", "f32", 64, 64, 64), ("swiglu", "bf16", 128, 128, 512),
+    ("swiglu", "bf16", 128, 64, 256),
+])
+def test_weight_norm_steps_follow_the_oracle(phi, dtype, d_k, d_v, d_phi):
+    # T decode steps from S0 against the oracle's weight-normalised forward
+    import torch
+    w = _case(phi, dtype, d_k, d_v, d_phi, "softplus", 0.9, 2, 2, 12)
+    say(f"[weight norm step] {w.name}")
+    x = make_inputs(w)
+    d = to_device(x)
+    lay = make_layer(w, d)
+    S = torch.from_numpy(x.S0).cuda()
+    M = torch.zeros_like(S)
+    outs = []
+    for t in range(w.T):
+        sl = lambda a: a[:, :, t:t + 1].contiguous()
+        outs.append(lay.step(sl(d["q"]), sl(d["k"]), sl(d["v"]), S, M, eta=d["a"][:, :, t].contiguous(),
+                             beta=w.beta, eta_mode=w.eta_mode, weight_norm=True))
+    torch.cuda.synchronize()
+    got_o = np.concatenate([from_device(o, w.dtype) for o in outs], axis=2)
+    ref_o, ref_S, ref_M = oracle.forward(x.q64, x.k64, x.v64, eta_mode=w.eta_mode, eta=x.a32, beta=w.beta,
+                                         phi=w.phi, w1=x.w1_64, w3=x.w3_64, S0=x.S0.astype(np.float64),
+                                         return_state=True, weight_norm=True)
+    tol = TOL[w.dtype]
+    for name, got, ref in (("o", got_o, ref_o), ("S", S.cpu().numpy().astype(np.float64), ref_S),
+                           ("M", M.cpu().numpy().astype(np.float64), ref_M)):
+        err = oracle.rel_err(got, ref)
+        say(f"  {name} rel err {err:.2e}")
+        assert err <= tol, name

@@ -465,10 +465,12 @@ class TTTLinearAttention:
             _record(ext, out)
         return out
 
-    def step(self, q, k, v, S, M, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", out=None, stream=None):
-        """One recurrent step: q, k, v [B, H, 1, d]; S, M fp32 [B, H, d_v, d_phi] updated in place."""
+    def step(self, q, k, v, S, M, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", out=None, stream=None,
+             weight_norm=False):
+        """One recurrent step: q, k, v [B, H, 1, d]; S, M fp32 [B, H, d_v, d_phi] updated in place.
+        weight_norm: Variant 1's step (TTT_LA_WEIGHT_NORM)."""
         import torch
-        mode = mode_bits(eta_mode, True)
+        mode = mode_bits(eta_mode, True, weight_norm=weight_norm)
         if S is None or M is None:
             raise ValueError("the step needs the state S and M")
         check_tensors(self.desc, "step", mode, q=q, k=k, v=v, eta=eta, out=out, S=S, M=M)

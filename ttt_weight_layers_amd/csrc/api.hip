@@ -176,7 +176,8 @@ int check_step(const ttt_la_desc* d, const void* q, const void* k, const void* v
     if (!aligned(S, 16) || !aligned(M, 16)) return TTT_LA_ERR_INVALID_ARG;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
-    if (mode & (TTT_LA_LOSS_MSE | TTT_LA_WEIGHT_NORM)) return TTT_LA_ERR_UNSUPPORTED;   // no such step
+    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // no delta-rule step
+    if ((mode & TTT_LA_WEIGHT_NORM) && !ttt::wn_supported(shape_of(*d))) return TTT_LA_ERR_UNSUPPORTED;
     const bool per_tok = (mode & TTT_LA_ETA_PER_TOKEN) != 0;
     const bool softp = (mode & TTT_LA_ETA_SOFTPLUS) != 0;
     if (per_tok && softp) return TTT_LA_ERR_INVALID_ARG;
@@ -1003,6 +1004,7 @@ int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const f
     a.M = M;
     a.o = o;
     a.stream = static_cast<hipStream_t>(hip_stream);
+    a.weight_norm = (mode & TTT_LA_WEIGHT_NORM) != 0;
     hipEvent_t eb, ee;
     next_events(h, &eb, &ee);
     const hipError_t e = ttt::launch_step(h->shape, a, eb, ee);

@@ -66,7 +66,7 @@ __device__ __forceinline__ void load16_as_f32(const float* p, float* out) {
     for (int i = 0; i < 4; ++i) out[i] = u[i];
 }
 
-template <typename TI, bool SWIGLU, int SR>
+template <typename TI, bool SWIGLU, int SR, bool WN>
 __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
     extern __shared__ float smem[];
     const int d_k = p.d_k, d_phi = p.d_phi;
@@ -213,6 +213,57 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
             *reinterpret_cast<f32x2*>(S + (size_t)rr * d_phi + c) = sv[rr];
         }
     };
+    if constexpr (WN) {
+        // Variant 1 (weight-normalised rows): the whole row is in registers (d_phi <=
+        // 128 NPRE); the new row is rescaled to the norm of the given one before it is
+        // written, and the readout takes the same factor
+        float n_old[RW], n_new[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) n_old[rr] = n_new[rr] = 0.0f;
+#pragma unroll
+        for (int it = 0; it < NPRE; ++it) {
+            const int c = c0 + 128 * it;
+            if (c < d_phi) {
+                const float pk0 = sPk[c], pk1 = sPk[c + 1], pq0 = sPq[c], pq1 = sPq[c + 1];
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    f32x2& m = m0[it][rr];
+                    f32x2& sv = s0[it][rr];
+                    n_old[rr] = fmaf(sv[0], sv[0], fmaf(sv[1], sv[1], n_old[rr]));
+                    m[0] = fmaf(beta, m[0], ev[rr] * pk0);
+                    m[1] = fmaf(beta, m[1], ev[rr] * pk1);
+                    sv[0] += m[0];
+                    sv[1] += m[1];
+                    n_new[rr] = fmaf(sv[0], sv[0], fmaf(sv[1], sv[1], n_new[rr]));
+                    acc[rr] = fmaf(sv[0], pq0, fmaf(sv[1], pq1, acc[rr]));
+                }
+            }
+        }
+        float fac[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                n_old[rr] += __shfl_xor(n_old[rr], off, 64);
+                n_new[rr] += __shfl_xor(n_new[rr], off, 64);
+            }
+            fac[rr] = n_new[rr] > 0.0f ? sqrtf(n_old[rr] / n_new[rr]) : 0.0f;
+        }
+#pragma unroll
+        for (int it = 0; it < NPRE; ++it) {
+            const int c = c0 + 128 * it;
+            if (c < d_phi) {
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) {
+                    *reinterpret_cast<f32x2*>(M + (size_t)rr * d_phi + c) = m0[it][rr];
+                    *reinterpret_cast<f32x2*>(S + (size_t)rr * d_phi + c) =
+                        f32x2{fac[rr] * s0[it][rr][0], fac[rr] * s0[it][rr][1]};
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) acc[rr] *= fac[rr];   // reduced below like the plain step
+    } else {
 #pragma unroll
     for (int it = 0; it < NPRE; ++it)
         if (c0 + 128 * it < d_phi) row_step(c0 + 128 * it, m0[it], s0[it]);
@@ -224,6 +275,7 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
             sv[rr] = *reinterpret_cast<const f32x2*>(S + (size_t)rr * d_phi + c);
         }
         row_step(c, m, sv);
+    }
     }
 #pragma unroll
     for (int rr = 0; rr < RW; ++rr) {
@@ -264,12 +316,27 @@ hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, h
     const dim3 grid((unsigned)(s.n_seq() * p.n_rblk)), block(STHREADS);
     void* args[] = {&p};
     const void* fn;
-    if (s.swiglu && sr == SR_SWIGLU)
-        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU> : (const void*)step_kernel<float, true, SR_SWIGLU>;
+    if (a.weight_norm) {
+        // the whole row must fit the registers of the first slices
+        if (s.d_phi > (s.swiglu ? 512 : 128)) return hipErrorInvalidValue;
+        if (s.swiglu && sr == SR_SWIGLU)
+            fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU, true>
+                        : (const void*)step_kernel<float, true, SR_SWIGLU, true>;
+        else if (s.swiglu)
+            fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN, true>
+                        : (const void*)step_kernel<float, true, SR_PLAIN, true>;
+        else
+            fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN, true>
+                        : (const void*)step_kernel<float, false, SR_PLAIN, true>;
+    } else if (s.swiglu && sr == SR_SWIGLU)
+        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU, false>
+                    : (const void*)step_kernel<float, true, SR_SWIGLU, false>;
     else if (s.swiglu)
-        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN> : (const void*)step_kernel<float, true, SR_PLAIN>;
+        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN, false>
+                    : (const void*)step_kernel<float, true, SR_PLAIN, false>;
     else
-        fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN> : (const void*)step_kernel<float, false, SR_PLAIN>;
+        fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN, false>
+                    : (const void*)step_kernel<float, false, SR_PLAIN, false>;
     return hipExtLaunchKernel(fn, grid, block, args, smem, a.stream, ev_begin, ev_end, 0);
 }
 

@@ -148,6 +148,7 @@ struct StepArgs {
     float* M;
     void* o;             // [B, H, d_v]
     hipStream_t stream;
+    bool weight_norm = false;   // rows of the new S rescaled to the norms of the given S
 };
 size_t step_smem_bytes(const Shape& s);
 // ev_begin/ev_end (may be null) take the step kernel's start and end timestamps
