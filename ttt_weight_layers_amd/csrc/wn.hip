@@ -51,7 +51,7 @@ struct WnParams {
     float* S_T;             // may be null
     float* M_T;             // may be null
     void* o;                // [seq][T][d_v] in TI
-    int T, d_v, n_rb;
+    int T, d_v, n_rb, n_units;
     size_t n_rows;          // seq * T: the slice stride of phq, phk
 };
 
@@ -96,8 +96,12 @@ __global__ void __launch_bounds__(NTH) wn_forward(WnParams p) {
 
     const int tid = threadIdx.x;
     const int r = tid >> 4, pp = tid & 15;
-    const int rb = blockIdx.x % p.n_rb;
-    const size_t seq = blockIdx.x / p.n_rb;
+    // XCD-aware: the row blocks of one sequence, which stage the same features, are
+    // consecutive units and share an XCD's L2
+    const int unit = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (unit >= p.n_units) return;
+    const int rb = unit % p.n_rb;
+    const size_t seq = unit / p.n_rb;
     const int row = rb * NR + r;                      // value row of S
     const size_t srow = seq * p.T;
     const int T = p.T, d_v = p.d_v;
@@ -248,7 +252,7 @@ __global__ void __launch_bounds__(NTH) wn_forward(WnParams p) {
 
 template <int FPT, typename TI>
 hipError_t launch_wn_one(const WnParams& p, int n_seq, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
-    const dim3 grid((unsigned)(n_seq * p.n_rb)), block(NTH);
+    const dim3 grid((unsigned)((n_seq * p.n_rb + 7) / 8 * 8)), block(NTH);
     if (eb || ee) {
         WnParams a = p;
         void* args[] = {&a};
@@ -301,6 +305,7 @@ hipError_t launch_wn(const Shape& s, void* workspace, const FwdArgs& a, hipEvent
     p.T = s.T;
     p.d_v = s.d_v;
     p.n_rb = s.d_v / NR;
+    p.n_units = s.n_seq() * p.n_rb;
     p.n_rows = (size_t)s.n_seq() * s.T;
     if (s.swiglu) {
         uint16_t* phq = static_cast<uint16_t*>(workspace);
