@@ -12,10 +12,11 @@
 // 16 rows of one sequence and walks its tokens in order: 16 lanes a row, d_phi / 16
 // features a lane, the row in registers.  S is kept as c U with a per-row scalar c
 // (U starts as S0 with c = 1): the token adds M / c to U, and the normalisation is
-// the new scalar c = ||S0 row|| / ||U row||.  One pass over the lane's features
-// gives the updates, ||U||^2 and U . phi(q) together; the two sums are reduced over
-// the row's 16 lanes at once and o_t = c (U . phi(q)).  Per feature and token that
-// is four fused multiply-adds on the vector ALUs.
+// the new scalar c = ||S0 row|| / ||U row||; likewise M is kept as rho Ms with
+// rho = beta^t.  One pass over the lane's features gives the updates, ||U||^2 and
+// U . phi(q) together; the two sums are reduced over the row's 16 lanes at once and
+// o_t = c (U . phi(q)).  Per feature and token that is four fused multiply-adds on
+// the vector ALUs.
 //
 // The features of q and k (the SwiGLU feature map's, formed beforehand into the
 // workspace, or q and k themselves), v of the workgroup's rows and the rates of
@@ -83,7 +84,7 @@ template <> __device__ __forceinline__ void st1<uint16_t>(uint16_t* p, size_t i,
 // FPT features a lane (d_phi = 16 FPT): lane pp of a row owns the contiguous features
 // pp FPT .. pp FPT + FPT - 1, staged with a pitch of PITCH floats between lanes so that
 // the 16 lanes' 16-byte reads fall on distinct banks
-template <int FPT, typename TI>
+template <int FPT, typename TI, bool MOM>
 __global__ void __launch_bounds__(NTH) wn_forward(WnParams p) {
     constexpr int DPHI = 16 * FPT;
     constexpr int PITCH = FPT == 4 ? 4 : FPT + 4;     // floats between two lanes' features
@@ -133,6 +134,8 @@ __global__ void __launch_bounds__(NTH) wn_forward(WnParams p) {
     const float inv_n0 = n0 > 0.0f ? 1.0f / n0 : 0.0f;
     // S = c U.  A zero row stays zero (c = 0, and U does not move).
     float c = n0 > 0.0f ? 1.0f : 0.0f, ic = c;
+    constexpr float RHO_MIN = 0x1p-60f;
+    float rho = 1.0f;
 
     // ---- staging: 16-byte groups of VE consecutive features; group i of a chunk is
     // token i / (DPHI / VE), features VE (i % (DPHI / VE)) ..; thread tid loads groups
@@ -209,19 +212,40 @@ __global__ void __launch_bounds__(NTH) wn_forward(WnParams p) {
             const float* kf = sK + tt * TOKF + pp * PITCH;
             const float* qf = sQ + tt * TOKF + pp * PITCH;
             const float cv = sE[tt] * sV[tt * NR + r];
-            float ss = 0.0f, dd = 0.0f;
+            // M = rho Ms with the workgroup-uniform scale rho = beta^t: the decay goes to
+            // rho, and the token adds (eta v / rho) phi(k) to Ms (one multiply-add); Ms
+            // absorbs rho when it would fall below RHO_MIN.  Without momentum M is the
+            // token's own term.
+            float cm, cu;
+            if constexpr (MOM) {
+                rho *= beta;
+                if (rho < RHO_MIN) {
+#pragma unroll
+                    for (int j = 0; j < FPT; ++j) m[j] *= rho;
+                    rho = 1.0f;
+                }
+                cm = cv * __builtin_amdgcn_rcpf(rho);
+                cu = ic * rho;
+            } else {
+                cm = cv;
+                cu = ic;
+            }
+            // four partial sums each, so that the accumulations are not one serial chain
+            float ss4[4] = {0.f, 0.f, 0.f, 0.f}, dd4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < FPT; j += 4) {
                 const f32x4 k4 = *reinterpret_cast<const f32x4*>(kf + j);
                 const f32x4 q4 = *reinterpret_cast<const f32x4*>(qf + j);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    m[j + e] = fmaf(beta, m[j + e], cv * k4[e]);
-                    u[j + e] = fmaf(ic, m[j + e], u[j + e]);
-                    ss = fmaf(u[j + e], u[j + e], ss);
-                    dd = fmaf(u[j + e], q4[e], dd);
+                    m[j + e] = MOM ? fmaf(cm, k4[e], m[j + e]) : cm * k4[e];
+                    u[j + e] = fmaf(cu, m[j + e], u[j + e]);
+                    ss4[e] = fmaf(u[j + e], u[j + e], ss4[e]);
+                    dd4[e] = fmaf(u[j + e], q4[e], dd4[e]);
                 }
             }
+            float ss = (ss4[0] + ss4[1]) + (ss4[2] + ss4[3]);
+            float dd = (dd4[0] + dd4[1]) + (dd4[2] + dd4[3]);
             row16_sum2(ss, dd);
             if (n0 > 0.0f) {
                 if (ss > 0.0f) {
@@ -246,21 +270,28 @@ __global__ void __launch_bounds__(NTH) wn_forward(WnParams p) {
     for (int j = 0; j < FPT; j += 4) {
         if (p.S_T)
             *reinterpret_cast<f32x4*>(p.S_T + base + j) = f32x4{c * u[j], c * u[j + 1], c * u[j + 2], c * u[j + 3]};
-        if (p.M_T) *reinterpret_cast<f32x4*>(p.M_T + base + j) = f32x4{m[j], m[j + 1], m[j + 2], m[j + 3]};
+        if (p.M_T)
+            *reinterpret_cast<f32x4*>(p.M_T + base + j) = f32x4{rho * m[j], rho * m[j + 1], rho * m[j + 2], rho * m[j + 3]};
     }
 }
 
-template <int FPT, typename TI>
-hipError_t launch_wn_one(const WnParams& p, int n_seq, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
+template <int FPT, typename TI, bool MOM>
+hipError_t launch_wn_mom(const WnParams& p, int n_seq, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
     const dim3 grid((unsigned)((n_seq * p.n_rb + 7) / 8 * 8)), block(NTH);
     if (eb || ee) {
         WnParams a = p;
         void* args[] = {&a};
-        return hipExtLaunchKernel(reinterpret_cast<const void*>(wn_forward<FPT, TI>), grid, block, args, 0, st, eb, ee,
-                                  0);
+        return hipExtLaunchKernel(reinterpret_cast<const void*>(wn_forward<FPT, TI, MOM>), grid, block, args, 0, st, eb,
+                                  ee, 0);
     }
-    hipLaunchKernelGGL((wn_forward<FPT, TI>), grid, block, 0, st, p);
+    hipLaunchKernelGGL((wn_forward<FPT, TI, MOM>), grid, block, 0, st, p);
     return hipGetLastError();
+}
+
+template <int FPT, typename TI>
+hipError_t launch_wn_one(const WnParams& p, int n_seq, hipStream_t st, hipEvent_t eb, hipEvent_t ee) {
+    return p.beta != 0.0f ? launch_wn_mom<FPT, TI, true>(p, n_seq, st, eb, ee)
+                          : launch_wn_mom<FPT, TI, false>(p, n_seq, st, eb, ee);
 }
 
 template <typename TI>
