@@ -307,6 +307,8 @@ int ttt_la_create_hinted(const ttt_la_desc* desc, const ttt_la_hints* hints, ttt
     // the workspace (the plan's areas are not in use during that call)
     if (ttt::wn_supported(h->shape))
         h->workspace_bytes = std::max(h->workspace_bytes, ttt::wn_workspace_bytes(h->shape));
+    // so does the delta rule its chunk inverses
+    h->workspace_bytes = std::max(h->workspace_bytes, ttt::delta_workspace_bytes(h->shape));
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return TTT_LA_ERR_HIP;
@@ -383,8 +385,8 @@ int enqueue_forward(ttt_la_s* h, const void* q, const void* k, const void* v, co
         if (ttt::wn_workspace_bytes(h->shape) > h->workspace_bytes || reverse) return TTT_LA_ERR_UNSUPPORTED;
         e = ttt::launch_wn(h->shape, h->workspace, a, eb, ee);
     } else if (mode & TTT_LA_LOSS_MSE) {
-        // validated by check_forward: the delta-rule kernel, no workspace
-        e = ttt::launch_delta(h->shape, a, eb, ee);
+        // validated by check_forward: the chunk inverses go to the handle's workspace
+        e = ttt::launch_delta(h->shape, a, h->workspace, h->workspace_bytes, eb, ee);
     } else if (h->fast && (h->fp.wide || !state_io)) {
         a.epoch = h->epoch + 1;
         e = ttt::launch_fast(h->shape, h->fp, workspace, a, eb, ee, nullptr);
@@ -950,7 +952,11 @@ int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, c
     a.stream = static_cast<hipStream_t>(hip_stream);
     hipError_t e;
     if (mode & TTT_LA_LOSS_MSE) {
-        e = ttt::launch_delta(s, a, nullptr, nullptr);
+        // the chunk inverses in the scratch array when they fit, else the one-pass walk
+        const size_t need = ttt::delta_workspace_bytes(s);
+        void* ws = nullptr;
+        if (need && need <= TTT_LA_NOALLOC_SCRATCH_BYTES && (st = device_scratch(&ws)) != TTT_LA_OK) return st;
+        e = ttt::launch_delta(s, a, ws, ws ? (size_t)TTT_LA_NOALLOC_SCRATCH_BYTES : 0, nullptr, nullptr);
     } else if (desc->dtype == TTT_LA_BF16 && ttt::fast_supported(s, desc->chunk)) {
         ttt::FastPlan p = ttt::fast_plan(s, desc->chunk, hn.segments, hn.value_split, hn.launch);
         // the single-launch form keeps counters that must persist from call to call

@@ -271,15 +271,337 @@ __global__ void __launch_bounds__(DTH, 1) delta_forward(DeltaParams p) {
     }
 }
 
+
+// ---- two-pass form -------------------------------------------------------------
+// (I + N) depends on the keys and rates of a chunk only, not on the state, so its
+// inverse can leave the sequential walk: a first pass over all chunks at once
+// writes A = (I + N)^{-1} diag(eta) for every chunk, and the walk then takes
+// U = A R as a product on the matrix cores (fp32 operands, v_mfma_f32_16x16x4_f32)
+// instead of a 32-step substitution.  This is the WY-style factoring of the cited
+// delta-rule paper's chunk form, with the triangular inverse kept explicit.
+//
+// A of one chunk is lower triangular; its three non-zero 16 x 16 blocks (token
+// tiles (0,0), (1,0), (1,1)) are stored in operand order: the f32x4 at index
+// 16 g + c16 of block (to, ts) holds A[16 to + c16][16 ts + 4 g .. 16 ts + 4 g + 3],
+// exactly what lane (c16, g) feeds the fp32 product over four k steps.
+constexpr int ABLK = 256;          // floats of one 16 x 16 block
+constexpr int ACH = 3 * ABLK;      // floats of one chunk's blocks
+constexpr int NSTR2 = DC + 4;      // row stride (floats) of N and A in the first pass
+
+struct DeltaPrepParams {
+    const uint16_t* k;
+    const float* eta;
+    float* a;                  // [sequence][chunk][ACH]
+    float eta_scalar;
+    int eta_kind;
+    int T;
+    int n_chunks;              // chunks per sequence
+    int n_units;               // sequences x n_chunks
+};
+
+// One wave per chunk: the 2 x 2 tiles of K K^T from 16-byte row loads of the keys
+// (no staging: each key row is an operand row as it stands in memory), N into the
+// wave's LDS rows, then the columns of A by forward substitution, lane j owning
+// column j (A[t][j] = eta_j [t == j] - sum_{i<t} N[t][i] A[i][j]; every lane reads
+// the same row of N, an LDS broadcast), and A back out through LDS in operand order.
+template <int DK>
+__global__ void __launch_bounds__(256) delta_prep(DeltaPrepParams p) {
+    constexpr int KK = DK / 32;
+    __shared__ __attribute__((aligned(16))) float sN[4][DC * NSTR2];
+    __shared__ __attribute__((aligned(16))) float sA[4][DC * NSTR2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int c16 = lane & 15, g = lane >> 4;
+    const int unit = blockIdx.x * 4 + wv;
+    if (unit >= p.n_units) return;   // waves share no data: no barrier below
+    const int seq = unit / p.n_chunks, c = unit % p.n_chunks;
+    const int t0 = c * DC, n = min(DC, p.T - t0);
+    const size_t row0 = (size_t)seq * p.T + t0;
+    float* N = sN[wv];
+    float* A = sA[wv];
+    auto rate = [&](int t) TTT_INLINE -> float {
+        return t < n ? eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + t) : 0.0f;
+    };
+
+    u32x4 kr[2][KK];
+#pragma unroll
+    for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const int r = 16 * ta + c16;
+            kr[ta][kk] = r < n ? *reinterpret_cast<const u32x4*>(p.k + (row0 + r) * DK + 32 * kk + 8 * g)
+                               : u32x4{0u, 0u, 0u, 0u};
+        }
+    // G tiles (ti, tj): lane holds G[16 ti + 4 g + r][16 tj + c16]
+    f32x4 g00 = {0.f, 0.f, 0.f, 0.f}, g10 = g00, g11 = g00;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 k0 = as_bf16x8(kr[0][kk]), k1 = as_bf16x8(kr[1][kk]);
+        g00 = mfma16(k0, k0, g00);
+        g10 = mfma16(k1, k0, g10);
+        g11 = mfma16(k1, k1, g11);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = 4 * g + r;
+        const float e0 = rate(t), e1 = rate(16 + t);
+        N[t * NSTR2 + c16] = c16 < t ? e0 * g00[r] : 0.0f;
+        N[(16 + t) * NSTR2 + c16] = e1 * g10[r];
+        N[(16 + t) * NSTR2 + 16 + c16] = c16 < t ? e1 * g11[r] : 0.0f;
+    }
+    // column j of A; lanes 32 .. 63 repeat lanes 0 .. 31 and write nothing
+    const int j = lane & (DC - 1);
+    const float ej = rate(j);
+    float x[DC];
+#pragma unroll
+    for (int t = 0; t < DC; ++t) {
+        float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+#pragma unroll
+        for (int i4 = 0; i4 < t / 4; ++i4) {
+            const f32x4 nr = *reinterpret_cast<const f32x4*>(N + t * NSTR2 + 4 * i4);
+            s0 = fmaf(nr[0], x[4 * i4], s0);
+            s1 = fmaf(nr[1], x[4 * i4 + 1], s1);
+            s2 = fmaf(nr[2], x[4 * i4 + 2], s2);
+            s3 = fmaf(nr[3], x[4 * i4 + 3], s3);
+        }
+#pragma unroll
+        for (int i = 4 * (t / 4); i < t; ++i) s0 = fmaf(N[t * NSTR2 + i], x[i], s0);
+        x[t] = (t == j ? ej : 0.0f) - ((s0 + s1) + (s2 + s3));
+    }
+    if (lane < DC) {
+#pragma unroll
+        for (int t = 0; t < DC; ++t) A[t * NSTR2 + j] = x[t];
+    }
+    float* dst = p.a + (size_t)unit * ACH + 4 * lane;
+    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(A + c16 * NSTR2 + 4 * g);
+    *reinterpret_cast<f32x4*>(dst + ABLK) = *reinterpret_cast<const f32x4*>(A + (16 + c16) * NSTR2 + 4 * g);
+    *reinterpret_cast<f32x4*>(dst + 2 * ABLK) =
+        *reinterpret_cast<const f32x4*>(A + (16 + c16) * NSTR2 + 16 + 4 * g);
+}
+
+struct DeltaWalkParams {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* a;            // the first pass's blocks
+    uint16_t* o;
+    int T;
+    int n_chunks;
+    int n_vsplit;
+    int n_units;               // sequences x n_vsplit (grid rounded up to a multiple of 8)
+};
+
+// The walk.  Workgroup and state as in delta_forward (64 value columns of one
+// sequence, wave w keeps rows 16w .. 16w+15 of S and writes its own columns of the
+// bf16 S^T copy), but now every wave's chain touches only its own columns: per chunk
+//   R = V - K S0^T, O0^T = S0 Q^T         (the S^T fragment serves both products)
+//   U = A R                               (fp32 products: lane (c16, g) holds R of
+//                                          tokens 4g + r and 16 + 4g + r, which are
+//                                          exactly the k index of step r)
+//   S += U^T K,  O^T = O0^T + U^T P^T     (the U tiles, packed to bf16, are the A
+//                                          operand with the contraction over tokens
+//                                          4g .. 4g+3, 16+4g .. 16+4g+3; the matching
+//                                          rows of K come from two transpose reads and
+//                                          those of P^T = K Q^T straight from its tiles)
+// so the waves meet only at the one barrier that hands over the staged q, k, v.
+template <int DK>
+__global__ void __launch_bounds__(DTH, 1) delta_walk(DeltaWalkParams p) {
+    constexpr int NT = DK / 16;
+    constexpr int KK = DK / 32;
+    constexpr int QL = DC * DK / 8 / DTH;
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][DC * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][DC * DK];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][DC * DVW];
+    __shared__ __attribute__((aligned(16))) uint16_t sST[DK * DVW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int c16 = lane & 15, g = lane >> 4, q4 = lane & 3;
+    const int T = p.T;
+    const int G = gridDim.x;
+    const int u = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    if (u >= p.n_units) return;
+    const int seq = u / p.n_vsplit;
+    const int vc0 = (u % p.n_vsplit) * DVW;
+    const size_t row0 = (size_t)seq * T;
+    const int vr0 = 16 * wv;
+    const float* Ablk = p.a + (size_t)seq * p.n_chunks * ACH + 4 * lane;
+
+    f32x4 St[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) St[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int e = tid; e < DVW * DK / 8; e += DTH) *reinterpret_cast<u32x4*>(sST + 8 * e) = u32x4{0u, 0u, 0u, 0u};
+
+    u32x4 rq[QL], rk[QL], rv;
+    f32x4 an[3];
+    auto fetch = [&](int c) TTT_INLINE {
+        const int t0 = c * DC, n = min(DC, T - t0);
+#pragma unroll
+        for (int l = 0; l < QL; ++l) {
+            const int e = tid + l * DTH, r = e / (DK / 8), col = 8 * (e % (DK / 8));
+            rq[l] = rk[l] = u32x4{0u, 0u, 0u, 0u};
+            if (r < n) {
+                rq[l] = *reinterpret_cast<const u32x4*>(p.q + (row0 + t0 + r) * DK + col);
+                rk[l] = *reinterpret_cast<const u32x4*>(p.k + (row0 + t0 + r) * DK + col);
+            }
+        }
+        {
+            const int r = tid / (DVW / 8), col = 8 * (tid % (DVW / 8));
+            rv = r < n ? *reinterpret_cast<const u32x4*>(p.v + (row0 + t0 + r) * DK + vc0 + col)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int b = 0; b < 3; ++b) an[b] = *reinterpret_cast<const f32x4*>(Ablk + (size_t)c * ACH + b * ABLK);
+    };
+    auto commit = [&](int b) TTT_INLINE {
+#pragma unroll
+        for (int l = 0; l < QL; ++l) {
+            const int e = tid + l * DTH, r = e / (DK / 8), col = 8 * (e % (DK / 8));
+            *reinterpret_cast<u32x4*>(sQ[b] + swz<DK>(r, col)) = rq[l];
+            *reinterpret_cast<u32x4*>(sK[b] + swz<DK>(r, col)) = rk[l];
+        }
+        const int r = tid / (DVW / 8), col = 8 * (tid % (DVW / 8));
+        *reinterpret_cast<u32x4*>(sV[b] + swz<DVW>(r, col)) = rv;
+    };
+
+    const int n_chunks = p.n_chunks;
+    fetch(0);
+    commit(0);
+    __syncthreads();
+    for (int c = 0; c < n_chunks; ++c) {
+        const int b = c & 1;
+        const int t0 = c * DC;
+        const int n = min(DC, T - t0);
+        const uint16_t* Q = sQ[b];
+        const uint16_t* K = sK[b];
+        const uint16_t* V = sV[b];
+        const f32x4 a00 = an[0], a10 = an[1], a11 = an[2];
+        if (c + 1 < n_chunks) fetch(c + 1);
+
+        // ---- K S0^T, S0 Q^T and the score tiles K Q^T (jb, ta) = (0,0), (0,1), (1,1) ----
+        f32x4 ks0 = {0.f, 0.f, 0.f, 0.f}, ks1 = ks0, ot0 = ks0, ot1 = ks0, p00 = ks0, p01 = ks0, p11 = ks0;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            const bf16x8 bS = as_bf16x8(tr_read8<DVW>(sST, 32 * kk + 8 * g, vr0 + 4 * q4));
+            const bf16x8 k0 = as_bf16x8(lds_read16(K + swz<DK>(c16, 32 * kk + 8 * g)));
+            const bf16x8 k1 = as_bf16x8(lds_read16(K + swz<DK>(16 + c16, 32 * kk + 8 * g)));
+            const bf16x8 q0 = as_bf16x8(lds_read16(Q + swz<DK>(c16, 32 * kk + 8 * g)));
+            const bf16x8 q1 = as_bf16x8(lds_read16(Q + swz<DK>(16 + c16, 32 * kk + 8 * g)));
+            ks0 = mfma16(k0, bS, ks0);
+            ks1 = mfma16(k1, bS, ks1);
+            ot0 = mfma16(bS, q0, ot0);
+            ot1 = mfma16(bS, q1, ot1);
+            p00 = mfma16(k0, q0, p00);
+            p01 = mfma16(k0, q1, p01);
+            p11 = mfma16(k1, q1, p11);
+        }
+        // ---- R = V - K S0^T (lane: tokens 4g + r and 16 + 4g + r of column vr0 + c16) ----
+        float r0[4], r1[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            r0[r] = bf16_bits_to_f32(V[swz<DVW>(4 * g + r, vr0 + c16)]) - ks0[r];
+            r1[r] = bf16_bits_to_f32(V[swz<DVW>(16 + 4 * g + r, vr0 + c16)]) - ks1[r];
+        }
+        // ---- U = A R in fp32 ----
+        f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = u0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a00[r], r0[r], u0, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a10[r], r0[r], u1, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a11[r], r1[r], u1, 0, 0, 0);
+        const bf16x8 aU = as_bf16x8(u32x4{pack_bf16x2(u0[0], u0[1]), pack_bf16x2(u0[2], u0[3]),
+                                          pack_bf16x2(u1[0], u1[1]), pack_bf16x2(u1[2], u1[3])});
+        // ---- S += U^T K, and its bf16 copy (this wave's columns) ----
+#pragma unroll
+        for (int bt = 0; bt < NT; ++bt) {
+            const bf16x8 bK = join8(tr_read<DK>(K, 4 * g, 16 * bt + 4 * q4), tr_read<DK>(K, 16 + 4 * g, 16 * bt + 4 * q4));
+            St[bt] = mfma16(aU, bK, St[bt]);
+            *reinterpret_cast<u32x2*>(sST + swz<DVW>(16 * bt + c16, vr0 + 4 * g)) =
+                u32x2{pack_bf16x2(St[bt][0], St[bt][1]), pack_bf16x2(St[bt][2], St[bt][3])};
+        }
+        if (c + 1 < n_chunks) commit(b ^ 1);
+        // ---- O^T = S0 Q^T + U^T P^T; P = tril(Q K^T), lane (c16, g) of tile (jb, ta) holds
+        //      P[16 ta + c16][16 jb + 4 g + r] ----
+        {
+            const bool keep[4] = {4 * g <= c16, 4 * g + 1 <= c16, 4 * g + 2 <= c16, 4 * g + 3 <= c16};
+            float m00[4], m11[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                m00[r] = keep[r] ? p00[r] : 0.0f;
+                m11[r] = keep[r] ? p11[r] : 0.0f;
+            }
+            const bf16x8 bP0 = as_bf16x8(u32x4{pack_bf16x2(m00[0], m00[1]), pack_bf16x2(m00[2], m00[3]), 0u, 0u});
+            const bf16x8 bP1 = as_bf16x8(u32x4{pack_bf16x2(p01[0], p01[1]), pack_bf16x2(p01[2], p01[3]),
+                                               pack_bf16x2(m11[0], m11[1]), pack_bf16x2(m11[2], m11[3])});
+            const f32x4 o0 = mfma16(aU, bP0, ot0);
+            const f32x4 o1 = mfma16(aU, bP1, ot1);
+            // lane holds O[t = 16 ta + c16][vr0 + 4g .. vr0 + 4g + 3]
+            if (c16 < n)
+                *reinterpret_cast<u32x2*>(p.o + (row0 + t0 + c16) * DK + vc0 + vr0 + 4 * g) =
+                    u32x2{pack_bf16x2(o0[0], o0[1]), pack_bf16x2(o0[2], o0[3])};
+            if (16 + c16 < n)
+                *reinterpret_cast<u32x2*>(p.o + (row0 + t0 + 16 + c16) * DK + vc0 + vr0 + 4 * g) =
+                    u32x2{pack_bf16x2(o1[0], o1[1]), pack_bf16x2(o1[2], o1[3])};
+        }
+        lds_barrier();
+    }
+}
+
 }  // namespace
 
 bool delta_supported(const Shape& s) {
     return s.bf16 && !s.swiglu && s.d_k == s.d_v && s.d_phi == s.d_k && (s.d_k == 64 || s.d_k == 128);
 }
 
-hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end) {
+size_t delta_workspace_bytes(const Shape& s) {
+    if (!delta_supported(s)) return 0;
+    return (size_t)s.n_seq() * (size_t)((s.T + DC - 1) / DC) * ACH * sizeof(float);
+}
+
+hipError_t launch_delta(const Shape& s, const FwdArgs& a, void* workspace, size_t workspace_bytes,
+                        hipEvent_t ev_begin, hipEvent_t ev_end) {
     if (!delta_supported(s) || a.bidirectional || a.beta != 0.0f || a.S0 || a.M0 || a.S_T || a.M_T || a.reverse)
         return hipErrorInvalidValue;
+    const size_t need = delta_workspace_bytes(s);
+    const dim3 block(DTH);
+    if (workspace && need > 0 && need <= workspace_bytes) {
+        // two passes: the chunk inverses, then the walk (which carries the timing events)
+        const int n_chunks = (s.T + DC - 1) / DC;
+        DeltaPrepParams pp;
+        pp.k = static_cast<const uint16_t*>(a.k);
+        pp.eta = a.eta;
+        pp.a = static_cast<float*>(workspace);
+        pp.eta_scalar = a.eta_scalar;
+        pp.eta_kind = a.eta_kind;
+        pp.T = s.T;
+        pp.n_chunks = n_chunks;
+        pp.n_units = s.n_seq() * n_chunks;
+        const dim3 pgrid((unsigned)((pp.n_units + 3) / 4));
+        if (s.d_k == 128) hipLaunchKernelGGL(delta_prep<128>, pgrid, block, 0, a.stream, pp);
+        else hipLaunchKernelGGL(delta_prep<64>, pgrid, block, 0, a.stream, pp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        DeltaWalkParams wp;
+        wp.q = static_cast<const uint16_t*>(a.q);
+        wp.k = static_cast<const uint16_t*>(a.k);
+        wp.v = static_cast<const uint16_t*>(a.v);
+        wp.a = static_cast<const float*>(workspace);
+        wp.o = static_cast<uint16_t*>(a.o);
+        wp.T = s.T;
+        wp.n_chunks = n_chunks;
+        wp.n_vsplit = s.d_v / DVW;
+        wp.n_units = s.n_seq() * wp.n_vsplit;
+        const dim3 grid((unsigned)((wp.n_units + 7) / 8 * 8));
+        if (ev_begin || ev_end) {
+            const void* fn = s.d_k == 128 ? reinterpret_cast<const void*>(delta_walk<128>)
+                                          : reinterpret_cast<const void*>(delta_walk<64>);
+            void* args[] = {&wp};
+            return hipExtLaunchKernel(fn, grid, block, args, 0, a.stream, ev_begin, ev_end, 0);
+        }
+        if (s.d_k == 128) hipLaunchKernelGGL(delta_walk<128>, grid, block, 0, a.stream, wp);
+        else hipLaunchKernelGGL(delta_walk<64>, grid, block, 0, a.stream, wp);
+        return hipGetLastError();
+    }
+    // one pass, no workspace: the substitution runs inside the walk
     DeltaParams p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -291,7 +613,7 @@ hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
     p.T = s.T;
     p.n_vsplit = s.d_v / DVW;
     p.n_units = s.n_seq() * p.n_vsplit;
-    const dim3 grid((unsigned)((p.n_units + 7) / 8 * 8)), block(DTH);
+    const dim3 grid((unsigned)((p.n_units + 7) / 8 * 8));
     const void* fn = s.d_k == 128 ? reinterpret_cast<const void*>(delta_forward<128>)
                                   : reinterpret_cast<const void*>(delta_forward<64>);
     if (ev_begin || ev_end) {

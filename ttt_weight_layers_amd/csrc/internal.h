@@ -103,8 +103,12 @@ hipError_t launch_short(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, h
 
 // delta rule (mean-squared binding loss, no momentum, causal; delta.hip): bf16,
 // identity map, d_k = d_v in {64, 128}
+// identity map, d_k = d_v in {64, 128}.  With a workspace of delta_workspace_bytes
+// (3 KiB per chunk of 32 tokens: the chunk inverses) two passes, else the one-pass walk.
 bool delta_supported(const Shape& s);
-hipError_t launch_delta(const Shape& s, const FwdArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
+size_t delta_workspace_bytes(const Shape& s);
+hipError_t launch_delta(const Shape& s, const FwdArgs& a, void* workspace, size_t workspace_bytes,
+                        hipEvent_t ev_begin, hipEvent_t ev_end);
 
 // weight-normalised recurrent forward (wn.hip): causal, entry state required; bf16 or
 // fp32 identity map (d_k = d_phi), or the bf16 SwiGLU map with d_k = 128; d_v a
