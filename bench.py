@@ -457,7 +457,7 @@ def roofline_of(w, chunk: int, seconds: float):
 def timed_kernel_name(plan, w, launch: str) -> str:
     """The kernel that carries the timing events (the output pass of the plan)."""
     if w.loss == "mse":
-        return "delta_forward"
+        return "delta_walk"
     if w.weight_norm:
         return "wn_forward"
     if plan.path == 3:
@@ -597,7 +597,7 @@ def run_forward(args, w, pool=None, n_workers: int = 1):
             "causal": w.causal, "loss": w.loss, "chunk": chunk,
             "segments": 1 if (w.loss == "mse" or w.weight_norm) else plan.segments, "dv_split": plan.dv_split,
             "phi_split": plan.phi_split, "launch": args.launch,
-            "kernels_per_step": 1 if w.loss == "mse" else (3 if w.weight_norm else plan.n_kernels),
+            "kernels_per_step": 2 if w.loss == "mse" else (3 if w.weight_norm else plan.n_kernels),
             "weight_norm": w.weight_norm,
             "input_sets": n_sets,
             "head_tokens_per_s": round(w.head_tokens / (ms_per_step * 1e-3), 1),

@@ -80,7 +80,10 @@ enum {
                                         (mlsanity.com page: Modular TTT abstract, MSE and inner-product
                                         losses; "Builds on": the delta-rule parallelisation paper).
                                         ttt_la_forward only; bf16, identity map, d_k = d_v in {64, 128},
-                                        causal, beta = 0; anything else TTT_LA_ERR_UNSUPPORTED */
+                                        causal, beta = 0; anything else TTT_LA_ERR_UNSUPPORTED.  On a
+                                        handle the per-chunk inverses (I + N)^-1 diag(eta), 3 KiB per 32
+                                        tokens of each sequence, go to the handle's workspace (sized for
+                                        them at creation) */
     TTT_LA_WEIGHT_NORM = 1u << 4     /* Variant 1 of Table 2 (thelatestinai.com page): the updated layer
                                         is weight-normalised, recurrent implementation only.  The pages
                                         do not define the normalisation; here, after each token's update,
@@ -188,6 +191,10 @@ int ttt_la_forward(ttt_la_t h, const void* q, const void* k, const void* v, cons
  * All calls on one device share its scratch and leave their contents in it:
  * calls that overlap in time on one device (streams that are not ordered with
  * each other) race and their results are undefined.
+ * With TTT_LA_LOSS_MSE the per-chunk inverses use the scratch when they fit
+ * (3 KiB per 32 tokens of each sequence); beyond that the call runs the one-pass
+ * delta-rule kernel, which needs no workspace (same results within rounding, not
+ * bit for bit).
  * Errors: as ttt_la_create_hinted and ttt_la_forward (all before any HIP call),
  * and TTT_LA_ERR_TOO_LARGE, before any HIP call, when the plan's workspace
  * exceeds TTT_LA_NOALLOC_SCRATCH_BYTES (for instance B*H*T*d_phi*2 bytes of

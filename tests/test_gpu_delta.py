@@ -71,3 +71,31 @@ def test_delta_is_not_the_dot_product_layer():
     dot = run_gpu(w.with_settings(loss="dot"), d_)
     np.testing.assert_allclose(mse[0, 0, 0], dot[0, 0, 0], rtol=0, atol=1e-6 * np.max(np.abs(dot)))
     assert np.max(np.abs(mse[0, 0, 40:] - dot[0, 0, 40:])) > 0.1 * np.max(np.abs(dot[0, 0, 40:]))
+
+
+def test_delta_one_pass_beyond_the_noalloc_scratch():
+    """ttt_la_forward_noalloc at a shape whose chunk inverses (3 KiB per 32 tokens of
+    each sequence: 72 MiB here) exceed the 64 MiB scratch runs the one-pass kernel;
+    sampled heads against the oracle."""
+    import torch
+    import ttt_weight_layers_amd as tla
+    from _gpu import from_device
+    w = DELTA.with_shape(B=1, H=12, T=65536).with_settings(d_k=64, d_v=64, d_phi=64)
+    assert w.B * w.H * (w.T // 32) * 3072 > tla.TTT_LA_NOALLOC_SCRATCH_BYTES
+    heads = [0, 7]
+    say(f"[delta one-pass] {w.B}x{w.H}x{w.T} d=64 heads {heads}")
+    x = make_inputs(w)
+    d_ = to_device(x)
+    desc = tla.make_desc(w.B, w.H, w.T, w.d_k, w.d_v, w.d_phi, dtype=w.dtype, phi=w.phi, chunk=w.chunk)
+    o = torch.empty_like(d_["v"])
+    st = tla.ttt_la_forward_noalloc(desc, None, d_["q"].data_ptr(), d_["k"].data_ptr(), d_["v"].data_ptr(),
+                                    d_["a"].data_ptr(), w.eta_scalar, w.beta, tla.mode_bits(w.eta_mode, True, "mse"),
+                                    o.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == tla.TTT_LA_OK, tla.ttt_la_status_string(st)
+    torch.cuda.synchronize()
+    got = select_heads(from_device(o, w.dtype), w, heads)
+    ref = run_oracle(w, x, heads=heads)
+    err = oracle.rel_err(got, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL[w.dtype]
+

@@ -31,7 +31,7 @@ def _noalloc(w, d, hints):
     eta = d["a"] if w.eta_mode != "scalar" else None
     st = tla.ttt_la_forward_noalloc(_desc(w, d), hints, d["q"].data_ptr(), d["k"].data_ptr(), d["v"].data_ptr(),
                                     None if eta is None else eta.data_ptr(), w.eta_scalar, w.beta,
-                                    tla.mode_bits(w.eta_mode, w.causal), o.data_ptr(),
+                                    tla.mode_bits(w.eta_mode, w.causal, w.loss), o.data_ptr(),
                                     torch.cuda.current_stream().cuda_stream)
     assert st == tla.TTT_LA_OK, tla.ttt_la_status_string(st)
     torch.cuda.synchronize()
@@ -57,6 +57,9 @@ CASES = {
     "swiglu_d64_slices": ("v2_swiglu_4x16x8192_d128_f512", dict(d_k=64, d_v=64, d_phi=256),
                           dict(B=1, H=2, T=300), dict(B=1, H=1, T=70), dict()),
     "f32": ("v5_f32_1x1x256_d64", dict(), dict(B=1, H=2, T=256), dict(B=1, H=1, T=100), dict()),
+    # delta rule: the chunk inverses in the scratch, then the walk
+    "delta": ("v3_softplus_8x16x4096_d128", dict(loss="mse", beta=0.0, l2norm=True),
+              dict(B=1, H=4, T=32 * 7 + 5), dict(B=1, H=2, T=100), dict()),
 }
 
 

@@ -39,13 +39,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libttt_la.so)")
 
 
-# Per-file options.  The 32x32-tile kernels keep their fp32 state in MFMA
+# Per-file options.  The 32x32-tile kernels (and the delta-rule walk) keep their fp32 state in MFMA
 # accumulators that the vector ALUs also scale and convert every chunk; asking
 # for the VGPR form of the MFMA results keeps the state in ordinary VGPRs
 # instead of AGPRs, which would need a copy for every such operation.
 FILE_FLAGS = {
     "chunk_wide.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "swiglu.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "delta.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
