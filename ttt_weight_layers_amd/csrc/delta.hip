@@ -299,58 +299,67 @@ struct DeltaPrepParams {
     int n_units;               // sequences x n_chunks
 };
 
-// One wave per chunk: the 2 x 2 tiles of K K^T from 16-byte row loads of the keys
-// (no staging: each key row is an operand row as it stands in memory), N into the
-// wave's LDS rows, then the columns of A by forward substitution, lane j owning
-// column j (A[t][j] = eta_j [t == j] - sum_{i<t} N[t][i] A[i][j]; every lane reads
-// the same row of N, an LDS broadcast), and A back out through LDS in operand order.
+// One wave per two chunks.  For each chunk the 2 x 2 tiles of K K^T come from
+// 16-byte row loads of the keys (no staging: each key row is an operand row as it
+// stands in memory) and N goes to the chunk's LDS rows; then each half of the wave
+// takes one chunk and finds the columns of its A by forward substitution, lane j
+// owning column j (A[t][j] = eta_j [t == j] - sum_{i<t} N[t][i] A[i][j]; the lanes of
+// a half read the same row of N, an LDS broadcast); A goes back out through the same
+// LDS rows in operand order.
 template <int DK>
 __global__ void __launch_bounds__(256) delta_prep(DeltaPrepParams p) {
     constexpr int KK = DK / 32;
-    __shared__ __attribute__((aligned(16))) float sN[4][DC * NSTR2];
-    __shared__ __attribute__((aligned(16))) float sA[4][DC * NSTR2];
+    __shared__ __attribute__((aligned(16))) float sN[4][2][DC * NSTR2];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int c16 = lane & 15, g = lane >> 4;
-    const int unit = blockIdx.x * 4 + wv;
-    if (unit >= p.n_units) return;   // waves share no data: no barrier below
-    const int seq = unit / p.n_chunks, c = unit % p.n_chunks;
-    const int t0 = c * DC, n = min(DC, p.T - t0);
-    const size_t row0 = (size_t)seq * p.T + t0;
-    float* N = sN[wv];
-    float* A = sA[wv];
-    auto rate = [&](int t) TTT_INLINE -> float {
-        return t < n ? eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + t) : 0.0f;
-    };
+    const int unit0 = 2 * (blockIdx.x * 4 + wv);
+    if (unit0 >= p.n_units) return;   // waves share no data: no barrier below
+    const int half = lane >> 5, j = lane & (DC - 1);
 
-    u32x4 kr[2][KK];
+    // N of chunk unit0 + h into sN[wv][h]
 #pragma unroll
-    for (int ta = 0; ta < 2; ++ta)
+    for (int h = 0; h < 2; ++h) {
+        // a missing second chunk reads no keys and writes nothing: its N is zero
+        const int unit = unit0 + h;
+        const bool live = unit < p.n_units;
+        const int seq = unit / p.n_chunks, c = unit % p.n_chunks;
+        const int t0 = c * DC, n = live ? min(DC, p.T - t0) : 0;
+        const size_t row0 = (size_t)seq * p.T + t0;
+        float* N = sN[wv][h];
+        u32x4 kr[2][KK];
+#pragma unroll
+        for (int ta = 0; ta < 2; ++ta)
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int r = 16 * ta + c16;
+                kr[ta][kk] = r < n ? *reinterpret_cast<const u32x4*>(p.k + (row0 + r) * DK + 32 * kk + 8 * g)
+                                   : u32x4{0u, 0u, 0u, 0u};
+            }
+        // G tiles (ti, tj): lane holds G[16 ti + 4 g + r][16 tj + c16]
+        f32x4 g00 = {0.f, 0.f, 0.f, 0.f}, g10 = g00, g11 = g00;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            const int r = 16 * ta + c16;
-            kr[ta][kk] = r < n ? *reinterpret_cast<const u32x4*>(p.k + (row0 + r) * DK + 32 * kk + 8 * g)
-                               : u32x4{0u, 0u, 0u, 0u};
+            const bf16x8 k0 = as_bf16x8(kr[0][kk]), k1 = as_bf16x8(kr[1][kk]);
+            g00 = mfma16(k0, k0, g00);
+            g10 = mfma16(k1, k0, g10);
+            g11 = mfma16(k1, k1, g11);
         }
-    // G tiles (ti, tj): lane holds G[16 ti + 4 g + r][16 tj + c16]
-    f32x4 g00 = {0.f, 0.f, 0.f, 0.f}, g10 = g00, g11 = g00;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 k0 = as_bf16x8(kr[0][kk]), k1 = as_bf16x8(kr[1][kk]);
-        g00 = mfma16(k0, k0, g00);
-        g10 = mfma16(k1, k0, g10);
-        g11 = mfma16(k1, k1, g11);
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * g + r;
+            const float e0 = t < n ? eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + t) : 0.0f;
+            const float e1 = 16 + t < n ? eta_at(p.eta_kind, p.eta, p.eta_scalar, row0 + 16 + t) : 0.0f;
+            N[t * NSTR2 + c16] = c16 < t ? e0 * g00[r] : 0.0f;
+            N[(16 + t) * NSTR2 + c16] = e1 * g10[r];
+            N[(16 + t) * NSTR2 + 16 + c16] = c16 < t ? e1 * g11[r] : 0.0f;
+        }
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int t = 4 * g + r;
-        const float e0 = rate(t), e1 = rate(16 + t);
-        N[t * NSTR2 + c16] = c16 < t ? e0 * g00[r] : 0.0f;
-        N[(16 + t) * NSTR2 + c16] = e1 * g10[r];
-        N[(16 + t) * NSTR2 + 16 + c16] = c16 < t ? e1 * g11[r] : 0.0f;
-    }
-    // column j of A; lanes 32 .. 63 repeat lanes 0 .. 31 and write nothing
-    const int j = lane & (DC - 1);
-    const float ej = rate(j);
+    // column j of the A of chunk unit0 + half
+    const int unit = unit0 + half;
+    const int seq = unit / p.n_chunks, c = unit % p.n_chunks;
+    const int t0 = c * DC, n = unit < p.n_units ? min(DC, p.T - t0) : 0;
+    const float ej = j < n ? eta_at(p.eta_kind, p.eta, p.eta_scalar, (size_t)seq * p.T + t0 + j) : 0.0f;
+    float* N = sN[wv][half];
     float x[DC];
 #pragma unroll
     for (int t = 0; t < DC; ++t) {
@@ -367,15 +376,19 @@ __global__ void __launch_bounds__(256) delta_prep(DeltaPrepParams p) {
         for (int i = 4 * (t / 4); i < t; ++i) s0 = fmaf(N[t * NSTR2 + i], x[i], s0);
         x[t] = (t == j ? ej : 0.0f) - ((s0 + s1) + (s2 + s3));
     }
-    if (lane < DC) {
+    // A over N (the wave's reads of N are all issued before these writes)
 #pragma unroll
-        for (int t = 0; t < DC; ++t) A[t * NSTR2 + j] = x[t];
+    for (int t = 0; t < DC; ++t) N[t * NSTR2 + j] = x[t];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (unit0 + h >= p.n_units) break;
+        const float* A = sN[wv][h];
+        float* dst = p.a + (size_t)(unit0 + h) * ACH + 4 * lane;
+        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(A + c16 * NSTR2 + 4 * g);
+        *reinterpret_cast<f32x4*>(dst + ABLK) = *reinterpret_cast<const f32x4*>(A + (16 + c16) * NSTR2 + 4 * g);
+        *reinterpret_cast<f32x4*>(dst + 2 * ABLK) =
+            *reinterpret_cast<const f32x4*>(A + (16 + c16) * NSTR2 + 16 + 4 * g);
     }
-    float* dst = p.a + (size_t)unit * ACH + 4 * lane;
-    *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(A + c16 * NSTR2 + 4 * g);
-    *reinterpret_cast<f32x4*>(dst + ABLK) = *reinterpret_cast<const f32x4*>(A + (16 + c16) * NSTR2 + 4 * g);
-    *reinterpret_cast<f32x4*>(dst + 2 * ABLK) =
-        *reinterpret_cast<const f32x4*>(A + (16 + c16) * NSTR2 + 16 + 4 * g);
 }
 
 struct DeltaWalkParams {
@@ -575,7 +588,7 @@ hipError_t launch_delta(const Shape& s, const FwdArgs& a, void* workspace, size_
         pp.T = s.T;
         pp.n_chunks = n_chunks;
         pp.n_units = s.n_seq() * n_chunks;
-        const dim3 pgrid((unsigned)((pp.n_units + 3) / 4));
+        const dim3 pgrid((unsigned)((pp.n_units + 7) / 8));   // two chunks a wave, four waves
         if (s.d_k == 128) hipLaunchKernelGGL(delta_prep<128>, pgrid, block, 0, a.stream, pp);
         else hipLaunchKernelGGL(delta_prep<64>, pgrid, block, 0, a.stream, pp);
         hipError_t e = hipGetLastError();
