@@ -192,7 +192,7 @@ def _delta_chunked(q, k, v, eta, chunk):
     return o, S
 
 
-@pytest.mark.parametrize("chunk", [1, 5, 16, 64])
+@pytest.mark.parametrize("chunk", [1, 5, 16, 32, 64])
 def test_delta_chunk_form_equals_recurrence(chunk):
     q, k, v, eta = _inputs(150, 8, 6, 31)
     got, S = _delta_chunked(q, k, v, eta, chunk)
