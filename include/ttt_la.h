@@ -140,7 +140,12 @@ typedef struct {
 /* Supported shapes (anything else well-formed returns TTT_LA_ERR_UNSUPPORTED):
  *   d_k, d_v in {64, 128}
  *   identity: d_phi == d_k;  SwiGLU: d_phi in {128, 256, 384, 512}
- *   B * H * T * max(d_k, d_v, d_phi) < 2^31
+ *   B * H * T * max(d_k, d_v, d_phi) < 2^31, except on the 32x32-tile plan (bf16,
+ *   identity map, d_k = d_v = 128, no value-split hint): there B * H * T < 2^31, and
+ *   past 2^31 elements a tensor only the forwards with the dot-product loss run
+ *   (ttt_la_forward, ttt_la_forward_state, ttt_la_forward_noalloc; weight
+ *   normalisation, the mean-squared loss and the backward return
+ *   TTT_LA_ERR_UNSUPPORTED)
  *
  * Layout: q, k are [B, H, T, d_k]; v and o are [B, H, T, d_v]; eta is
  * [B, H, T] fp32; all C-contiguous.  Pointers to q, k, v, o, W1, W3 must be

@@ -127,7 +127,24 @@ def test_swiglu_descriptor():
 
 
 def test_size_limit():
+    # 2^32 tokens: past the token-count limit on every plan
     assert check(d=desc(B=1024, H=64, T=65536), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    # past 2^31 elements a tensor: the 32x32-tile plan (bf16, identity, d = 128) only
+    big = dict(B=1, H=16, T=(1 << 20) + 96)
+    assert check(d=desc(**big), q=None) == tla.TTT_LA_OK
+    assert check(d=desc(**big, chunk=128), q=None) == tla.TTT_LA_OK
+    assert check(d=desc(B=1, H=16, T=(1 << 21) + 96, d_k=64, d_v=64), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(**big, d_v=64), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(**big, dtype="f32"), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check(d=desc(**big, phi="swiglu", d_phi=128, w1=W1, w3=W3), q=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    # and there only the forwards with the dot-product loss (pointers far apart: no overlap)
+    far = dict(q=1 << 40, k=2 << 40, v=3 << 40, o=4 << 40)
+    assert check(d=desc(**big), **far) == tla.TTT_LA_OK
+    assert check(d=desc(**big), **far, mode=tla.TTT_LA_LOSS_MSE) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert tla.ttt_la_check_backward(desc(**big), None, 1 << 40, 2 << 40, 3 << 40, None, 0.5, 0.9, 0, 5 << 40,
+                                     6 << 40, 7 << 40, 8 << 40, None, 9 << 40, 1 << 44) == tla.TTT_LA_ERR_UNSUPPORTED
+    # just below 2^31 elements every plan is open
+    assert check(d=desc(B=1, H=16, T=(1 << 21) - 1, d_k=64, d_v=64), q=None) == tla.TTT_LA_OK
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "o"])

@@ -53,6 +53,15 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
+Shape shape_of(const ttt_la_desc& d);
+
+// a tensor of B*H*T*max(d_k, d_v, d_phi) elements reaches 2^31: such shapes run the
+// plain and carried-state forwards on the 32x32-tile plan only
+bool big_shape(const ttt_la_desc& d) {
+    const long long widest = std::max(d.d_k, std::max(d.d_v, d.d_phi));
+    return (long long)d.B * d.H * d.T * widest >= (1LL << 31);
+}
+
 int check_desc(const ttt_la_desc* d) {
     if (!d) return TTT_LA_ERR_INVALID_ARG;
     if (d->B < 1 || d->H < 1 || d->T < 1) return TTT_LA_ERR_INVALID_ARG;
@@ -72,8 +81,13 @@ int check_desc(const ttt_la_desc* d) {
     if (d->d_v != 64 && d->d_v != 128) return TTT_LA_ERR_UNSUPPORTED;
     if (d->phi == TTT_LA_PHI_SWIGLU && (d->d_phi % 128 != 0 || d->d_phi > 512)) return TTT_LA_ERR_UNSUPPORTED;
     if (d->chunk != 0 && d->chunk != 64 && d->chunk != 128) return TTT_LA_ERR_UNSUPPORTED;
-    const long long widest = std::max(d->d_k, std::max(d->d_v, d->d_phi));
-    if ((long long)d->B * d->H * d->T * widest >= (1LL << 31)) return TTT_LA_ERR_UNSUPPORTED;
+    // past 2^31 elements a tensor: only the 32x32-tile plan, whose kernels offset rows
+    // in 64 bits (the token count itself stays below 2^31)
+    if (big_shape(*d)) {
+        if ((long long)d->B * d->H * d->T >= (1LL << 31)) return TTT_LA_ERR_UNSUPPORTED;
+        if (!ttt::fast_supported(shape_of(*d), d->chunk) || !ttt::wide_supported(shape_of(*d)))
+            return TTT_LA_ERR_UNSUPPORTED;
+    }
     return TTT_LA_OK;
 }
 
@@ -121,6 +135,8 @@ int check_forward(const ttt_la_desc* d, const void* q, const void* k, const void
         if (overlaps(o, v_bytes, d->w1, w_bytes) || overlaps(o, v_bytes, d->w3, w_bytes))
             return TTT_LA_ERR_INVALID_ARG;
     }
+    // beyond 2^31 elements a tensor: the dot-product loss without weight normalisation
+    if (big_shape(*d) && (mode & (TTT_LA_LOSS_MSE | TTT_LA_WEIGHT_NORM))) return TTT_LA_ERR_UNSUPPORTED;
     // the delta rule runs for one configuration (no momentum, causal, bf16 identity map,
     // square state of width 64 or 128)
     if ((mode & TTT_LA_LOSS_MSE) &&
@@ -307,13 +323,19 @@ int ttt_la_create_hinted(const ttt_la_desc* desc, const ttt_la_hints* hints, ttt
     // the workspace (the plan's areas are not in use during that call)
     if (ttt::wn_supported(h->shape))
         h->workspace_bytes = std::max(h->workspace_bytes, ttt::wn_workspace_bytes(h->shape));
-    // so does the delta rule its chunk inverses
-    h->workspace_bytes = std::max(h->workspace_bytes, ttt::delta_workspace_bytes(h->shape));
+    // so does the delta rule its chunk inverses (not past 2^31 elements, where the
+    // delta rule is not run)
+    if (!big_shape(*desc)) h->workspace_bytes = std::max(h->workspace_bytes, ttt::delta_workspace_bytes(h->shape));
     if (hipGetDevice(&h->device) != hipSuccess) {
         delete h;
         return TTT_LA_ERR_HIP;
     }
     if (!h->fast && ttt::generic_smem_bytes(h->shape) > 160 * 1024) {
+        delete h;
+        return TTT_LA_ERR_UNSUPPORTED;
+    }
+    // past 2^31 elements only the 32x32-tile plan (a value-split hint picks another)
+    if (big_shape(*desc) && !(h->fast && h->fp.wide)) {
         delete h;
         return TTT_LA_ERR_UNSUPPORTED;
     }
@@ -509,6 +531,7 @@ int check_backward(const ttt_la_desc* d, const ttt_la_hints& hn, const void* q, 
     int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, dQ);
     if (st == TTT_LA_OK && (mode & TTT_LA_LOSS_MSE)) return TTT_LA_ERR_UNSUPPORTED;   // no delta-rule backward
     if (st != TTT_LA_OK) return st;
+    if (big_shape(*d)) return TTT_LA_ERR_UNSUPPORTED;
     if (!backward_supported(*d)) return TTT_LA_ERR_UNSUPPORTED;
     if (!dO || !dK || !dV) return TTT_LA_ERR_INVALID_ARG;
     if (!aligned(dO, 16) || !aligned(dK, 16) || !aligned(dV, 16)) return TTT_LA_ERR_INVALID_ARG;
@@ -595,6 +618,7 @@ int check_backward_swiglu(const ttt_la_desc* d, const void* q, const void* k, co
                           size_t ws_bytes) {
     int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, dQ);
     if (st != TTT_LA_OK) return st;
+    if (big_shape(*d)) return TTT_LA_ERR_UNSUPPORTED;
     if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;
     if (!swiglu_backward_ok(*d)) return TTT_LA_ERR_UNSUPPORTED;
     if (!dO || !dQ || !dK || !dV || !dW1 || !dW3) return TTT_LA_ERR_INVALID_ARG;
@@ -959,6 +983,7 @@ int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, c
         e = ttt::launch_delta(s, a, ws, ws ? (size_t)TTT_LA_NOALLOC_SCRATCH_BYTES : 0, nullptr, nullptr);
     } else if (desc->dtype == TTT_LA_BF16 && ttt::fast_supported(s, desc->chunk)) {
         ttt::FastPlan p = ttt::fast_plan(s, desc->chunk, hn.segments, hn.value_split, hn.launch);
+        if (big_shape(*desc) && !p.wide) return TTT_LA_ERR_UNSUPPORTED;
         // the single-launch form keeps counters that must persist from call to call
         // of one handle: three launches instead, which compute the same
         p.fused = false;
