@@ -277,8 +277,8 @@ __global__ void __launch_bounds__(DTH, 1) delta_forward(DeltaParams p) {
 // inverse can leave the sequential walk: a first pass over all chunks at once
 // writes A = (I + N)^{-1} diag(eta) for every chunk, and the walk then takes
 // U = A R as a product on the matrix cores (fp32 operands, v_mfma_f32_16x16x4_f32)
-// instead of a 32-step substitution.  This is the WY-style factoring of the cited
-// delta-rule paper's chunk form, with the triangular inverse kept explicit.
+// instead of a 32-step substitution: the chunk form above with the triangular
+// inverse made explicit and formed for every chunk before the walk starts.
 //
 // A of one chunk is lower triangular; its three non-zero 16 x 16 blocks (token
 // tiles (0,0), (1,0), (1,1)) are stored in operand order: the f32x4 at index
