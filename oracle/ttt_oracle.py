@@ -258,12 +258,21 @@ def forward(q, k, v, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 
 
 
 def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: float = 1.0,
-         beta: float = 0.0, phi: str = "identity", w1=None, w3=None, weight_norm: bool = False):
+         beta: float = 0.0, phi: str = "identity", w1=None, w3=None, weight_norm: bool = False,
+         loss: str = "dot"):
     """One recurrent step (decode) for every sequence: the token q1, k1, v1
     ([B, H, d]) with rate eta ([B, H], per_token / softplus modes) updates the
     carried state (S, M) ([B, H, d_v, d_phi]) and is read out after its update:
 
       M' = beta M + eta v phi(k)^T,   S' = S + M',   o = S' phi(q).
+
+    ``loss="mse"``: the step of the mean-squared binding loss 1/2 ||S phi(k) - v||^2
+    (the MSE inner-loop loss of the Modular TTT abstract on the mlsanity.com page),
+    whose gradient at the given S is (S phi(k) - v) phi(k)^T, so that
+
+      M' = beta M + eta (v - S phi(k)) phi(k)^T,   S' = S + M',   o = S' phi(q)
+
+    (the delta rule of the paper that page cites, with heavy-ball momentum).
 
     ``weight_norm``: Variant 1's step (the reading in ``forward``): each row of S'
     is rescaled to the norm of the same row of S (which a weight-normalised run
@@ -295,7 +304,15 @@ def step(q1, k1, v1, S, M, *, eta_mode: str = "scalar", eta=None, eta_scalar: fl
     d_v, d_phi = v1.shape[1], pk.shape[1]
     S = np.asarray(S, np.float64).reshape(N, d_v, d_phi)
     M = np.asarray(M, np.float64).reshape(N, d_v, d_phi)
-    M_new = beta * M + e[:, None, None] * v1[:, :, None] * pk[:, None, :]
+    if loss == "dot":
+        target = v1                                      # -grad = v phi(k)^T for -<S phi(k), v>
+    elif loss == "mse":
+        if weight_norm:
+            raise ValueError("weight normalisation is defined here for the dot-product loss only")
+        target = v1 - np.einsum("nvf,nf->nv", S, pk)     # -grad = (v - S phi(k)) phi(k)^T at the given S
+    else:
+        raise ValueError(f"unknown binding loss {loss!r}")
+    M_new = beta * M + e[:, None, None] * target[:, :, None] * pk[:, None, :]
     S_new = S + M_new
     if weight_norm:
         target = np.sqrt(np.sum(S * S, axis=2))

@@ -160,3 +160,77 @@ def test_planted_mistakes_fail_a_delta_pin(monkeypatch, mistake):
             "...v,...f->...vf", np.einsum("...fv,...f->...v", S, pk) - v, pk))
     monkeypatch.setattr(oracle, "mse_loss_grad", O.mse_loss_grad)
     assert not _delta_pins_pass()
+
+
+# ---- the recurrent step (decode) of the delta rule ----
+
+def test_delta_step_hand_example():
+    g = _load("hand_delta_step.json")
+    q, k, v = (np.array(g[n], float)[None, None] for n in "qkv")
+    S = np.array(g["S"], float)[None, None]
+    M = np.array(g["M"], float)[None, None]
+    o, S1, M1 = oracle.step(q, k, v, S, M, eta_scalar=g["eta"], beta=g["beta"], loss="mse")
+    np.testing.assert_allclose(o[0, 0], g["o"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(S1[0, 0], g["S_new"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(M1[0, 0], g["M_new"], rtol=0, atol=1e-15)
+    od, Sd, _ = oracle.step(q, k, v, S, M, eta_scalar=g["eta"], beta=g["beta"])
+    np.testing.assert_allclose(od[0, 0], g["o_dot"], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(Sd[0, 0], g["S_new_dot"], rtol=0, atol=1e-15)
+
+
+def test_delta_step_from_zero_state_is_the_dot_step():
+    # at S = 0 the residual is v itself, so both losses take the same step
+    rng = np.random.default_rng(21)
+    q, k = rng.standard_normal((2, 2, 3, 8))
+    v = rng.standard_normal((2, 3, 6))
+    M = rng.standard_normal((2, 3, 6, 8))
+    S = np.zeros((2, 3, 6, 8))
+    a = oracle.step(q, k, v, S, M, eta_scalar=0.3, beta=0.7, loss="mse")
+    b = oracle.step(q, k, v, S, M, eta_scalar=0.3, beta=0.7)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_delta_step_leaves_an_exact_binding_alone():
+    # S k = v: the gradient vanishes and only the momentum moves S
+    rng = np.random.default_rng(22)
+    S = rng.standard_normal((1, 2, 5, 4))
+    k = rng.standard_normal((1, 2, 4))
+    v = np.einsum("bhvf,bhf->bhv", S, k)
+    q = rng.standard_normal((1, 2, 4))
+    M = rng.standard_normal((1, 2, 5, 4))
+    o, S1, M1 = oracle.step(q, k, v, S, M, eta_scalar=0.9, beta=0.6, loss="mse")
+    np.testing.assert_allclose(M1, 0.6 * M, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(S1, S + 0.6 * M, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(o, np.einsum("bhvf,bhf->bhv", S + 0.6 * M, q), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("beta,eta_mode", [(0.0, "scalar"), (0.9, "softplus"), (0.5, "per_token")])
+def test_delta_steps_match_the_forward_from_an_entry_state(beta, eta_mode):
+    # T steps from (S0, M0) against the token loop of forward(loss="mse")
+    rng = np.random.default_rng(23)
+    B, H, T, d = 2, 2, 7, 5
+    q, k, v = rng.standard_normal((3, B, H, T, d)) / np.sqrt(d)
+    a = rng.standard_normal((B, H, T)) - 1.0
+    eta = None if eta_mode == "scalar" else (np.abs(a) if eta_mode == "per_token" else a)
+    S0 = rng.standard_normal((B, H, d, d))
+    M0 = rng.standard_normal((B, H, d, d)) if beta else np.zeros((B, H, d, d))
+    o_ref, S_ref, M_ref = oracle.forward(q, k, v, eta_mode=eta_mode, eta=eta, eta_scalar=0.4, beta=beta,
+                                         S0=S0, M0=M0, loss="mse", return_state=True)
+    S, M = S0, M0
+    for t in range(T):
+        e_t = None if eta is None else eta[:, :, t]
+        o, S, M = oracle.step(q[:, :, t], k[:, :, t], v[:, :, t], S, M, eta_mode=eta_mode, eta=e_t,
+                              eta_scalar=0.4, beta=beta, loss="mse")
+        np.testing.assert_allclose(o, o_ref[:, :, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(M, M_ref, rtol=1e-12, atol=1e-12)
+
+
+def test_delta_step_rejects_weight_norm_and_unknown_losses():
+    z = np.zeros((1, 1, 2))
+    Z = np.zeros((1, 1, 2, 2))
+    with pytest.raises(ValueError):
+        oracle.step(z, z, z, Z, Z, loss="mse", weight_norm=True)
+    with pytest.raises(ValueError):
+        oracle.step(z, z, z, Z, Z, loss="l1")
