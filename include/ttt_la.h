@@ -79,11 +79,18 @@ enum {
                                         the delta rule S_t = S_{t-1} - eta_t (S_{t-1} k_t - v_t) k_t^T
                                         (mlsanity.com page: Modular TTT abstract, MSE and inner-product
                                         losses; "Builds on": the delta-rule parallelisation paper).
-                                        ttt_la_forward only; bf16, identity map, d_k = d_v in {64, 128},
-                                        causal, beta = 0; anything else TTT_LA_ERR_UNSUPPORTED.  On a
-                                        handle the per-chunk inverses (I + N)^-1 diag(eta), 3 KiB per 32
-                                        tokens of each sequence, go to the handle's workspace (sized for
-                                        them at creation) */
+                                        ttt_la_forward and ttt_la_forward_state: bf16, identity map,
+                                        d_k = d_v in {64, 128}, causal, beta = 0; anything else
+                                        TTT_LA_ERR_UNSUPPORTED.  The carried state is S alone: S0 and
+                                        S_T as for the other losses, M0 and M_T must be NULL
+                                        (TTT_LA_ERR_INVALID_ARG).  On a handle the per-chunk inverses
+                                        (I + N)^-1 diag(eta), 3 KiB per 32 tokens of each sequence, go
+                                        to the handle's workspace (sized for them at creation).
+                                        ttt_la_step: M <- beta M + eta (v - S phi(k)) phi(k)^T,
+                                        S <- S + M, o = S phi(q) (momentum allowed), for every dtype and
+                                        feature map with d_phi <= 128 (identity) or <= 512 (SwiGLU),
+                                        else TTT_LA_ERR_UNSUPPORTED; with TTT_LA_WEIGHT_NORM
+                                        TTT_LA_ERR_INVALID_ARG */
     TTT_LA_WEIGHT_NORM = 1u << 4     /* Variant 1 of Table 2 (thelatestinai.com page): the updated layer
                                         is weight-normalised, recurrent implementation only.  The pages
                                         do not define the normalisation; here, after each token's update,
@@ -221,10 +228,14 @@ int ttt_la_forward_noalloc(const ttt_la_desc* desc, const ttt_la_hints* hints, c
  *            state is then updated in place); apart from that the outputs must
  *            not overlap each other or any input, and S0, M0 must not overlap
  *            q, k, v, eta or o.
+ * With TTT_LA_LOSS_MSE (the delta rule, no momentum) only S0 and S_T are
+ * taken; M0 and M_T must be NULL.
  * Errors: as ttt_la_forward, and TTT_LA_ERR_INVALID_ARG for the bidirectional
- * mode bit or a misaligned or overlapping state pointer.
+ * mode bit, a misaligned or overlapping state pointer, or M0 / M_T with
+ * TTT_LA_LOSS_MSE.
  * TTT_LA_ERR_UNSUPPORTED for a handle created with TTT_LA_LAUNCH_PREFIX on the
- * 32x32-tile plan (that plan has no workspace for the entry state). */
+ * 32x32-tile plan (that plan has no workspace for the entry state; the delta
+ * rule is not affected). */
 int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta,
                          float eta_scalar, float beta, uint32_t mode, const float* S0, const float* M0,
                          void* o, float* S_T, float* M_T, void* hip_stream);
@@ -238,8 +249,9 @@ int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v
  *   S, M     device fp32 [B, H, d_v, d_phi] as in ttt_la_forward_state,
  *            updated in place; they must not overlap each other or any other
  *            argument.
- *   mode     rate bits, and TTT_LA_WEIGHT_NORM (Variant 1's step: see the mode
- *            bits); TTT_LA_BIDIRECTIONAL is invalid here.
+ *   mode     rate bits, and TTT_LA_WEIGHT_NORM (Variant 1's step) or
+ *            TTT_LA_LOSS_MSE (the delta-rule step, value factor v - S phi(k) at
+ *            the given S): see the mode bits; TTT_LA_BIDIRECTIONAL is invalid here.
  * The handle's T is ignored; its B, H, widths, dtype and feature map (W1, W3)
  * apply.  Allocates nothing, does not synchronise; errors as ttt_la_forward. */
 int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const float* eta, float eta_scalar,

@@ -362,9 +362,22 @@ def test_mse_loss_mode():
     assert check(d=desc(dtype="f32", d_k=64, d_v=64), mode=mse) == tla.TTT_LA_ERR_UNSUPPORTED
     assert check(d=desc(d_k=64, d_v=128), mode=mse) == tla.TTT_LA_ERR_UNSUPPORTED
     assert check(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=W3), mode=mse) == tla.TTT_LA_ERR_UNSUPPORTED
-    # no carried-state forward, step or backward for the delta rule
-    assert check_fs(mode=mse, beta=0.0) == tla.TTT_LA_ERR_UNSUPPORTED
-    assert check_step(mode=mse, beta=0.0) == tla.TTT_LA_ERR_UNSUPPORTED
+    # carried state: S alone (the delta rule runs without momentum)
+    assert check_fs(mode=mse, beta=0.0, m0=None, mt=None) == tla.TTT_LA_OK
+    assert check_fs(mode=mse, beta=0.0, m0=None, mt=None, st=S0) == tla.TTT_LA_OK      # in place
+    assert check_fs(mode=mse, beta=0.0, s0=None, m0=None, mt=None) == tla.TTT_LA_OK    # zero entry state
+    assert check_fs(mode=mse, beta=0.0) == tla.TTT_LA_ERR_INVALID_ARG                  # M0 and M_T given
+    assert check_fs(mode=mse, beta=0.0, m0=None) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check_fs(mode=mse, beta=0.0, mt=None) == tla.TTT_LA_ERR_INVALID_ARG
+    assert check_fs(mode=mse, beta=0.5, m0=None, mt=None) == tla.TTT_LA_ERR_UNSUPPORTED
+    assert check_fs(d=desc(dtype="f32", d_k=64, d_v=64), mode=mse, beta=0.0, m0=None, mt=None) == \
+        tla.TTT_LA_ERR_UNSUPPORTED
+    # the step: momentum allowed, every dtype and feature map while a row of S fits the registers
+    assert check_step(mode=mse, beta=0.9) == tla.TTT_LA_OK
+    assert check_step(d=desc(dtype="f32", d_k=64, d_v=64), mode=mse, beta=0.0) == tla.TTT_LA_OK
+    assert check_step(d=desc(phi="swiglu", d_phi=512, w1=W1, w3=W3), mode=mse | tla.TTT_LA_ETA_SOFTPLUS,
+                      eta=ETA, beta=0.9) == tla.TTT_LA_OK
+    assert check_step(mode=mse | tla.TTT_LA_WEIGHT_NORM) == tla.TTT_LA_ERR_INVALID_ARG
     assert tla.mode_bits("softplus", True, "mse") == tla.TTT_LA_ETA_SOFTPLUS | mse
 
 

@@ -445,12 +445,13 @@ class TTTLinearAttention:
         return out
 
     def forward_state(self, q, k, v, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", S0=None, M0=None,
-                      out=None, S_T=None, M_T=None, stream=None, weight_norm=False):
+                      out=None, S_T=None, M_T=None, stream=None, weight_norm=False, loss="dot"):
         """Causal forward from the carried state (S0, M0) (None = zero); writes the state
         after the last token to S_T, M_T when given (fp32 [B, H, d_v, d_phi]).
-        weight_norm: the weight-normalised recurrence (TTT_LA_WEIGHT_NORM; S0 required)."""
+        weight_norm: the weight-normalised recurrence (TTT_LA_WEIGHT_NORM; S0 required).
+        loss "mse": the delta rule (TTT_LA_LOSS_MSE), whose state is S alone (M0, M_T None)."""
         import torch
-        mode = mode_bits(eta_mode, True, weight_norm=weight_norm)
+        mode = mode_bits(eta_mode, True, loss, weight_norm=weight_norm)
         check_tensors(self.desc, "forward_state", mode, q=q, k=k, v=v, eta=eta, out=out, S0=S0, M0=M0, S_T=S_T,
                       M_T=M_T)
         s, ext = _launch_stream(q, stream)
@@ -466,11 +467,11 @@ class TTTLinearAttention:
         return out
 
     def step(self, q, k, v, S, M, eta=None, eta_scalar=1.0, beta=0.0, eta_mode="scalar", out=None, stream=None,
-             weight_norm=False):
+             weight_norm=False, loss="dot"):
         """One recurrent step: q, k, v [B, H, 1, d]; S, M fp32 [B, H, d_v, d_phi] updated in place.
-        weight_norm: Variant 1's step (TTT_LA_WEIGHT_NORM)."""
+        weight_norm: Variant 1's step (TTT_LA_WEIGHT_NORM); loss "mse": the delta-rule step."""
         import torch
-        mode = mode_bits(eta_mode, True, weight_norm=weight_norm)
+        mode = mode_bits(eta_mode, True, loss, weight_norm=weight_norm)
         if S is None or M is None:
             raise ValueError("the step needs the state S and M")
         check_tensors(self.desc, "step", mode, q=q, k=k, v=v, eta=eta, out=out, S=S, M=M)

@@ -160,7 +160,8 @@ int check_forward_state(const ttt_la_desc* d, const void* q, const void* k, cons
     int st = check_forward(d, q, k, v, eta, eta_scalar, beta, mode, o, true);
     if (st != TTT_LA_OK) return st;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
-    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // the delta rule has no carried state here
+    // the delta rule carries S alone (it runs without momentum)
+    if ((mode & TTT_LA_LOSS_MSE) && (M0 || M_T)) return TTT_LA_ERR_INVALID_ARG;
     if ((mode & TTT_LA_WEIGHT_NORM) && !S0) return TTT_LA_ERR_INVALID_ARG;   // the target row norms
     if (!state_ok(S0) || !state_ok(M0) || !state_ok(S_T) || !state_ok(M_T)) return TTT_LA_ERR_INVALID_ARG;
     const size_t eb = elem_bytes(d->dtype);
@@ -192,7 +193,9 @@ int check_step(const ttt_la_desc* d, const void* q, const void* k, const void* v
     if (!aligned(S, 16) || !aligned(M, 16)) return TTT_LA_ERR_INVALID_ARG;
     if (mode & ~kModeMask) return TTT_LA_ERR_INVALID_ARG;
     if (mode & TTT_LA_BIDIRECTIONAL) return TTT_LA_ERR_INVALID_ARG;
-    if (mode & TTT_LA_LOSS_MSE) return TTT_LA_ERR_UNSUPPORTED;   // no delta-rule step
+    if ((mode & TTT_LA_LOSS_MSE) && (mode & TTT_LA_WEIGHT_NORM)) return TTT_LA_ERR_INVALID_ARG;
+    // the delta-rule step holds a whole row of S in registers
+    if ((mode & TTT_LA_LOSS_MSE) && !ttt::step_row_in_registers(shape_of(*d))) return TTT_LA_ERR_UNSUPPORTED;
     if ((mode & TTT_LA_WEIGHT_NORM) && !ttt::wn_supported(shape_of(*d))) return TTT_LA_ERR_UNSUPPORTED;
     const bool per_tok = (mode & TTT_LA_ETA_PER_TOKEN) != 0;
     const bool softp = (mode & TTT_LA_ETA_SOFTPLUS) != 0;
@@ -1014,7 +1017,8 @@ int ttt_la_forward_state(ttt_la_t h, const void* q, const void* k, const void* v
     int st = check_forward_state(&h->desc, q, k, v, eta, eta_scalar, beta, mode, S0, M0, o, S_T, M_T);
     if (st != TTT_LA_OK) return st;
     // the prefix plan of the 32x32-tile kernels has no workspace for the entry state
-    if (h->fast && h->fp.wide && h->fp.prefix) return TTT_LA_ERR_UNSUPPORTED;
+    // (the delta rule has kernels of its own, outside the plan)
+    if (!(mode & TTT_LA_LOSS_MSE) && h->fast && h->fp.wide && h->fp.prefix) return TTT_LA_ERR_UNSUPPORTED;
     return enqueue_forward(h, q, k, v, eta, eta_scalar, beta, mode, S0, M0, o, S_T, M_T, hip_stream);
 }
 
@@ -1036,6 +1040,7 @@ int ttt_la_step(ttt_la_t h, const void* q, const void* k, const void* v, const f
     a.o = o;
     a.stream = static_cast<hipStream_t>(hip_stream);
     a.weight_norm = (mode & TTT_LA_WEIGHT_NORM) != 0;
+    a.mse = (mode & TTT_LA_LOSS_MSE) != 0;
     hipEvent_t eb, ee;
     next_events(h, &eb, &ee);
     const hipError_t e = ttt::launch_step(h->shape, a, eb, ee);

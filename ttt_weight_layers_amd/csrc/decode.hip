@@ -6,7 +6,11 @@
 // the token-by-token form that Table 2 of the thelatestinai.com page lists as
 // the recurrent implementation of each variant (per-token lr and momentum in
 // SGD; the SwiGLU feature map of Variant 2), one gradient step per entry on a
-// fixed-size matrix (wpnews.pro commentary).
+// fixed-size matrix (wpnews.pro commentary).  With the mean-squared binding
+// loss (the MSE inner-loop loss of the Modular TTT abstract, mlsanity.com page)
+// the value factor of the step is the residual at the given state:
+//
+//   M <- beta M + eta (v - S phi(k)) phi(k)^T,   S <- S + M,   o = S phi(q).
 //
 // The step reads and writes the whole fp32 state once and does under half a
 // flop per byte of it: it is bound by HBM bandwidth.  One workgroup of four waves owns 16
@@ -20,6 +24,8 @@
 // features are formed.
 
 #include <hip/hip_ext.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "internal.h"
@@ -66,8 +72,13 @@ __device__ __forceinline__ void load16_as_f32(const float* p, float* out) {
     for (int i = 0; i < 4; ++i) out[i] = u[i];
 }
 
-template <typename TI, bool SWIGLU, int SR, bool WN>
+// what a step does with each row: the plain step, the weight-normalised one
+// (Variant 1), the mean-squared loss (the last two hold the whole row in registers)
+enum RowRule { ROW_PLAIN = 0, ROW_WN = 1, ROW_MSE = 2 };
+
+template <typename TI, bool SWIGLU, int SR, int RULE>
 __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
+    constexpr bool WN = RULE == ROW_WN;
     extern __shared__ float smem[];
     const int d_k = p.d_k, d_phi = p.d_phi;
     float* sPq = smem;                 // phi(q) [d_phi]
@@ -263,6 +274,31 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
         }
 #pragma unroll
         for (int rr = 0; rr < RW; ++rr) acc[rr] *= fac[rr];   // reduced below like the plain step
+    } else if constexpr (RULE == ROW_MSE) {
+        // the residual v - S phi(k) of each row at the given S (the whole row is in
+        // registers: d_phi <= 128 NPRE), reduced across the wave, is the value
+        // factor of the plain step that follows
+        float pr[RW];
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) pr[rr] = 0.0f;
+#pragma unroll
+        for (int it = 0; it < NPRE; ++it) {
+            const int c = c0 + 128 * it;
+            if (c < d_phi) {
+                const float pk0 = sPk[c], pk1 = sPk[c + 1];
+#pragma unroll
+                for (int rr = 0; rr < RW; ++rr) pr[rr] = fmaf(s0[it][rr][0], pk0, fmaf(s0[it][rr][1], pk1, pr[rr]));
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < RW; ++rr) {
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) pr[rr] += __shfl_xor(pr[rr], off, 64);
+            ev[rr] = fmaf(-et, pr[rr], ev[rr]);    // eta (v - S phi(k))
+        }
+#pragma unroll
+        for (int it = 0; it < NPRE; ++it)
+            if (c0 + 128 * it < d_phi) row_step(c0 + 128 * it, m0[it], s0[it]);
     } else {
 #pragma unroll
     for (int it = 0; it < NPRE; ++it)
@@ -287,6 +323,8 @@ __global__ void __launch_bounds__(STHREADS) step_kernel(StepParams p) {
 }
 
 }  // namespace
+
+bool step_row_in_registers(const Shape& s) { return s.d_phi <= (s.swiglu ? 512 : 128); }
 
 size_t step_smem_bytes(const Shape& s) {
     return (size_t)(2 * s.d_phi + (s.swiglu ? 2 * s.d_k : 0)) * sizeof(float);
@@ -315,28 +353,26 @@ hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, h
     const size_t smem = step_smem_bytes(s);
     const dim3 grid((unsigned)(s.n_seq() * p.n_rblk)), block(STHREADS);
     void* args[] = {&p};
-    const void* fn;
-    if (a.weight_norm) {
-        // the whole row must fit the registers of the first slices
-        if (s.d_phi > (s.swiglu ? 512 : 128)) return hipErrorInvalidValue;
-        if (s.swiglu && sr == SR_SWIGLU)
-            fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU, true>
-                        : (const void*)step_kernel<float, true, SR_SWIGLU, true>;
+    if ((a.weight_norm || a.mse) && !step_row_in_registers(s)) return hipErrorInvalidValue;
+    if (a.weight_norm && a.mse) return hipErrorInvalidValue;
+    const int rule = a.weight_norm ? ROW_WN : (a.mse ? ROW_MSE : ROW_PLAIN);
+    const bool wide_rows = s.swiglu && sr == SR_SWIGLU;
+    const void* fn = nullptr;
+    auto pick = [&](auto tag) {
+        constexpr int R = decltype(tag)::value;
+        if (wide_rows)
+            fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU, R>
+                        : (const void*)step_kernel<float, true, SR_SWIGLU, R>;
         else if (s.swiglu)
-            fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN, true>
-                        : (const void*)step_kernel<float, true, SR_PLAIN, true>;
+            fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN, R>
+                        : (const void*)step_kernel<float, true, SR_PLAIN, R>;
         else
-            fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN, true>
-                        : (const void*)step_kernel<float, false, SR_PLAIN, true>;
-    } else if (s.swiglu && sr == SR_SWIGLU)
-        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_SWIGLU, false>
-                    : (const void*)step_kernel<float, true, SR_SWIGLU, false>;
-    else if (s.swiglu)
-        fn = s.bf16 ? (const void*)step_kernel<uint16_t, true, SR_PLAIN, false>
-                    : (const void*)step_kernel<float, true, SR_PLAIN, false>;
-    else
-        fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN, false>
-                    : (const void*)step_kernel<float, false, SR_PLAIN, false>;
+            fn = s.bf16 ? (const void*)step_kernel<uint16_t, false, SR_PLAIN, R>
+                        : (const void*)step_kernel<float, false, SR_PLAIN, R>;
+    };
+    if (rule == ROW_WN) pick(std::integral_constant<int, ROW_WN>{});
+    else if (rule == ROW_MSE) pick(std::integral_constant<int, ROW_MSE>{});
+    else pick(std::integral_constant<int, ROW_PLAIN>{});
     return hipExtLaunchKernel(fn, grid, block, args, smem, a.stream, ev_begin, ev_end, 0);
 }
 

@@ -397,6 +397,8 @@ struct DeltaWalkParams {
     const uint16_t* v;
     const float* a;            // the first pass's blocks
     uint16_t* o;
+    const float* S0;           // entry state, fp32 [seq][d_v][d_k] (null: zero)
+    float* S_T;                // state after the last token (null: not written)
     int T;
     int n_chunks;
     int n_vsplit;
@@ -438,10 +440,17 @@ __global__ void __launch_bounds__(DTH, 1) delta_walk(DeltaWalkParams p) {
     const int vr0 = 16 * wv;
     const float* Ablk = p.a + (size_t)seq * p.n_chunks * ACH + 4 * lane;
 
+    // the lane's entries of S: row vc0 + vr0 + 4g + r, column 16 bt + c16 (the entry
+    // state, or zero), and this wave's columns of the bf16 copy of S^T
+    const size_t srow = ((size_t)seq * DK + vc0 + vr0 + 4 * g) * DK + c16;
     f32x4 St[NT];
 #pragma unroll
-    for (int b = 0; b < NT; ++b) St[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int e = tid; e < DVW * DK / 8; e += DTH) *reinterpret_cast<u32x4*>(sST + 8 * e) = u32x4{0u, 0u, 0u, 0u};
+    for (int bt = 0; bt < NT; ++bt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) St[bt][r] = p.S0 ? p.S0[srow + (size_t)r * DK + 16 * bt] : 0.0f;
+        *reinterpret_cast<u32x2*>(sST + swz<DVW>(16 * bt + c16, vr0 + 4 * g)) =
+            u32x2{pack_bf16x2(St[bt][0], St[bt][1]), pack_bf16x2(St[bt][2], St[bt][3])};
+    }
 
     u32x4 rq[QL], rk[QL], rv;
     f32x4 an[3];
@@ -557,6 +566,12 @@ __global__ void __launch_bounds__(DTH, 1) delta_walk(DeltaWalkParams p) {
         }
         lds_barrier();
     }
+    if (p.S_T) {
+#pragma unroll
+        for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.S_T[srow + (size_t)r * DK + 16 * bt] = St[bt][r];
+    }
 }
 
 }  // namespace
@@ -572,11 +587,14 @@ size_t delta_workspace_bytes(const Shape& s) {
 
 hipError_t launch_delta(const Shape& s, const FwdArgs& a, void* workspace, size_t workspace_bytes,
                         hipEvent_t ev_begin, hipEvent_t ev_end) {
-    if (!delta_supported(s) || a.bidirectional || a.beta != 0.0f || a.S0 || a.M0 || a.S_T || a.M_T || a.reverse)
+    // the carried state is S alone (no momentum); only the two-pass form takes it
+    if (!delta_supported(s) || a.bidirectional || a.beta != 0.0f || a.M0 || a.M_T || a.reverse)
         return hipErrorInvalidValue;
     const size_t need = delta_workspace_bytes(s);
     const dim3 block(DTH);
-    if (workspace && need > 0 && need <= workspace_bytes) {
+    const bool two_pass = workspace && need > 0 && need <= workspace_bytes;
+    if (!two_pass && (a.S0 || a.S_T)) return hipErrorInvalidValue;
+    if (two_pass) {
         // two passes: the chunk inverses, then the walk (which carries the timing events)
         const int n_chunks = (s.T + DC - 1) / DC;
         DeltaPrepParams pp;
@@ -599,6 +617,8 @@ hipError_t launch_delta(const Shape& s, const FwdArgs& a, void* workspace, size_
         wp.v = static_cast<const uint16_t*>(a.v);
         wp.a = static_cast<const float*>(workspace);
         wp.o = static_cast<uint16_t*>(a.o);
+        wp.S0 = a.S0;
+        wp.S_T = a.S_T;
         wp.T = s.T;
         wp.n_chunks = n_chunks;
         wp.n_vsplit = s.d_v / DVW;

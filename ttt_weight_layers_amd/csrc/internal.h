@@ -153,8 +153,11 @@ struct StepArgs {
     void* o;             // [B, H, d_v]
     hipStream_t stream;
     bool weight_norm = false;   // rows of the new S rescaled to the norms of the given S
+    bool mse = false;           // mean-squared loss: value factor v - S phi(k) at the given S
 };
 size_t step_smem_bytes(const Shape& s);
+// the weight-normalised and the mean-squared step keep a whole row of S in registers
+bool step_row_in_registers(const Shape& s);
 // ev_begin/ev_end (may be null) take the step kernel's start and end timestamps
 hipError_t launch_step(const Shape& s, const StepArgs& a, hipEvent_t ev_begin, hipEvent_t ev_end);
 
