@@ -215,3 +215,31 @@ def test_delta_state_rejects_momentum_buffers():
         lay.forward_state(dd["q"], dd["k"], dd["v"], eta_scalar=0.5, beta=0.5, S0=Z, loss="mse")
     assert e.value.status == tla.TTT_LA_ERR_UNSUPPORTED
     torch.cuda.synchronize()
+
+
+def test_delta_forward_state_full_shape():
+    # the 8 x 16 x 4096 workload from a drawn entry state, eight heads (the first
+    # and the last among them) against the oracle at full T, outputs and final state
+    import torch
+    from ttt_workloads import head_subset
+    w = DELTA
+    heads = head_subset(w, 8)
+    say(f"[delta state full] heads {heads}")
+    x = make_inputs(w)
+    dd = to_device(x)
+    lay = make_layer(w, dd)
+    S0 = entry_state(w.B, w.H, 128, 128, 3, 1.0 / np.sqrt(128))
+    S_T = torch.full_like(dev32(S0), float("nan"))
+    got = gpu_forward_state(lay, w, dd, dev32(S0), S_T)
+    got_S = S_T.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got_S))
+    for n in heads:
+        b, h = divmod(n, w.H)
+        sub = lambda t: None if t is None else t[b:b + 1, h:h + 1]
+        ref_o, ref_S, _ = oracle.forward(sub(x.q64), sub(x.k64), sub(x.v64), eta_mode=w.eta_mode, eta=sub(x.a32),
+                                         beta=0.0, S0=S0[b:b + 1, h:h + 1].astype(np.float64), loss="mse",
+                                         return_state=True)
+        e_o = oracle.rel_err(got[b:b + 1, h:h + 1], ref_o)
+        e_s = oracle.rel_err(got_S[b:b + 1, h:h + 1], ref_S)
+        say(f"  head ({b},{h}): o {e_o:.2e}, S_T {e_s:.2e}")
+        assert e_o <= TOL[w.dtype] and e_s <= STATE_TOL[w.dtype]
