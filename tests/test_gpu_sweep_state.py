@@ -84,11 +84,11 @@ def _dev32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda")
 
 
-def _oracle(w, x, S0, M0):
+def _oracle(w, x, S0, M0, loss="dot"):
     return oracle.forward(x.q64, x.k64, x.v64, eta_mode=w.eta_mode, eta=x.a32, eta_scalar=w.eta_scalar,
                           beta=w.beta, phi=w.phi, w1=x.w1_64, w3=x.w3_64,
                           S0=None if S0 is None else S0.astype(np.float64),
-                          M0=None if M0 is None else M0.astype(np.float64), return_state=True)
+                          M0=None if M0 is None else M0.astype(np.float64), return_state=True, loss=loss)
 
 
 @pytest.mark.parametrize("c", FORWARD_CASES, ids=[_id(c) for c in FORWARD_CASES])
@@ -121,9 +121,22 @@ def test_forward_state_sweep(c):
 
 @pytest.mark.parametrize("c", STEP_CASES, ids=[_id(c) for c in STEP_CASES])
 def test_step_sweep(c):
+    _step_sweep(c, "dot")
+
+
+# the delta-rule step (mean-squared loss) over the same space of shapes, rates and momentum
+MSE_STEP_CASES = _step_cases(n=16, seed=20261206)
+
+
+@pytest.mark.parametrize("c", MSE_STEP_CASES, ids=[_id(c) for c in MSE_STEP_CASES])
+def test_step_sweep_mse(c):
+    _step_sweep(c, "mse")
+
+
+def _step_sweep(c, loss):
     import torch
     w = _workload(c)
-    print(f"[step sweep] {_id(c)}", flush=True)
+    print(f"[step sweep {loss}] {_id(c)}", flush=True)
     sys.stdout.flush()
     x = make_inputs(w)
     d = to_device(x)
@@ -135,10 +148,10 @@ def test_step_sweep(c):
         tok = lambda a: a[:, :, t:t + 1].contiguous()
         eta = None if d["a"] is None else d["a"][:, :, t].contiguous()
         outs.append(lay.step(tok(d["q"]), tok(d["k"]), tok(d["v"]), S, M, eta=eta, eta_scalar=w.eta_scalar,
-                             beta=w.beta, eta_mode=w.eta_mode))
+                             beta=w.beta, eta_mode=w.eta_mode, loss=loss))
     torch.cuda.synchronize()
     got = np.concatenate([from_device(o, w.dtype) for o in outs], axis=2)
-    ref_o, ref_S, ref_M = _oracle(w, x, S0, M0)
+    ref_o, ref_S, ref_M = _oracle(w, x, S0, M0, loss)
     assert oracle.rel_err(got, ref_o) <= TOL[w.dtype]
     # fp32 arithmetic on the exact inputs: the state is fp32-accurate
     assert oracle.rel_err(S.cpu().numpy(), ref_S) <= 1e-4
