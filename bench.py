@@ -299,7 +299,8 @@ def run_decode(args, w):
                torch.randn((w.B, w.H, w.d_v, w.d_phi), generator=g, device=dev) * 0.05) for _ in range(n_sets)]
     outs = [torch.empty((w.B, w.H, 1, w.d_v), dtype=v.dtype, device=dev) for _ in range(n_tok)]
     stream = torch.cuda.current_stream()
-    mode = tla.mode_bits(w.eta_mode, True)
+    # the workload's own step: the mean-squared loss and the weight normalisation included
+    mode = tla.mode_bits(w.eta_mode, True, w.loss, weight_norm=w.weight_norm)
 
     def step(i):
         qt, kt, vt, et = toks[i % n_tok]
@@ -336,7 +337,7 @@ def run_decode(args, w):
         "vs_baseline": None, "dtype": "f32 state, " + w.dtype + " tokens", "data": "synthetic",
         "config": {"workload": w.name + " (decode)", "B": w.B, "H": w.H, "d_k": w.d_k, "d_v": w.d_v,
                    "d_phi": w.d_phi, "phi": w.phi, "eta": w.eta_mode if w.eta_mode != "scalar" else w.eta_scalar,
-                   "beta": w.beta, "state_sets": n_sets},
+                   "beta": w.beta, "loss": w.loss, "weight_norm": w.weight_norm, "state_sets": n_sets},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "step_kernel",
                      "kernel_ms": round(kms, 5), "bytes_per_step": nbytes},
